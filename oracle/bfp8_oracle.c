@@ -1,0 +1,293 @@
+/*
+ * bfp8_oracle.c - plain, slow CPU oracle for the block-scaled FP8 linear path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path links, loads or
+ * calls this file; only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg do.  It shares no source, header, table or constant with
+ * the HIP library.
+ *
+ * What it computes, and where the pages state it:
+ *   - "Data flow - deepseek-ai/DeepSeek-V3" (codevetter), the FP8
+ *     quantization bullet: act_quant yields a float8_e4m3fn tensor plus fp32
+ *     scales, one per 128-element block; fp8_gemm multiplies the scaled
+ *     blocks and accumulates in fp32; each 1-byte Linear weight carries a
+ *     .scale tensor.
+ *   - pyshine "DeepSeek-V3" tour, "The Three Ideas That Make V3 Fast",
+ *     paragraph "FP8 with per-block scales": weights are e4m3 with a grid of
+ *     per-128-block scales; act_quant clamps each tile's max and divides it
+ *     by 448 (the e4m3 ceiling); weight_dequant expands weights for an
+ *     ordinary BF16 matmul; fp8_gemm accumulates FP8 products rescaled by
+ *     their block scales.
+ *   - "Behavior traces" (codevetter), the fp8->bf16 trace bullet: each
+ *     1-byte tensor is dequantized with its (renamed) scale_inv, i.e. the
+ *     stored scale is a multiplier.
+ * The e4m3 format itself is the OCP 8-bit floating point E4M3 encoding
+ * (torch.float8_e4m3fn): bias 7, no infinities, NaN only at S.1111.111,
+ * largest finite value 448.
+ *
+ * Readings where the pages are silent (each is listed with its reason in the
+ * design notes): the clamp is a lower floor ORACLE_AMAX_FLOOR on the block
+ * max; the quantizer divides in IEEE fp32 and then rounds to nearest-even
+ * with saturation at +-448; weight scales tile the weight in 128x128 blocks;
+ * the GEMM reference is accumulated in fp64.
+ *
+ * Parity status: every function here is pinned by the CPU tests against
+ * brute force, closed forms, torch's own e4m3/bf16 casts or exact rational
+ * arithmetic, except the value of ORACLE_AMAX_FLOOR (the pages give none),
+ * which is "parity unpinned".
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_BLOCK 128
+#define ORACLE_E4M3_MAX 448.0f
+#define ORACLE_AMAX_FLOOR 1e-4f
+
+/* ---------------------------------------------------------------- formats */
+
+static float bits_to_f32(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+static uint32_t f32_to_bits(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+
+/* bf16 is the upper half of a binary32, so widening is exact. */
+float oracle_bf16_to_f32(uint16_t h) { return bits_to_f32((uint32_t)h << 16); }
+
+/* binary32 -> bf16, round to nearest, ties to even (NaN stays a quiet NaN).
+ * Written as: keep the upper 16 bits, and add one unit in the last kept place
+ * when the dropped half is above one half, or exactly one half and the kept
+ * part is odd. */
+uint16_t oracle_f32_to_bf16(float f) {
+    uint32_t u = f32_to_bits(f);
+    if (isnan(f)) return (uint16_t)((u >> 16) | 0x0040u);
+    uint32_t kept = u >> 16;
+    uint32_t dropped = u & 0xFFFFu;
+    if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u))) kept += 1u;
+    return (uint16_t)kept;
+}
+
+/* e4m3 code -> value.  Layout s.eeee.mmm, bias 7:
+ *   E == 0          : subnormal  m * 2^-9
+ *   E in 1..15      : (1 + m/8) * 2^(E-7)
+ *   E == 15, m == 7 : NaN (no infinities) */
+float oracle_e4m3_decode(uint8_t c) {
+    int sign = c >> 7, E = (c >> 3) & 15, m = c & 7;
+    float mag;
+    if (E == 15 && m == 7) return sign ? -NAN : NAN;
+    if (E == 0) mag = ldexpf((float)m, -9);
+    else mag = ldexpf(1.0f + (float)m / 8.0f, E - 7);
+    return sign ? -mag : mag;
+}
+
+/* value -> e4m3 code, round to nearest with ties to even, saturating at the
+ * largest finite magnitude 448 (code 0x7E).  The sign is kept, so a negative
+ * value that rounds to zero gives 0x80. */
+uint8_t oracle_e4m3_encode(float v) {
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    if (isnan(v)) return sign | 0x7F;               /* outside the contract */
+    double a = fabs((double)v);
+    if (a >= 448.0) return sign | 0x7E;             /* saturate (also +-inf) */
+    if (a == 0.0) return sign;
+    /* binade of a, limited below by the smallest normal exponent -6 */
+    int e2;
+    frexp(a, &e2);                                  /* a = f * 2^e2, f in [0.5,1) */
+    int E = e2 - 1;                                 /* floor(log2 a) */
+    if (E < -6) E = -6;
+    double quantum = ldexp(1.0, E - 3);             /* spacing of 3-bit mantissas */
+    double r = a / quantum;                         /* exact: power-of-two scaling */
+    double n = floor(r);
+    double frac = r - n;
+    if (frac > 0.5 || (frac == 0.5 && fmod(n, 2.0) != 0.0)) n += 1.0;
+    double mag = n * quantum;                       /* nearest representable */
+    if (mag == 0.0) return sign;
+    if (mag < ldexp(1.0, -6))                       /* subnormal: m * 2^-9 */
+        return sign | (uint8_t)(mag / ldexp(1.0, -9));
+    int e3;
+    frexp(mag, &e3);
+    int Eb = e3 - 1;                                /* may have carried upward */
+    double mant = mag / ldexp(1.0, Eb);             /* in [1, 2) */
+    int m = (int)((mant - 1.0) * 8.0);
+    return sign | (uint8_t)(((Eb + 7) << 3) | m);
+}
+
+void oracle_e4m3_encode_array(const float* v, uint8_t* out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_encode(v[i]);
+}
+
+void oracle_e4m3_decode_array(const uint8_t* c, float* out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_decode(c[i]);
+}
+
+void oracle_f32_to_bf16_array(const float* v, uint16_t* out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_f32_to_bf16(v[i]);
+}
+
+float oracle_amax_floor(void) { return ORACLE_AMAX_FLOOR; }
+
+/* ------------------------------------------------------------- act_quant */
+
+/* For each row m and each 128-wide block kb of the last dimension:
+ *   amax = max |x| over the block (exact, on the bf16 values)
+ *   s    = max(amax, ORACLE_AMAX_FLOOR) / 448        (fp32 division)
+ *   q    = e4m3(x / s)                               (fp32 division, then RNE+sat)
+ * x is bf16 [M,K] row-major, q is [M,K], s is [M, K/128].
+ * Returns 0, or -1 when K is not a multiple of 128. */
+int oracle_act_quant(const uint16_t* x, uint8_t* q, float* s, int64_t M, int64_t K) {
+    if (K <= 0 || K % ORACLE_BLOCK != 0 || M < 0) return -1;
+    int64_t KB = K / ORACLE_BLOCK;
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t kb = 0; kb < KB; ++kb) {
+            const uint16_t* xb = x + m * K + kb * ORACLE_BLOCK;
+            uint8_t* qb = q + m * K + kb * ORACLE_BLOCK;
+            float amax = 0.0f;
+            for (int j = 0; j < ORACLE_BLOCK; ++j) {
+                float a = fabsf(oracle_bf16_to_f32(xb[j]));
+                if (a > amax) amax = a;
+            }
+            float clamped = amax < ORACLE_AMAX_FLOOR ? ORACLE_AMAX_FLOOR : amax;
+            float scale = clamped / ORACLE_E4M3_MAX;
+            for (int j = 0; j < ORACLE_BLOCK; ++j) {
+                float quotient = oracle_bf16_to_f32(xb[j]) / scale;
+                qb[j] = oracle_e4m3_encode(quotient);
+            }
+            s[m * KB + kb] = scale;
+        }
+    }
+    return 0;
+}
+
+/* -------------------------------------------------------- weight_dequant */
+
+/* out[n,k] = bf16( e4m3_value(w[n,k]) * S[n/128][k/128] ), the product
+ * rounded once to fp32 and then once to bf16.  w is [N,K], S is
+ * [ceil(N/128), ceil(K/128)], out is bf16 [N,K]. */
+void oracle_weight_dequant(const uint8_t* w, const float* S, uint16_t* out,
+                           int64_t N, int64_t K) {
+    int64_t KB = (K + ORACLE_BLOCK - 1) / ORACLE_BLOCK;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            float scale = S[(n / ORACLE_BLOCK) * KB + k / ORACLE_BLOCK];
+            float product = oracle_e4m3_decode(w[n * K + k]) * scale;
+            out[n * K + k] = oracle_f32_to_bf16(product);
+        }
+}
+
+/* ------------------------------------------------------------------ GEMM */
+
+/* ref[m,n] = sum over blocks kb of
+ *              ( sum_{k in kb} a[m,k] * b[n,k] ) * sa[m,kb] * sb[n/128,kb]
+ * in fp64.  a is e4m3 [M,K], sa is [M,K/128], b is e4m3 [N,K] (a Linear
+ * weight, out_features x in_features, so C = A * B^T), sb is
+ * [ceil(N/128), K/128].  The per-block sum of e4m3 products is exact in fp64
+ * (each product is an integer multiple of 2^-18 below 2^18 in size, and 128 of
+ * them stay below 2^53 units).  Only the listed rows are computed, into
+ * out[i*N + n] for rows[i]. */
+typedef struct {
+    const uint8_t *a, *b;
+    const float *sa, *sb;
+    int64_t N, K;
+    const int32_t* off;   /* grouped only: int32 [G+1] row offsets, else NULL */
+    int32_t G;
+    const int64_t* rows;
+    int64_t nrows;
+    double* out;
+    int tid, nthreads;
+    float table[256];
+} gemm_job;
+
+static void gemm_row(const gemm_job* J, const uint8_t* b, const float* sb,
+                     int64_t m, double* out_row) {
+    int64_t KB = J->K / ORACLE_BLOCK;
+    const uint8_t* arow = J->a + m * J->K;
+    for (int64_t n = 0; n < J->N; ++n) {
+        const uint8_t* brow = b + n * J->K;
+        double total = 0.0;
+        for (int64_t kb = 0; kb < KB; ++kb) {
+            double block_sum = 0.0;
+            for (int j = 0; j < ORACLE_BLOCK; ++j) {
+                int64_t k = kb * ORACLE_BLOCK + j;
+                block_sum += (double)J->table[arow[k]] * (double)J->table[brow[k]];
+            }
+            total += block_sum * (double)J->sa[m * KB + kb]
+                               * (double)sb[(n / ORACLE_BLOCK) * KB + kb];
+        }
+        out_row[n] = total;
+    }
+}
+
+static void* gemm_worker(void* arg) {
+    gemm_job* J = (gemm_job*)arg;
+    int64_t KB = J->K / ORACLE_BLOCK;
+    int64_t NB = (J->N + ORACLE_BLOCK - 1) / ORACLE_BLOCK;
+    for (int64_t i = J->tid; i < J->nrows; i += J->nthreads) {
+        int64_t m = J->rows[i];
+        double* out_row = J->out + i * J->N;
+        if (!J->off) { gemm_row(J, J->b, J->sb, m, out_row); continue; }
+        int32_t g = -1;
+        for (int32_t h = 0; h < J->G; ++h)
+            if (m >= J->off[h] && m < J->off[h + 1]) { g = h; break; }
+        if (g < 0) {
+            for (int64_t n = 0; n < J->N; ++n) out_row[n] = NAN;
+            continue;
+        }
+        gemm_row(J, J->b + (int64_t)g * J->N * J->K, J->sb + (int64_t)g * NB * KB,
+                 m, out_row);
+    }
+    return NULL;
+}
+
+static int run_gemm_rows(const uint8_t* a, const float* sa, const uint8_t* b,
+                         const float* sb, const int32_t* off, int32_t G,
+                         int64_t N, int64_t K, const int64_t* rows, int64_t nrows,
+                         double* out, int nthreads) {
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    gemm_job* jobs = (gemm_job*)calloc((size_t)nthreads, sizeof(gemm_job));
+    pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+    if (!jobs || !th) { free(jobs); free(th); return -2; }
+    for (int t = 0; t < nthreads; ++t) {
+        gemm_job* J = &jobs[t];
+        J->a = a; J->b = b; J->sa = sa; J->sb = sb; J->N = N; J->K = K;
+        J->off = off; J->G = G;
+        J->rows = rows; J->nrows = nrows; J->out = out;
+        J->tid = t; J->nthreads = nthreads;
+        for (int c = 0; c < 256; ++c) J->table[c] = oracle_e4m3_decode((uint8_t)c);
+    }
+    int started = 0;
+    for (int t = 1; t < nthreads; ++t) {
+        if (pthread_create(&th[t], NULL, gemm_worker, &jobs[t]) != 0) break;
+        started = t;
+    }
+    /* rows of threads that failed to start are done on this thread */
+    for (int t = started + 1; t < nthreads; ++t) gemm_worker(&jobs[t]);
+    gemm_worker(&jobs[0]);
+    for (int t = 1; t <= started; ++t) pthread_join(th[t], NULL);
+    free(jobs); free(th);
+    return 0;
+}
+
+int oracle_gemm_rows(const uint8_t* a, const float* sa, const uint8_t* b,
+                     const float* sb, int64_t M, int64_t N, int64_t K,
+                     const int64_t* rows, int64_t nrows, double* out, int nthreads) {
+    if (K <= 0 || K % ORACLE_BLOCK != 0 || M < 0 || N < 0) return -1;
+    for (int64_t i = 0; i < nrows; ++i)
+        if (rows[i] < 0 || rows[i] >= M) return -1;
+    return run_gemm_rows(a, sa, b, sb, NULL, 0, N, K, rows, nrows, out, nthreads);
+}
+
+/* Grouped GEMM: rows [off[g], off[g+1]) of a (and sa) are multiplied by
+ * expert g's weight b[g] with its scale grid sb[g].  For each requested row
+ * the owning group is found from the offsets; a row that lies in no group
+ * yields NaN in every column.  b is [G,N,K], sb is [G, ceil(N/128), K/128],
+ * off is int32 [G+1]. */
+int oracle_gemm_grouped_rows(const uint8_t* a, const float* sa, const uint8_t* b,
+                             const float* sb, const int32_t* off, int32_t G,
+                             int64_t total_M, int64_t N, int64_t K,
+                             const int64_t* rows, int64_t nrows, double* out,
+                             int nthreads) {
+    if (K <= 0 || K % ORACLE_BLOCK != 0 || G < 1 || N < 0 || total_M < 0) return -1;
+    for (int64_t i = 0; i < nrows; ++i)
+        if (rows[i] < 0 || rows[i] >= total_M) return -1;
+    return run_gemm_rows(a, sa, b, sb, off, G, N, K, rows, nrows, out, nthreads);
+}

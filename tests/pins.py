@@ -1,0 +1,524 @@
+"""Checks that pin the CPU oracle to facts outside itself.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` and raises AssertionError
+when the oracle disagrees with a fact that the pages, the e4m3 / bf16 format
+definitions or plain mathematics fix: hand-derived closed forms (the golden
+files), brute force, torch's own e4m3 and bf16 casts, exact rational
+arithmetic, and invariants of the method.  The same functions are run against
+deliberately broken builds of the oracle to show that each plausible mistake
+fails at least one pin.
+
+Sources: "Data flow - deepseek-ai/DeepSeek-V3" (codevetter), FP8 quantization
+bullet (128-element activation blocks, fp32 scales, fp32 accumulation, a
+.scale on each 1-byte weight); pyshine "DeepSeek-V3" tour, "FP8 with per-block
+scales" (block max clamped and divided by 448, the e4m3 ceiling; weight scale
+grid; dequantize-then-BF16-matmul is the other branch of linear());
+"Behavior traces" (codevetter), fp8->bf16 trace bullet (dequant multiplies by
+the stored scale).
+"""
+import os
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+BLOCK = 128
+
+
+# ------------------------------------------------------------ independent helpers
+
+def torch_e4m3_values() -> np.ndarray:
+    """All 256 e4m3 code values as float64, decoded by torch (a library, not the oracle)."""
+    return torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn) \
+        .to(torch.float64).numpy()
+
+
+def torch_e4m3_cast(v: np.ndarray) -> np.ndarray:
+    """torch's float32 -> float8_e4m3fn cast (nearest-even, NOT saturating)."""
+    return torch.from_numpy(np.ascontiguousarray(v, np.float32)).to(torch.float8_e4m3fn) \
+        .view(torch.uint8).numpy()
+
+
+def torch_bf16(v: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(v, np.float32)).to(torch.bfloat16) \
+        .view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def brute_encode(v: np.ndarray) -> np.ndarray:
+    """Nearest of the 127 finite e4m3 magnitudes, ties to the even code, sign kept.
+
+    Brute force over the code table that torch decodes; +-inf saturate.
+    """
+    v = np.asarray(v, np.float32).ravel()
+    mags = torch_e4m3_values()[:0x7F]             # codes 0x00..0x7E, increasing
+    even = (np.arange(0x7F) % 2) == 0
+    out = np.empty(v.size, np.uint8)
+    step = 1 << 15
+    for i in range(0, v.size, step):
+        a = np.abs(v[i:i + step].astype(np.float64))
+        # beyond 1000 the nearest magnitude is 448 for every a; clamping keeps the
+        # distances below exact in float64 (and maps +-inf in)
+        a = np.minimum(a, 1000.0)
+        d = np.abs(a[:, None] - mags[None, :])
+        dmin = d.min(axis=1, keepdims=True)
+        cand = d == dmin
+        two = cand.sum(axis=1) > 1
+        pick = np.where(two, np.argmax(cand & even[None, :], axis=1), np.argmax(cand, axis=1))
+        out[i:i + step] = pick.astype(np.uint8)
+    sign = np.signbit(v)
+    return np.where(sign, out | 0x80, out).astype(np.uint8)
+
+
+def read_golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                rows.append(line.split())
+    return rows
+
+
+def finite_f32_bit_sets(seed=7, n_random=1 << 18):
+    """float32 inputs for the codec pins: every bf16 pattern, midpoints +-ulps, random."""
+    allbf = (np.arange(1 << 16, dtype=np.uint32) << 16).view(np.float32)
+    allbf = allbf[np.isfinite(allbf)]
+    mags = torch_e4m3_values()[:0x7F]
+    mids = ((mags[1:] + mags[:-1]) / 2).astype(np.float32)      # exact in f32
+    near = [mids]
+    for k in (1, 2):
+        up = mids.copy(); dn = mids.copy()
+        for _ in range(k):
+            up = np.nextafter(up, np.float32(np.inf)); dn = np.nextafter(dn, np.float32(0))
+        near += [up, dn]
+    near = np.concatenate(near)
+    near = np.concatenate([near, -near, np.float32([464.0, 463.99997, 448.0, 447.99997, 480.0])])
+    rng = np.random.default_rng(seed)
+    sign = rng.integers(0, 2, n_random, dtype=np.uint32) << 31
+    expo = rng.integers(127 - 14, 127 + 11, n_random, dtype=np.uint32) << 23
+    mant = rng.integers(0, 1 << 23, n_random, dtype=np.uint32)
+    rnd = (sign | expo | mant).view(np.float32)
+    return np.concatenate([allbf, near, rnd]).astype(np.float32)
+
+
+# ---------------------------------------------------------------- codec pins
+
+def pin_decode_table(orc):
+    """Q1: all 256 codes decode as torch decodes them; 0x7E is the 448 ceiling."""
+    ours = orc.e4m3_decode(np.arange(256, dtype=np.uint8)).astype(np.float64)
+    ref = torch_e4m3_values()
+    nan_o, nan_r = np.isnan(ours), np.isnan(ref)
+    assert np.array_equal(nan_o, nan_r), "NaN codes differ"
+    assert set(np.flatnonzero(nan_o)) == {0x7F, 0xFF}
+    assert np.array_equal(ours[~nan_o], ref[~nan_r]), "decoded values differ from torch"
+    assert ours[0x7E] == 448.0 and ours[0xFE] == -448.0
+    assert np.nanmax(ours) == 448.0
+    assert ours[0x01] == 2.0 ** -9 and ours[0x08] == 2.0 ** -6
+
+
+def pin_encode_golden(orc):
+    """Hand-derived codes (tests/golden/e4m3_hand_examples.txt)."""
+    rows = read_golden("e4m3_hand_examples.txt")
+    vals = np.array([float(r[0]) for r in rows], np.float32)
+    want = np.array([int(r[1], 16) for r in rows], np.uint8)
+    got = orc.e4m3_encode(vals)
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, f"golden codes differ at {[(rows[i][0], hex(got[i])) for i in bad]}"
+
+
+def pin_encode_brute_force(orc):
+    """Q2: encode equals brute-force nearest-even over the 127 magnitudes."""
+    v = finite_f32_bit_sets()
+    got = orc.e4m3_encode(v)
+    want = brute_encode(v)
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, f"{bad.size} mismatches, first {v[bad[:5]]} -> {got[bad[:5]]} want {want[bad[:5]]}"
+
+
+def pin_encode_vs_torch(orc):
+    """Q3: encode equals torch's cast wherever that cast cannot overflow (|v| < 464)."""
+    v = finite_f32_bit_sets(seed=11)
+    v = v[np.abs(v) < 464.0]
+    assert np.array_equal(orc.e4m3_encode(v), torch_e4m3_cast(v))
+
+
+def pin_roundtrip(orc):
+    """Q4: encode(decode(c)) == c for every non-NaN code."""
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    assert np.array_equal(orc.e4m3_encode(orc.e4m3_decode(codes)), codes)
+
+
+def pin_bf16_round(orc):
+    """f32 -> bf16 nearest-even equals torch's cast (random patterns and exact ties)."""
+    rng = np.random.default_rng(3)
+    bits = rng.integers(0, 1 << 32, 1 << 18, dtype=np.uint64).astype(np.uint32)
+    ties = (rng.integers(0, 1 << 16, 4096, dtype=np.uint32) << 16) | np.uint32(0x8000)
+    v = np.concatenate([bits, ties]).view(np.float32)
+    v = v[np.isfinite(v)]
+    v = v[np.abs(v) < 3.0e38]                 # keep clear of rounding up to inf
+    assert np.array_equal(orc.f32_to_bf16(v), torch_bf16(v))
+
+
+# ------------------------------------------------------------ act_quant pins
+
+def _rand_bf16(M, K, seed, scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    x = (torch.randn(M, K, generator=g) * scale).to(torch.bfloat16)
+    return x.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def pin_act_quant_golden(orc):
+    """Hand-worked blocks (tests/golden/act_quant_hand_block.txt): scale 1 and scale 2."""
+    rows = read_golden("act_quant_hand_block.txt")
+    x = np.zeros(256, np.float32)
+    want_q = np.zeros(256, np.uint8)
+    want_s = {}
+    for r in rows:
+        if r[0] == "scale":
+            want_s[int(r[1])] = float(r[2])
+            continue
+        blk, pos = int(r[0]), int(r[1])
+        x[blk * BLOCK + pos] = float(r[2])
+        want_q[blk * BLOCK + pos] = int(r[3], 16)
+    xb = torch_bf16(x)
+    assert np.array_equal(bf16_bits_to_f32(xb), x), "golden inputs must be exact in bf16"
+    q, s = orc.act_quant(xb[None, :])
+    assert s[0, 0] == want_s[0] and s[0, 1] == want_s[1], f"scales {s}"
+    bad = np.flatnonzero(q[0] != want_q)
+    assert bad.size == 0, f"codes differ at {bad}: {q[0][bad]} want {want_q[bad]}"
+
+
+def pin_act_quant_ceiling_hit(orc):
+    """A1: every block whose max is above the floor holds a +-448 code (0x7E / 0xFE)."""
+    x = _rand_bf16(64, 1024, 21)
+    q, s = orc.act_quant(x)
+    blocks = (q & 0x7F).reshape(64, -1, BLOCK)
+    assert np.all((blocks == 0x7E).any(axis=2))
+
+
+def ulp_e4m3(v):
+    """Spacing of e4m3 values around |v| (2^-9 in the subnormal range)."""
+    a = np.abs(np.asarray(v, np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -40)))
+    return np.exp2(np.maximum(e, -6) - 3)
+
+
+def pin_act_quant_error_bound(orc):
+    """A2: |dec(q)*s - x| <= s * (ulp/2 at x/s + 2^-23 * |x|/s) for every element."""
+    x = _rand_bf16(32, 2048, 22)
+    x[5, 100:228] = torch_bf16(np.full(128, 1e-3, np.float32) * np.linspace(-1, 1, 128))
+    q, s = orc.act_quant(x)
+    xf = bf16_bits_to_f32(x).astype(np.float64)
+    sf = np.repeat(s.astype(np.float64), BLOCK, axis=1)
+    deq = torch_e4m3_values()[q] * sf
+    ratio = np.abs(xf) / sf
+    bound = sf * (0.5 * ulp_e4m3(ratio) + 2.0 ** -23 * ratio)
+    assert np.all(np.abs(deq - xf) <= bound * (1 + 1e-12))
+
+
+def pin_act_quant_scale_value(orc):
+    """Each scale is the fp32 quotient of the block max |x| and 448 (numpy float32)."""
+    x = _rand_bf16(16, 1024, 23, scale=3.0)
+    _, s = orc.act_quant(x)
+    amax = np.abs(bf16_bits_to_f32(x)).reshape(16, -1, BLOCK).max(axis=2)
+    assert np.array_equal(s, (amax.astype(np.float32) / np.float32(448.0)).astype(np.float32))
+
+
+def pin_act_quant_constant_block(orc):
+    """A3: a constant block c gives all codes +-448 and scale |c|/448."""
+    for c in (1.0, -3.5, 0.15625, 1000.0, -2.0 ** -6):
+        x = torch_bf16(np.full((1, 128), c, np.float32))
+        q, s = orc.act_quant(x)
+        assert np.all(q == (0xFE if c < 0 else 0x7E)), (c, q[0, :4])
+        assert s[0, 0] == np.float32(abs(c)) / np.float32(448.0)
+
+
+def pin_act_quant_power_of_two(orc):
+    """A4: x * 2^k gives the same codes and the scale times 2^k, exactly."""
+    x = _rand_bf16(8, 512, 24)
+    q0, s0 = orc.act_quant(x)
+    for k in (-5, 3, 7):
+        xk = torch_bf16(bf16_bits_to_f32(x) * np.float32(2.0 ** k))
+        qk, sk = orc.act_quant(xk)
+        assert np.array_equal(qk, q0)
+        assert np.array_equal(sk, (s0 * np.float32(2.0 ** k)).astype(np.float32))
+
+
+def pin_act_quant_negation(orc):
+    """A5: -x flips every code's sign bit and keeps the scales."""
+    x = _rand_bf16(8, 512, 25)
+    q0, s0 = orc.act_quant(x)
+    q1, s1 = orc.act_quant(x ^ np.uint16(0x8000))
+    assert np.array_equal(q1, q0 ^ np.uint8(0x80)) and np.array_equal(s1, s0)
+
+
+def pin_act_quant_row_gather(orc):
+    """A6: quantizing gathered rows equals gathering quantized rows."""
+    x = _rand_bf16(32, 384, 26)
+    idx = np.array([5, 0, 31, 5, 17, 2, 2, 9])
+    q, s = orc.act_quant(x)
+    qg, sg = orc.act_quant(x[idx])
+    assert np.array_equal(qg, q[idx]) and np.array_equal(sg, s[idx])
+
+
+def pin_act_quant_zero_block(orc):
+    """A7: an all-zero block gives zero codes and scale floor/448 (floor value unpinned)."""
+    x = np.zeros((2, 256), np.uint16)
+    x[1, 128:] = 0x8000                                     # -0.0
+    q, s = orc.act_quant(x)
+    assert np.all(q[:, :128] == 0) and np.all(q[0, 128:] == 0) and np.all(q[1, 128:] == 0x80)
+    floor = np.float32(orc.amax_floor())
+    assert floor > 0 and np.all(s == floor / np.float32(448.0))
+
+
+def pin_act_quant_directed_quotients(orc):
+    """The codes come from the IEEE fp32 quotient x/s, not from x * (1/s).
+
+    For several block maxima, every bf16 value of the block's range is tried;
+    where the two quotient forms round to different codes, those values are
+    packed into blocks (with the maximum in position 0) and the expected codes
+    come from numpy's float32 division plus torch's cast.
+    """
+    allx = bf16_bits_to_f32(np.arange(1 << 16, dtype=np.uint16))
+    allx = allx[np.isfinite(allx)]
+    found = 0
+    for amax in (np.float32(3.0), np.float32(0.7265625), np.float32(11.5), np.float32(97.0)):
+        s = np.float32(amax / np.float32(448.0))
+        xs = allx[np.abs(allx) <= amax]
+        q_div = (xs / s).astype(np.float32)
+        q_rcp = (xs * (np.float32(1.0) / s)).astype(np.float32)
+        diff = xs[torch_e4m3_cast(np.clip(q_div, -448, 448)) != torch_e4m3_cast(np.clip(q_rcp, -448, 448))]
+        if diff.size == 0:
+            continue
+        found += diff.size
+        n = -(-diff.size // 127)
+        blocks = np.zeros((n, 128), np.float32)
+        blocks[:, 0] = amax
+        flat = blocks[:, 1:].reshape(-1)
+        flat[:diff.size] = diff
+        blocks[:, 1:] = flat.reshape(n, 127)
+        xb = torch_bf16(blocks)
+        q, sc = orc.act_quant(xb)
+        assert np.all(sc == s)
+        want = torch_e4m3_cast(np.clip((blocks / s).astype(np.float32), -448, 448))
+        assert np.array_equal(q, want), "codes do not follow the fp32 quotient x/s"
+    assert found > 0, "no directed near-tie cases found"
+
+
+# ------------------------------------------------------- weight_dequant pins
+
+def _rand_codes(shape, seed, maxmag=0x7E):
+    rng = np.random.default_rng(seed)
+    c = rng.integers(0, maxmag + 1, size=shape, dtype=np.int32).astype(np.uint8)
+    sign = rng.integers(0, 2, size=shape).astype(np.uint8) << 7
+    return c | sign
+
+
+def _expand(S, N, K):
+    return np.repeat(np.repeat(S, BLOCK, axis=0), BLOCK, axis=1)[:N, :K]
+
+
+def pin_dequant_unit_and_pow2(orc):
+    """D1: with S = 1 the output is the code's value in bf16; S = 2^k scales exactly."""
+    w = _rand_codes((256, 384), 31)
+    vals = torch_e4m3_values()[w].astype(np.float32)
+    one = np.ones((2, 3), np.float32)
+    assert np.array_equal(orc.weight_dequant(w, one), torch_bf16(vals))
+    S = np.float32([[2.0 ** -3, 2.0 ** 5, 1.0], [0.5, 2.0 ** -10, 4.0]])
+    assert np.array_equal(orc.weight_dequant(w, S), torch_bf16(vals * _expand(S, 256, 384)))
+
+
+def pin_dequant_vs_torch(orc):
+    """D2: equals torch (code value * expanded scale in fp32, then bf16), ragged edges too."""
+    for (N, K, seed) in ((256, 256, 32), (300, 200, 33), (1, 129, 34), (129, 1, 35)):
+        w = _rand_codes((N, K), seed)
+        rng = np.random.default_rng(seed)
+        S = np.exp2(rng.uniform(-10, -2, size=(-(-N // BLOCK), -(-K // BLOCK)))).astype(np.float32)
+        vals = torch_e4m3_values()[w].astype(np.float32)
+        want = torch_bf16((vals * _expand(S, N, K)).astype(np.float32))
+        assert np.array_equal(orc.weight_dequant(w, S), want), (N, K)
+
+
+# ------------------------------------------------------------------ GEMM pins
+
+def _rand_scales(shape, seed, lo=-8, hi=-2):
+    rng = np.random.default_rng(seed)
+    return np.exp2(rng.uniform(lo, hi, size=shape)).astype(np.float32)
+
+
+def _terms_abs(a, sa, b, sb):
+    """sum_k |a_k * sa * b_k * sb| in fp64: the natural scale for rounding errors."""
+    av = np.abs(torch_e4m3_values()[a]) * np.repeat(sa, BLOCK, axis=1)
+    bv = np.abs(torch_e4m3_values()[b]) * np.repeat(np.repeat(sb, BLOCK, axis=0)[:b.shape[0]], BLOCK, axis=1)
+    return av @ bv.T
+
+
+def pin_gemm_fraction_exact(orc):
+    """G1: equals an exact rational computation on tiny shapes."""
+    vals = torch_e4m3_values()
+    cases = ((2, 3, 128, 41, None), (4, 4, 256, 42, None), (3, 130, 128, 43, (0, 1, 127, 128, 129)))
+    for (M, N, K, seed, cols) in cases:
+        a = _rand_codes((M, K), seed); b = _rand_codes((N, K), seed + 100)
+        sa = _rand_scales((M, K // BLOCK), seed + 200)
+        sb = _rand_scales((-(-N // BLOCK), K // BLOCK), seed + 300)
+        got = orc.gemm(a, sa, b, sb)
+        bound = _terms_abs(a, sa, b, sb)
+        for m in range(M):
+            for n in (cols if cols is not None else range(N)):
+                total = Fraction(0)
+                for kb in range(K // BLOCK):
+                    blk = sum(Fraction(float(vals[a[m, k]])) * Fraction(float(vals[b[n, k]]))
+                              for k in range(kb * BLOCK, (kb + 1) * BLOCK))
+                    total += blk * Fraction(float(sa[m, kb])) * Fraction(float(sb[n // BLOCK, kb]))
+                err = abs(Fraction(float(got[m, n])) - total)
+                assert err <= Fraction(1e-14) * Fraction(float(bound[m, n])), (M, N, K, m, n)
+
+
+def pin_gemm_vs_torch_f64(orc):
+    """G2: equals torch float64 (dec(a)*sa) @ (dec(b)*sb)^T, the scales factored into operands."""
+    vals = torch.from_numpy(torch_e4m3_values())
+    for (M, N, K, seed) in ((16, 256, 256, 51), (37, 300, 384, 52), (5, 1, 128, 53)):
+        a = _rand_codes((M, K), seed); b = _rand_codes((N, K), seed + 1)
+        sa = _rand_scales((M, K // BLOCK), seed + 2); sb = _rand_scales((-(-N // BLOCK), K // BLOCK), seed + 3)
+        A = vals[torch.from_numpy(a).long()] * torch.from_numpy(np.repeat(sa, BLOCK, 1)).double()
+        Bs = np.repeat(np.repeat(sb, BLOCK, 0)[:N], BLOCK, 1)
+        B = vals[torch.from_numpy(b).long()] * torch.from_numpy(Bs).double()
+        ref = (A @ B.T).numpy()
+        got = orc.gemm(a, sa, b, sb)
+        assert np.all(np.abs(got - ref) <= 1e-12 * _terms_abs(a, sa, b, sb) + 1e-300), (M, N, K)
+
+
+def pin_gemm_identity(orc):
+    """G3: W = identity (code 0x38 = 1.0, S = 1) reproduces dec(q_a) * s_a exactly."""
+    K = 256
+    a = _rand_codes((16, K), 61); sa = _rand_scales((16, 2), 62)
+    b = np.zeros((K, K), np.uint8); np.fill_diagonal(b, 0x38)
+    got = orc.gemm(a, sa, b, np.ones((2, 2), np.float32))
+    want = torch_e4m3_values()[a] * np.repeat(sa.astype(np.float64), BLOCK, axis=1)
+    assert np.array_equal(got, want)
+
+
+def pin_gemm_one_hot(orc):
+    """G4: row n of W is 1.0 at column pi(n); scales 2^k -> dec(q_a[m, pi(n)]) * s_a * 2^k."""
+    K, N = 384, 256
+    rng = np.random.default_rng(63)
+    perm = rng.permutation(K)[:N]
+    a = _rand_codes((8, K), 64); sa = _rand_scales((8, 3), 65)
+    b = np.zeros((N, K), np.uint8); b[np.arange(N), perm] = 0x38
+    ksb = rng.integers(-4, 5, size=(2, 3))
+    sb = np.exp2(ksb).astype(np.float32)
+    got = orc.gemm(a, sa, b, sb)
+    want = torch_e4m3_values()[a[:, perm]] * sa.astype(np.float64)[:, perm // BLOCK] \
+        * sb.astype(np.float64)[np.arange(N)[None, :] // BLOCK, perm[None, :] // BLOCK]
+    assert np.array_equal(got, want)
+
+
+def pin_gemm_integer_exact(orc):
+    """G5: integer-valued codes with unit scales give the exact integer product."""
+    vals = torch_e4m3_values()
+    small = np.array([c for c in range(256) if c not in (0x7F, 0xFF)
+                      and vals[c] == np.round(vals[c]) and abs(vals[c]) <= 4], np.uint8)
+    rng = np.random.default_rng(66)
+    M, N, K = 12, 140, 1024
+    a = small[rng.integers(0, small.size, (M, K))]; b = small[rng.integers(0, small.size, (N, K))]
+    got = orc.gemm(a, np.ones((M, K // BLOCK), np.float32), b,
+                   np.ones((2, K // BLOCK), np.float32))
+    want = vals[a].astype(np.int64) @ vals[b].astype(np.int64).T
+    assert np.array_equal(got, want.astype(np.float64))
+
+
+def pin_gemm_scale_pow2(orc):
+    """G6: multiplying the weight scales by 2^k multiplies the result by 2^k exactly."""
+    a = _rand_codes((6, 256), 67); b = _rand_codes((200, 256), 68)
+    sa = _rand_scales((6, 2), 69); sb = _rand_scales((2, 2), 70)
+    r0 = orc.gemm(a, sa, b, sb)
+    r1 = orc.gemm(a, sa, b, (sb * np.float32(2.0 ** 6)).astype(np.float32))
+    assert np.array_equal(r1, r0 * 2.0 ** 6)
+
+
+def pin_fp8_vs_bf16_branch(orc):
+    """G7: the FP8 branch (act_quant then gemm) and the exact linear map x * (dec(W) S)^T
+    differ by at most the activation-quantization error sum_k |x_k - dec(q_k) s| |w_k S|."""
+    M, N, K = 8, 256, 512
+    x = _rand_bf16(M, K, 71)
+    w = _rand_codes((N, K), 72)
+    S = _rand_scales((2, 4), 73)
+    q, s = orc.act_quant(x)
+    got = orc.gemm(q, s, w, S)
+    xf = bf16_bits_to_f32(x).astype(np.float64)
+    wf = torch_e4m3_values()[w] * _expand(S, N, K).astype(np.float64)
+    exact = xf @ wf.T
+    sf = np.repeat(s.astype(np.float64), BLOCK, 1)
+    ratio = np.abs(xf) / sf
+    per_elem = sf * (0.5 * ulp_e4m3(ratio) + 2.0 ** -23 * ratio)
+    bound = per_elem @ np.abs(wf).T
+    assert np.all(np.abs(got - exact) <= bound * (1 + 1e-9) + 1e-12 * (np.abs(xf) @ np.abs(wf).T))
+
+
+def pin_gemm_brute_force(orc):
+    """G8: plain loops in fp64 over random tiny shapes (ragged N)."""
+    vals = torch_e4m3_values()
+    rng = np.random.default_rng(81)
+    for t in range(4):
+        M = int(rng.integers(1, 5))
+        N = int(rng.integers(1, 9)) + 125 * (t % 2)
+        K = 128 * int(rng.integers(1, 4))
+        a = _rand_codes((M, K), 82 + t); b = _rand_codes((N, K), 92 + t)
+        sa = _rand_scales((M, K // BLOCK), 102 + t)
+        sb = _rand_scales((-(-N // BLOCK), K // BLOCK), 112 + t)
+        got = orc.gemm(a, sa, b, sb)
+        bound = 1e-13 * _terms_abs(a, sa, b, sb)
+        for m in range(M):
+            for n in range(N):
+                acc = 0.0
+                for kb in range(K // BLOCK):
+                    blk = 0.0
+                    for k in range(kb * BLOCK, kb * BLOCK + BLOCK):
+                        blk += vals[a[m, k]] * vals[b[n, k]]
+                    acc += blk * float(sa[m, kb]) * float(sb[n // BLOCK, kb])
+                assert abs(got[m, n] - acc) <= bound[m, n], (M, N, K, m, n)
+
+
+def pin_gemm_row_subset(orc):
+    """Computing a subset of rows gives exactly those rows of the full result."""
+    a = _rand_codes((20, 256), 121); b = _rand_codes((130, 256), 122)
+    sa = _rand_scales((20, 2), 123); sb = _rand_scales((2, 2), 124)
+    full = orc.gemm(a, sa, b, sb)
+    rows = np.array([19, 0, 7, 7])
+    assert np.array_equal(orc.gemm(a, sa, b, sb, rows=rows), full[rows])
+
+
+# --------------------------------------------------------------- grouped pins
+
+def pin_grouped_reduces_to_gemm(orc):
+    """R1: grouped == per-group plain GEMMs (torch f64 cross-check); G=1 == gemm; empty groups."""
+    K, N = 256, 200
+    counts = [3, 0, 5, 1, 0, 4]
+    G = len(counts)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    T = int(off[-1])
+    a = _rand_codes((T, K), 131); sa = _rand_scales((T, 2), 132)
+    b = _rand_codes((G, N, K), 133); sb = _rand_scales((G, 2, 2), 134)
+    got = orc.gemm_grouped(a, sa, b, sb, off)
+    vals = torch.from_numpy(torch_e4m3_values())
+    for g in range(G):
+        lo, hi = off[g], off[g + 1]
+        if hi == lo:
+            continue
+        A = vals[torch.from_numpy(a[lo:hi]).long()] * torch.from_numpy(np.repeat(sa[lo:hi], BLOCK, 1)).double()
+        B = vals[torch.from_numpy(b[g]).long()] * torch.from_numpy(np.repeat(np.repeat(sb[g], BLOCK, 0)[:N], BLOCK, 1)).double()
+        ref = (A @ B.T).numpy()
+        assert np.all(np.abs(got[lo:hi] - ref) <= 1e-12 * _terms_abs(a[lo:hi], sa[lo:hi], b[g], sb[g]) + 1e-300), g
+    one = orc.gemm_grouped(a, sa, b[:1], sb[:1], np.array([0, T], np.int32))
+    assert np.array_equal(one, orc.gemm(a, sa, b[0], sb[0]))
+    # a row that belongs to no group (offsets ending early) is reported as NaN
+    partial = orc.gemm_grouped(a, sa, b[:2], sb[:2], np.array([0, 2, 4], np.int32))
+    assert np.all(np.isnan(partial[4:])) and not np.any(np.isnan(partial[:4]))
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

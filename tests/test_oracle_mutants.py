@@ -1,0 +1,81 @@
+"""Plants plausible mistakes in copies of the CPU oracle and checks that the pins catch each.
+
+Every mutant is a text edit of ``oracle/bfp8_oracle.c`` compiled into a
+temporary folder; the real oracle is never touched.  A mutant survives only if
+every pin in tests/pins.py still passes, which would mean the pins cannot tell
+that mistake from the method.
+"""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import pins
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "bfp8_oracle.c")
+
+MUTANTS = {
+    # quantizer ceiling of a different fp8 flavour (e4m3 "fnuz" tops out at 240)
+    "ceiling_240": ("float scale = clamped / ORACLE_E4M3_MAX;", "float scale = clamped / 240.0f;"),
+    # no floor on the block max: an all-zero block divides by zero
+    "no_floor": ("float scale = clamped / ORACLE_E4M3_MAX;", "float scale = amax / ORACLE_E4M3_MAX;"),
+    # quotient through a reciprocal instead of an fp32 division
+    "reciprocal_quotient": ("oracle_bf16_to_f32(xb[j]) / scale;", "oracle_bf16_to_f32(xb[j]) * (1.0f / scale);"),
+    # ties away from zero instead of to even
+    "ties_away": ("(frac == 0.5 && fmod(n, 2.0) != 0.0)", "(frac == 0.5)"),
+    # overflow to the NaN code instead of saturating
+    "no_saturation": ("if (a >= 448.0) return sign | 0x7E;", "if (a >= 464.0) return sign | 0x7F;"),
+    # sign of zero lost
+    "unsigned_zero": ("if (mag == 0.0) return sign;", "if (mag == 0.0) return 0;"),
+    # exponent bias off by one in decode
+    "decode_bias": ("ldexpf(1.0f + (float)m / 8.0f, E - 7)", "ldexpf(1.0f + (float)m / 8.0f, E - 8)"),
+    # subnormal spacing wrong in decode
+    "decode_subnormal": ("ldexpf((float)m, -9)", "ldexpf((float)m, -10)"),
+    # block max taken without the absolute value
+    "signed_amax": ("float a = fabsf(oracle_bf16_to_f32(xb[j]));", "float a = oracle_bf16_to_f32(xb[j]);"),
+    # bf16 rounding: ties away
+    "bf16_ties_away": ("(dropped == 0x8000u && (kept & 1u))", "(dropped == 0x8000u)"),
+    # bf16 rounding: truncation
+    "bf16_truncate": ("if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u))) kept += 1u;", ""),
+    # dequant uses the first k-block's scale for the whole row
+    "dequant_scale_index": ("S[(n / ORACLE_BLOCK) * KB + k / ORACLE_BLOCK]", "S[(n / ORACLE_BLOCK) * KB]"),
+    # dequant divides by the scale (the other reading of scale_inv)
+    "dequant_divides": ("oracle_e4m3_decode(w[n * K + k]) * scale;", "oracle_e4m3_decode(w[n * K + k]) / scale;"),
+    # GEMM drops the activation scale
+    "gemm_no_sa": ("total += block_sum * (double)J->sa[m * KB + kb]", "total += block_sum * 1.0"),
+    # GEMM reads the activation scale of the first block only
+    "gemm_sa_index": ("(double)J->sa[m * KB + kb]", "(double)J->sa[m * KB]"),
+    # GEMM weight-scale row taken from k instead of n
+    "gemm_sb_index": ("(double)sb[(n / ORACLE_BLOCK) * KB + kb]", "(double)sb[kb]"),
+    # GEMM weight column instead of row (transposed operand on a square weight)
+    "gemm_transposed_b": ("(double)J->table[brow[k]]", "(double)J->table[b[(k % J->N) * J->K + n % J->K]]"),
+    # grouped: row at an upper offset counted in the group
+    "grouped_off_by_one": ("m >= J->off[h] && m < J->off[h + 1]", "m >= J->off[h] && m <= J->off[h + 1]"),
+}
+
+
+@pytest.fixture(scope="module")
+def mutant_dir(tmp_path_factory):
+    return tmp_path_factory.mktemp("oracle_mutants")
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, mutant_dir):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation target for {name} not found"
+    mutated = src.replace(old, new)
+    c_path = mutant_dir / f"{name}.c"
+    so_path = mutant_dir / f"lib_{name}.so"
+    c_path.write_text(mutated)
+    subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared", "-pthread",
+                    str(c_path), "-o", str(so_path), "-lm"], check=True)
+    orc = oracle.Oracle(str(so_path))
+    failed = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(orc)
+        except Exception:            # an assertion, or an error the mistake provoked
+            failed.append(pin.__name__)
+    assert failed, f"mutant {name} passes every pin"
