@@ -1,0 +1,313 @@
+"""Benchmark of the block-scaled FP8 linear path on one MI355X.
+
+One step is one pass of the whole path over one batch of seeded synthetic
+input already resident in HBM.  For the default workload (the dense MLP
+layer-0 shape of DeepSeek-V3: x [8192, 7168], W_up [18432, 7168],
+W_down [7168, 18432]) a step is
+
+    act_quant(x) -> fp8 GEMM up -> act_quant(H) -> fp8 GEMM down -> weight_dequant(W_up)
+
+Printed: one JSON line.  `value` is the step's GEMM FLOP divided by the step's
+wall time (TFLOP/s); `kernels` gives each kernel's average duration from HIP
+events recorded around every launch inside the timed region, with its
+algorithmic FLOP or bytes per launch and its fraction of the MI355X peak that
+bounds it; `roofline` repeats that for the dominant kernel; `cpu_baseline`
+times the CPU oracle on a bounded, proportional sample of the same step.
+
+Other workloads (parity-test shapes, measured on demand): --workload tiny |
+decode | moe-pair | dense-mlp | grouped.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import block_scaled_fp8_04_amd as bfp8  # noqa: E402
+from block_scaled_fp8_04_amd import synth  # noqa: E402
+
+BLOCK = 128
+PEAK_FP8_TFLOPS = 5000.0          # MI355X dense fp8 MFMA (no sparsity)
+PEAK_HBM_GBS = 8000.0             # MI355X HBM3E
+
+WORKLOADS = {"tiny": 0, "decode": 1, "moe-pair": 2, "dense-mlp": 3, "grouped": 4}
+
+
+# ------------------------------------------------------------------ accounting
+
+def act_quant_bytes(M, K):
+    return 2 * M * K + M * K + 4 * M * (K // BLOCK)
+
+
+def dequant_bytes(N, K):
+    return N * K + 2 * N * K + 4 * (-(-N // BLOCK)) * (-(-K // BLOCK))
+
+
+def gemm_bytes(M, N, K, G=1):
+    return M * K + G * N * K + 2 * M * N + 4 * M * (K // BLOCK) + 4 * G * (-(-N // BLOCK)) * (K // BLOCK)
+
+
+def sha_of(t: torch.Tensor) -> str:
+    return hashlib.sha256(t.contiguous().view(torch.uint8).numpy().tobytes()).hexdigest()[:16]
+
+
+# ------------------------------------------------------------------ the steps
+
+class Step:
+    """Device buffers and the ordered launches of one step; every launch is named."""
+
+    def __init__(self, wl, dev):
+        self.wl = wl
+        self.dev = dev
+        t = wl.tensors
+        c = wl.config
+        self.launches = []            # (name, callable, flops, bytes, bound)
+        self.hashes = {}
+        for k, v in t.items():
+            if k != "token_ids":
+                self.hashes[k] = sha_of(v)
+        if c in (0, 1):
+            M, N, K = wl.meta["M"], wl.meta["N"], wl.meta["K"]
+            x = t["x"].to(dev)
+            w, s = t["w1"].to(dev), t["s1"].to(dev)
+            q = torch.empty(M, K, dtype=torch.uint8, device=dev)
+            qs = torch.empty(M, K // BLOCK, dtype=torch.float32, device=dev)
+            y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+            ws_bytes = bfp8.bfp8_gemm_workspace_size(M, N, K)
+            work = torch.empty(max(1, ws_bytes // 4), dtype=torch.float32, device=dev) if ws_bytes else None
+            self.launches += [
+                ("act_quant", lambda: bfp8.bfp8_act_quant(x, q, qs), 0, act_quant_bytes(M, K), "hbm"),
+                ("fp8_gemm", lambda: bfp8.bfp8_gemm(q, qs, w, s, y, work), 2 * M * N * K,
+                 gemm_bytes(M, N, K), "mfma" if c == 0 else "hbm"),
+            ]
+            self.shape = dict(M=M, N=N, K=K)
+            self.dominant, self.dominant_kernel = ["fp8_gemm"], "gemm"
+        elif c in (2, 3):
+            M, N1, K1, N2, K2 = (wl.meta[k] for k in ("M", "N1", "K1", "N2", "K2"))
+            x = t["x"].to(dev)
+            w1, s1 = t["w1"].to(dev), t["s1"].to(dev)
+            w2, s2 = t["w2"].to(dev), t["s2"].to(dev)
+            q = torch.empty(M, K1, dtype=torch.uint8, device=dev)
+            qs = torch.empty(M, K1 // BLOCK, dtype=torch.float32, device=dev)
+            h = torch.empty(M, N1, dtype=torch.bfloat16, device=dev)
+            qh = torch.empty(M, K2, dtype=torch.uint8, device=dev)
+            qhs = torch.empty(M, K2 // BLOCK, dtype=torch.float32, device=dev)
+            y = torch.empty(M, N2, dtype=torch.bfloat16, device=dev)
+            self.launches += [
+                ("act_quant_x", lambda: bfp8.bfp8_act_quant(x, q, qs), 0, act_quant_bytes(M, K1), "hbm"),
+                ("fp8_gemm_1", lambda: bfp8.bfp8_gemm(q, qs, w1, s1, h), 2 * M * N1 * K1,
+                 gemm_bytes(M, N1, K1), "mfma"),
+                ("act_quant_h", lambda: bfp8.bfp8_act_quant(h, qh, qhs), 0, act_quant_bytes(M, K2), "hbm"),
+                ("fp8_gemm_2", lambda: bfp8.bfp8_gemm(qh, qhs, w2, s2, y), 2 * M * N2 * K2,
+                 gemm_bytes(M, N2, K2), "mfma"),
+            ]
+            if c == 3:
+                wd = torch.empty(N1, K1, dtype=torch.bfloat16, device=dev)
+                self.launches.append(("weight_dequant", lambda: bfp8.bfp8_weight_dequant(w1, s1, wd), 0,
+                                      dequant_bytes(N1, K1), "hbm"))
+            self.shape = dict(M=M, N1=N1, K1=K1, N2=N2, K2=K2)
+            # both GEMMs run the same kernel with the same FLOP count per launch
+            self.dominant, self.dominant_kernel = ["fp8_gemm_1", "fp8_gemm_2"], "gemm"
+        elif c == 4:
+            ids, off = t["token_ids"], t["offsets"]
+            T, G, N, K = int(off[-1]), wl.meta["G"], wl.meta["N"], wl.meta["K"]
+            xg = t["x"][ids].contiguous().to(dev)          # tokens already gathered in expert order
+            self.hashes["x_gathered"] = sha_of(t["x"][ids])
+            b, bs = t["w1"].to(dev), t["s1"].to(dev)
+            off_d = off.to(dev)
+            q = torch.empty(T, K, dtype=torch.uint8, device=dev)
+            qs = torch.empty(T, K // BLOCK, dtype=torch.float32, device=dev)
+            y = torch.empty(T, N, dtype=torch.bfloat16, device=dev)
+            self.launches += [
+                ("act_quant", lambda: bfp8.bfp8_act_quant(xg, q, qs), 0, act_quant_bytes(T, K), "hbm"),
+                ("fp8_gemm_grouped", lambda: bfp8.bfp8_gemm_grouped(q, qs, b, bs, y, off_d),
+                 2 * T * N * K, gemm_bytes(T, N, K, G), "hbm"),
+            ]
+            counts = (off[1:] - off[:-1]).tolist()
+            self.shape = dict(T=T, G=G, N=N, K=K, tokens_per_expert_min=min(counts),
+                              tokens_per_expert_max=max(counts))
+            self.dominant, self.dominant_kernel = ["fp8_gemm_grouped"], "gemm_grouped"
+        else:
+            raise ValueError(c)
+
+    def run(self, events=None):
+        for i, (_, fn, _, _, _) in enumerate(self.launches):
+            if events is not None:
+                events[i].record()
+            fn()
+        if events is not None:
+            events[len(self.launches)].record()
+
+
+# ------------------------------------------------------------------ CPU oracle leg
+
+def cpu_baseline(wl, target_s=12.0):
+    """Time the CPU oracle on a proportional sample of one step: a fraction f of the
+    rows of every stage (activation rows, and weight rows for dequant)."""
+    import oracle
+
+    threads = min(oracle.default_threads(), int(os.environ.get("OMP_NUM_THREADS", "1024")))
+    t = wl.tensors
+    c = wl.config
+    x_bits = t["x"].contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    def run(rows):
+        done = 0.0
+        t0 = time.perf_counter()
+        if c in (0, 1):
+            q, s = oracle.act_quant(x_bits[:rows])
+            oracle.gemm(q, s, t["w1"].numpy(), t["s1"].numpy(), threads=threads)
+            done = 2.0 * rows * wl.meta["N"] * wl.meta["K"]
+        elif c in (2, 3):
+            q, s = oracle.act_quant(x_bits[:rows])
+            h = oracle.gemm(q, s, t["w1"].numpy(), t["s1"].numpy(), threads=threads)
+            hb = oracle.f32_to_bf16(h.astype(np.float32))
+            qh, sh = oracle.act_quant(hb)
+            oracle.gemm(qh, sh, t["w2"].numpy(), t["s2"].numpy(), threads=threads)
+            done = 2.0 * rows * (wl.meta["N1"] * wl.meta["K1"] + wl.meta["N2"] * wl.meta["K2"])
+            if c == 3:
+                wrows = max(1, int(round(t["w1"].shape[0] * rows / wl.meta["M"])))
+                oracle.weight_dequant(t["w1"].numpy()[:wrows], t["s1"].numpy()[:-(-wrows // BLOCK)])
+        else:
+            ids, off = t["token_ids"].numpy(), t["offsets"].numpy()
+            xg = x_bits[ids[:rows]]
+            q, s = oracle.act_quant(xg)
+            full_q = np.zeros((int(off[-1]), q.shape[1]), np.uint8)
+            full_s = np.ones((int(off[-1]), s.shape[1]), np.float32)
+            full_q[:rows], full_s[:rows] = q, s
+            oracle.gemm_grouped(full_q, full_s, t["w1"].numpy(), t["s1"].numpy(), off,
+                                rows=np.arange(rows), threads=threads)
+            done = 2.0 * rows * wl.meta["N"] * wl.meta["K"]
+        return time.perf_counter() - t0, done
+
+    M = wl.meta.get("M", wl.meta.get("T"))
+    probe = min(M, max(1, threads))
+    dt, _ = run(probe)
+    rows = int(min(M, max(probe, probe * target_s / max(dt, 1e-6))))
+    dt, flop = run(rows)
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows} of {M} rows of every stage of one step ({dt:.1f} s of CPU work)"}
+
+
+# ------------------------------------------------------------------ traffic
+
+def read_traffic(kernel_name):
+    """HBM bytes per launch measured by rocprofv3 counters, if the kernel source is unchanged."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_name}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    src = os.path.join(ROOT, "block_scaled_fp8_04_amd", "csrc", kv.get("source", "gemm.hip"))
+    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != kv.get("source_sha256"):
+        return None
+    try:
+        return float(kv["bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="dense-mlp")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build runs the path on a single MI355X "
+              "(multi-GPU sharding is a design note, not measured). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    bfp8.library()
+    dev = torch.device("cuda:0")
+
+    t0 = time.time()
+    wl = synth.make(WORKLOADS[args.workload])
+    step = Step(wl, dev)
+    gen_s = time.time() - t0
+    print(f"# workload {wl.name}: inputs built in {gen_s:.1f}s; launches "
+          f"{[l[0] for l in step.launches]}", file=sys.stderr, flush=True)
+
+    nl = len(step.launches)
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nl + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        step.run(events[k])
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    ms_per_step = (t_end - t_start) * 1e3 / args.steps
+
+    kernels = {}
+    for i, (name, _, flop, nbytes, bound) in enumerate(step.launches):
+        ms = float(np.mean([events[k][i].elapsed_time(events[k][i + 1]) for k in range(args.steps)]))
+        entry = {"avg_us": ms * 1e3, "flop": flop, "bytes": nbytes, "bound": bound}
+        if flop:
+            entry["tflops"] = flop / (ms * 1e-3) / 1e12
+        entry["gbs"] = nbytes / (ms * 1e-3) / 1e9
+        entry["frac"] = (entry["tflops"] / PEAK_FP8_TFLOPS) if bound == "mfma" else (entry["gbs"] / PEAK_HBM_GBS)
+        kernels[name] = entry
+
+    gemm_flop = sum(l[2] for l in step.launches)
+    value = gemm_flop / (ms_per_step * 1e-3) / 1e12
+
+    # dominant kernel: the launches of the kernel that takes most of the step
+    dom = step.dominant
+    avg_us = float(np.mean([kernels[n]["avg_us"] for n in dom]))
+    d = kernels[dom[0]]
+    traffic = read_traffic(step.dominant_kernel)
+    if d["bound"] == "mfma":
+        ach = d["flop"] / (avg_us * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                "frac": ach / PEAK_FP8_TFLOPS, "traffic": traffic, "kernel": step.dominant_kernel,
+                "launches": dom, "avg_us": avg_us}
+    else:
+        nbytes = float(np.mean([kernels[n]["bytes"] for n in dom]))
+        ach = nbytes / (avg_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": ach / PEAK_HBM_GBS, "traffic": traffic, "kernel": step.dominant_kernel,
+                "launches": dom, "avg_us": avg_us}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+
+    config = {"workload": wl.name, "shape": step.shape,
+              "step": " -> ".join(l[0] for l in step.launches),
+              "value_definition": "GEMM FLOP per step / wall time per step",
+              "input_sha256_16": step.hashes, "seeds": "1000*config+tensor_id",
+              "parallelism": "single-gpu"}
+    out = {"metric": "block-FP8 GEMM TFLOP/s & % of fp8 MFMA peak; act_quant/dequant HBM GB/s",
+           "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3 (fp32 accumulate, bf16 out)",
+           "data": "synthetic (seeded; DeepSeek-V3 projection shapes, random-init)",
+           "config": config, "kernels": kernels, "roofline": roof, "cpu_baseline": cpu}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

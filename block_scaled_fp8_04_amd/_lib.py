@@ -1,0 +1,225 @@
+"""ctypes binding of libbfp8.so: the C ABI of include/bfp8.h, one Python function per entry point.
+
+Argument marshalling only: every function takes torch tensors that already
+live on the GPU, checks that their dtypes and shapes agree with the C
+signature, and passes their device pointers, the sizes and the current HIP
+stream to the library.  No arithmetic of the path happens here, and there is
+no fallback: if the library is missing the call raises.
+"""
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "libbfp8.so")
+
+BLOCK = 128
+
+# status codes of include/bfp8.h
+BFP8_OK = 0
+BFP8_ERR_NULL = 1
+BFP8_ERR_SHAPE = 2
+BFP8_ERR_ALIGN = 3
+BFP8_ERR_WORKSPACE = 4
+BFP8_ERR_GROUPS = 5
+BFP8_ERR_HIP = 6
+BFP8_ERR_ARG = 7
+
+EXPORTS = ("bfp8_act_quant", "bfp8_weight_dequant", "bfp8_gemm", "bfp8_gemm_workspace_size",
+           "bfp8_gemm_grouped", "bfp8_e4m3_encode_range", "bfp8_status_string", "bfp8_version")
+
+_lib = None
+
+
+class Bfp8Error(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed: {status_string(status)} (status {status})")
+
+
+def library():
+    """Load libbfp8.so (built by __graft_entry__.build()); raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIBRARY):
+        raise RuntimeError(f"{LIBRARY} is not built; run __graft_entry__.build() first "
+                           "(there is no fallback path)")
+    lib = ctypes.CDLL(LIBRARY)
+    P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.bfp8_act_quant.argtypes = [P, P, P, I64, I64, P]
+    lib.bfp8_act_quant.restype = ctypes.c_int
+    lib.bfp8_weight_dequant.argtypes = [P, P, P, I64, I64, P]
+    lib.bfp8_weight_dequant.restype = ctypes.c_int
+    lib.bfp8_gemm.argtypes = [P, P, P, P, P, I64, I64, I64, P, ctypes.c_size_t, P]
+    lib.bfp8_gemm.restype = ctypes.c_int
+    lib.bfp8_gemm_workspace_size.argtypes = [I64, I64, I64]
+    lib.bfp8_gemm_workspace_size.restype = ctypes.c_size_t
+    lib.bfp8_gemm_grouped.argtypes = [P, P, P, P, P, P, I32, I64, I64, I64, P]
+    lib.bfp8_gemm_grouped.restype = ctypes.c_int
+    lib.bfp8_e4m3_encode_range.argtypes = [ctypes.c_uint32, I64, P, ctypes.c_int, P]
+    lib.bfp8_e4m3_encode_range.restype = ctypes.c_int
+    lib.bfp8_status_string.argtypes = [ctypes.c_int]
+    lib.bfp8_status_string.restype = ctypes.c_char_p
+    lib.bfp8_version.argtypes = []
+    lib.bfp8_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return library().bfp8_status_string(int(status)).decode()
+
+
+def _check(fn, status):
+    if status != BFP8_OK:
+        raise Bfp8Error(fn, status)
+
+
+def _stream(stream, device):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _bytes_view(t):
+    """e4m3 tensors may arrive as torch.float8_e4m3fn or as raw uint8 codes."""
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8)
+    if t.dtype != torch.uint8:
+        raise TypeError(f"expected e4m3 codes (uint8 or float8_e4m3fn), got {t.dtype}")
+    return t
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _cuda_contig(*ts):
+    for t in ts:
+        if t is not None:
+            _need(t.is_cuda, "all tensors must be on the GPU")
+            _need(t.is_contiguous(), "all tensors must be contiguous")
+
+
+# ------------------------------------------------------------------ entry points
+
+def bfp8_version() -> int:
+    return int(library().bfp8_version())
+
+
+def bfp8_status_string(status: int) -> str:
+    return status_string(status)
+
+
+def bfp8_act_quant(x, q, scales, stream=None):
+    """x bf16 [M,K] -> q e4m3 [M,K], scales fp32 [M,K/128] (written in place)."""
+    q = _bytes_view(q)
+    _cuda_contig(x, q, scales)
+    _need(x.dtype == torch.bfloat16 and scales.dtype == torch.float32, "x must be bf16, scales fp32")
+    _need(x.dim() == 2, "x must be [M, K]")
+    M, K = x.shape
+    _need(q.shape == (M, K) and scales.shape == (M, K // BLOCK), "output shapes do not match x")
+    _check("bfp8_act_quant", library().bfp8_act_quant(_ptr(x), _ptr(q), _ptr(scales), M, K,
+                                                      _stream(stream, x.device)))
+
+
+def bfp8_weight_dequant(w, s, out, stream=None):
+    """w e4m3 [N,K], s fp32 [ceil(N/128), ceil(K/128)] -> out bf16 [N,K]."""
+    w = _bytes_view(w)
+    _cuda_contig(w, s, out)
+    _need(out.dtype == torch.bfloat16 and s.dtype == torch.float32, "out must be bf16, s fp32")
+    N, K = w.shape
+    _need(out.shape == (N, K), "out must match w")
+    _need(s.shape == (-(-N // BLOCK), -(-K // BLOCK)), "scale grid must tile w by 128x128")
+    _check("bfp8_weight_dequant", library().bfp8_weight_dequant(_ptr(w), _ptr(s), _ptr(out), N, K,
+                                                                _stream(stream, w.device)))
+
+
+def bfp8_gemm_workspace_size(M, N, K) -> int:
+    return int(library().bfp8_gemm_workspace_size(int(M), int(N), int(K)))
+
+
+def bfp8_gemm(a, a_s, b, b_s, c, workspace=None, stream=None):
+    """c bf16 [M,N] = block-scaled a e4m3 [M,K] x b e4m3 [N,K]^T."""
+    a, b = _bytes_view(a), _bytes_view(b)
+    _cuda_contig(a, a_s, b, b_s, c, workspace)
+    M, K = a.shape
+    N = b.shape[0]
+    _need(b.shape[1] == K, "a and b must share K")
+    _need(a_s.dtype == torch.float32 and b_s.dtype == torch.float32, "scales must be fp32")
+    _need(a_s.shape == (M, K // BLOCK), "a_s must be [M, K/128]")
+    _need(b_s.shape == (-(-N // BLOCK), K // BLOCK), "b_s must be [ceil(N/128), K/128]")
+    _need(c.dtype == torch.bfloat16 and c.shape == (M, N), "c must be bf16 [M, N]")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("bfp8_gemm", library().bfp8_gemm(_ptr(a), _ptr(a_s), _ptr(b), _ptr(b_s), _ptr(c),
+                                            M, N, K, _ptr(workspace), ws_bytes,
+                                            _stream(stream, a.device)))
+
+
+def bfp8_gemm_grouped(a, a_s, b, b_s, c, group_offsets, stream=None):
+    """Rows [off[g], off[g+1]) of a times b[g]^T into the same rows of c."""
+    a, b = _bytes_view(a), _bytes_view(b)
+    _cuda_contig(a, a_s, b, b_s, c, group_offsets)
+    T, K = a.shape
+    G, N, Kb = b.shape
+    _need(Kb == K, "a and b must share K")
+    _need(group_offsets.dtype == torch.int32 and group_offsets.shape == (G + 1,),
+          "group_offsets must be int32 [G+1] on the GPU")
+    _need(a_s.shape == (T, K // BLOCK), "a_s must be [total_M, K/128]")
+    _need(b_s.shape == (G, -(-N // BLOCK), K // BLOCK), "b_s must be [G, ceil(N/128), K/128]")
+    _need(c.dtype == torch.bfloat16 and c.shape == (T, N), "c must be bf16 [total_M, N]")
+    _check("bfp8_gemm_grouped", library().bfp8_gemm_grouped(
+        _ptr(a), _ptr(a_s), _ptr(b), _ptr(b_s), _ptr(c), _ptr(group_offsets), G, T, N, K,
+        _stream(stream, a.device)))
+
+
+def bfp8_e4m3_encode_range(first, count, out, variant=0, stream=None):
+    """Device encode of the fp32 bit patterns first .. first+count-1 into out (uint8)."""
+    _cuda_contig(out)
+    _need(out.dtype == torch.uint8 and out.numel() >= count, "out must be uint8 with count bytes")
+    _check("bfp8_e4m3_encode_range", library().bfp8_e4m3_encode_range(
+        int(first), int(count), _ptr(out), int(variant), _stream(stream, out.device)))
+
+
+# ------------------------------------------------------- allocating conveniences
+
+def act_quant(x, stream=None):
+    """(q e4m3 as uint8 [M,K], scales fp32 [M,K/128]) = act_quant(x bf16 [M,K])."""
+    M, K = x.shape
+    q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    s = torch.empty((M, K // BLOCK), dtype=torch.float32, device=x.device)
+    bfp8_act_quant(x, q, s, stream)
+    return q, s
+
+
+def weight_dequant(w, s, stream=None):
+    out = torch.empty(w.shape, dtype=torch.bfloat16, device=w.device)
+    bfp8_weight_dequant(w, s, out, stream)
+    return out
+
+
+def gemm(a, a_s, b, b_s, workspace=None, stream=None):
+    c = torch.empty((a.shape[0], b.shape[0]), dtype=torch.bfloat16, device=a.device)
+    bfp8_gemm(a, a_s, b, b_s, c, workspace, stream)
+    return c
+
+
+def gemm_grouped(a, a_s, b, b_s, group_offsets, stream=None):
+    c = torch.empty((a.shape[0], b.shape[1]), dtype=torch.bfloat16, device=a.device)
+    bfp8_gemm_grouped(a, a_s, b, b_s, c, group_offsets, stream)
+    return c
+
+
+def linear_fp8(x, w, w_s, workspace=None, stream=None):
+    """The FP8 branch of linear(): act_quant(x) then the block-scaled GEMM with (w, w.scale)."""
+    q, s = act_quant(x, stream)
+    return gemm(q, s, w, w_s, workspace, stream)

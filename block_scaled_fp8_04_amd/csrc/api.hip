@@ -1,0 +1,117 @@
+// api.hip - the C ABI declared in include/bfp8.h: host-side validation, then
+// one launcher call.  Validation touches no HIP API, so every error code can
+// be exercised on a machine without a GPU.
+#include <mutex>
+
+#include "../../include/bfp8.h"
+#include "internal.hpp"
+
+namespace bfp8 {
+
+int device_cu_count() {
+    static std::mutex mu;
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cached[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+        cached[dev] = cus;
+    }
+    return cached[dev];
+}
+
+}  // namespace bfp8
+
+namespace {
+
+bool aligned(const void* p, uintptr_t n) { return ((uintptr_t)p % n) == 0; }
+
+int from_hip(hipError_t e) { return e == hipSuccess ? BFP8_OK : BFP8_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int bfp8_version(void) { return BFP8_VERSION; }
+
+const char* bfp8_status_string(int status) {
+    switch (status) {
+        case BFP8_OK: return "ok";
+        case BFP8_ERR_NULL: return "a required pointer is NULL";
+        case BFP8_ERR_SHAPE: return "invalid shape (negative size, or K not a multiple of 128)";
+        case BFP8_ERR_ALIGN: return "pointer misaligned";
+        case BFP8_ERR_WORKSPACE: return "workspace smaller than bfp8_gemm_workspace_size()";
+        case BFP8_ERR_GROUPS: return "group count must be at least 1";
+        case BFP8_ERR_HIP: return "HIP runtime error at launch";
+        case BFP8_ERR_ARG: return "invalid argument";
+        default: return "unknown status";
+    }
+}
+
+int bfp8_act_quant(const void* x_bf16, void* q_e4m3, float* scales, int64_t M, int64_t K,
+                   void* stream) {
+    if (M < 0 || K <= 0 || K % BFP8_BLOCK != 0) return BFP8_ERR_SHAPE;
+    if (M == 0) return BFP8_OK;
+    if (!x_bf16 || !q_e4m3 || !scales) return BFP8_ERR_NULL;
+    if (!aligned(x_bf16, 16) || !aligned(q_e4m3, 16) || !aligned(scales, 4)) return BFP8_ERR_ALIGN;
+    return from_hip(bfp8::launch_act_quant(x_bf16, q_e4m3, scales, M, K, (hipStream_t)stream));
+}
+
+int bfp8_weight_dequant(const void* w_e4m3, const float* s, void* out_bf16, int64_t N, int64_t K,
+                        void* stream) {
+    if (N < 0 || K < 0) return BFP8_ERR_SHAPE;
+    if (N == 0 || K == 0) return BFP8_OK;
+    if (!w_e4m3 || !s || !out_bf16) return BFP8_ERR_NULL;
+    if (!aligned(out_bf16, 2) || !aligned(s, 4)) return BFP8_ERR_ALIGN;
+    return from_hip(bfp8::launch_weight_dequant(w_e4m3, s, out_bf16, N, K, (hipStream_t)stream));
+}
+
+size_t bfp8_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
+    if (M <= 0 || N <= 0 || K <= 0 || K % BFP8_BLOCK != 0) return 0;
+    return bfp8::gemm_workspace_bytes(M, N, K);
+}
+
+int bfp8_gemm(const void* a, const float* a_s, const void* b, const float* b_s, void* c_bf16,
+              int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+              void* stream) {
+    if (M < 0 || N < 0 || K <= 0 || K % BFP8_BLOCK != 0) return BFP8_ERR_SHAPE;
+    if (M == 0 || N == 0) return BFP8_OK;
+    if (!a || !a_s || !b || !b_s || !c_bf16) return BFP8_ERR_NULL;
+    if (!aligned(a, 16) || !aligned(b, 16) || !aligned(a_s, 4) || !aligned(b_s, 4) ||
+        !aligned(c_bf16, 2))
+        return BFP8_ERR_ALIGN;
+    if (workspace) {
+        if (!aligned(workspace, 16)) return BFP8_ERR_ALIGN;
+        if (workspace_bytes < bfp8::gemm_workspace_bytes(M, N, K)) return BFP8_ERR_WORKSPACE;
+    }
+    return from_hip(bfp8::launch_gemm(a, a_s, b, b_s, c_bf16, M, N, K, workspace,
+                                      workspace ? workspace_bytes : 0, (hipStream_t)stream));
+}
+
+int bfp8_gemm_grouped(const void* a, const float* a_s, const void* b, const float* b_s,
+                      void* c_bf16, const int32_t* group_offsets, int32_t G, int64_t total_M,
+                      int64_t N, int64_t K, void* stream) {
+    if (total_M < 0 || N < 0 || K <= 0 || K % BFP8_BLOCK != 0) return BFP8_ERR_SHAPE;
+    if (G < 1) return BFP8_ERR_GROUPS;
+    if (total_M == 0 || N == 0) return BFP8_OK;
+    if (!a || !a_s || !b || !b_s || !c_bf16 || !group_offsets) return BFP8_ERR_NULL;
+    if (!aligned(a, 16) || !aligned(b, 16) || !aligned(a_s, 4) || !aligned(b_s, 4) ||
+        !aligned(c_bf16, 2) || !aligned(group_offsets, 4))
+        return BFP8_ERR_ALIGN;
+    return from_hip(bfp8::launch_gemm_grouped(a, a_s, b, b_s, c_bf16, group_offsets, G, total_M,
+                                              N, K, (hipStream_t)stream));
+}
+
+int bfp8_e4m3_encode_range(uint32_t first, int64_t count, void* out, int variant, void* stream) {
+    if (count < 0 || (uint64_t)first + (uint64_t)count > (uint64_t)1 << 32) return BFP8_ERR_SHAPE;
+    if (variant != 0 && variant != 1) return BFP8_ERR_ARG;
+    if (count == 0) return BFP8_OK;
+    if (!out) return BFP8_ERR_NULL;
+    return from_hip(bfp8::launch_encode_range(first, count, out, variant, (hipStream_t)stream));
+}
+
+}  // extern "C"

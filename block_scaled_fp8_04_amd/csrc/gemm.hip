@@ -1,0 +1,287 @@
+// gemm.hip - block-scaled fp8 GEMM (plain and grouped) on gfx950.
+//
+// c[m, n] = bf16( sum_kb P_kb[m, n] * a_s[m, kb] * b_s[n/128, kb] ),
+// P_kb[m, n] = sum_{k in block kb} a[m, k] * b[n, k]
+// ("Data flow - deepseek-ai/DeepSeek-V3", FP8 quantization bullet: fp8_gemm
+// multiplies scaled blocks and accumulates in fp32; pyshine tour, "FP8 with
+// per-block scales").  a is [M, K] and b is a Linear weight [N, K], both
+// K-contiguous, so C = A * B^T.
+//
+// Design (gfx950, wave64):
+//  * One 128-wide K block is exactly the K extent of one
+//    v_mfma_f32_16x16x128_f8f6f4 (e4m3 x e4m3 -> fp32).  Each 16x16 sub-tile
+//    of a wave's output gets one MFMA per K block into a zeroed accumulator,
+//    and that block product is folded into the running fp32 sum with one FMA
+//    per element: acc += P * (a_s[row] * b_s).  The weight-scale block is the
+//    same for all of a wave's columns (a wave's N range lies inside one
+//    128-column block), so the fold needs one scale per row.
+//  * A workgroup is 4 waves in a 2 x 2 layout over a BM x BN tile.  A and B
+//    tiles of one K block (BM x 128 and BN x 128 bytes) are staged through LDS,
+//    double buffered: while the waves multiply stage s, the next K block's
+//    global loads are in flight in registers and are written to stage s^1.
+//    One barrier per K block.
+//  * LDS rows are 128 bytes; the eight 16-byte chunks of row r are stored at
+//    chunk position (chunk ^ (r & 7)), so both the row-wise writes and the
+//    fragment reads (16 rows at the same chunk) touch all banks once.
+//  * MFMA operand layout: lane l supplies row (l & 15) of the sub-tile and the
+//    32 K-bytes starting at 32 * (l >> 4), for A and B alike, so each K index
+//    pairs the same position of A and B.  The accumulator layout of a 16x16
+//    fp32 result is: lane l holds column (l & 15), rows 4*(l >> 4) + 0..3.
+//  * Rows past M (or past a group's end) and columns past N read a clamped,
+//    valid row and are never stored.
+#include "device_codec.hpp"
+#include "internal.hpp"
+
+namespace bfp8 {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+template <int BM_, int BN_>
+struct Tile {
+    static constexpr int BM = BM_, BN = BN_;
+    static constexpr int WM = BM / 2, WN = BN / 2;      // per-wave extent (2 x 2 waves)
+    static constexpr int TM = WM / 16, TN = WN / 16;    // 16 x 16 sub-tiles per wave
+    static constexpr int A_BYTES = BM * kBlock;
+    static constexpr int B_BYTES = BN * kBlock;
+    static constexpr int A_LOADS = A_BYTES / (256 * 16);
+    static constexpr int B_LOADS = B_BYTES / (256 * 16);
+    static constexpr int STAGE = A_BYTES + B_BYTES + BM * 4;
+    static_assert(A_LOADS >= 1 && B_LOADS >= 1, "tile too small for 256 threads");
+    static_assert(TM >= 1 && TN >= 1, "wave tile must hold a 16x16 sub-tile");
+    static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns must share one scale block");
+};
+
+__device__ __forceinline__ v8i frag_from(const uint4 x0, const uint4 x1) {
+    v8i f;
+    f[0] = (int)x0.x; f[1] = (int)x0.y; f[2] = (int)x0.z; f[3] = (int)x0.w;
+    f[4] = (int)x1.x; f[5] = (int)x1.y; f[6] = (int)x1.z; f[7] = (int)x1.w;
+    return f;
+}
+
+// Computes rows [m0, min(m0 + BM, m_end)) x columns [n0, min(n0 + BN, N)) of c.
+template <class T>
+__device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a,
+                                          const float* __restrict__ as,
+                                          const uint8_t* __restrict__ b,
+                                          const float* __restrict__ bs,
+                                          uint16_t* __restrict__ c, int64_t m0, int64_t m_end,
+                                          int64_t n0, int64_t N, int64_t K, uint8_t* lds) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm0 = (wave >> 1) * T::WM;
+    const int wn0 = (wave & 1) * T::WN;
+    const int64_t KB = K / kBlock;
+    const int64_t NB = (N + kBlock - 1) / kBlock;
+
+    // global sources and LDS destinations of this thread's 16-byte chunks
+    const uint8_t* a_src[T::A_LOADS];
+    const uint8_t* b_src[T::B_LOADS];
+    int a_dst[T::A_LOADS], b_dst[T::B_LOADS];
+#pragma unroll
+    for (int i = 0; i < T::A_LOADS; ++i) {
+        const int ch = tid + 256 * i, row = ch >> 3, col = ch & 7;
+        int64_t grow = m0 + row;
+        grow = grow < m_end ? grow : m_end - 1;
+        a_src[i] = a + grow * K + col * 16;
+        a_dst[i] = row * kBlock + ((col ^ (row & 7)) << 4);
+    }
+#pragma unroll
+    for (int i = 0; i < T::B_LOADS; ++i) {
+        const int ch = tid + 256 * i, row = ch >> 3, col = ch & 7;
+        int64_t gcol = n0 + row;
+        gcol = gcol < N ? gcol : N - 1;
+        b_src[i] = b + gcol * K + col * 16;
+        b_dst[i] = T::A_BYTES + row * kBlock + ((col ^ (row & 7)) << 4);
+    }
+    const float* sa_src = nullptr;
+    if (tid < T::BM) {
+        int64_t grow = m0 + tid;
+        grow = grow < m_end ? grow : m_end - 1;
+        sa_src = as + grow * KB;
+    }
+    int64_t nblk = (n0 + wn0) >> 7;
+    nblk = nblk < NB ? nblk : NB - 1;
+    const float* sb_src = bs + nblk * KB;
+
+    v4f acc[T::TM][T::TN];
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    uint4 ra[T::A_LOADS], rb[T::B_LOADS];
+    float rsa = 0.f;
+
+    auto load_regs = [&](int64_t kb) {
+#pragma unroll
+        for (int i = 0; i < T::A_LOADS; ++i) ra[i] = *(const uint4*)(a_src[i] + kb * kBlock);
+#pragma unroll
+        for (int i = 0; i < T::B_LOADS; ++i) rb[i] = *(const uint4*)(b_src[i] + kb * kBlock);
+        if (tid < T::BM) rsa = sa_src[kb];
+    };
+    auto store_lds = [&](int stage) {
+        uint8_t* base = lds + stage * T::STAGE;
+#pragma unroll
+        for (int i = 0; i < T::A_LOADS; ++i) *(uint4*)(base + a_dst[i]) = ra[i];
+#pragma unroll
+        for (int i = 0; i < T::B_LOADS; ++i) *(uint4*)(base + b_dst[i]) = rb[i];
+        if (tid < T::BM) ((float*)(base + T::A_BYTES + T::B_BYTES))[tid] = rsa;
+    };
+
+    load_regs(0);
+    store_lds(0);
+    __syncthreads();
+
+    const int lr = lane & 15;
+    const int lk = (lane >> 4) * 2;               // first of this lane's two 16-byte chunks
+    const int off0 = ((lk ^ (lr & 7)) << 4);
+    const int off1 = (((lk + 1) ^ (lr & 7)) << 4);
+    const int srow = 4 * (lane >> 4);
+
+    for (int64_t kb = 0; kb < KB; ++kb) {
+        const int cur = (int)(kb & 1);
+        const bool more = kb + 1 < KB;
+        if (more) load_regs(kb + 1);
+
+        const uint8_t* As = lds + cur * T::STAGE;
+        const uint8_t* Bs = As + T::A_BYTES;
+        const float* Ss = (const float*)(Bs + T::B_BYTES);
+        v8i fa[T::TM], fb[T::TN];
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i) {
+            const uint8_t* r = As + (wm0 + 16 * i + lr) * kBlock;
+            fa[i] = frag_from(*(const uint4*)(r + off0), *(const uint4*)(r + off1));
+        }
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j) {
+            const uint8_t* r = Bs + (wn0 + 16 * j + lr) * kBlock;
+            fb[j] = frag_from(*(const uint4*)(r + off0), *(const uint4*)(r + off1));
+        }
+        const float sbv = sb_src[kb];
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i) {
+            const v4f sa4 = *(const v4f*)(Ss + wm0 + 16 * i + srow);
+            const v4f sc = sa4 * sbv;
+#pragma unroll
+            for (int j = 0; j < T::TN; ++j) {
+                const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    fa[i], fb[j], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                acc[i][j] = p * sc + acc[i][j];
+            }
+        }
+        if (more) store_lds(cur ^ 1);
+        __syncthreads();
+    }
+
+    // epilogue: fp32 -> bf16 (nearest even), masked to the valid rows / columns
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j) {
+            const int64_t col = n0 + wn0 + 16 * j + lr;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t row = m0 + wm0 + 16 * i + srow + r;
+                if (row < m_end && col < N) c[row * N + col] = (uint16_t)bf16_rne_bits(acc[i][j][r]);
+            }
+        }
+    }
+}
+
+template <class T>
+__global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t* __restrict__ a,
+                                                      const float* __restrict__ as,
+                                                      const uint8_t* __restrict__ b,
+                                                      const float* __restrict__ bs,
+                                                      uint16_t* __restrict__ c, int64_t M,
+                                                      int64_t N, int64_t K, int mt, int nt) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * T::STAGE];
+    // bands of 8 M-tiles: within a band, consecutive workgroups walk down the
+    // band's M-tiles for one N-tile, then move to the next N-tile.
+    constexpr int GM = 8;
+    const int id = blockIdx.x;
+    const int band = id / (GM * nt);
+    const int first_m = band * GM;
+    const int rows_in_band = (mt - first_m) < GM ? (mt - first_m) : GM;
+    const int in_band = id - band * GM * nt;
+    const int tm = first_m + in_band % rows_in_band;
+    const int tn = in_band / rows_in_band;
+    gemm_tile<T>(a, as, b, bs, c, (int64_t)tm * T::BM, M, (int64_t)tn * T::BN, N, K, lds);
+}
+
+// Persistent grouped kernel: workgroups stride over the tiles of all groups.
+// Group g owns ceil(rows_g / BM) * nt tiles, M-tiles fastest.
+template <class T>
+__global__ __launch_bounds__(256, 2) void gemm_grouped_kernel(const uint8_t* __restrict__ a,
+                                                              const float* __restrict__ as,
+                                                              const uint8_t* __restrict__ b,
+                                                              const float* __restrict__ bs,
+                                                              uint16_t* __restrict__ c,
+                                                              const int32_t* __restrict__ off,
+                                                              int G, int64_t N, int64_t K,
+                                                              int nt) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * T::STAGE];
+    const int64_t KB = K / kBlock;
+    const int64_t NB = (N + kBlock - 1) / kBlock;
+    int64_t total = 0;
+    for (int g = 0; g < G; ++g) {
+        const int64_t rows = (int64_t)off[g + 1] - off[g];
+        total += ((rows + T::BM - 1) / T::BM) * nt;
+    }
+    for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
+        int64_t start = 0;
+        int g = 0;
+        int64_t mtiles = 0;
+        for (; g < G; ++g) {
+            const int64_t rows = (int64_t)off[g + 1] - off[g];
+            mtiles = (rows + T::BM - 1) / T::BM;
+            if (t < start + mtiles * nt) break;
+            start += mtiles * nt;
+        }
+        const int64_t local = t - start;
+        const int64_t tm = local % mtiles;
+        const int64_t tn = local / mtiles;
+        gemm_tile<T>(a, as, b + (int64_t)g * N * K, bs + (int64_t)g * NB * KB, c,
+                     (int64_t)off[g] + tm * T::BM, (int64_t)off[g + 1], tn * T::BN, N, K, lds);
+    }
+}
+
+using TileLarge = Tile<128, 128>;
+using TileSmall = Tile<64, 64>;
+
+size_t gemm_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
+
+hipError_t launch_gemm(const void* a, const float* as, const void* b, const float* bs, void* c,
+                       int64_t M, int64_t N, int64_t K, void* /*workspace*/,
+                       size_t /*workspace_bytes*/, hipStream_t stream) {
+    if (M <= 64) {
+        using T = TileSmall;
+        const int mt = (int)((M + T::BM - 1) / T::BM), nt = (int)((N + T::BN - 1) / T::BN);
+        hipLaunchKernelGGL(gemm_kernel<T>, dim3(mt * nt), dim3(256), 0, stream, (const uint8_t*)a,
+                           as, (const uint8_t*)b, bs, (uint16_t*)c, M, N, K, mt, nt);
+    } else {
+        using T = TileLarge;
+        const int mt = (int)((M + T::BM - 1) / T::BM), nt = (int)((N + T::BN - 1) / T::BN);
+        hipLaunchKernelGGL(gemm_kernel<T>, dim3(mt * nt), dim3(256), 0, stream, (const uint8_t*)a,
+                           as, (const uint8_t*)b, bs, (uint16_t*)c, M, N, K, mt, nt);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_grouped(const void* a, const float* as, const void* b, const float* bs,
+                               void* c, const int32_t* off, int32_t G, int64_t total_M,
+                               int64_t N, int64_t K, hipStream_t stream) {
+    using T = TileLarge;
+    const int nt = (int)((N + T::BN - 1) / T::BN);
+    const int64_t max_tiles = ((total_M + T::BM - 1) / T::BM + G) * (int64_t)nt;
+    const int64_t cap = (int64_t)device_cu_count() * 2;
+    const int grid = (int)(max_tiles < cap ? max_tiles : cap);
+    hipLaunchKernelGGL(gemm_grouped_kernel<T>, dim3(grid), dim3(256), 0, stream,
+                       (const uint8_t*)a, as, (const uint8_t*)b, bs, (uint16_t*)c, off, (int)G, N,
+                       K, nt);
+    return hipGetLastError();
+}
+
+}  // namespace bfp8

@@ -1,0 +1,29 @@
+// internal.hpp - launchers behind the C ABI (include/bfp8.h).  Each launcher
+// assumes its arguments were validated by the ABI layer and only enqueues
+// kernels on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bfp8 {
+
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
+hipError_t launch_act_quant(const void* x, void* q, float* s, int64_t M, int64_t K,
+                            hipStream_t stream);
+hipError_t launch_encode_range(uint32_t first, int64_t count, void* out, int variant,
+                               hipStream_t stream);
+hipError_t launch_weight_dequant(const void* w, const float* s, void* out, int64_t N, int64_t K,
+                                 hipStream_t stream);
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm(const void* a, const float* as, const void* b, const float* bs, void* c,
+                       int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+hipError_t launch_gemm_grouped(const void* a, const float* as, const void* b, const float* bs,
+                               void* c, const int32_t* off, int32_t G, int64_t total_M,
+                               int64_t N, int64_t K, hipStream_t stream);
+
+}  // namespace bfp8

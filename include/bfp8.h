@@ -1,0 +1,148 @@
+/*
+ * bfp8.h - C ABI of the block-scaled FP8 linear path on AMD Instinct MI355X (gfx950).
+ *
+ * The path is the FP8 branch of DeepSeek-V3's quantization-aware linear():
+ * activations are quantized to e4m3 with one fp32 scale per 128-element block
+ * (act_quant), weights are e4m3 with one fp32 scale per 128x128 block, the
+ * GEMM multiplies the scaled blocks and accumulates in fp32 (fp8_gemm), and
+ * weights can be expanded to bf16 for an ordinary BF16 matmul
+ * (weight_dequant).  Sources:
+ *   [DF]  "Data flow - deepseek-ai/DeepSeek-V3" (codevetter), bullet
+ *         "FP8 quantization data flow".
+ *   [BT]  "Behavior traces - deepseek-ai/DeepSeek-V3" (codevetter), bullets
+ *         "MoE trace" and "fp8->bf16 trace".
+ *   [PY]  pyshine "DeepSeek-V3" tour, section "The Three Ideas That Make V3
+ *         Fast", paragraph "FP8 with per-block scales", and section "Honest
+ *         Limits" (Python expert loop vs a fused grouped GEMM).
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a DEVICE pointer to row-major, densely packed
+ *     memory owned by the caller.  The library never allocates, frees or
+ *     keeps a pointer after the call returns.
+ *   - e4m3 means the OCP FP8 E4M3 format (torch.float8_e4m3fn): bias 7, no
+ *     infinities, largest finite value 448 (code 0x7E); one byte per element.
+ *   - bf16 is the upper half of an IEEE binary32; two bytes per element.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is only enqueued; no call synchronizes.  Faults inside a kernel
+ *     surface at the caller's next synchronization, as with any HIP launch.
+ *   - Arguments are validated on the host BEFORE any HIP call; a rejected call
+ *     launches nothing and returns the status code.  A zero-sized problem
+ *     (M == 0, N == 0, total_M == 0) returns BFP8_OK without a launch.
+ *   - Outputs must not alias inputs.  Calls on different streams that write
+ *     different outputs may overlap; the library keeps no state between calls.
+ *   - Block edge: BFP8_BLOCK = 128 everywhere (every call site on the pages uses
+ *     128-element activation blocks and a 128x128 weight-scale grid).
+ */
+#ifndef BFP8_H
+#define BFP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BFP8_BLOCK 128
+#define BFP8_VERSION 1
+
+typedef enum bfp8_status {
+    BFP8_OK = 0,
+    BFP8_ERR_NULL = 1,      /* a required pointer is NULL */
+    BFP8_ERR_SHAPE = 2,     /* a size is negative, or K is not a multiple of 128 where required */
+    BFP8_ERR_ALIGN = 3,     /* a pointer is not aligned as documented */
+    BFP8_ERR_WORKSPACE = 4, /* workspace given but smaller than bfp8_gemm_workspace_size() */
+    BFP8_ERR_GROUPS = 5,    /* G < 1 (grouped GEMM) */
+    BFP8_ERR_HIP = 6,       /* the HIP runtime reported an error at launch */
+    BFP8_ERR_ARG = 7        /* any other invalid argument */
+} bfp8_status;
+
+/* act_quant ([DF] FP8 bullet; [PY] "FP8 with per-block scales").
+ * For each row m and each 128-element block kb of the last dimension:
+ *     amax  = max |x[m, 128kb + j]|                       (exact, on bf16 values)
+ *     s     = max(amax, 1e-4f) / 448                      (fp32, correctly rounded)
+ *     q[..] = e4m3_rne_saturating( x[..] / s )            (fp32 quotient, correctly rounded)
+ *     scales[m, kb] = s
+ * The floor 1e-4 on amax is this library's reading of "clamping each tile's
+ * max" (it only matters for blocks whose max |x| is below 1e-4).
+ *   x_bf16 : bf16 [M, K], 16-byte aligned
+ *   q_e4m3 : e4m3 [M, K] output, 16-byte aligned
+ *   scales : fp32 [M, K/128] output, 4-byte aligned
+ * Errors: BFP8_ERR_SHAPE if M < 0, K <= 0 or K % 128 != 0; BFP8_ERR_NULL if a
+ * pointer is NULL while M > 0; BFP8_ERR_ALIGN on misalignment. */
+int bfp8_act_quant(const void* x_bf16, void* q_e4m3, float* scales,
+                   int64_t M, int64_t K, void* stream);
+
+/* weight_dequant ([PY] "FP8 with per-block scales": dequantize then an
+ * ordinary BF16 matmul; [BT] "fp8->bf16 trace": each 1-byte tensor is
+ * dequantized with its scale, which is a multiplier).
+ *     out[n, k] = bf16_rne( fp32( e4m3_value(w[n, k]) * s[n/128, k/128] ) )
+ *   w_e4m3  : e4m3 [N, K]
+ *   s       : fp32 [ceil(N/128), ceil(K/128)]; partial edge blocks allowed
+ *   out_bf16: bf16 [N, K] output
+ * Any N, K >= 0.  A vectorized kernel is used when K % 16 == 0 and w/out are
+ * 16-byte aligned, a scalar one otherwise.
+ * Errors: BFP8_ERR_SHAPE if N < 0 or K < 0; BFP8_ERR_NULL for a NULL pointer
+ * when N*K > 0; BFP8_ERR_ALIGN if out is not 2-byte or s not 4-byte aligned. */
+int bfp8_weight_dequant(const void* w_e4m3, const float* s, void* out_bf16,
+                        int64_t N, int64_t K, void* stream);
+
+/* fp8_gemm ([DF] "fp8_gemm multiplies scaled blocks accumulating in fp32";
+ * [PY] products of FP8 operands rescaled by their block scales).
+ * C = A * B^T with B a Linear weight (out_features x in_features):
+ *     c[m, n] = bf16_rne( sum_kb ( sum_{k in kb} a[m,k] * b[n,k] ) * a_s[m,kb] * b_s[n/128,kb] )
+ * where each inner 128-term block product runs on fp8 MFMA into a fresh fp32
+ * accumulator and is folded into the running fp32 sum with its two scales.
+ *   a   : e4m3 [M, K], 16-byte aligned         a_s : fp32 [M, K/128]
+ *   b   : e4m3 [N, K], 16-byte aligned         b_s : fp32 [ceil(N/128), K/128]
+ *   c_bf16 : bf16 [M, N] output, 4-byte aligned (N odd: 2-byte)
+ *   workspace : optional fp32 scratch for split-K on skinny problems; NULL
+ *     disables split-K.  If non-NULL it must hold at least
+ *     bfp8_gemm_workspace_size(M, N, K) bytes and be 16-byte aligned.
+ * Errors: BFP8_ERR_SHAPE if M, N < 0 or K <= 0 or K % 128 != 0; BFP8_ERR_NULL;
+ * BFP8_ERR_ALIGN; BFP8_ERR_WORKSPACE if workspace_bytes is too small. */
+int bfp8_gemm(const void* a, const float* a_s, const void* b, const float* b_s,
+              void* c_bf16, int64_t M, int64_t N, int64_t K,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of fp32 workspace bfp8_gemm would use for split-K at this shape
+ * (0 when the shape does not use split-K).  Pure host function. */
+size_t bfp8_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
+
+/* Grouped fp8_gemm over one GPU's share of routed experts ([BT] "MoE trace":
+ * each local expert with tokens runs expert(x[idx]); [PY] "Honest Limits":
+ * a fused grouped GEMM replaces the per-expert Python loop).
+ * Rows [off[g], off[g+1]) of a belong to expert g and are multiplied by its
+ * weight b[g]:
+ *     c[r, n] = bf16_rne( sum_kb P_kb[r, n] * a_s[r, kb] * b_s[g, n/128, kb] )
+ *   a     : e4m3 [total_M, K] rows sorted by group       a_s : fp32 [total_M, K/128]
+ *   b     : e4m3 [G, N, K]                               b_s : fp32 [G, ceil(N/128), K/128]
+ *   c_bf16: bf16 [total_M, N] output
+ *   group_offsets : DEVICE int32 [G+1]; must satisfy off[0] = 0,
+ *     off[g] <= off[g+1], off[G] = total_M.  Empty groups are allowed.  The
+ *     kernel trusts the offsets (they live on the device); rows outside every
+ *     group are never written.
+ * Errors: as bfp8_gemm, plus BFP8_ERR_GROUPS if G < 1. */
+int bfp8_gemm_grouped(const void* a, const float* a_s, const void* b, const float* b_s,
+                      void* c_bf16, const int32_t* group_offsets, int32_t G,
+                      int64_t total_M, int64_t N, int64_t K, void* stream);
+
+/* Test helper: encodes the 2^32 float32 bit patterns first .. first+count-1
+ * to e4m3 codes with the same device routine act_quant uses (variant 0), or
+ * with the alternative routine (variant 1), into out[count] (device).
+ * Lets a test compare the device encoder with the oracle on every input.
+ * Errors: BFP8_ERR_NULL, BFP8_ERR_SHAPE (count < 0 or first+count > 2^32),
+ * BFP8_ERR_ARG (unknown variant). */
+int bfp8_e4m3_encode_range(uint32_t first, int64_t count, void* out, int variant, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* bfp8_status_string(int status);
+
+/* BFP8_VERSION of the built library. */
+int bfp8_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BFP8_H */

@@ -1,0 +1,148 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point that
+include/bfp8.h declares, and rejects bad arguments with the documented status code
+before making any HIP call (so no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_scaled_fp8_04_amd as bfp8
+from block_scaled_fp8_04_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bfp8.h")
+
+P = ctypes.c_void_p
+FAKE = ctypes.c_void_p(0x10000)           # aligned, never dereferenced: every call below is rejected
+ODD = ctypes.c_void_p(0x10001)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(bfp8_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIBRARY):
+        pytest.fail("libbfp8.so is not built (run __graft_entry__.build())")
+    return _lib.library()
+
+
+def test_header_declares_the_path():
+    names = declared_functions()
+    for n in ("bfp8_act_quant", "bfp8_weight_dequant", "bfp8_gemm", "bfp8_gemm_grouped",
+              "bfp8_gemm_workspace_size", "bfp8_status_string", "bfp8_version"):
+        assert n in names
+    assert set(names) == set(_lib.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in bfp8.h but not exported"
+
+
+def test_version_and_status_strings(lib):
+    assert bfp8.bfp8_version() == 1
+    for code in range(8):
+        assert bfp8.bfp8_status_string(code)
+    assert bfp8.bfp8_status_string(0) == "ok"
+    assert "unknown" in bfp8.bfp8_status_string(99)
+
+
+def test_act_quant_validation(lib):
+    f = lib.bfp8_act_quant
+    assert f(FAKE, FAKE, FAKE, 4, 100, None) == _lib.BFP8_ERR_SHAPE     # K % 128
+    assert f(FAKE, FAKE, FAKE, 4, 0, None) == _lib.BFP8_ERR_SHAPE
+    assert f(FAKE, FAKE, FAKE, -1, 128, None) == _lib.BFP8_ERR_SHAPE
+    assert f(None, FAKE, FAKE, 4, 128, None) == _lib.BFP8_ERR_NULL
+    assert f(FAKE, None, FAKE, 4, 128, None) == _lib.BFP8_ERR_NULL
+    assert f(FAKE, FAKE, None, 4, 128, None) == _lib.BFP8_ERR_NULL
+    assert f(ODD, FAKE, FAKE, 4, 128, None) == _lib.BFP8_ERR_ALIGN
+    assert f(FAKE, ctypes.c_void_p(0x10008), FAKE, 4, 128, None) == _lib.BFP8_ERR_ALIGN
+    assert f(FAKE, FAKE, ctypes.c_void_p(0x10002), 4, 128, None) == _lib.BFP8_ERR_ALIGN
+    assert f(None, None, None, 0, 128, None) == _lib.BFP8_OK               # empty: no launch
+
+
+def test_weight_dequant_validation(lib):
+    f = lib.bfp8_weight_dequant
+    assert f(FAKE, FAKE, FAKE, -1, 128, None) == _lib.BFP8_ERR_SHAPE
+    assert f(FAKE, FAKE, FAKE, 128, -5, None) == _lib.BFP8_ERR_SHAPE
+    assert f(None, FAKE, FAKE, 128, 128, None) == _lib.BFP8_ERR_NULL
+    assert f(FAKE, None, FAKE, 128, 128, None) == _lib.BFP8_ERR_NULL
+    assert f(FAKE, FAKE, None, 128, 128, None) == _lib.BFP8_ERR_NULL
+    assert f(FAKE, FAKE, ODD, 128, 128, None) == _lib.BFP8_ERR_ALIGN
+    assert f(FAKE, ctypes.c_void_p(0x10002), FAKE, 128, 128, None) == _lib.BFP8_ERR_ALIGN
+    assert f(None, None, None, 0, 128, None) == _lib.BFP8_OK
+    assert f(None, None, None, 128, 0, None) == _lib.BFP8_OK
+
+
+def test_gemm_validation(lib):
+    f = lib.bfp8_gemm
+    ok = dict(M=64, N=64, K=256)
+
+    def call(a=FAKE, a_s=FAKE, b=FAKE, b_s=FAKE, c=FAKE, M=64, N=64, K=256, ws=None, wsb=0):
+        return f(a, a_s, b, b_s, c, M, N, K, ws, wsb, None)
+
+    assert call(K=200) == _lib.BFP8_ERR_SHAPE
+    assert call(K=0) == _lib.BFP8_ERR_SHAPE
+    assert call(M=-1) == _lib.BFP8_ERR_SHAPE
+    assert call(N=-1) == _lib.BFP8_ERR_SHAPE
+    for name in ("a", "a_s", "b", "b_s", "c"):
+        assert call(**{name: None}) == _lib.BFP8_ERR_NULL, name
+    assert call(a=ODD) == _lib.BFP8_ERR_ALIGN
+    assert call(b=ctypes.c_void_p(0x10004)) == _lib.BFP8_ERR_ALIGN
+    assert call(a_s=ctypes.c_void_p(0x10002)) == _lib.BFP8_ERR_ALIGN
+    assert call(c=ODD) == _lib.BFP8_ERR_ALIGN
+    assert call(ws=ODD, wsb=1 << 20) == _lib.BFP8_ERR_ALIGN
+    assert call(a=None, M=0) == _lib.BFP8_OK
+    assert call(a=None, N=0) == _lib.BFP8_OK
+    del ok
+
+
+def test_gemm_workspace_contract(lib):
+    for (M, N, K) in ((64, 1536, 7168), (16, 256, 256), (8192, 18432, 7168), (1, 1, 128)):
+        need = bfp8.bfp8_gemm_workspace_size(M, N, K)
+        assert need >= 0 and need % 16 == 0
+        if need > 0:
+            rc = lib.bfp8_gemm(FAKE, FAKE, FAKE, FAKE, FAKE, M, N, K, FAKE, need - 16, None)
+            assert rc == _lib.BFP8_ERR_WORKSPACE
+    assert bfp8.bfp8_gemm_workspace_size(0, 5, 128) == 0
+    assert bfp8.bfp8_gemm_workspace_size(5, 5, 100) == 0
+
+
+def test_gemm_grouped_validation(lib):
+    f = lib.bfp8_gemm_grouped
+
+    def call(a=FAKE, a_s=FAKE, b=FAKE, b_s=FAKE, c=FAKE, off=FAKE, G=4, T=100, N=256, K=256):
+        return f(a, a_s, b, b_s, c, off, G, T, N, K, None)
+
+    assert call(K=100) == _lib.BFP8_ERR_SHAPE
+    assert call(T=-1) == _lib.BFP8_ERR_SHAPE
+    assert call(G=0) == _lib.BFP8_ERR_GROUPS
+    assert call(G=-3) == _lib.BFP8_ERR_GROUPS
+    for name in ("a", "a_s", "b", "b_s", "c", "off"):
+        assert call(**{name: None}) == _lib.BFP8_ERR_NULL, name
+    assert call(off=ctypes.c_void_p(0x10002)) == _lib.BFP8_ERR_ALIGN
+    assert call(a=ODD) == _lib.BFP8_ERR_ALIGN
+    assert call(a=None, T=0) == _lib.BFP8_OK
+
+
+def test_encode_range_validation(lib):
+    f = lib.bfp8_e4m3_encode_range
+    assert f(0, -1, FAKE, 0, None) == _lib.BFP8_ERR_SHAPE
+    assert f(0xFFFFFFFF, 2, FAKE, 0, None) == _lib.BFP8_ERR_SHAPE
+    assert f(0, 16, FAKE, 2, None) == _lib.BFP8_ERR_ARG
+    assert f(0, 16, None, 0, None) == _lib.BFP8_ERR_NULL
+    assert f(0, 0, None, 0, None) == _lib.BFP8_OK
+
+
+def test_python_binding_rejects_bad_tensors():
+    import torch
+    x = torch.zeros(4, 256, dtype=torch.bfloat16)            # CPU tensor: refused before any call
+    with pytest.raises(ValueError):
+        bfp8.bfp8_act_quant(x, torch.zeros(4, 256, dtype=torch.uint8),
+                            torch.zeros(4, 2, dtype=torch.float32))
+    with pytest.raises(TypeError):
+        bfp8.bfp8_gemm(torch.zeros(4, 256, dtype=torch.int16), None, None, None, None)
