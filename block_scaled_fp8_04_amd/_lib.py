@@ -27,7 +27,8 @@ BFP8_ERR_HIP = 6
 BFP8_ERR_ARG = 7
 
 EXPORTS = ("bfp8_act_quant", "bfp8_weight_dequant", "bfp8_gemm", "bfp8_gemm_workspace_size",
-           "bfp8_gemm_grouped", "bfp8_e4m3_encode_range", "bfp8_status_string", "bfp8_version")
+           "bfp8_gemm_grouped", "bfp8_e4m3_encode_range", "bfp8_gemm_kernel_name",
+           "bfp8_status_string", "bfp8_version")
 
 _lib = None
 
@@ -60,6 +61,8 @@ def library():
     lib.bfp8_gemm_grouped.restype = ctypes.c_int
     lib.bfp8_e4m3_encode_range.argtypes = [ctypes.c_uint32, I64, P, ctypes.c_int, P]
     lib.bfp8_e4m3_encode_range.restype = ctypes.c_int
+    lib.bfp8_gemm_kernel_name.argtypes = [I64, I64, I64]
+    lib.bfp8_gemm_kernel_name.restype = ctypes.c_char_p
     lib.bfp8_status_string.argtypes = [ctypes.c_int]
     lib.bfp8_status_string.restype = ctypes.c_char_p
     lib.bfp8_version.argtypes = []
@@ -118,6 +121,11 @@ def bfp8_version() -> int:
 
 def bfp8_status_string(status: int) -> str:
     return status_string(status)
+
+
+def bfp8_gemm_kernel_name(M, N, K) -> str:
+    """Name of the tile configuration bfp8_gemm uses for this shape on the current device."""
+    return library().bfp8_gemm_kernel_name(int(M), int(N), int(K)).decode()
 
 
 def bfp8_act_quant(x, q, scales, stream=None):

@@ -106,6 +106,11 @@ int bfp8_gemm_grouped(const void* a, const float* a_s, const void* b, const floa
                                               N, K, (hipStream_t)stream));
 }
 
+const char* bfp8_gemm_kernel_name(int64_t M, int64_t N, int64_t K) {
+    if (M <= 0 || N <= 0 || K <= 0 || K % BFP8_BLOCK != 0) return "none";
+    return bfp8::gemm_config_name(bfp8::gemm_config(M, N, K));
+}
+
 int bfp8_e4m3_encode_range(uint32_t first, int64_t count, void* out, int variant, void* stream) {
     if (count < 0 || (uint64_t)first + (uint64_t)count > (uint64_t)1 << 32) return BFP8_ERR_SHAPE;
     if (variant != 0 && variant != 1) return BFP8_ERR_ARG;

@@ -248,24 +248,269 @@ __global__ __launch_bounds__(256, 2) void gemm_grouped_kernel(const uint8_t* __r
     }
 }
 
+// ---------------------------------------------------------------------------
+// Large-tile kernel: direct global -> LDS loads, 8 waves.
+//
+// WG tile BM x BN with WAVES_M x WAVES_N waves (wave tile WM x WN).  The A and
+// B tiles of one 128-wide K block are fetched with global_load_lds_dwordx4:
+// one wave instruction fills 1 KB of LDS (eight 128-byte rows), lane l writing
+// bytes [16 l, 16 l + 16).  The XOR swizzle is applied on the source side:
+// lane l of an instruction covering rows r0..r0+7 fetches logical chunk
+// (l & 7) ^ ((l >> 3) & 7) of row r0 + (l >> 3), so LDS chunk c of row r holds
+// logical chunk c ^ (r & 7), exactly the layout the fragment reads expect.
+// The row scales of the K block arrive the same way (4 bytes per lane).
+// Loads for K block kb+1 are issued before the MFMAs of block kb; one
+// s_waitcnt + barrier per K block closes the step.
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
+struct BigTile {
+    static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+    static constexpr int WAVES = WAVES_M * WAVES_N, THREADS = 64 * WAVES;
+    static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+    static constexpr int TM = WM / 16, TN = WN / 16;
+    static constexpr int A_BYTES = BM * kBlock, B_BYTES = BN * kBlock;
+    static constexpr int STAGE = A_BYTES + B_BYTES + BM * 4;
+    static constexpr int A_INSTR = BM / 8 / WAVES;      // 1 KB instructions per wave for A
+    static constexpr int B_INSTR = BN / 8 / WAVES;
+    static constexpr int S_INSTR = (BM + 63) / 64;      // 256 B scale instructions (waves 0..)
+    static_assert(BM % (8 * WAVES) == 0 && BN % (8 * WAVES) == 0, "tile rows must split over waves");
+    static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns must share one scale block");
+    static_assert(S_INSTR <= WAVES, "one scale instruction per wave at most");
+    static_assert(BM % 64 == 0, "scale rows are fetched 64 at a time");
+};
+
+typedef __attribute__((address_space(3))) void* lds_void_t;
+typedef const __attribute__((address_space(1))) void* gbl_void_t;
+
+__device__ __forceinline__ void load_lds16(const void* src, void* lds_dst) {
+    __builtin_amdgcn_global_load_lds((gbl_void_t)src, (lds_void_t)lds_dst, 16, 0, 0);
+}
+__device__ __forceinline__ void load_lds4(const void* src, void* lds_dst) {
+    __builtin_amdgcn_global_load_lds((gbl_void_t)src, (lds_void_t)lds_dst, 4, 0, 0);
+}
+
+template <class T>
+__device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
+                                              const float* __restrict__ as,
+                                              const uint8_t* __restrict__ b,
+                                              const float* __restrict__ bs,
+                                              uint16_t* __restrict__ c, int64_t m0, int64_t m_end,
+                                              int64_t n0, int64_t N, int64_t K, uint8_t* lds) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm0 = (wave / T::WAVES_N) * T::WM;
+    const int wn0 = (wave % T::WAVES_N) * T::WN;
+    const int64_t KB = K / kBlock;
+    const int64_t NB = (N + kBlock - 1) / kBlock;
+
+    // per-lane sources of the direct loads (byte offset of K block 0)
+    const int lrow = lane >> 3;                                  // row within an 8-row group
+    const int lchunk = (lane & 7) ^ (lrow & 7);                  // logical 16-byte chunk fetched
+    const uint8_t* a_src[T::A_INSTR];
+    const uint8_t* b_src[T::B_INSTR];
+#pragma unroll
+    for (int i = 0; i < T::A_INSTR; ++i) {
+        const int row = (wave * T::A_INSTR + i) * 8 + lrow;
+        int64_t grow = m0 + row;
+        grow = grow < m_end ? grow : m_end - 1;
+        a_src[i] = a + grow * K + lchunk * 16;
+    }
+#pragma unroll
+    for (int i = 0; i < T::B_INSTR; ++i) {
+        const int row = (wave * T::B_INSTR + i) * 8 + lrow;
+        int64_t gcol = n0 + row;
+        gcol = gcol < N ? gcol : N - 1;
+        b_src[i] = b + gcol * K + lchunk * 16;
+    }
+    const float* s_src = as;
+    if (wave < T::S_INSTR) {
+        int64_t grow = m0 + wave * 64 + lane;
+        grow = grow < m_end ? grow : m_end - 1;
+        s_src = as + grow * KB;
+    }
+    int64_t nblk = (n0 + wn0) >> 7;
+    nblk = nblk < NB ? nblk : NB - 1;
+    const float* sb_src = bs + nblk * KB;
+
+    auto issue = [&](int64_t kb, int stage) {
+        uint8_t* base = lds + stage * T::STAGE;
+#pragma unroll
+        for (int i = 0; i < T::A_INSTR; ++i)
+            load_lds16(a_src[i] + kb * kBlock, base + (wave * T::A_INSTR + i) * 1024);
+#pragma unroll
+        for (int i = 0; i < T::B_INSTR; ++i)
+            load_lds16(b_src[i] + kb * kBlock, base + T::A_BYTES + (wave * T::B_INSTR + i) * 1024);
+        if (wave < T::S_INSTR)
+            load_lds4(s_src + kb, base + T::A_BYTES + T::B_BYTES + wave * 256);
+    };
+
+    v4f acc[T::TM][T::TN];
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    issue(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    const int lr = lane & 15;
+    const int lk = (lane >> 4) * 2;
+    const int off0 = ((lk ^ (lr & 7)) << 4);
+    const int off1 = (((lk + 1) ^ (lr & 7)) << 4);
+    const int srow = 4 * (lane >> 4);
+
+    for (int64_t kb = 0; kb < KB; ++kb) {
+        const int cur = (int)(kb & 1);
+        if (kb + 1 < KB) issue(kb + 1, cur ^ 1);
+
+        const uint8_t* As = lds + cur * T::STAGE;
+        const uint8_t* Bs = As + T::A_BYTES;
+        const float* Ss = (const float*)(Bs + T::B_BYTES);
+        v8i fb[T::TN];
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j) {
+            const uint8_t* r = Bs + (wn0 + 16 * j + lr) * kBlock;
+            fb[j] = frag_from(*(const uint4*)(r + off0), *(const uint4*)(r + off1));
+        }
+        const float sbv = sb_src[kb];
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i) {
+            const uint8_t* r = As + (wm0 + 16 * i + lr) * kBlock;
+            const v8i fa = frag_from(*(const uint4*)(r + off0), *(const uint4*)(r + off1));
+            const v4f sc = *(const v4f*)(Ss + wm0 + 16 * i + srow) * sbv;
+#pragma unroll
+            for (int j = 0; j < T::TN; ++j) {
+                const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    fa, fb[j], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                acc[i][j] = p * sc + acc[i][j];
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+
+    const bool interior = (m0 + T::BM <= m_end) && (n0 + T::BN <= N);
+    uint16_t* cbase = c + (m0 + wm0 + srow) * N + n0 + wn0 + lr;
+    if (interior) {
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+            for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    cbase[(16 * i + r) * N + 16 * j] = (uint16_t)bf16_rne_bits(acc[i][j][r]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i) {
+#pragma unroll
+            for (int j = 0; j < T::TN; ++j) {
+                const int64_t col = n0 + wn0 + 16 * j + lr;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t row = m0 + wm0 + 16 * i + srow + r;
+                    if (row < m_end && col < N)
+                        c[row * N + col] = (uint16_t)bf16_rne_bits(acc[i][j][r]);
+                }
+            }
+        }
+    }
+}
+
+// Maps a workgroup id to a tile so that the workgroups resident on one XCD
+// (ids are dealt round-robin over the 8 XCDs) work on a compact block of
+// tiles: ids are first regrouped XCD by XCD, then walked in bands of GM
+// M-tiles (M fastest inside a band).
+__device__ __forceinline__ void tile_of(int id, int nwg, int mt, int nt, int& tm, int& tn) {
+    constexpr int XCDS = 8, GM = 4;
+    const int xcd = id % XCDS, local = id / XCDS;
+    const int per = nwg / XCDS, rem = nwg % XCDS;
+    const int lin = xcd * per + (xcd < rem ? xcd : rem) + local;
+    const int band = lin / (GM * nt);
+    const int first_m = band * GM;
+    const int rows_in_band = (mt - first_m) < GM ? (mt - first_m) : GM;
+    const int in_band = lin - band * GM * nt;
+    tm = first_m + in_band % rows_in_band;
+    tn = in_band / rows_in_band;
+}
+
+template <class T>
+__global__ __launch_bounds__(T::THREADS, 1) void gemm_big_kernel(const uint8_t* __restrict__ a,
+                                                                 const float* __restrict__ as,
+                                                                 const uint8_t* __restrict__ b,
+                                                                 const float* __restrict__ bs,
+                                                                 uint16_t* __restrict__ c,
+                                                                 int64_t M, int64_t N, int64_t K,
+                                                                 int mt, int nt) {
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * T::STAGE];
+    int tm, tn;
+    tile_of(blockIdx.x, gridDim.x, mt, nt, tm, tn);
+    gemm_tile_big<T>(a, as, b, bs, c, (int64_t)tm * T::BM, M, (int64_t)tn * T::BN, N, K, lds);
+}
+
 using TileLarge = Tile<128, 128>;
 using TileSmall = Tile<64, 64>;
 
 size_t gemm_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
 
+using BigSquare = BigTile<256, 256, 2, 4>;   // 8 waves of 128 x 64
+using BigWide = BigTile<256, 128, 4, 2>;     // 8 waves of 64 x 64
+
+template <class T>
+static void launch_big(const void* a, const float* as, const void* b, const float* bs, void* c,
+                       int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+    const int mt = (int)((M + T::BM - 1) / T::BM), nt = (int)((N + T::BN - 1) / T::BN);
+    hipLaunchKernelGGL(gemm_big_kernel<T>, dim3(mt * nt), dim3(T::THREADS), 0, stream,
+                       (const uint8_t*)a, as, (const uint8_t*)b, bs, (uint16_t*)c, M, N, K, mt, nt);
+}
+
+// Which kernel configuration serves an M x N x K problem (the tile table).
+GemmConfig gemm_config(int64_t M, int64_t N, int64_t /*K*/) {
+    const int64_t cus = device_cu_count();
+    const int64_t tiles_sq = ((M + 255) / 256) * ((N + 255) / 256);
+    const int64_t tiles_wide = ((M + 255) / 256) * ((N + 127) / 128);
+    if (M > 128 && tiles_sq >= 2 * cus) return GemmConfig::kBig256x256;
+    if (M > 128 && tiles_wide >= cus / 2) return GemmConfig::kBig256x128;
+    if (M <= 64) return GemmConfig::kReg64x64;
+    return GemmConfig::kReg128x128;
+}
+
+const char* gemm_config_name(GemmConfig cfg) {
+    switch (cfg) {
+        case GemmConfig::kBig256x256: return "lds-direct 256x256, 8 waves of 128x64";
+        case GemmConfig::kBig256x128: return "lds-direct 256x128, 8 waves of 64x64";
+        case GemmConfig::kReg64x64: return "register-staged 64x64, 4 waves of 32x32";
+        case GemmConfig::kReg128x128: return "register-staged 128x128, 4 waves of 64x64";
+    }
+    return "unknown";
+}
+
 hipError_t launch_gemm(const void* a, const float* as, const void* b, const float* bs, void* c,
                        int64_t M, int64_t N, int64_t K, void* /*workspace*/,
                        size_t /*workspace_bytes*/, hipStream_t stream) {
-    if (M <= 64) {
-        using T = TileSmall;
-        const int mt = (int)((M + T::BM - 1) / T::BM), nt = (int)((N + T::BN - 1) / T::BN);
-        hipLaunchKernelGGL(gemm_kernel<T>, dim3(mt * nt), dim3(256), 0, stream, (const uint8_t*)a,
-                           as, (const uint8_t*)b, bs, (uint16_t*)c, M, N, K, mt, nt);
-    } else {
-        using T = TileLarge;
-        const int mt = (int)((M + T::BM - 1) / T::BM), nt = (int)((N + T::BN - 1) / T::BN);
-        hipLaunchKernelGGL(gemm_kernel<T>, dim3(mt * nt), dim3(256), 0, stream, (const uint8_t*)a,
-                           as, (const uint8_t*)b, bs, (uint16_t*)c, M, N, K, mt, nt);
+    switch (gemm_config(M, N, K)) {
+        case GemmConfig::kBig256x256:
+            launch_big<BigSquare>(a, as, b, bs, c, M, N, K, stream);
+            break;
+        case GemmConfig::kBig256x128:
+            launch_big<BigWide>(a, as, b, bs, c, M, N, K, stream);
+            break;
+        case GemmConfig::kReg64x64: {
+            using T = TileSmall;
+            const int mt = (int)((M + T::BM - 1) / T::BM), nt = (int)((N + T::BN - 1) / T::BN);
+            hipLaunchKernelGGL(gemm_kernel<T>, dim3(mt * nt), dim3(256), 0, stream,
+                               (const uint8_t*)a, as, (const uint8_t*)b, bs, (uint16_t*)c, M, N, K,
+                               mt, nt);
+            break;
+        }
+        case GemmConfig::kReg128x128: {
+            using T = TileLarge;
+            const int mt = (int)((M + T::BM - 1) / T::BM), nt = (int)((N + T::BN - 1) / T::BN);
+            hipLaunchKernelGGL(gemm_kernel<T>, dim3(mt * nt), dim3(256), 0, stream,
+                               (const uint8_t*)a, as, (const uint8_t*)b, bs, (uint16_t*)c, M, N, K,
+                               mt, nt);
+            break;
+        }
     }
     return hipGetLastError();
 }

@@ -19,6 +19,10 @@ hipError_t launch_encode_range(uint32_t first, int64_t count, void* out, int var
 hipError_t launch_weight_dequant(const void* w, const float* s, void* out, int64_t N, int64_t K,
                                  hipStream_t stream);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+enum class GemmConfig { kBig256x256, kBig256x128, kReg64x64, kReg128x128 };
+GemmConfig gemm_config(int64_t M, int64_t N, int64_t K);
+const char* gemm_config_name(GemmConfig cfg);
 hipError_t launch_gemm(const void* a, const float* as, const void* b, const float* bs, void* c,
                        int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
                        hipStream_t stream);

@@ -135,6 +135,12 @@ int bfp8_gemm_grouped(const void* a, const float* a_s, const void* b, const floa
  * BFP8_ERR_ARG (unknown variant). */
 int bfp8_e4m3_encode_range(uint32_t first, int64_t count, void* out, int variant, void* stream);
 
+/* Introspection helper: the name of the kernel configuration bfp8_gemm uses
+ * for an M x N x K problem on the current device (static storage; "none" for
+ * a shape bfp8_gemm would reject or skip).  Lets tests and benchmarks record
+ * which tile configuration ran. */
+const char* bfp8_gemm_kernel_name(int64_t M, int64_t N, int64_t K);
+
 /* Human-readable name of a status code (static storage). */
 const char* bfp8_status_string(int status);
 

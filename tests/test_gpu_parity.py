@@ -247,12 +247,18 @@ def test_gemm_chain_full_size(config):
 def test_gemm_ragged_shapes():
     from block_scaled_fp8_04_amd import synth
     g = torch.Generator().manual_seed(5)
+    seen = set()
     for (M, N, K) in ((1, 1, 128), (37, 300, 384), (130, 129, 256), (64, 257, 640), (200, 64, 128),
-                      (129, 1000, 1152), (65, 130, 128)):
+                      (129, 1000, 1152), (65, 130, 128), (2000, 4001, 384), (4000, 8100, 256),
+                      (4096, 8192, 128)):
         x = torch.randn(M, K, generator=g).to(torch.bfloat16).to(dev())
         q, s = bfp8.act_quant(x)
         w, ws = synth.weight(N, K, 700 + M, 800 + N)
-        _gemm_case(q, s, w.to(dev()), ws.to(dev()), f"ragged[{M},{N},{K}]")
+        name = bfp8.bfp8_gemm_kernel_name(M, N, K)
+        seen.add(name)
+        rows = None if M <= 256 else sample_rows(M, seed=M)
+        _gemm_case(q, s, w.to(dev()), ws.to(dev()), f"ragged[{M},{N},{K}] via {name}", rows=rows)
+    assert len(seen) >= 4, f"every kernel configuration should be exercised, saw {seen}"
 
 
 def test_gemm_identity_bit_exact():
