@@ -6,7 +6,8 @@ package does not load the library; the first call does, and raises if it has
 not been built (``__graft_entry__.build()``).
 """
 from ._lib import (  # noqa: F401
-    BLOCK, Bfp8Error, EXPORTS, LIBRARY, act_quant, bfp8_act_quant, bfp8_e4m3_encode_range,
+    BLOCK, Bfp8Error, EXPORTS, LIBRARY, act_quant, bfp8_act_quant, bfp8_bf16_round_range,
+    bfp8_e4m3_encode_range,
     bfp8_gemm, bfp8_gemm_grouped, bfp8_gemm_kernel_name, bfp8_gemm_workspace_size, bfp8_status_string, bfp8_version,
     bfp8_weight_dequant, gemm, gemm_grouped, library, linear_fp8, status_string, weight_dequant,
 )

@@ -27,7 +27,8 @@ BFP8_ERR_HIP = 6
 BFP8_ERR_ARG = 7
 
 EXPORTS = ("bfp8_act_quant", "bfp8_weight_dequant", "bfp8_gemm", "bfp8_gemm_workspace_size",
-           "bfp8_gemm_grouped", "bfp8_e4m3_encode_range", "bfp8_gemm_kernel_name",
+           "bfp8_gemm_grouped", "bfp8_e4m3_encode_range", "bfp8_bf16_round_range",
+           "bfp8_gemm_kernel_name",
            "bfp8_status_string", "bfp8_version")
 
 _lib = None
@@ -61,6 +62,8 @@ def library():
     lib.bfp8_gemm_grouped.restype = ctypes.c_int
     lib.bfp8_e4m3_encode_range.argtypes = [ctypes.c_uint32, I64, P, ctypes.c_int, P]
     lib.bfp8_e4m3_encode_range.restype = ctypes.c_int
+    lib.bfp8_bf16_round_range.argtypes = [ctypes.c_uint32, I64, P, ctypes.c_int, P]
+    lib.bfp8_bf16_round_range.restype = ctypes.c_int
     lib.bfp8_gemm_kernel_name.argtypes = [I64, I64, I64]
     lib.bfp8_gemm_kernel_name.restype = ctypes.c_char_p
     lib.bfp8_status_string.argtypes = [ctypes.c_int]
@@ -195,6 +198,14 @@ def bfp8_e4m3_encode_range(first, count, out, variant=0, stream=None):
     _cuda_contig(out)
     _need(out.dtype == torch.uint8 and out.numel() >= count, "out must be uint8 with count bytes")
     _check("bfp8_e4m3_encode_range", library().bfp8_e4m3_encode_range(
+        int(first), int(count), _ptr(out), int(variant), _stream(stream, out.device)))
+
+
+def bfp8_bf16_round_range(first, count, out, variant=0, stream=None):
+    """Device bf16 rounding of the fp32 bit patterns first .. first+count-1 into out (int16/uint16)."""
+    _cuda_contig(out)
+    _need(out.element_size() == 2 and out.numel() >= count, "out must be 2-byte elements, count long")
+    _check("bfp8_bf16_round_range", library().bfp8_bf16_round_range(
         int(first), int(count), _ptr(out), int(variant), _stream(stream, out.device)))
 
 

@@ -119,4 +119,13 @@ int bfp8_e4m3_encode_range(uint32_t first, int64_t count, void* out, int variant
     return from_hip(bfp8::launch_encode_range(first, count, out, variant, (hipStream_t)stream));
 }
 
+int bfp8_bf16_round_range(uint32_t first, int64_t count, void* out, int variant, void* stream) {
+    if (count < 0 || (uint64_t)first + (uint64_t)count > (uint64_t)1 << 32) return BFP8_ERR_SHAPE;
+    if (variant != 0 && variant != 1) return BFP8_ERR_ARG;
+    if (count == 0) return BFP8_OK;
+    if (!out) return BFP8_ERR_NULL;
+    if (!aligned(out, 2)) return BFP8_ERR_ALIGN;
+    return from_hip(bfp8::launch_bf16_round_range(first, count, out, variant, (hipStream_t)stream));
+}
+
 }  // extern "C"

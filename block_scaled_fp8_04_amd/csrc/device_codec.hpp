@@ -80,8 +80,17 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
     if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+__device__ __forceinline__ uint32_t pack_bf16x2_sw(float a, float b) {
     return bf16_rne_bits(a) | (bf16_rne_bits(b) << 16);
+}
+
+// The same rounding by the gfx950 packed conversion (v_cvt_pk_bf16_f32,
+// round to nearest even); the GPU tests compare it with the bit rule above
+// and with the oracle on every fp32 input.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 // Decode of a packed pair of e4m3 codes (bytes 0-1 or 2-3 of w) by the gfx950

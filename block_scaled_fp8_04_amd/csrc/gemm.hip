@@ -21,8 +21,8 @@
 //    global loads are in flight in registers and are written to stage s^1.
 //    One barrier per K block.
 //  * LDS rows are 128 bytes; the eight 16-byte chunks of row r are stored at
-//    chunk position (chunk ^ (r & 7)), so both the row-wise writes and the
-//    fragment reads (16 rows at the same chunk) touch all banks once.
+//    chunk position (chunk ^ swz(r)) (see swz below), so the 16 rows read
+//    together by a fragment load (same logical chunk) hit no bank twice.
 //  * MFMA operand layout: lane l supplies row (l & 15) of the sub-tile and the
 //    32 K-bytes starting at 32 * (l >> 4), for A and B alike, so each K index
 //    pairs the same position of A and B.  The accumulator layout of a 16x16
@@ -51,6 +51,13 @@ struct Tile {
     static_assert(TM >= 1 && TN >= 1, "wave tile must hold a 16x16 sub-tile");
     static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns must share one scale block");
 };
+
+// LDS chunk swizzle of a 128-byte row: logical 16-byte chunk c of row r is
+// stored at chunk position c ^ swz(r).  Measured on MI355X with the fragment
+// read pattern (16 rows x one chunk per 16 lanes), xor-ing with (r & 7) alone,
+// or with ((r >> 1) & 7), leaves two-way bank conflicts; additionally flipping
+// the low bit for rows 8..15 of each 16-row group removes them.
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 __device__ __forceinline__ v8i frag_from(const uint4 x0, const uint4 x1) {
     v8i f;
@@ -85,7 +92,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a,
         int64_t grow = m0 + row;
         grow = grow < m_end ? grow : m_end - 1;
         a_src[i] = a + grow * K + col * 16;
-        a_dst[i] = row * kBlock + ((col ^ (row & 7)) << 4);
+        a_dst[i] = row * kBlock + ((col ^ swz(row)) << 4);
     }
 #pragma unroll
     for (int i = 0; i < T::B_LOADS; ++i) {
@@ -93,7 +100,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a,
         int64_t gcol = n0 + row;
         gcol = gcol < N ? gcol : N - 1;
         b_src[i] = b + gcol * K + col * 16;
-        b_dst[i] = T::A_BYTES + row * kBlock + ((col ^ (row & 7)) << 4);
+        b_dst[i] = T::A_BYTES + row * kBlock + ((col ^ swz(row)) << 4);
     }
     const float* sa_src = nullptr;
     if (tid < T::BM) {
@@ -136,8 +143,8 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a,
 
     const int lr = lane & 15;
     const int lk = (lane >> 4) * 2;               // first of this lane's two 16-byte chunks
-    const int off0 = ((lk ^ (lr & 7)) << 4);
-    const int off1 = (((lk + 1) ^ (lr & 7)) << 4);
+    const int off0 = ((lk ^ swz(lr)) << 4);
+    const int off1 = (((lk + 1) ^ swz(lr)) << 4);
     const int srow = 4 * (lane >> 4);
 
     for (int64_t kb = 0; kb < KB; ++kb) {
@@ -261,25 +268,58 @@ __global__ __launch_bounds__(256, 2) void gemm_grouped_kernel(const uint8_t* __r
 // The row scales of the K block arrive the same way (4 bytes per lane).
 // Loads for K block kb+1 are issued before the MFMAs of block kb; one
 // s_waitcnt + barrier per K block closes the step.
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int NSTAGE_>
 struct BigTile {
     static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+    static constexpr int NSTAGE = NSTAGE_;                  // LDS stages (prefetch distance NSTAGE-1)
     static constexpr int WAVES = WAVES_M * WAVES_N, THREADS = 64 * WAVES;
     static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
     static constexpr int TM = WM / 16, TN = WN / 16;
     static constexpr int A_BYTES = BM * kBlock, B_BYTES = BN * kBlock;
-    static constexpr int STAGE = A_BYTES + B_BYTES + BM * 4;
-    static constexpr int A_INSTR = BM / 8 / WAVES;      // 1 KB instructions per wave for A
+    // Row scales of one K block, permuted for the fragment layout: row 16 i + t
+    // sits at float t * SPITCH + i.  SPITCH = BM/16 + 4 keeps the 16 lanes of a
+    // read on distinct bank groups and each lane's TM values 16-byte aligned.
+    static constexpr int SPITCH = BM / 16 + 4;
+    static constexpr int S_FLOATS = 16 * SPITCH;
+    static constexpr int S_INSTR = (S_FLOATS + 63) / 64;   // 256-byte scale instructions
+    // every wave issues one scale instruction (waves past S_INSTR fill unused
+    // slots), so all waves have the same number of loads in flight per stage
+    static constexpr int S_BYTES = (WAVES * 256 + 1023) / 1024 * 1024;
+    static constexpr int LOADS_PER_STAGE = BM / 8 / WAVES + BN / 8 / WAVES + 1;
+    static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
+    static constexpr int A_INSTR = BM / 8 / WAVES;          // 1 KB instructions per wave for A
     static constexpr int B_INSTR = BN / 8 / WAVES;
-    static constexpr int S_INSTR = (BM + 63) / 64;      // 256 B scale instructions (waves 0..)
     static_assert(BM % (8 * WAVES) == 0 && BN % (8 * WAVES) == 0, "tile rows must split over waves");
     static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns must share one scale block");
     static_assert(S_INSTR <= WAVES, "one scale instruction per wave at most");
-    static_assert(BM % 64 == 0, "scale rows are fetched 64 at a time");
+    static_assert(TM % 4 == 0, "scales are read four at a time");
+    static_assert(STAGE % 1024 == 0, "stages stay 1 KB aligned");
+    static_assert(NSTAGE >= 2 && NSTAGE * STAGE <= 160 * 1024, "stages must fit in LDS");
 };
 
 typedef __attribute__((address_space(3))) void* lds_void_t;
 typedef const __attribute__((address_space(1))) void* gbl_void_t;
+
+// s_waitcnt that waits only for vmcnt <= n (gfx9 encoding: vmcnt[3:0] in bits
+// 3:0 and vmcnt[5:4] in bits 15:14; expcnt and lgkmcnt left at their maxima).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(n >= 0 && n < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+
+// Workgroup barrier whose memory fence covers LDS only: outstanding global
+// loads are not waited for here (the direct-to-LDS loads are counted with
+// wait_vmcnt by each wave before it arrives).
+// The empty asm statements are compiler-only memory barriers (they emit no
+// instruction) so that no LDS access is moved across the hardware barrier.
+__device__ __forceinline__ void barrier_lds() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+}
 
 __device__ __forceinline__ void load_lds16(const void* src, void* lds_dst) {
     __builtin_amdgcn_global_load_lds((gbl_void_t)src, (lds_void_t)lds_dst, 16, 0, 0);
@@ -288,6 +328,11 @@ __device__ __forceinline__ void load_lds4(const void* src, void* lds_dst) {
     __builtin_amdgcn_global_load_lds((gbl_void_t)src, (lds_void_t)lds_dst, 4, 0, 0);
 }
 
+// The MFMA is issued with the weight fragment as its first operand and the
+// activation fragment as its second, so the 16 x 16 result is C^T: lane l
+// holds output row m = l & 15 of the sub-tile and the four consecutive columns
+// n = 4 (l >> 4) + 0..3.  Each lane therefore needs one activation scale per
+// sub-tile row block, and the epilogue writes 8 contiguous bytes per sub-tile.
 template <class T>
 __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
                                               const float* __restrict__ as,
@@ -303,45 +348,57 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
     const int64_t KB = K / kBlock;
     const int64_t NB = (N + kBlock - 1) / kBlock;
 
-    // per-lane sources of the direct loads (byte offset of K block 0)
-    const int lrow = lane >> 3;                                  // row within an 8-row group
-    const int lchunk = (lane & 7) ^ (lrow & 7);                  // logical 16-byte chunk fetched
-    const uint8_t* a_src[T::A_INSTR];
-    const uint8_t* b_src[T::B_INSTR];
+    // Direct-load sources.  Instruction i of this wave fills LDS rows
+    // r0 .. r0+7 (r0 = 8 * (wave * INSTR + i)); lane l writes physical chunk
+    // l & 7 of row r0 + (l >> 3), which must hold logical chunk
+    // (l & 7) ^ swz(row).  Offsets are 32-bit, relative to the tile's
+    // first row, so the K-block step is one scalar add on the base pointer.
+    const int lrow = lane >> 3;
+    uint32_t a_off[T::A_INSTR], b_off[T::B_INSTR];
 #pragma unroll
     for (int i = 0; i < T::A_INSTR; ++i) {
         const int row = (wave * T::A_INSTR + i) * 8 + lrow;
+        const int chunk = (lane & 7) ^ swz(row);
         int64_t grow = m0 + row;
         grow = grow < m_end ? grow : m_end - 1;
-        a_src[i] = a + grow * K + lchunk * 16;
+        a_off[i] = (uint32_t)((grow - m0) * K) + chunk * 16;
     }
 #pragma unroll
     for (int i = 0; i < T::B_INSTR; ++i) {
         const int row = (wave * T::B_INSTR + i) * 8 + lrow;
+        const int chunk = (lane & 7) ^ swz(row);
         int64_t gcol = n0 + row;
         gcol = gcol < N ? gcol : N - 1;
-        b_src[i] = b + gcol * K + lchunk * 16;
+        b_off[i] = (uint32_t)((gcol - n0) * K) + chunk * 16;
     }
-    const float* s_src = as;
-    if (wave < T::S_INSTR) {
-        int64_t grow = m0 + wave * 64 + lane;
+    // scale slot p = t * SPITCH + i holds row 16 i + t (pad slots load row 0)
+    uint32_t s_off = 0;
+    {
+        const int p = wave * 64 + lane;
+        const int t = p / T::SPITCH, i = p % T::SPITCH;
+        int row = (t < 16 && i < T::BM / 16) ? 16 * i + t : 0;
+        int64_t grow = m0 + row;
         grow = grow < m_end ? grow : m_end - 1;
-        s_src = as + grow * KB;
+        s_off = (uint32_t)((grow - m0) * KB);
     }
+    const uint8_t* a_tile = a + m0 * K;
+    const uint8_t* b_tile = b + n0 * K;
+    const float* s_tile = as + m0 * KB;
     int64_t nblk = (n0 + wn0) >> 7;
     nblk = nblk < NB ? nblk : NB - 1;
     const float* sb_src = bs + nblk * KB;
 
     auto issue = [&](int64_t kb, int stage) {
         uint8_t* base = lds + stage * T::STAGE;
+        const uint8_t* ak = a_tile + kb * kBlock;
+        const uint8_t* bk = b_tile + kb * kBlock;
 #pragma unroll
         for (int i = 0; i < T::A_INSTR; ++i)
-            load_lds16(a_src[i] + kb * kBlock, base + (wave * T::A_INSTR + i) * 1024);
+            load_lds16(ak + a_off[i], base + (wave * T::A_INSTR + i) * 1024);
 #pragma unroll
         for (int i = 0; i < T::B_INSTR; ++i)
-            load_lds16(b_src[i] + kb * kBlock, base + T::A_BYTES + (wave * T::B_INSTR + i) * 1024);
-        if (wave < T::S_INSTR)
-            load_lds4(s_src + kb, base + T::A_BYTES + T::B_BYTES + wave * 256);
+            load_lds16(bk + b_off[i], base + T::A_BYTES + (wave * T::B_INSTR + i) * 1024);
+        load_lds4(s_tile + kb + s_off, base + T::A_BYTES + T::B_BYTES + wave * 256);
     };
 
     v4f acc[T::TM][T::TN];
@@ -350,19 +407,32 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
 #pragma unroll
         for (int j = 0; j < T::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    issue(0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    // prologue: K blocks 0 .. NSTAGE-2 in flight
+#pragma unroll
+    for (int st = 0; st + 1 < T::NSTAGE; ++st)
+        if (st < KB) issue(st, st);
 
     const int lr = lane & 15;
     const int lk = (lane >> 4) * 2;
-    const int off0 = ((lk ^ (lr & 7)) << 4);
-    const int off1 = (((lk + 1) ^ (lr & 7)) << 4);
-    const int srow = 4 * (lane >> 4);
+    const int off0 = ((lk ^ swz(lr)) << 4);
+    const int off1 = (((lk + 1) ^ swz(lr)) << 4);
+    const int sread = lr * T::SPITCH + wm0 / 16;
 
+    int cur = 0;
     for (int64_t kb = 0; kb < KB; ++kb) {
-        const int cur = (int)(kb & 1);
-        if (kb + 1 < KB) issue(kb + 1, cur ^ 1);
+        // this wave's loads of block kb are done once at most the later
+        // blocks' loads are outstanding; the barrier then makes every wave's
+        // loads visible and guarantees stage (kb-1) is no longer being read
+        if (kb + T::NSTAGE - 2 < KB)
+            wait_vmcnt<T::LOADS_PER_STAGE * (T::NSTAGE - 2)>();
+        else
+            wait_vmcnt<0>();
+        barrier_lds();
+        if (kb + T::NSTAGE - 1 < KB) {
+            int st = cur + T::NSTAGE - 1;
+            st = st >= T::NSTAGE ? st - T::NSTAGE : st;
+            issue(kb + T::NSTAGE - 1, st);
+        }
 
         const uint8_t* As = lds + cur * T::STAGE;
         const uint8_t* Bs = As + T::A_BYTES;
@@ -374,41 +444,86 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
             fb[j] = frag_from(*(const uint4*)(r + off0), *(const uint4*)(r + off1));
         }
         const float sbv = sb_src[kb];
+        float sc[T::TM];
+#pragma unroll
+        for (int i = 0; i < T::TM; i += 4) {
+            const v4f s4 = *(const v4f*)(Ss + sread + i);
+            sc[i] = s4[0] * sbv; sc[i + 1] = s4[1] * sbv; sc[i + 2] = s4[2] * sbv; sc[i + 3] = s4[3] * sbv;
+        }
+        // MFMAs of sub-tile row i are issued before the fold of row i - 1, so
+        // each block product has TN MFMAs of distance before it is read; the
+        // A fragment of row i + 1 is read from LDS while row i multiplies.
+        v4f prev[T::TN];
+        v8i fa_next;
+        {
+            const uint8_t* r = As + (wm0 + lr) * kBlock;
+            fa_next = frag_from(*(const uint4*)(r + off0), *(const uint4*)(r + off1));
+        }
 #pragma unroll
         for (int i = 0; i < T::TM; ++i) {
-            const uint8_t* r = As + (wm0 + 16 * i + lr) * kBlock;
-            const v8i fa = frag_from(*(const uint4*)(r + off0), *(const uint4*)(r + off1));
-            const v4f sc = *(const v4f*)(Ss + wm0 + 16 * i + srow) * sbv;
-#pragma unroll
-            for (int j = 0; j < T::TN; ++j) {
-                const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    fa, fb[j], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-                acc[i][j] = p * sc + acc[i][j];
+            const v8i fa = fa_next;
+            if (i + 1 < T::TM) {
+                const uint8_t* r = As + (wm0 + 16 * (i + 1) + lr) * kBlock;
+                fa_next = frag_from(*(const uint4*)(r + off0), *(const uint4*)(r + off1));
             }
-        }
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-    }
-
-    const bool interior = (m0 + T::BM <= m_end) && (n0 + T::BN <= N);
-    uint16_t* cbase = c + (m0 + wm0 + srow) * N + n0 + wn0 + lr;
-    if (interior) {
-#pragma unroll
-        for (int i = 0; i < T::TM; ++i)
+            v4f cur[T::TN];
 #pragma unroll
             for (int j = 0; j < T::TN; ++j)
+                cur[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    fb[j], fa, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+            if (i > 0) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    cbase[(16 * i + r) * N + 16 * j] = (uint16_t)bf16_rne_bits(acc[i][j][r]);
+                for (int j = 0; j < T::TN; ++j) acc[i - 1][j] = prev[j] * sc[i - 1] + acc[i - 1][j];
+            }
+#pragma unroll
+            for (int j = 0; j < T::TN; ++j) prev[j] = cur[j];
+        }
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j) acc[T::TM - 1][j] = prev[j] * sc[T::TM - 1] + acc[T::TM - 1][j];
+        // Instruction order of this K block, given to the scheduler: the
+        // direct loads, the B / scale / first-A reads and the scale products,
+        // then per sub-tile row the next A read and TN x (1 MFMA, 4 fold FMAs).
+        __builtin_amdgcn_sched_group_barrier(0x020, T::A_INSTR + T::B_INSTR + 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * T::TN + T::TM / 4 + 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, T::TM, 0);
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i) {
+            if (i + 1 < T::TM) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+            for (int j = 0; j < T::TN; ++j) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            }
+        }
+        __builtin_amdgcn_sched_group_barrier(0x002, 4 * T::TN, 0);
+        cur = cur + 1 == T::NSTAGE ? 0 : cur + 1;
+    }
+
+    // epilogue: lane holds row m0 + wm0 + 16 i + lr, columns n0 + wn0 + 16 j + 4 (lane >> 4) + 0..3
+    const int cq = 4 * (lane >> 4);
+    const bool interior = (m0 + T::BM <= m_end) && (n0 + T::BN <= N);
+    const bool vec = interior && (N % 4 == 0) && (((uintptr_t)c & 7u) == 0);
+    if (vec) {
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i) {
+            uint16_t* crow = c + (m0 + wm0 + 16 * i + lr) * N + n0 + wn0 + cq;
+#pragma unroll
+            for (int j = 0; j < T::TN; ++j) {
+                uint2 v;
+                v.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+                v.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+                *(uint2*)(crow + 16 * j) = v;
+            }
+        }
     } else {
 #pragma unroll
         for (int i = 0; i < T::TM; ++i) {
+            const int64_t row = m0 + wm0 + 16 * i + lr;
 #pragma unroll
             for (int j = 0; j < T::TN; ++j) {
-                const int64_t col = n0 + wn0 + 16 * j + lr;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int64_t row = m0 + wm0 + 16 * i + srow + r;
+                    const int64_t col = n0 + wn0 + 16 * j + cq + r;
                     if (row < m_end && col < N)
                         c[row * N + col] = (uint16_t)bf16_rne_bits(acc[i][j][r]);
                 }
@@ -442,7 +557,7 @@ __global__ __launch_bounds__(T::THREADS, 1) void gemm_big_kernel(const uint8_t* 
                                                                  uint16_t* __restrict__ c,
                                                                  int64_t M, int64_t N, int64_t K,
                                                                  int mt, int nt) {
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * T::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[T::NSTAGE * T::STAGE];
     int tm, tn;
     tile_of(blockIdx.x, gridDim.x, mt, nt, tm, tn);
     gemm_tile_big<T>(a, as, b, bs, c, (int64_t)tm * T::BM, M, (int64_t)tn * T::BN, N, K, lds);
@@ -453,8 +568,8 @@ using TileSmall = Tile<64, 64>;
 
 size_t gemm_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
 
-using BigSquare = BigTile<256, 256, 2, 4>;   // 8 waves of 128 x 64
-using BigWide = BigTile<256, 128, 4, 2>;     // 8 waves of 64 x 64
+using BigSquare = BigTile<256, 256, 2, 4, 2>;   // 8 waves of 128 x 64, 2 stages
+using BigWide = BigTile<256, 128, 4, 2, 3>;     // 8 waves of 64 x 64, 3 stages
 
 template <class T>
 static void launch_big(const void* a, const float* as, const void* b, const float* bs, void* c,

@@ -16,6 +16,8 @@ hipError_t launch_act_quant(const void* x, void* q, float* s, int64_t M, int64_t
                             hipStream_t stream);
 hipError_t launch_encode_range(uint32_t first, int64_t count, void* out, int variant,
                                hipStream_t stream);
+hipError_t launch_bf16_round_range(uint32_t first, int64_t count, void* out, int variant,
+                                   hipStream_t stream);
 hipError_t launch_weight_dequant(const void* w, const float* s, void* out, int64_t N, int64_t K,
                                  hipStream_t stream);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);

@@ -14,26 +14,29 @@
 // bound (3.03 bytes per element); two independent blocks per lane are in
 // flight per iteration to keep enough loads outstanding.
 //
-// Quotient: fl(x / s) is needed only up to which e4m3 rounding interval it
-// falls in.  y = x * fl(1/s) is within 3 ulp of fl(x/s); when y is more than
-// 8 ulp away from every e4m3 rounding midpoint both land on the same code, so
-// the exact IEEE division is only evaluated for lanes near a midpoint (and for
-// quotients in the e4m3 subnormal range, below 2^-6).  The result equals
-// encoding the correctly rounded quotient for every input.
+// Per element the work is: widen bf16, one max, a three-operation correctly
+// rounded quotient (see quotient()), and the gfx950 fp32 -> e4m3 conversion
+// after a clamp to +-448 (proven equal to the oracle's encoder on all 2^32
+// fp32 inputs by the GPU tests).  The two divisions per block (scale and its
+// reciprocal) are shared by the 8 lanes of the block.
 #include "device_codec.hpp"
 #include "internal.hpp"
 
 namespace bfp8 {
 
-// fl(x / s) as far as e4m3 rounding can tell; r = fl(1 / s).
-__device__ __forceinline__ float quotient_for_e4m3(float x, float s, float r) {
-    float y = x * r;
-    const uint32_t ay = __float_as_uint(y) & 0x7FFFFFFFu;
-    const int d = (int)(ay & 0xFFFFFu) - 0x80000;
-    const bool near_midpoint = (d >= -8) & (d <= 8);
-    const bool small = (ay < 0x3C800000u) & (ay != 0u);
-    if (near_midpoint | small) y = x / s;        // correctly rounded fp32 division
-    return y;
+// Correctly rounded fp32 quotient x / s from the correctly rounded reciprocal
+// r = fl(1 / s): y0 = fl(x r) is within one ulp of x / s, the remainder
+// x - y0 s is exact as one fused multiply-add, and one more fused step
+// y0 + (x - y0 s) r rounds to fl(x / s) (Markstein's correction step).  The
+// GPU tests check the kernel against the oracle's fp32 division on every pair
+// of bf16 block maximum and bf16 element.
+// The correction step turns a quotient of -0 into +0 (-0 + +0 rounds to +0),
+// so the sign of x is put back; for x != 0 it is already the quotient's sign
+// because s > 0.
+__device__ __forceinline__ float quotient(float x, float s, float r) {
+    const float y0 = x * r;
+    const float e = __builtin_fmaf(-y0, s, x);
+    return __builtin_copysignf(__builtin_fmaf(e, r, y0), x);
 }
 
 template <bool kHw>
@@ -48,7 +51,7 @@ __device__ __forceinline__ void quant_block_part(const uint4 v0, const uint4 v1,
     }
     float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
+    for (int i = 0; i < 16; i += 2) amax = fmaxf(amax, fmaxf(fabsf(f[i]), fabsf(f[i + 1])));
     amax = fmaxf(amax, __shfl_xor(amax, 1, 8));
     amax = fmaxf(amax, __shfl_xor(amax, 2, 8));
     amax = fmaxf(amax, __shfl_xor(amax, 4, 8));
@@ -56,7 +59,7 @@ __device__ __forceinline__ void quant_block_part(const uint4 v0, const uint4 v1,
     const float r = 1.0f / s;
     float y[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) y[i] = quotient_for_e4m3(f[i], s, r);
+    for (int i = 0; i < 16; ++i) y[i] = quotient(f[i], s, r);
     out.x = e4m3_encode4<kHw>(y[0], y[1], y[2], y[3]);
     out.y = e4m3_encode4<kHw>(y[4], y[5], y[6], y[7]);
     out.z = e4m3_encode4<kHw>(y[8], y[9], y[10], y[11]);
@@ -119,8 +122,38 @@ __global__ __launch_bounds__(256) void encode_range_kernel(uint32_t first, int64
     }
 }
 
+// Rounds the fp32 bit patterns first .. first+count-1 to bf16 with the
+// packed conversion the dequant and GEMM epilogues use (variant 0) or with the
+// bit rule (variant 1) (test helper).
+template <bool kHw>
+__global__ __launch_bounds__(256) void bf16_round_range_kernel(uint32_t first, int64_t count,
+                                                               uint16_t* __restrict__ out) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) {
+        const float v = __uint_as_float(first + (uint32_t)i);
+        uint32_t h;
+        if constexpr (kHw) h = pack_bf16x2(v, 0.0f) & 0xFFFFu;
+        else h = bf16_rne_bits(v);
+        out[i] = (uint16_t)h;
+    }
+}
+
+hipError_t launch_bf16_round_range(uint32_t first, int64_t count, void* out, int variant,
+                                   hipStream_t stream) {
+    const int64_t wg_needed = (count + 255) / 256;
+    const int64_t wg_cap = (int64_t)device_cu_count() * 16;
+    const int grid = (int)(wg_needed < wg_cap ? (wg_needed > 0 ? wg_needed : 1) : wg_cap);
+    if (variant == 0)
+        hipLaunchKernelGGL(bf16_round_range_kernel<true>, dim3(grid), dim3(256), 0, stream, first,
+                           count, (uint16_t*)out);
+    else
+        hipLaunchKernelGGL(bf16_round_range_kernel<false>, dim3(grid), dim3(256), 0, stream, first,
+                           count, (uint16_t*)out);
+    return hipGetLastError();
+}
+
 // The encoder act_quant uses.
-constexpr bool kActQuantHwEncode = false;
+constexpr bool kActQuantHwEncode = true;
 
 hipError_t launch_act_quant(const void* x, void* q, float* s, int64_t M, int64_t K,
                             hipStream_t stream) {

@@ -135,6 +135,13 @@ int bfp8_gemm_grouped(const void* a, const float* a_s, const void* b, const floa
  * BFP8_ERR_ARG (unknown variant). */
 int bfp8_e4m3_encode_range(uint32_t first, int64_t count, void* out, int variant, void* stream);
 
+/* Test helper: rounds the float32 bit patterns first .. first+count-1 to
+ * bf16 with the device routine the dequant kernel and the GEMM epilogue use
+ * (variant 0) or with the alternative bit-level routine (variant 1), into
+ * out[count] (device, uint16 bf16 bit patterns, 2-byte aligned).
+ * Errors: BFP8_ERR_NULL, BFP8_ERR_SHAPE, BFP8_ERR_ALIGN, BFP8_ERR_ARG. */
+int bfp8_bf16_round_range(uint32_t first, int64_t count, void* out, int variant, void* stream);
+
 /* Introspection helper: the name of the kernel configuration bfp8_gemm uses
  * for an M x N x K problem on the current device (static storage; "none" for
  * a shape bfp8_gemm would reject or skip).  Lets tests and benchmarks record

@@ -138,6 +138,16 @@ def test_encode_range_validation(lib):
     assert f(0, 0, None, 0, None) == _lib.BFP8_OK
 
 
+def test_bf16_round_range_validation(lib):
+    f = lib.bfp8_bf16_round_range
+    assert f(0, -1, FAKE, 0, None) == _lib.BFP8_ERR_SHAPE
+    assert f(0xFFFFFFFF, 2, FAKE, 0, None) == _lib.BFP8_ERR_SHAPE
+    assert f(0, 16, FAKE, 5, None) == _lib.BFP8_ERR_ARG
+    assert f(0, 16, None, 0, None) == _lib.BFP8_ERR_NULL
+    assert f(0, 16, ODD, 0, None) == _lib.BFP8_ERR_ALIGN
+    assert f(0, 0, None, 0, None) == _lib.BFP8_OK
+
+
 def test_python_binding_rejects_bad_tensors():
     import torch
     x = torch.zeros(4, 256, dtype=torch.bfloat16)            # CPU tensor: refused before any call

@@ -392,3 +392,100 @@ def test_grouped_single_group_equals_gemm():
     c2 = bfp8.gemm_grouped(q, s, w[None].contiguous(), ws[None].contiguous(), off)
     torch.cuda.synchronize()
     assert torch.equal(c1, c2)
+
+
+# ------------------------------------------------------- exhaustive sweeps
+
+def _oracle_bf16_parallel(v, threads=16):
+    out = np.empty(v.size, np.uint16)
+    bounds = np.linspace(0, v.size, threads + 1).astype(np.int64)
+
+    def work(i):
+        out[bounds[i]:bounds[i + 1]] = oracle.f32_to_bf16(v[bounds[i]:bounds[i + 1]])
+
+    with cf.ThreadPoolExecutor(threads) as ex:
+        list(ex.map(work, range(threads)))
+    return out
+
+
+@pytest.mark.parametrize("variant", [0, 1], ids=["native_conversion", "bit_rule"])
+def test_bf16_rounding_exhaustive(variant):
+    """The device bf16 rounding used by dequant and the GEMM epilogue equals the oracle
+    on all 2^32 fp32 patterns (NaNs excluded)."""
+    chunk = 1 << 28
+    out = torch.empty(chunk, dtype=torch.int16, device=dev())
+    mismatches, first_bad = 0, None
+    for c in range(1 << 4):
+        first = c * chunk
+        announce(f"bf16_round_range variant={variant} chunk {c}/16 first=0x{first:08x}")
+        bfp8.bfp8_bf16_round_range(first, chunk, out, variant)
+        got = out.cpu().numpy().view(np.uint16)
+        bits = np.arange(first, first + chunk, dtype=np.uint64).astype(np.uint32)
+        want = _oracle_bf16_parallel(bits.view(np.float32))
+        keep = (bits & 0x7FFFFFFF) <= 0x7F800000
+        bad = np.flatnonzero((got != want) & keep)
+        mismatches += bad.size
+        if bad.size and first_bad is None:
+            first_bad = [(hex(int(bits[i])), hex(int(got[i])), hex(int(want[i]))) for i in bad[:5]]
+    assert mismatches == 0, f"{mismatches} mismatches, first {first_bad}"
+
+
+def _pair_blocks(v_lo, v_hi):
+    """Blocks [amax, x...] covering, for every bf16 bit pattern v in [v_lo, v_hi) taken as
+    the block maximum, every bf16 x with |x| <= v (both signs), 127 per block."""
+    vs = np.arange(v_lo, v_hi, dtype=np.int64)
+    counts = 2 * (vs + 1)
+    nblk = -(-counts // 127)
+    lengths = nblk * 127
+    starts = np.concatenate([[0], np.cumsum(lengths)[:-1]])
+    p = np.arange(int(lengths.sum()), dtype=np.int64) - np.repeat(starts, lengths)
+    v_rep = np.repeat(vs, lengths)
+    x = np.where(p <= v_rep, p, np.where(p <= 2 * v_rep + 1, 0x8000 + p - v_rep - 1, 0))
+    blocks = np.zeros((int(nblk.sum()), 128), np.uint16)
+    blocks[:, 0] = np.repeat(vs, nblk).astype(np.uint16)
+    blocks[:, 1:] = x.astype(np.uint16).reshape(-1, 127)
+    return blocks
+
+
+def _oracle_act_quant_parallel(xb, threads=16):
+    q = np.empty(xb.shape, np.uint8)
+    s = np.empty((xb.shape[0], xb.shape[1] // BLOCK), np.float32)
+    bounds = np.linspace(0, xb.shape[0], threads + 1).astype(np.int64)
+
+    def work(i):
+        lo, hi = bounds[i], bounds[i + 1]
+        if hi > lo:
+            q[lo:hi], s[lo:hi] = oracle.act_quant(xb[lo:hi])
+
+    with cf.ThreadPoolExecutor(threads) as ex:
+        list(ex.map(work, range(threads)))
+    return q, s
+
+
+def test_act_quant_exhaustive_max_element_pairs():
+    """act_quant equals the oracle for every (block max, element) pair of bf16 values:
+    each finite positive bf16 value as a block's max, with every bf16 value of no
+    larger magnitude (both signs) as an element of that block."""
+    v_end = 0x7F80                                   # positive finite bf16 patterns 1 .. 0x7F7F
+    edges = [1]
+    target = 1 << 27                                 # elements per chunk
+    while edges[-1] < v_end:
+        v = edges[-1]
+        nxt = int(np.sqrt(v * v + target)) + 1
+        edges.append(min(v_end, max(nxt, v + 1)))
+    total = 0
+    for lo, hi in zip(edges[:-1], edges[1:]):
+        xb = _pair_blocks(lo, hi)
+        announce(f"act_quant pairs amax bits [0x{lo:04x}, 0x{hi:04x}): {xb.shape[0]} blocks")
+        x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev())
+        q, s = bfp8.act_quant(x)
+        torch.cuda.synchronize()
+        q_ref, s_ref = _oracle_act_quant_parallel(xb)
+        q_got = u8(q)
+        bad = np.flatnonzero(q_got.ravel() != q_ref.ravel())
+        assert bad.size == 0, (f"amax bits [{lo:#x},{hi:#x}): {bad.size} codes differ; first "
+                               f"(block, pos) {[(int(i) // 128, int(i) % 128) for i in bad[:5]]}")
+        assert np.array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+        total += xb.size
+        del x, q, s
+    announce(f"act_quant pairs: {total} elements checked")
