@@ -66,14 +66,19 @@ __device__ __forceinline__ v8i frag_from(const uint4 x0, const uint4 x1) {
     return f;
 }
 
-// Computes rows [m0, min(m0 + BM, m_end)) x columns [n0, min(n0 + BN, N)) of c.
+// Computes rows [m0, min(m0 + BM, m_end)) x columns [n0, min(n0 + BN, N)),
+// summing K blocks [kb_begin, kb_end).  With partial == nullptr the result is
+// rounded to bf16 into c; otherwise the fp32 partial sum goes to
+// partial[row * N + col] (split-K).
 template <class T>
 __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a,
                                           const float* __restrict__ as,
                                           const uint8_t* __restrict__ b,
                                           const float* __restrict__ bs,
                                           uint16_t* __restrict__ c, int64_t m0, int64_t m_end,
-                                          int64_t n0, int64_t N, int64_t K, uint8_t* lds) {
+                                          int64_t n0, int64_t N, int64_t K, uint8_t* lds,
+                                          int64_t kb_begin, int64_t kb_end,
+                                          float* __restrict__ partial) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -137,7 +142,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a,
         if (tid < T::BM) ((float*)(base + T::A_BYTES + T::B_BYTES))[tid] = rsa;
     };
 
-    load_regs(0);
+    load_regs(kb_begin);
     store_lds(0);
     __syncthreads();
 
@@ -147,9 +152,9 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a,
     const int off1 = (((lk + 1) ^ swz(lr)) << 4);
     const int srow = 4 * (lane >> 4);
 
-    for (int64_t kb = 0; kb < KB; ++kb) {
-        const int cur = (int)(kb & 1);
-        const bool more = kb + 1 < KB;
+    for (int64_t kb = kb_begin; kb < kb_end; ++kb) {
+        const int cur = (int)((kb - kb_begin) & 1);
+        const bool more = kb + 1 < kb_end;
         if (more) load_regs(kb + 1);
 
         const uint8_t* As = lds + cur * T::STAGE;
@@ -182,7 +187,8 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a,
         __syncthreads();
     }
 
-    // epilogue: fp32 -> bf16 (nearest even), masked to the valid rows / columns
+    // epilogue: fp32 -> bf16 (nearest even) or the fp32 partial, masked to
+    // the valid rows / columns
 #pragma unroll
     for (int i = 0; i < T::TM; ++i) {
 #pragma unroll
@@ -191,7 +197,10 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a,
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int64_t row = m0 + wm0 + 16 * i + srow + r;
-                if (row < m_end && col < N) c[row * N + col] = (uint16_t)bf16_rne_bits(acc[i][j][r]);
+                if (row < m_end && col < N) {
+                    if (partial) partial[row * N + col] = acc[i][j][r];
+                    else c[row * N + col] = (uint16_t)bf16_rne_bits(acc[i][j][r]);
+                }
             }
         }
     }
@@ -215,59 +224,41 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t* __restrict_
     const int in_band = id - band * GM * nt;
     const int tm = first_m + in_band % rows_in_band;
     const int tn = in_band / rows_in_band;
-    gemm_tile<T>(a, as, b, bs, c, (int64_t)tm * T::BM, M, (int64_t)tn * T::BN, N, K, lds);
+    gemm_tile<T>(a, as, b, bs, c, (int64_t)tm * T::BM, M, (int64_t)tn * T::BN, N, K, lds, 0,
+                 K / kBlock, nullptr);
 }
 
-// Persistent grouped kernel: workgroups stride over the tiles of all groups.
-// Group g owns ceil(rows_g / BM) * nt tiles, M-tiles fastest.
+// Split-K for skinny problems: blockIdx.y picks a run of kb_per K blocks and
+// the fp32 partial sums go to ws[split][M][N]; split_reduce_kernel adds the
+// splits in index order (a fixed order, so results are reproducible).
 template <class T>
-__global__ __launch_bounds__(256, 2) void gemm_grouped_kernel(const uint8_t* __restrict__ a,
-                                                              const float* __restrict__ as,
-                                                              const uint8_t* __restrict__ b,
-                                                              const float* __restrict__ bs,
-                                                              uint16_t* __restrict__ c,
-                                                              const int32_t* __restrict__ off,
-                                                              int G, int64_t N, int64_t K,
-                                                              int nt) {
+__global__ __launch_bounds__(256, 2) void gemm_splitk_kernel(const uint8_t* __restrict__ a,
+                                                             const float* __restrict__ as,
+                                                             const uint8_t* __restrict__ b,
+                                                             const float* __restrict__ bs,
+                                                             float* __restrict__ ws, int64_t M,
+                                                             int64_t N, int64_t K, int mt,
+                                                             int kb_per) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * T::STAGE];
+    const int tm = blockIdx.x % mt, tn = blockIdx.x / mt;
     const int64_t KB = K / kBlock;
-    const int64_t NB = (N + kBlock - 1) / kBlock;
-    int64_t total = 0;
-    for (int g = 0; g < G; ++g) {
-        const int64_t rows = (int64_t)off[g + 1] - off[g];
-        total += ((rows + T::BM - 1) / T::BM) * nt;
-    }
-    for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
-        int64_t start = 0;
-        int g = 0;
-        int64_t mtiles = 0;
-        for (; g < G; ++g) {
-            const int64_t rows = (int64_t)off[g + 1] - off[g];
-            mtiles = (rows + T::BM - 1) / T::BM;
-            if (t < start + mtiles * nt) break;
-            start += mtiles * nt;
-        }
-        const int64_t local = t - start;
-        const int64_t tm = local % mtiles;
-        const int64_t tn = local / mtiles;
-        gemm_tile<T>(a, as, b + (int64_t)g * N * K, bs + (int64_t)g * NB * KB, c,
-                     (int64_t)off[g] + tm * T::BM, (int64_t)off[g + 1], tn * T::BN, N, K, lds);
+    const int64_t kb0 = (int64_t)blockIdx.y * kb_per;
+    const int64_t kb1 = kb0 + kb_per < KB ? kb0 + kb_per : KB;
+    gemm_tile<T>(a, as, b, bs, nullptr, (int64_t)tm * T::BM, M, (int64_t)tn * T::BN, N, K, lds,
+                 kb0, kb1, ws + (int64_t)blockIdx.y * M * N);
+}
+
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ ws,
+                                                           uint16_t* __restrict__ c,
+                                                           int64_t MN, int splits) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < MN; i += stride) {
+        float sum = ws[i];
+        for (int sp = 1; sp < splits; ++sp) sum += ws[(int64_t)sp * MN + i];
+        c[i] = (uint16_t)bf16_rne_bits(sum);
     }
 }
 
-// ---------------------------------------------------------------------------
-// Large-tile kernel: direct global -> LDS loads, 8 waves.
-//
-// WG tile BM x BN with WAVES_M x WAVES_N waves (wave tile WM x WN).  The A and
-// B tiles of one 128-wide K block are fetched with global_load_lds_dwordx4:
-// one wave instruction fills 1 KB of LDS (eight 128-byte rows), lane l writing
-// bytes [16 l, 16 l + 16).  The XOR swizzle is applied on the source side:
-// lane l of an instruction covering rows r0..r0+7 fetches logical chunk
-// (l & 7) ^ ((l >> 3) & 7) of row r0 + (l >> 3), so LDS chunk c of row r holds
-// logical chunk c ^ (r & 7), exactly the layout the fragment reads expect.
-// The row scales of the K block arrive the same way (4 bytes per lane).
-// Loads for K block kb+1 are issued before the MFMAs of block kb; one
-// s_waitcnt + barrier per K block closes the step.
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int NSTAGE_>
 struct BigTile {
     static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
@@ -286,6 +277,7 @@ struct BigTile {
     // slots), so all waves have the same number of loads in flight per stage
     static constexpr int S_BYTES = (WAVES * 256 + 1023) / 1024 * 1024;
     static constexpr int LOADS_PER_STAGE = BM / 8 / WAVES + BN / 8 / WAVES + 1;
+
     static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
     static constexpr int A_INSTR = BM / 8 / WAVES;          // 1 KB instructions per wave for A
     static constexpr int B_INSTR = BN / 8 / WAVES;
@@ -333,7 +325,11 @@ __device__ __forceinline__ void load_lds4(const void* src, void* lds_dst) {
 // holds output row m = l & 15 of the sub-tile and the four consecutive columns
 // n = 4 (l >> 4) + 0..3.  Each lane therefore needs one activation scale per
 // sub-tile row block, and the epilogue writes 8 contiguous bytes per sub-tile.
-template <class T>
+// kGuard: some rows of this tile lie past m_end.  Each wave then skips the
+// MFMAs and folds of its 16-row sub-tile rows that lie entirely past m_end
+// (a wave-uniform test); full tiles run the unguarded, explicitly scheduled
+// loop.
+template <class T, bool kGuard>
 __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
                                               const float* __restrict__ as,
                                               const uint8_t* __restrict__ b,
@@ -407,6 +403,16 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
 #pragma unroll
         for (int j = 0; j < T::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
+    // a workgroup that walks several tiles must not refill a stage that a
+    // slower wave still reads for the previous tile
+    barrier_lds();
+    int tm_valid = T::TM;
+    if (kGuard) {
+        const int64_t rows = m_end - (m0 + wm0);
+        tm_valid = rows <= 0 ? 0 : (rows >= 16 * T::TM ? T::TM : (int)((rows + 15) / 16));
+        tm_valid = __builtin_amdgcn_readfirstlane(tm_valid);
+    }
+
     // prologue: K blocks 0 .. NSTAGE-2 in flight
 #pragma unroll
     for (int st = 0; st + 1 < T::NSTAGE; ++st)
@@ -423,6 +429,8 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
         // this wave's loads of block kb are done once at most the later
         // blocks' loads are outstanding; the barrier then makes every wave's
         // loads visible and guarantees stage (kb-1) is no longer being read
+        // loads complete in issue order; after block kb's loads, at most the
+        // loads of blocks kb+1 .. kb+NSTAGE-2 may be outstanding
         if (kb + T::NSTAGE - 2 < KB)
             wait_vmcnt<T::LOADS_PER_STAGE * (T::NSTAGE - 2)>();
         else
@@ -450,52 +458,69 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
             const v4f s4 = *(const v4f*)(Ss + sread + i);
             sc[i] = s4[0] * sbv; sc[i + 1] = s4[1] * sbv; sc[i + 2] = s4[2] * sbv; sc[i + 3] = s4[3] * sbv;
         }
-        // MFMAs of sub-tile row i are issued before the fold of row i - 1, so
-        // each block product has TN MFMAs of distance before it is read; the
-        // A fragment of row i + 1 is read from LDS while row i multiplies.
-        v4f prev[T::TN];
-        v8i fa_next;
-        {
-            const uint8_t* r = As + (wm0 + lr) * kBlock;
-            fa_next = frag_from(*(const uint4*)(r + off0), *(const uint4*)(r + off1));
-        }
-#pragma unroll
-        for (int i = 0; i < T::TM; ++i) {
-            const v8i fa = fa_next;
-            if (i + 1 < T::TM) {
-                const uint8_t* r = As + (wm0 + 16 * (i + 1) + lr) * kBlock;
+        if (!kGuard) {
+            // MFMAs of sub-tile row i are issued before the fold of row i - 1,
+            // so each block product has TN MFMAs of distance before it is
+            // read; the A fragment of row i + 1 is read while row i multiplies.
+            v4f prev[T::TN];
+            v8i fa_next;
+            {
+                const uint8_t* r = As + (wm0 + lr) * kBlock;
                 fa_next = frag_from(*(const uint4*)(r + off0), *(const uint4*)(r + off1));
             }
-            v4f cur[T::TN];
+#pragma unroll
+            for (int i = 0; i < T::TM; ++i) {
+                const v8i fa = fa_next;
+                if (i + 1 < T::TM) {
+                    const uint8_t* r = As + (wm0 + 16 * (i + 1) + lr) * kBlock;
+                    fa_next = frag_from(*(const uint4*)(r + off0), *(const uint4*)(r + off1));
+                }
+                v4f cur_p[T::TN];
+#pragma unroll
+                for (int j = 0; j < T::TN; ++j)
+                    cur_p[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        fb[j], fa, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                if (i > 0) {
+#pragma unroll
+                    for (int j = 0; j < T::TN; ++j)
+                        acc[i - 1][j] = prev[j] * sc[i - 1] + acc[i - 1][j];
+                }
+#pragma unroll
+                for (int j = 0; j < T::TN; ++j) prev[j] = cur_p[j];
+            }
 #pragma unroll
             for (int j = 0; j < T::TN; ++j)
-                cur[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    fb[j], fa, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-            if (i > 0) {
+                acc[T::TM - 1][j] = prev[j] * sc[T::TM - 1] + acc[T::TM - 1][j];
+            // Instruction order of this K block, given to the scheduler: the
+            // B / scale / first-A reads and the scale products, then per
+            // sub-tile row the next A read and TN x (1 MFMA, 4 fold FMAs).
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * T::TN + T::TM / 4 + 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, T::TM, 0);
 #pragma unroll
-                for (int j = 0; j < T::TN; ++j) acc[i - 1][j] = prev[j] * sc[i - 1] + acc[i - 1][j];
+            for (int i = 0; i < T::TM; ++i) {
+                if (i + 1 < T::TM) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+                for (int j = 0; j < T::TN; ++j) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                }
             }
+            __builtin_amdgcn_sched_group_barrier(0x002, 4 * T::TN, 0);
+        } else {
 #pragma unroll
-            for (int j = 0; j < T::TN; ++j) prev[j] = cur[j];
-        }
+            for (int i = 0; i < T::TM; ++i) {
+                if (i < tm_valid) {
+                    const uint8_t* r = As + (wm0 + 16 * i + lr) * kBlock;
+                    const v8i fa = frag_from(*(const uint4*)(r + off0), *(const uint4*)(r + off1));
 #pragma unroll
-        for (int j = 0; j < T::TN; ++j) acc[T::TM - 1][j] = prev[j] * sc[T::TM - 1] + acc[T::TM - 1][j];
-        // Instruction order of this K block, given to the scheduler: the
-        // direct loads, the B / scale / first-A reads and the scale products,
-        // then per sub-tile row the next A read and TN x (1 MFMA, 4 fold FMAs).
-        __builtin_amdgcn_sched_group_barrier(0x020, T::A_INSTR + T::B_INSTR + 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * T::TN + T::TM / 4 + 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, T::TM, 0);
-#pragma unroll
-        for (int i = 0; i < T::TM; ++i) {
-            if (i + 1 < T::TM) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-            for (int j = 0; j < T::TN; ++j) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                    for (int j = 0; j < T::TN; ++j) {
+                        const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            fb[j], fa, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                        acc[i][j] = p * sc[i] + acc[i][j];
+                    }
+                }
             }
         }
-        __builtin_amdgcn_sched_group_barrier(0x002, 4 * T::TN, 0);
         cur = cur + 1 == T::NSTAGE ? 0 : cur + 1;
     }
 
@@ -560,13 +585,113 @@ __global__ __launch_bounds__(T::THREADS, 1) void gemm_big_kernel(const uint8_t* 
     __shared__ __attribute__((aligned(1024))) uint8_t lds[T::NSTAGE * T::STAGE];
     int tm, tn;
     tile_of(blockIdx.x, gridDim.x, mt, nt, tm, tn);
-    gemm_tile_big<T>(a, as, b, bs, c, (int64_t)tm * T::BM, M, (int64_t)tn * T::BN, N, K, lds);
+    const int64_t m0 = (int64_t)tm * T::BM;
+    if (m0 + T::BM <= M)
+        gemm_tile_big<T, false>(a, as, b, bs, c, m0, M, (int64_t)tn * T::BN, N, K, lds);
+    else
+        gemm_tile_big<T, true>(a, as, b, bs, c, m0, M, (int64_t)tn * T::BN, N, K, lds);
+}
+
+// Persistent grouped kernel on the large tiles.
+//
+// Tiles.  Group g (rows off[g] .. off[g+1]) has n_g / BM full M-tiles and,
+// when BM does not divide n_g, one partial M-tile.  A tile is "heavy" when
+// at least half of its rows exist, "light" otherwise; routed experts hold a
+// few rows more or fewer than a multiple of the tile height, so a light tile
+// is typically a handful of rows.  The heavy tiles and the light tiles are
+// two launches of this kernel (kLight): heavy tiles run the full-tile loop
+// (rows past the group's end are computed on clamped inputs and not
+// stored), light tiles the guarded loop that skips sub-tile rows past the
+// group's end.  Keeping the two loops in separate kernels keeps each one's
+// registers to itself, and the light tiles fill a pass of their own instead
+// of stretching every round of the heavy pass.
+//
+// Order and placement.  Inside each list: group by group, N-tile by N-tile,
+// M-tile fastest.  Workgroups are dealt round-robin over the 8 XCDs; in each
+// round the workgroups of one XCD take a contiguous run of tiles, so one XCD
+// works on a few experts' weights and rows at a time.  Every workgroup
+// leaves the loop once the rounds cover all tiles of its list.
+struct GroupTiles {
+    int64_t m_heavy, m_light;   // M-tiles of one group by kind
+};
+
+template <int BM>
+__device__ __forceinline__ GroupTiles group_tiles(int64_t rows) {
+    const int64_t full = rows / BM;
+    const int64_t rem = rows - full * BM;
+    GroupTiles t;
+    t.m_heavy = full + (rem >= BM / 2 ? 1 : 0);
+    t.m_light = (rem > 0 && rem < BM / 2) ? 1 : 0;
+    return t;
+}
+
+template <class T, bool kLight>
+__global__ __launch_bounds__(T::THREADS, 1) void gemm_grouped_big_kernel(
+    const uint8_t* __restrict__ a, const float* __restrict__ as, const uint8_t* __restrict__ b,
+    const float* __restrict__ bs, uint16_t* __restrict__ c, const int32_t* __restrict__ off,
+    int G, int64_t N, int64_t K, int nt) {
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[T::NSTAGE * T::STAGE];
+    const int64_t KB = K / kBlock;
+    const int64_t NB = (N + kBlock - 1) / kBlock;
+    int64_t total = 0;
+    for (int g = 0; g < G; ++g) {
+        const GroupTiles gt = group_tiles<T::BM>((int64_t)off[g + 1] - off[g]);
+        total += (kLight ? gt.m_light : gt.m_heavy) * nt;
+    }
+    const int nwg = gridDim.x;                    // a multiple of 8
+    const int xcd = blockIdx.x % 8, local = blockIdx.x / 8;
+    const int per_xcd = nwg / 8;
+    for (int64_t round = 0; round * nwg < total; ++round) {
+        const int64_t t = round * nwg + (int64_t)xcd * per_xcd + local;
+        if (t >= total) continue;
+        int64_t rest = t;
+        int g = 0;
+        int64_t tm = 0, tn = 0;
+        for (; g < G; ++g) {
+            const GroupTiles gt = group_tiles<T::BM>((int64_t)off[g + 1] - off[g]);
+            const int64_t mcount = kLight ? gt.m_light : gt.m_heavy;
+            if (rest < mcount * nt) {
+                tm = (kLight ? gt.m_heavy : 0) + rest % mcount;
+                tn = rest / mcount;
+                break;
+            }
+            rest -= mcount * nt;
+        }
+        const int64_t m0 = (int64_t)off[g] + tm * T::BM, m_end = off[g + 1];
+        gemm_tile_big<T, kLight>(a, as, b + (int64_t)g * N * K, bs + (int64_t)g * NB * KB, c, m0,
+                                 m_end, tn * T::BN, N, K, lds);
+    }
 }
 
 using TileLarge = Tile<128, 128>;
 using TileSmall = Tile<64, 64>;
 
-size_t gemm_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
+// Split-K plan for skinny problems (M <= 64): enough (tile, split) pairs for
+// about 512 workgroups, at least 2 K blocks per split.  Host-only arithmetic,
+// so bfp8_gemm_workspace_size needs no device.
+struct SplitPlan {
+    int splits, kb_per;
+};
+
+static SplitPlan split_plan(int64_t M, int64_t N, int64_t K) {
+    SplitPlan p{1, (int)(K / kBlock)};
+    if (M > 64) return p;
+    const int64_t tiles = ((M + 63) / 64) * ((N + 63) / 64);
+    const int64_t KB = K / kBlock;
+    int64_t want = (512 + tiles - 1) / tiles;
+    if (want > KB / 2) want = KB / 2;
+    if (want < 2) return p;
+    const int64_t kb_per = (KB + want - 1) / want;
+    p.kb_per = (int)kb_per;
+    p.splits = (int)((KB + kb_per - 1) / kb_per);
+    return p;
+}
+
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    const SplitPlan p = split_plan(M, N, K);
+    if (p.splits < 2) return 0;
+    return (size_t)p.splits * (size_t)M * (size_t)N * sizeof(float);
+}
 
 using BigSquare = BigTile<256, 256, 2, 4, 2>;   // 8 waves of 128 x 64, 2 stages
 using BigWide = BigTile<256, 128, 4, 2, 3>;     // 8 waves of 64 x 64, 3 stages
@@ -601,8 +726,26 @@ const char* gemm_config_name(GemmConfig cfg) {
 }
 
 hipError_t launch_gemm(const void* a, const float* as, const void* b, const float* bs, void* c,
-                       int64_t M, int64_t N, int64_t K, void* /*workspace*/,
-                       size_t /*workspace_bytes*/, hipStream_t stream) {
+                       int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+    const SplitPlan plan = split_plan(M, N, K);
+    if (workspace && plan.splits >= 2 &&
+        workspace_bytes >= (size_t)plan.splits * (size_t)M * (size_t)N * sizeof(float)) {
+        using T = TileSmall;
+        const int mt = (int)((M + T::BM - 1) / T::BM), nt = (int)((N + T::BN - 1) / T::BN);
+        hipLaunchKernelGGL(gemm_splitk_kernel<T>, dim3(mt * nt, plan.splits), dim3(256), 0,
+                           stream, (const uint8_t*)a, as, (const uint8_t*)b, bs, (float*)workspace,
+                           M, N, K, mt, plan.kb_per);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int64_t MN = M * N;
+        int64_t grid = (MN + 255) / 256;
+        const int64_t cap = (int64_t)device_cu_count() * 8;
+        grid = grid < cap ? grid : cap;
+        hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                           (const float*)workspace, (uint16_t*)c, MN, plan.splits);
+        return hipGetLastError();
+    }
     switch (gemm_config(M, N, K)) {
         case GemmConfig::kBig256x256:
             launch_big<BigSquare>(a, as, b, bs, c, M, N, K, stream);
@@ -633,14 +776,24 @@ hipError_t launch_gemm(const void* a, const float* as, const void* b, const floa
 hipError_t launch_gemm_grouped(const void* a, const float* as, const void* b, const float* bs,
                                void* c, const int32_t* off, int32_t G, int64_t total_M,
                                int64_t N, int64_t K, hipStream_t stream) {
-    using T = TileLarge;
+    using T = BigSquare;
     const int nt = (int)((N + T::BN - 1) / T::BN);
-    const int64_t max_tiles = ((total_M + T::BM - 1) / T::BM + G) * (int64_t)nt;
-    const int64_t cap = (int64_t)device_cu_count() * 2;
-    const int grid = (int)(max_tiles < cap ? max_tiles : cap);
-    hipLaunchKernelGGL(gemm_grouped_kernel<T>, dim3(grid), dim3(256), 0, stream,
-                       (const uint8_t*)a, as, (const uint8_t*)b, bs, (uint16_t*)c, off, (int)G, N,
-                       K, nt);
+    // upper bounds of the tile counts (the exact ones depend on the device offsets)
+    const int64_t max_heavy = ((total_M + T::BM / 2 - 1) / (T::BM / 2)) * (int64_t)nt;
+    const int64_t max_light = (int64_t)G * nt;
+    const int64_t cus = device_cu_count();
+    int64_t grid_h = max_heavy < cus ? max_heavy : cus;
+    int64_t grid_l = max_light < cus ? max_light : cus;
+    grid_h = (grid_h + 7) / 8 * 8;
+    grid_l = (grid_l + 7) / 8 * 8;
+    hipLaunchKernelGGL((gemm_grouped_big_kernel<T, false>), dim3((unsigned)grid_h),
+                       dim3(T::THREADS), 0, stream, (const uint8_t*)a, as, (const uint8_t*)b, bs,
+                       (uint16_t*)c, off, (int)G, N, K, nt);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((gemm_grouped_big_kernel<T, true>), dim3((unsigned)grid_l),
+                       dim3(T::THREADS), 0, stream, (const uint8_t*)a, as, (const uint8_t*)b, bs,
+                       (uint16_t*)c, off, (int)G, N, K, nt);
     return hipGetLastError();
 }
 

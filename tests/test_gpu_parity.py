@@ -261,6 +261,29 @@ def test_gemm_ragged_shapes():
     assert len(seen) >= 4, f"every kernel configuration should be exercised, saw {seen}"
 
 
+def test_gemm_split_k_workspace():
+    """Skinny shapes with a workspace take the split-K path; same tolerance, and the
+    result does not depend on what the workspace held before."""
+    from block_scaled_fp8_04_amd import synth
+    g = torch.Generator().manual_seed(6)
+    for (M, N, K) in ((64, 1536, 7168), (37, 300, 1152), (1, 3000, 1024), (64, 7168, 2048),
+                      (50, 129, 640)):
+        need = bfp8.bfp8_gemm_workspace_size(M, N, K)
+        assert need > 0, (M, N, K)
+        x = torch.randn(M, K, generator=g).to(torch.bfloat16).to(dev())
+        q, s = bfp8.act_quant(x)
+        w, ws = synth.weight(N, K, 900 + M, 950 + N)
+        w, ws = w.to(dev()), ws.to(dev())
+        work = torch.full((need // 4,), float("nan"), dtype=torch.float32, device=dev())
+        c1 = _gemm_case(q, s, w, ws, f"split-k[{M},{N},{K}]", workspace=work)
+        work.fill_(1e30)
+        c2 = bfp8.gemm(q, s, w, ws, workspace=work)
+        torch.cuda.synchronize()
+        assert torch.equal(c1, c2), "split-K result depends on the workspace contents"
+        with pytest.raises(bfp8.Bfp8Error):
+            bfp8.bfp8_gemm(q, s, w, ws, torch.empty_like(c1), work[: need // 4 - 4])
+
+
 def test_gemm_identity_bit_exact():
     """G3: W = I (code 0x38, scale 1) gives bf16(fl32(dec(q) * s)) exactly."""
     wl = workload(0)
