@@ -228,6 +228,9 @@ def main():
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="dense-mlp")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 512 MiB device copy three times (reference for the "
+                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -237,8 +240,18 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
-    bfp8.library()
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = 512 * 1024 * 1024
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
+        return
+    bfp8.library()
 
     t0 = time.time()
     wl = synth.make(WORKLOADS[args.workload])
