@@ -5,18 +5,20 @@
 // with per-block scales"), also what the offline fp8->bf16 conversion does to
 // each 1-byte tensor with its scale ("Behavior traces", fp8->bf16 trace).
 //
-// Vector kernel (K % 16 == 0, 16-byte aligned w and out): each lane turns one
-// 16-byte chunk of codes (16 elements, inside one 128-wide scale block) into
-// two 16-byte bf16 stores, so the kernel streams 3 bytes per element at HBM
-// rate.  The gfx950 packed fp8 -> fp32 conversion decodes, one fp32 multiply
-// applies the block scale, and the bf16 rounding is the nearest-even bit rule.
-// Scalar kernel: one element per lane for any other shape or alignment.
+// Vector kernel (K % 8 == 0, N*K a multiple of 1024, 8-byte aligned codes,
+// 16-byte aligned output): fully contiguous 512-byte loads and 1 KB stores per
+// wave instruction (see dequant_vec_kernel), so the kernel streams 3 bytes
+// per element.  The gfx950 packed fp8 -> fp32 conversion decodes, one fp32
+// multiply applies the block scale, and the packed fp32 -> bf16 conversion
+// rounds to nearest even.  Scalar kernel: one element per lane for any other
+// shape or alignment.
 #include "device_codec.hpp"
 #include "internal.hpp"
 
 namespace bfp8 {
 
-__device__ __forceinline__ uint4 dequant16_lo(uint32_t w0, uint32_t w1, float s) {
+// Eight codes (two dwords) -> eight bf16 (one 16-byte store), one scale.
+__device__ __forceinline__ uint4 dequant8(uint32_t w0, uint32_t w1, float s) {
     float f[8];
     e4m3_decode2<false>(w0, f[0], f[1]);
     e4m3_decode2<true>(w0, f[2], f[3]);
@@ -30,22 +32,37 @@ __device__ __forceinline__ uint4 dequant16_lo(uint32_t w0, uint32_t w1, float s)
     return o;
 }
 
-// chunks = N * K / 16 (< 2^31); kc = K / 16; kb = ceil(K / 128).
-__global__ __launch_bounds__(256) void dequant_vec_kernel(const uint4* __restrict__ w,
+__device__ __forceinline__ uint2 load_nt8(const uint2* p) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 v = __builtin_nontemporal_load((const u32x2*)p);
+    return make_uint2(v.x, v.y);
+}
+
+// A wave's unit of work is 1 KB of codes -> 2 KB of bf16.  Lane l converts
+// the 8 codes at 8 l and the 8 codes at 512 + 8 l and stores 16 bytes at 16 l
+// and at 1024 + 16 l, so every load instruction reads 512 contiguous bytes and
+// every store instruction writes 1 KB contiguous bytes.  Eight codes never
+// straddle a 128-wide scale block (8 divides 128).
+// units = N * K / 1024 (< 2^31); kc = K / 8 (8-code groups per row); kb = ceil(K / 128).
+__global__ __launch_bounds__(256) void dequant_vec_kernel(const uint2* __restrict__ w,
                                                           const float* __restrict__ s,
                                                           uint4* __restrict__ out,
-                                                          uint32_t chunks, uint32_t kc,
+                                                          uint32_t units, uint32_t kc,
                                                           uint32_t kb) {
-    const uint32_t stride = gridDim.x * blockDim.x;
-    for (uint32_t c = blockIdx.x * blockDim.x + threadIdx.x; c < chunks; c += stride) {
-        const uint4 v = load_nt(w + c);
-        const uint32_t n = c / kc;
-        const uint32_t k16 = c - n * kc;
-        const float sc = s[(n >> 7) * kb + (k16 >> 3)];
-        const uint4 o0 = dequant16_lo(v.x, v.y, sc);
-        const uint4 o1 = dequant16_lo(v.z, v.w, sc);
-        store_nt(out + 2 * (size_t)c, o0);
-        store_nt(out + 2 * (size_t)c + 1, o1);
+    const int lane = threadIdx.x & 63;
+    const uint32_t wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const uint32_t waves = (gridDim.x * blockDim.x) >> 6;
+    for (uint32_t u = wave; u < units; u += waves) {
+        const uint32_t g0 = u * 128 + lane;          // 8-code group index
+        const uint32_t g1 = g0 + 64;
+        const uint2 v0 = load_nt8(w + g0);
+        const uint2 v1 = load_nt8(w + g1);
+        const uint32_t n0 = g0 / kc, n1 = g1 / kc;
+        const uint32_t k0 = g0 - n0 * kc, k1 = g1 - n1 * kc;
+        const float s0 = s[(n0 >> 7) * kb + (k0 >> 4)];
+        const float s1 = s[(n1 >> 7) * kb + (k1 >> 4)];
+        store_nt(out + g0, dequant8(v0.x, v0.y, s0));
+        store_nt(out + g1, dequant8(v1.x, v1.y, s1));
     }
 }
 
@@ -67,15 +84,16 @@ __global__ __launch_bounds__(256) void dequant_scalar_kernel(const uint8_t* __re
 hipError_t launch_weight_dequant(const void* w, const float* s, void* out, int64_t N, int64_t K,
                                  hipStream_t stream) {
     const int64_t total = N * K;
-    const bool vec = (K % 16 == 0) && (((uintptr_t)w & 15u) == 0) &&
-                     (((uintptr_t)out & 15u) == 0) && (total / 16 < ((int64_t)1 << 31));
+    const bool vec = (K % 8 == 0) && (total % 1024 == 0) && (((uintptr_t)w & 7u) == 0) &&
+                     (((uintptr_t)out & 15u) == 0) && (total / 1024 < ((int64_t)1 << 31)) &&
+                     (total / 8 < ((int64_t)1 << 32));
     const int64_t cap = (int64_t)device_cu_count() * 8;
     if (vec) {
-        const int64_t chunks = total / 16;
-        const int64_t need = (chunks + 255) / 256;
+        const int64_t units = total / 1024;                 // one unit per wave step
+        const int64_t need = (units + 3) / 4;                // 4 waves per workgroup
         const int grid = (int)(need < cap ? (need > 0 ? need : 1) : cap);
-        hipLaunchKernelGGL(dequant_vec_kernel, dim3(grid), dim3(256), 0, stream, (const uint4*)w,
-                           s, (uint4*)out, (uint32_t)chunks, (uint32_t)(K / 16),
+        hipLaunchKernelGGL(dequant_vec_kernel, dim3(grid), dim3(256), 0, stream, (const uint2*)w,
+                           s, (uint4*)out, (uint32_t)units, (uint32_t)(K / 8),
                            (uint32_t)((K + kBlock - 1) / kBlock));
     } else {
         const int64_t need = (total + 255) / 256;

@@ -80,8 +80,8 @@ int bfp8_act_quant(const void* x_bf16, void* q_e4m3, float* scales,
  *   w_e4m3  : e4m3 [N, K]
  *   s       : fp32 [ceil(N/128), ceil(K/128)]; partial edge blocks allowed
  *   out_bf16: bf16 [N, K] output
- * Any N, K >= 0.  A vectorized kernel is used when K % 16 == 0 and w/out are
- * 16-byte aligned, a scalar one otherwise.
+ * Any N, K >= 0.  A vectorized kernel is used when K % 8 == 0, N*K is a
+ * multiple of 1024, w is 8-byte and out 16-byte aligned; a scalar one otherwise.
  * Errors: BFP8_ERR_SHAPE if N < 0 or K < 0; BFP8_ERR_NULL for a NULL pointer
  * when N*K > 0; BFP8_ERR_ALIGN if out is not 2-byte or s not 4-byte aligned. */
 int bfp8_weight_dequant(const void* w_e4m3, const float* s, void* out_bf16,

@@ -181,7 +181,8 @@ def test_weight_dequant_configs(config, key):
 
 def test_weight_dequant_ragged_and_unaligned():
     from block_scaled_fp8_04_amd import synth
-    for (N, K, off) in ((300, 200, 0), (129, 144, 0), (1, 16, 0), (257, 384, 1), (130, 272, 3)):
+    for (N, K, off) in ((300, 200, 0), (129, 144, 0), (1, 16, 0), (257, 384, 1), (130, 272, 3),
+                        (128, 136, 0), (1000, 1024, 0), (8, 128, 0)):
         w, s = synth.weight(N, K, 500 + N, 600 + K)
         _dequant_case(w, s, f"ragged[{N},{K}]", offset=off)
     # every code with unit and power-of-two scales
