@@ -228,30 +228,33 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t* __restrict_
                  K / kBlock, nullptr);
 }
 
-// Split-K for skinny problems: blockIdx.y picks a run of kb_per K blocks and
-// the fp32 partial sums go to ws[split][M][N]; split_reduce_kernel adds the
-// splits in index order (a fixed order, so results are reproducible).
-template <class T>
-__global__ __launch_bounds__(256, 2) void gemm_splitk_kernel(const uint8_t* __restrict__ a,
-                                                             const float* __restrict__ as,
-                                                             const uint8_t* __restrict__ b,
-                                                             const float* __restrict__ bs,
-                                                             float* __restrict__ ws, int64_t M,
-                                                             int64_t N, int64_t K, int mt,
-                                                             int kb_per) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * T::STAGE];
-    const int tm = blockIdx.x % mt, tn = blockIdx.x / mt;
-    const int64_t KB = K / kBlock;
-    const int64_t kb0 = (int64_t)blockIdx.y * kb_per;
-    const int64_t kb1 = kb0 + kb_per < KB ? kb0 + kb_per : KB;
-    gemm_tile<T>(a, as, b, bs, nullptr, (int64_t)tm * T::BM, M, (int64_t)tn * T::BN, N, K, lds,
-                 kb0, kb1, ws + (int64_t)blockIdx.y * M * N);
-}
-
+// Adds the split-K partial sums ws[0..splits)[M][N] in index order (a fixed
+// order, so results are reproducible) and rounds to bf16.
 __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ ws,
                                                            uint16_t* __restrict__ c,
                                                            int64_t MN, int splits) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    if (MN % 4 == 0 && ((uintptr_t)c & 7u) == 0) {
+        const int64_t n4 = MN / 4;
+        for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+            // loads of up to 8 splits are issued together, then added in index order
+            v4f sum = v4f{0.f, 0.f, 0.f, 0.f};
+            for (int sp0 = 0; sp0 < splits; sp0 += 8) {
+                v4f part[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    if (sp0 + q < splits) part[q] = ((const v4f*)(ws + (int64_t)(sp0 + q) * MN))[i];
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    if (sp0 + q < splits) sum = (sp0 + q == 0) ? part[q] : sum + part[q];
+            }
+            uint2 o;
+            o.x = pack_bf16x2(sum[0], sum[1]);
+            o.y = pack_bf16x2(sum[2], sum[3]);
+            ((uint2*)c)[i] = o;
+        }
+        return;
+    }
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < MN; i += stride) {
         float sum = ws[i];
         for (int sp = 1; sp < splits; ++sp) sum += ws[(int64_t)sp * MN + i];
@@ -270,6 +273,8 @@ struct BigTile {
     // Row scales of one K block, permuted for the fragment layout: row 16 i + t
     // sits at float t * SPITCH + i.  SPITCH = BM/16 + 4 keeps the 16 lanes of a
     // read on distinct bank groups and each lane's TM values 16-byte aligned.
+    // The weight scale of the tile's n-th 128-column block sits in the first
+    // pad slot of line n, at float n * SPITCH + BM/16.
     static constexpr int SPITCH = BM / 16 + 4;
     static constexpr int S_FLOATS = 16 * SPITCH;
     static constexpr int S_INSTR = (S_FLOATS + 63) / 64;   // 256-byte scale instructions
@@ -285,6 +290,7 @@ struct BigTile {
     static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns must share one scale block");
     static_assert(S_INSTR <= WAVES, "one scale instruction per wave at most");
     static_assert(TM % 4 == 0, "scales are read four at a time");
+    static_assert(BN / 128 <= 16 || BN < 128, "weight scales use one pad slot per line");
     static_assert(STAGE % 1024 == 0, "stages stay 1 KB aligned");
     static_assert(NSTAGE >= 2 && NSTAGE * STAGE <= 160 * 1024, "stages must fit in LDS");
 };
@@ -342,7 +348,6 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
     const int wm0 = (wave / T::WAVES_N) * T::WM;
     const int wn0 = (wave % T::WAVES_N) * T::WN;
     const int64_t KB = K / kBlock;
-    const int64_t NB = (N + kBlock - 1) / kBlock;
 
     // Direct-load sources.  Instruction i of this wave fills LDS rows
     // r0 .. r0+7 (r0 = 8 * (wave * INSTR + i)); lane l writes physical chunk
@@ -367,22 +372,28 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
         gcol = gcol < N ? gcol : N - 1;
         b_off[i] = (uint32_t)((gcol - n0) * K) + chunk * 16;
     }
-    // scale slot p = t * SPITCH + i holds row 16 i + t (pad slots load row 0)
-    uint32_t s_off = 0;
+    // scale slot p = t * SPITCH + i holds the activation scale of row 16 i + t;
+    // slot t * SPITCH + BM/16 holds the weight scale of the tile's 128-column
+    // block t; other pad slots load row 0's scale (never read)
+    const int64_t NBK = (N + kBlock - 1) / kBlock;
+    const float* s_src;
     {
         const int p = wave * 64 + lane;
         const int t = p / T::SPITCH, i = p % T::SPITCH;
-        int row = (t < 16 && i < T::BM / 16) ? 16 * i + t : 0;
-        int64_t grow = m0 + row;
-        grow = grow < m_end ? grow : m_end - 1;
-        s_off = (uint32_t)((grow - m0) * KB);
+        if (i == T::BM / 16 && t < (T::BN + 127) / 128) {
+            int64_t nb = (n0 >> 7) + t;
+            nb = nb < NBK ? nb : NBK - 1;
+            s_src = bs + nb * KB;
+        } else {
+            const int row = (t < 16 && i < T::BM / 16) ? 16 * i + t : 0;
+            int64_t grow = m0 + row;
+            grow = grow < m_end ? grow : m_end - 1;
+            s_src = as + grow * KB;
+        }
     }
     const uint8_t* a_tile = a + m0 * K;
     const uint8_t* b_tile = b + n0 * K;
-    const float* s_tile = as + m0 * KB;
-    int64_t nblk = (n0 + wn0) >> 7;
-    nblk = nblk < NB ? nblk : NB - 1;
-    const float* sb_src = bs + nblk * KB;
+    const int sb_slot = ((wn0 >> 7) * T::SPITCH + T::BM / 16);   // this wave's weight scale
 
     auto issue = [&](int64_t kb, int stage) {
         uint8_t* base = lds + stage * T::STAGE;
@@ -394,7 +405,7 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
 #pragma unroll
         for (int i = 0; i < T::B_INSTR; ++i)
             load_lds16(bk + b_off[i], base + T::A_BYTES + (wave * T::B_INSTR + i) * 1024);
-        load_lds4(s_tile + kb + s_off, base + T::A_BYTES + T::B_BYTES + wave * 256);
+        load_lds4(s_src + kb, base + T::A_BYTES + T::B_BYTES + wave * 256);
     };
 
     v4f acc[T::TM][T::TN];
@@ -445,68 +456,94 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
         const uint8_t* As = lds + cur * T::STAGE;
         const uint8_t* Bs = As + T::A_BYTES;
         const float* Ss = (const float*)(Bs + T::B_BYTES);
-        v8i fb[T::TN];
-#pragma unroll
-        for (int j = 0; j < T::TN; ++j) {
-            const uint8_t* r = Bs + (wn0 + 16 * j + lr) * kBlock;
-            fb[j] = frag_from(*(const uint4*)(r + off0), *(const uint4*)(r + off1));
-        }
-        const float sbv = sb_src[kb];
-        float sc[T::TM];
-#pragma unroll
-        for (int i = 0; i < T::TM; i += 4) {
-            const v4f s4 = *(const v4f*)(Ss + sread + i);
-            sc[i] = s4[0] * sbv; sc[i + 1] = s4[1] * sbv; sc[i + 2] = s4[2] * sbv; sc[i + 3] = s4[3] * sbv;
-        }
         if (!kGuard) {
-            // MFMAs of sub-tile row i are issued before the fold of row i - 1,
-            // so each block product has TN MFMAs of distance before it is
-            // read; the A fragment of row i + 1 is read while row i multiplies.
-            v4f prev[T::TN];
-            v8i fa_next;
+            // The K block as a fixed sequence of small scheduling regions
+            // (sched_barrier keeps the compiler from reordering across them):
+            // a wave starts multiplying once A row 0 and B fragment 0 are in
+            // registers; each further B fragment is read during the previous
+            // MFMA; the scales arrive with the last MFMA of row 0; then every
+            // sub-tile row issues its TN MFMAs interleaved with the folds of
+            // the previous row while the next A row is read.
+            v8i fb[T::TN];
+            v8i fa_cur, fa_nxt;
+            v4f cur_p[T::TN], prev[T::TN];
+            float sc[T::TM];
             {
                 const uint8_t* r = As + (wm0 + lr) * kBlock;
-                fa_next = frag_from(*(const uint4*)(r + off0), *(const uint4*)(r + off1));
+                fa_cur = frag_from(*(const uint4*)(r + off0), *(const uint4*)(r + off1));
+                const uint8_t* q = Bs + (wn0 + lr) * kBlock;
+                fb[0] = frag_from(*(const uint4*)(q + off0), *(const uint4*)(q + off1));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            v4f s4[T::TM / 4];
+            float sbv = 0.f;
+#pragma unroll
+            for (int j = 0; j < T::TN; ++j) {
+                if (j + 1 < T::TN) {
+                    const uint8_t* q = Bs + (wn0 + 16 * (j + 1) + lr) * kBlock;
+                    fb[j + 1] = frag_from(*(const uint4*)(q + off0), *(const uint4*)(q + off1));
+                } else {
+#pragma unroll
+                    for (int i = 0; i < T::TM; i += 4) s4[i / 4] = *(const v4f*)(Ss + sread + i);
+                    sbv = Ss[sb_slot];
+                }
+                cur_p[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    fb[j], fa_cur, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            {
+                const uint8_t* r = As + (wm0 + 16 + lr) * kBlock;
+                fa_nxt = frag_from(*(const uint4*)(r + off0), *(const uint4*)(r + off1));
             }
 #pragma unroll
-            for (int i = 0; i < T::TM; ++i) {
-                const v8i fa = fa_next;
+            for (int i = 0; i < T::TM; i += 4) {
+                sc[i] = s4[i / 4][0] * sbv; sc[i + 1] = s4[i / 4][1] * sbv;
+                sc[i + 2] = s4[i / 4][2] * sbv; sc[i + 3] = s4[i / 4][3] * sbv;
+            }
+#pragma unroll
+            for (int j = 0; j < T::TN; ++j) prev[j] = cur_p[j];
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 1; i < T::TM; ++i) {
+                fa_cur = fa_nxt;
                 if (i + 1 < T::TM) {
                     const uint8_t* r = As + (wm0 + 16 * (i + 1) + lr) * kBlock;
-                    fa_next = frag_from(*(const uint4*)(r + off0), *(const uint4*)(r + off1));
+                    fa_nxt = frag_from(*(const uint4*)(r + off0), *(const uint4*)(r + off1));
                 }
-                v4f cur_p[T::TN];
 #pragma unroll
-                for (int j = 0; j < T::TN; ++j)
+                for (int j = 0; j < T::TN; ++j) {
                     cur_p[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        fb[j], fa, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-                if (i > 0) {
-#pragma unroll
-                    for (int j = 0; j < T::TN; ++j)
-                        acc[i - 1][j] = prev[j] * sc[i - 1] + acc[i - 1][j];
+                        fb[j], fa_cur, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                    acc[i - 1][j] = prev[j] * sc[i - 1] + acc[i - 1][j];
                 }
 #pragma unroll
                 for (int j = 0; j < T::TN; ++j) prev[j] = cur_p[j];
-            }
-#pragma unroll
-            for (int j = 0; j < T::TN; ++j)
-                acc[T::TM - 1][j] = prev[j] * sc[T::TM - 1] + acc[T::TM - 1][j];
-            // Instruction order of this K block, given to the scheduler: the
-            // B / scale / first-A reads and the scale products, then per
-            // sub-tile row the next A read and TN x (1 MFMA, 4 fold FMAs).
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * T::TN + T::TM / 4 + 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, T::TM, 0);
-#pragma unroll
-            for (int i = 0; i < T::TM; ++i) {
                 if (i + 1 < T::TM) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
                 for (int j = 0; j < T::TN; ++j) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                     __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x002, 4 * T::TN, 0);
+#pragma unroll
+            for (int j = 0; j < T::TN; ++j)
+                acc[T::TM - 1][j] = prev[j] * sc[T::TM - 1] + acc[T::TM - 1][j];
         } else {
+            v8i fb[T::TN];
+#pragma unroll
+            for (int j = 0; j < T::TN; ++j) {
+                const uint8_t* q = Bs + (wn0 + 16 * j + lr) * kBlock;
+                fb[j] = frag_from(*(const uint4*)(q + off0), *(const uint4*)(q + off1));
+            }
+            const float sbv = Ss[sb_slot];
+            float sc[T::TM];
+#pragma unroll
+            for (int i = 0; i < T::TM; i += 4) {
+                const v4f s4 = *(const v4f*)(Ss + sread + i);
+                sc[i] = s4[0] * sbv; sc[i + 1] = s4[1] * sbv;
+                sc[i + 2] = s4[2] * sbv; sc[i + 3] = s4[3] * sbv;
+            }
 #pragma unroll
             for (int i = 0; i < T::TM; ++i) {
                 if (i < tm_valid) {
@@ -663,6 +700,121 @@ __global__ __launch_bounds__(T::THREADS, 1) void gemm_grouped_big_kernel(
     }
 }
 
+// Split-K kernel for skinny problems (M <= 64).  A workgroup owns a 64 x 64
+// output tile and a run of at most SK_MAX_KB K blocks; it issues every
+// direct-to-LDS load of that run at once (one memory latency per workgroup
+// instead of one per K block), waits once, then multiplies.  Four waves of
+// 32 x 32 (2 x 2 sub-tiles), MFMA operands weight-first as in the large-tile
+// kernel (a lane owns one output row and four consecutive columns), scales
+// read straight from global memory.  The fp32 partial sums of split s go to
+// ws[s][M][N]; split_reduce_kernel adds the splits in index order.
+constexpr int SK_MAX_KB = 4;          // 64 KB of LDS at most
+
+__global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint8_t* __restrict__ a,
+                                                          const float* __restrict__ as,
+                                                          const uint8_t* __restrict__ b,
+                                                          const float* __restrict__ bs,
+                                                          float* __restrict__ ws, int64_t M,
+                                                          int64_t N, int64_t K, int mt,
+                                                          int kb_per) {
+    constexpr int BM = 64, BN = 64, BLK = (BM + BN) * kBlock;       // 16 KB per K block
+    extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];  // kb_per * BLK bytes
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tm = blockIdx.x % mt, tn = blockIdx.x / mt;
+    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+    const int64_t KB = K / kBlock;
+    const int64_t kb0 = (int64_t)blockIdx.y * kb_per;
+    const int nkb = (int)((kb0 + kb_per < KB ? kb0 + kb_per : KB) - kb0);
+    const int64_t NBK = (N + kBlock - 1) / kBlock;
+
+    // loads: per K block, 16 instructions of 1 KB (8 for A rows, 8 for B rows),
+    // wave w issues instructions w, w+4, w+8, w+12
+    const int lrow = lane >> 3;
+    for (int kb = 0; kb < nkb; ++kb) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int ins = wave + 4 * q;              // 0..15
+            const bool is_a = ins < 8;
+            const int row = (is_a ? ins : ins - 8) * 8 + lrow;
+            const int chunk = (lane & 7) ^ swz(row);
+            const uint8_t* src;
+            if (is_a) {
+                int64_t g = m0 + row;
+                g = g < M ? g : M - 1;
+                src = a + g * K;
+            } else {
+                int64_t g = n0 + row;
+                g = g < N ? g : N - 1;
+                src = b + g * K;
+            }
+            load_lds16(src + (kb0 + kb) * kBlock + chunk * 16, lds + kb * BLK + ins * 1024);
+        }
+    }
+    const int wm0 = (wave >> 1) * 32, wn0 = (wave & 1) * 32;
+    const int lr = lane & 15;
+    // activation scales of this lane's two rows and the wave's weight scale, per K block
+    int64_t r0 = m0 + wm0 + lr, r1 = r0 + 16;
+    r0 = r0 < M ? r0 : M - 1;
+    r1 = r1 < M ? r1 : M - 1;
+    int64_t nb = (n0 + wn0) >> 7;
+    nb = nb < NBK ? nb : NBK - 1;
+    wait_vmcnt<0>();
+    barrier_lds();
+
+    const int lk = (lane >> 4) * 2;
+    const int off0 = ((lk ^ swz(lr)) << 4);
+    const int off1 = (((lk + 1) ^ swz(lr)) << 4);
+    v4f acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int kb = 0; kb < nkb; ++kb) {
+        const uint8_t* As = lds + kb * BLK;
+        const uint8_t* Bs = As + BM * kBlock;
+        v8i fa[2], fb[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint8_t* r = As + (wm0 + 16 * i + lr) * kBlock;
+            fa[i] = frag_from(*(const uint4*)(r + off0), *(const uint4*)(r + off1));
+            const uint8_t* q = Bs + (wn0 + 16 * i + lr) * kBlock;
+            fb[i] = frag_from(*(const uint4*)(q + off0), *(const uint4*)(q + off1));
+        }
+        const int64_t k = kb0 + kb;
+        const float sbv = bs[nb * KB + k];
+        const float sc0 = as[r0 * KB + k] * sbv, sc1 = as[r1 * KB + k] * sbv;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const v4f p0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                fb[j], fa[0], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+            const v4f p1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                fb[j], fa[1], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+            acc[0][j] = p0 * sc0 + acc[0][j];
+            acc[1][j] = p1 * sc1 + acc[1][j];
+        }
+    }
+    float* part = ws + (int64_t)blockIdx.y * M * N;
+    const int cq = 4 * (lane >> 4);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int64_t row = m0 + wm0 + 16 * i + lr;
+        if (row >= M) continue;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int64_t col = n0 + wn0 + 16 * j + cq;
+            float* dst = part + row * N + col;
+            if (col + 3 < N && (N % 4 == 0)) {
+                *(v4f*)dst = acc[i][j];
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (col + r < N) dst[r] = acc[i][j][r];
+            }
+        }
+    }
+}
+
 using TileLarge = Tile<128, 128>;
 using TileSmall = Tile<64, 64>;
 
@@ -678,10 +830,11 @@ static SplitPlan split_plan(int64_t M, int64_t N, int64_t K) {
     if (M > 64) return p;
     const int64_t tiles = ((M + 63) / 64) * ((N + 63) / 64);
     const int64_t KB = K / kBlock;
-    int64_t want = (512 + tiles - 1) / tiles;
+    int64_t want = (384 + tiles - 1) / tiles;
     if (want > KB / 2) want = KB / 2;
     if (want < 2) return p;
-    const int64_t kb_per = (KB + want - 1) / want;
+    int64_t kb_per = (KB + want - 1) / want;
+    kb_per = kb_per < SK_MAX_KB ? kb_per : SK_MAX_KB;
     p.kb_per = (int)kb_per;
     p.splits = (int)((KB + kb_per - 1) / kb_per);
     return p;
@@ -694,6 +847,7 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 }
 
 using BigSquare = BigTile<256, 256, 2, 4, 2>;   // 8 waves of 128 x 64, 2 stages
+
 using BigWide = BigTile<256, 128, 4, 2, 3>;     // 8 waves of 64 x 64, 3 stages
 
 template <class T>
@@ -731,11 +885,12 @@ hipError_t launch_gemm(const void* a, const float* as, const void* b, const floa
     const SplitPlan plan = split_plan(M, N, K);
     if (workspace && plan.splits >= 2 &&
         workspace_bytes >= (size_t)plan.splits * (size_t)M * (size_t)N * sizeof(float)) {
-        using T = TileSmall;
-        const int mt = (int)((M + T::BM - 1) / T::BM), nt = (int)((N + T::BN - 1) / T::BN);
-        hipLaunchKernelGGL(gemm_splitk_kernel<T>, dim3(mt * nt, plan.splits), dim3(256), 0,
-                           stream, (const uint8_t*)a, as, (const uint8_t*)b, bs, (float*)workspace,
-                           M, N, K, mt, plan.kb_per);
+        const int mt = (int)((M + 63) / 64), nt = (int)((N + 63) / 64);
+        const size_t lds_bytes = (size_t)plan.kb_per * 2 * 64 * kBlock;
+        hipLaunchKernelGGL(gemm_skinny_kernel, dim3(mt * nt, plan.splits), dim3(256), lds_bytes,
+                           stream,
+                           (const uint8_t*)a, as, (const uint8_t*)b, bs, (float*)workspace, M, N,
+                           K, mt, plan.kb_per);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         const int64_t MN = M * N;
@@ -776,7 +931,7 @@ hipError_t launch_gemm(const void* a, const float* as, const void* b, const floa
 hipError_t launch_gemm_grouped(const void* a, const float* as, const void* b, const float* bs,
                                void* c, const int32_t* off, int32_t G, int64_t total_M,
                                int64_t N, int64_t K, hipStream_t stream) {
-    using T = BigSquare;
+    using T = BigWide;
     const int nt = (int)((N + T::BN - 1) / T::BN);
     // upper bounds of the tile counts (the exact ones depend on the device offsets)
     const int64_t max_heavy = ((total_M + T::BM / 2 - 1) / (T::BM / 2)) * (int64_t)nt;
