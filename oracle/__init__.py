@@ -55,6 +55,9 @@ class Oracle:
         lib.oracle_gemm_grouped_rows.argtypes = [P, P, P, P, P, ctypes.c_int32, I64, I64, I64,
                                                  P, I64, P, ctypes.c_int]
         lib.oracle_gemm_grouped_rows.restype = ctypes.c_int
+        lib.oracle_moe_dispatch.argtypes = [P, I64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                            P, P, P]
+        lib.oracle_moe_combine.argtypes = [P, P, P, I64, ctypes.c_int32, I64, P]
         self.lib = lib
         self.path = path
 
@@ -168,6 +171,35 @@ class Oracle:
         return out
 
 
+    # ---------------------------------------------------------------- MoE
+
+    def moe_dispatch(self, topk, expert_lo, G):
+        """Stable dispatch of routed tokens to local experts expert_lo .. expert_lo+G-1.
+
+        topk: int32 [T, k].  Returns (offsets int32 [G+1], row_token int32 [rows],
+        slot_row int32 [T, k] with -1 for non-local slots).
+        """
+        tk = _c(topk, np.int32)
+        T, k = tk.shape
+        offsets = np.empty(G + 1, np.int32)
+        row_token = np.empty(max(1, T * k), np.int32)
+        slot_row = np.empty((T, k), np.int32)
+        self.lib.oracle_moe_dispatch(_ptr(tk), T, k, int(expert_lo), int(G), _ptr(offsets),
+                                     _ptr(row_token), _ptr(slot_row))
+        return offsets, row_token[:int(offsets[-1])].copy(), slot_row
+
+    def moe_combine(self, out_bits, slot_row, weights):
+        """fp64 y [T, N] = sum over local slots of weight * out[row] (out: bf16 bits [rows, N])."""
+        o = _c(out_bits, np.uint16)
+        sr = _c(slot_row, np.int32)
+        w = _c(weights, np.float32)
+        T, k = sr.shape
+        N = o.shape[1]
+        y = np.empty((T, N), np.float64)
+        self.lib.oracle_moe_combine(_ptr(o), _ptr(sr), _ptr(w), T, k, N, _ptr(y))
+        return y
+
+
 def _ptr(a: np.ndarray):
     return ctypes.c_void_p(a.ctypes.data)
 
@@ -235,3 +267,11 @@ def gemm(a, sa, b, sb, rows=None, threads=None):
 
 def gemm_grouped(a, sa, b, sb, offsets, rows=None, threads=None):
     return default().gemm_grouped(a, sa, b, sb, offsets, rows, threads)
+
+
+def moe_dispatch(topk, expert_lo, G):
+    return default().moe_dispatch(topk, expert_lo, G)
+
+
+def moe_combine(out_bits, slot_row, weights):
+    return default().moe_combine(out_bits, slot_row, weights)

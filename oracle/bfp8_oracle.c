@@ -21,6 +21,11 @@
  *   - "Behavior traces" (codevetter), the fp8->bf16 trace bullet: each
  *     1-byte tensor is dequantized with its (renamed) scale_inv, i.e. the
  *     stored scale is a multiplier.
+ *   - "Behavior traces" (codevetter), the MoE trace bullet: per-expert token
+ *     counts; for each local expert with tokens, the tokens routed to it are
+ *     selected in ascending order, run through the expert, and added into a
+ *     zero-initialised y after multiplication by their routing weight.
+ *     "Data flow" (codevetter): a GPU holds a contiguous range of experts.
  * The e4m3 format itself is the OCP 8-bit floating point E4M3 encoding
  * (torch.float8_e4m3fn): bias 7, no infinities, NaN only at S.1111.111,
  * largest finite value 448.
@@ -29,7 +34,8 @@
  * design notes): the clamp is a lower floor ORACLE_AMAX_FLOOR on the block
  * max; the quantizer divides in IEEE fp32 and then rounds to nearest-even
  * with saturation at +-448; weight scales tile the weight in 128x128 blocks;
- * the GEMM reference is accumulated in fp64.
+ * the GEMM reference is accumulated in fp64; the MoE combine sums in fp64
+ * (the pages accumulate y in the activation dtype, expert by expert).
  *
  * Parity status: every function here is pinned by the CPU tests against
  * brute force, closed forms, torch's own e4m3/bf16 casts or exact rational
@@ -290,4 +296,51 @@ int oracle_gemm_grouped_rows(const uint8_t* a, const float* sa, const uint8_t* b
     for (int64_t i = 0; i < nrows; ++i)
         if (rows[i] < 0 || rows[i] >= total_M) return -1;
     return run_gemm_rows(a, sa, b, sb, off, G, N, K, rows, nrows, out, nthreads);
+}
+
+/* ------------------------------------------------- MoE dispatch and combine */
+
+/* Dispatch of one GPU's share of routed experts ("Behavior traces", MoE
+ * trace: for each local expert with tokens, the tokens routed to it, in
+ * ascending order, are gathered; "Data flow", Expert sharding: the local
+ * experts are a contiguous range of expert ids).
+ *   topk: int32 [T, topk] expert ids per token; local experts are
+ *         expert_lo .. expert_lo + G - 1.
+ * Outputs: offsets [G+1] (rows of local expert g are offsets[g] ..
+ * offsets[g+1]); row_token [offsets[G]] (token of each gathered row);
+ * slot_row [T, topk] (gathered row of each (token, slot), -1 when the slot's
+ * expert is not local).  Written as the pages' loop: expert by expert, token
+ * by token. */
+void oracle_moe_dispatch(const int32_t* topk, int64_t T, int32_t k, int32_t expert_lo,
+                         int32_t G, int32_t* offsets, int32_t* row_token, int32_t* slot_row) {
+    for (int64_t i = 0; i < T * k; ++i) slot_row[i] = -1;
+    int32_t row = 0;
+    for (int32_t g = 0; g < G; ++g) {
+        offsets[g] = row;
+        for (int64_t t = 0; t < T; ++t)
+            for (int32_t j = 0; j < k; ++j)
+                if (topk[t * k + j] == expert_lo + g) {
+                    row_token[row] = (int32_t)t;
+                    slot_row[t * k + j] = row;
+                    ++row;
+                }
+    }
+    offsets[G] = row;
+}
+
+/* Combine: y[t, n] = sum over slots j with slot_row[t, j] >= 0 of
+ *          weight[t, j] * out[slot_row[t, j], n], in fp64.
+ * out is bf16 [rows, N] (the grouped GEMM's output), y is fp64 [T, N]. */
+void oracle_moe_combine(const uint16_t* out, const int32_t* slot_row, const float* weight,
+                        int64_t T, int32_t k, int64_t N, double* y) {
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int32_t j = 0; j < k; ++j) {
+                const int32_t r = slot_row[t * k + j];
+                if (r >= 0)
+                    acc += (double)weight[t * k + j] * (double)oracle_bf16_to_f32(out[(int64_t)r * N + n]);
+            }
+            y[t * N + n] = acc;
+        }
 }

@@ -521,4 +521,144 @@ def pin_grouped_reduces_to_gemm(orc):
     assert np.all(np.isnan(partial[4:])) and not np.any(np.isnan(partial[:4]))
 
 
+# ------------------------------------------------------ MoE dispatch / combine pins
+#
+# Source: "Behavior traces - deepseek-ai/DeepSeek-V3" (codevetter), MoE trace
+# bullet (per local expert with tokens: select the tokens routed to it in
+# ascending order, add expert(x[idx]) times the routing weight into y, which
+# starts at zero); "Data flow" (codevetter), expert sharding (a GPU holds a
+# contiguous range of expert ids).
+
+def _read_moe_golden():
+    lines = [ln.split() for ln in open(os.path.join(GOLDEN, "moe_dispatch_combine_hand.txt"))
+             if ln.strip() and not ln.startswith("#")]
+    common, cases = {}, []
+    for key, *vals in lines:
+        if key == "case":
+            cases.append({"expert_lo": int(vals[0]), "G": int(vals[1])})
+        elif cases and key in ("offsets", "row_token", "slot_row"):
+            cases[-1][key] = np.array(vals, np.int64)
+        else:
+            common[key] = np.array(vals, np.float64)
+    return common, cases
+
+
+def _routing_table(T, k, n_experts, seed, distinct=True):
+    rng = np.random.default_rng(seed)
+    if distinct:
+        return np.argsort(rng.random((T, n_experts)), axis=1)[:, :k].astype(np.int32)
+    return rng.integers(-3, n_experts + 3, size=(T, k)).astype(np.int32)
+
+
+def _dispatch_by_stable_sort(topk, lo, G):
+    """Independent construction: a stable argsort of the flat (token, slot) list by local expert id."""
+    T, k = topk.shape
+    flat = topk.astype(np.int64).ravel()
+    local = (flat >= lo) & (flat < lo + G)
+    key = np.where(local, flat - lo, G)                 # non-local entries sort last
+    order = np.argsort(key, kind="stable")[:int(local.sum())]
+    counts = np.bincount(flat[local] - lo, minlength=G)
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    slot_row = np.full(T * k, -1, np.int64)
+    slot_row[order] = np.arange(order.size)
+    return offsets, order // k, slot_row.reshape(T, k)
+
+
+def pin_moe_dispatch_golden(orc):
+    """M1: the hand-worked dispatch of four tokens, two expert ranges."""
+    common, cases = _read_moe_golden()
+    topk = common["topk"].astype(np.int32).reshape(int(common["T"][0]), int(common["k"][0]))
+    for c in cases:
+        off, rt, sr = orc.moe_dispatch(topk, c["expert_lo"], c["G"])
+        assert np.array_equal(off, c["offsets"]), c
+        assert np.array_equal(rt, c["row_token"]), c
+        assert np.array_equal(sr.ravel(), c["slot_row"]), c
+
+
+def pin_moe_dispatch_vs_stable_sort(orc):
+    """M2: dispatch == a stable sort by expert id (numpy argsort + bincount), any expert range."""
+    for seed, (T, k, E, lo, G, distinct) in enumerate(
+            [(300, 8, 64, 16, 24, True), (97, 6, 40, 0, 40, True), (128, 4, 10, 3, 5, False),
+             (50, 8, 256, 200, 56, True), (64, 2, 8, 8, 4, True)]):
+        topk = _routing_table(T, k, E, 900 + seed, distinct)
+        off, rt, sr = orc.moe_dispatch(topk, lo, G)
+        ref_off, ref_rt, ref_sr = _dispatch_by_stable_sort(topk, lo, G)
+        assert np.array_equal(off, ref_off) and np.array_equal(rt, ref_rt) and np.array_equal(sr, ref_sr)
+        # invariants: each local slot owns one row, that row names the slot's token,
+        # and rows of an expert hold ascending tokens
+        rows = sr[sr >= 0]
+        assert np.array_equal(np.sort(rows), np.arange(off[-1]))
+        t_of = np.nonzero(sr >= 0)[0]
+        assert np.array_equal(rt[sr[sr >= 0]], t_of)
+        for g in range(G):
+            assert np.all(np.diff(rt[off[g]:off[g + 1]]) >= 0)
+
+
+def pin_moe_dispatch_degenerate(orc):
+    """M3: no local expert hit, every slot local, a single token."""
+    topk = _routing_table(20, 4, 16, 950)
+    off, rt, sr = orc.moe_dispatch(topk, 16, 8)             # experts 16..23 do not exist
+    assert np.all(off == 0) and rt.size == 0 and np.all(sr == -1)
+    off, rt, sr = orc.moe_dispatch(topk, 0, 16)             # every expert is local
+    assert off[-1] == 80 and np.array_equal(np.sort(sr.ravel()), np.arange(80))
+    off, rt, sr = orc.moe_dispatch(np.array([[5, 2, 7]], np.int32), 2, 6)
+    assert np.array_equal(off, [0, 1, 1, 1, 2, 2, 3]) and np.array_equal(rt, [0, 0, 0])
+    assert np.array_equal(sr, [[1, 0, 2]])
+
+
+def pin_moe_combine_golden(orc):
+    """M4: the hand-worked combine of the golden file (exact in fp64)."""
+    common, cases = _read_moe_golden()
+    T, k, N = int(common["T"][0]), int(common["k"][0]), int(common["N"][0])
+    topk = common["topk"].astype(np.int32).reshape(T, k)
+    _, _, sr = orc.moe_dispatch(topk, cases[0]["expert_lo"], cases[0]["G"])
+    out = torch_bf16(common["out"].astype(np.float32)).reshape(-1, N)
+    y = orc.moe_combine(out, sr, common["weights"].astype(np.float32).reshape(T, k))
+    assert np.array_equal(y.ravel(), common["y"])
+
+
+def pin_moe_combine_vs_dense_matmul(orc):
+    """M5: combine == R @ out with R[t, slot_row[t, j]] = weight[t, j] (numpy fp64 matmul)."""
+    T, k, E, lo, G, N = 120, 8, 64, 8, 20, 72
+    topk = _routing_table(T, k, E, 960)
+    _, _, sr = orc.moe_dispatch(topk, lo, G)
+    rows = int((sr >= 0).sum())
+    rng = np.random.default_rng(961)
+    out = torch_bf16(rng.standard_normal((rows, N)).astype(np.float32))
+    w = rng.random((T, k)).astype(np.float32)
+    R = np.zeros((T, rows))
+    for t in range(T):
+        for j in range(k):
+            if sr[t, j] >= 0:
+                R[t, sr[t, j]] += w[t, j]
+    ref = R @ bf16_bits_to_f32(out).astype(np.float64)
+    y = orc.moe_combine(out, sr, w)
+    assert np.all(np.abs(y - ref) <= 1e-12 * (np.abs(R) @ np.abs(bf16_bits_to_f32(out).astype(np.float64))) + 1e-300)
+
+
+def pin_moe_layer_matches_per_expert_loop(orc):
+    """M6: dispatch -> per-expert function on gathered rows -> combine == the pages' loop.
+
+    The expert of id e is x -> 2**(e % 5 - 2) * x (exact in bf16 for these inputs), so
+    the loop over local experts with where(indices == e) can be written in plain
+    numpy and compared exactly."""
+    T, k, E, lo, G, N = 90, 6, 32, 4, 12, 16
+    topk = _routing_table(T, k, E, 970)
+    rng = np.random.default_rng(971)
+    x = rng.integers(-64, 64, size=(T, N)).astype(np.float32)
+    w = (rng.integers(1, 16, size=(T, k)) / 16.0).astype(np.float32)
+    off, rt, sr = orc.moe_dispatch(topk, lo, G)
+    out = np.empty((int(off[-1]), N), np.float32)
+    for g in range(G):
+        out[off[g]:off[g + 1]] = x[rt[off[g]:off[g + 1]]] * np.float32(2.0 ** ((lo + g) % 5 - 2))
+    y = orc.moe_combine(torch_bf16(out), sr, w)
+    ref = np.zeros((T, N))
+    for e in range(lo, lo + G):
+        idx, top = np.nonzero(topk == e)
+        if idx.size == 0:
+            continue
+        ref[idx] += (x[idx].astype(np.float64) * 2.0 ** (e % 5 - 2)) * w[idx, top][:, None]
+    assert np.array_equal(y, ref)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

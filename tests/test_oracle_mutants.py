@@ -16,6 +16,20 @@ import pins
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "bfp8_oracle.c")
 
 MUTANTS = {
+    # dispatch: slots ordered slot-major instead of token-major inside an expert
+    "dispatch_slot_major": ("for (int64_t t = 0; t < T; ++t)\n            for (int32_t j = 0; j < k; ++j)\n                if (topk",
+                            "for (int32_t j = 0; j < k; ++j)\n            for (int64_t t = 0; t < T; ++t)\n                if (topk"),
+    # dispatch: local range taken to start at expert 0
+    "dispatch_ignores_lo": ("if (topk[t * k + j] == expert_lo + g)", "if (topk[t * k + j] == g)"),
+    # dispatch: non-local slots marked 0 instead of -1
+    "dispatch_nonlocal_zero": ("for (int64_t i = 0; i < T * k; ++i) slot_row[i] = -1;",
+                               "for (int64_t i = 0; i < T * k; ++i) slot_row[i] = 0;"),
+    # combine: routing weight dropped
+    "combine_no_weight": ("acc += (double)weight[t * k + j] * (double)", "acc += (double)"),
+    # combine: weight of the first slot used for every slot
+    "combine_weight_index": ("(double)weight[t * k + j]", "(double)weight[t * k]"),
+    # combine: reads the token's own row instead of the slot's gathered row
+    "combine_row_index": ("oracle_bf16_to_f32(out[(int64_t)r * N + n])", "oracle_bf16_to_f32(out[(int64_t)t * N + n])"),
     # quantizer ceiling of a different fp8 flavour (e4m3 "fnuz" tops out at 240)
     "ceiling_240": ("float scale = clamped / ORACLE_E4M3_MAX;", "float scale = clamped / 240.0f;"),
     # no floor on the block max: an all-zero block divides by zero
