@@ -15,7 +15,10 @@ bounds it; `roofline` repeats that for the dominant kernel; `cpu_baseline`
 times the CPU oracle on a bounded, proportional sample of the same step.
 
 Other workloads (parity-test shapes, measured on demand): --workload tiny |
-decode | moe-pair | dense-mlp | grouped.
+decode | moe-pair | dense-mlp | grouped | moe-layer.  moe-layer is the routed
+experts of one GPU end to end on the device: moe_dispatch(topk) ->
+act_quant_rows(x, row_token) -> grouped GEMM (row buffers sized for T*k rows)
+-> moe_combine (weighted sum back to token order).
 """
 import argparse
 import hashlib
@@ -38,7 +41,7 @@ BLOCK = 128
 PEAK_FP8_TFLOPS = 5000.0          # MI355X dense fp8 MFMA (no sparsity)
 PEAK_HBM_GBS = 8000.0             # MI355X HBM3E
 
-WORKLOADS = {"tiny": 0, "decode": 1, "moe-pair": 2, "dense-mlp": 3, "grouped": 4}
+WORKLOADS = {"tiny": 0, "decode": 1, "moe-pair": 2, "dense-mlp": 3, "grouped": 4, "moe-layer": 4}
 
 
 # ------------------------------------------------------------------ accounting
@@ -55,6 +58,14 @@ def gemm_bytes(M, N, K, G=1):
     return M * K + G * N * K + 2 * M * N + 4 * M * (K // BLOCK) + 4 * G * (-(-N // BLOCK)) * (K // BLOCK)
 
 
+def dispatch_bytes(T, k, rows, G):
+    return 4 * T * k + 4 * T * k + 4 * rows + 4 * (G + 1)
+
+
+def combine_bytes(T, k, rows, N):
+    return 2 * rows * N + 8 * T * k + 2 * T * N
+
+
 def sha_of(t: torch.Tensor) -> str:
     return hashlib.sha256(t.contiguous().view(torch.uint8).numpy().tobytes()).hexdigest()[:16]
 
@@ -64,11 +75,13 @@ def sha_of(t: torch.Tensor) -> str:
 class Step:
     """Device buffers and the ordered launches of one step; every launch is named."""
 
-    def __init__(self, wl, dev):
+    def __init__(self, wl, dev, kind=None):
         self.wl = wl
         self.dev = dev
         t = wl.tensors
         c = wl.config
+        if kind == "moe-layer":
+            c = "moe-layer"
         self.launches = []            # (name, callable, flops, bytes, bound)
         self.hashes = {}
         for k, v in t.items():
@@ -135,6 +148,39 @@ class Step:
             self.shape = dict(T=T, G=G, N=N, K=K, tokens_per_expert_min=min(counts),
                               tokens_per_expert_max=max(counts))
             self.dominant, self.dominant_kernel = ["fp8_gemm_grouped"], "gemm_grouped"
+        elif c == "moe-layer":
+            topk, wts, off = t["topk"], t["weights"], t["offsets"]
+            Tt, k = topk.shape
+            rows, G, N, K = int(off[-1]), wl.meta["G"], wl.meta["N"], wl.meta["K"]
+            cap = Tt * k                                     # worst case: every slot local
+            x = t["x"].to(dev)
+            topk_d, w_d = topk.to(dev), wts.to(dev)
+            b, bs = t["w1"].to(dev), t["s1"].to(dev)
+            off_d = torch.empty(G + 1, dtype=torch.int32, device=dev)
+            row_token = torch.empty(cap, dtype=torch.int32, device=dev)
+            slot_row = torch.empty(Tt, k, dtype=torch.int32, device=dev)
+            ws = torch.empty(max(1, bfp8.bfp8_moe_dispatch_workspace_size(Tt, k, G) // 4),
+                             dtype=torch.int32, device=dev)
+            q = torch.empty(cap, K, dtype=torch.uint8, device=dev)
+            qs = torch.empty(cap, K // BLOCK, dtype=torch.float32, device=dev)
+            h = torch.empty(cap, N, dtype=torch.bfloat16, device=dev)
+            y = torch.empty(Tt, N, dtype=torch.bfloat16, device=dev)
+            nrows = off_d[G:]
+            self.launches += [
+                ("moe_dispatch", lambda: bfp8.bfp8_moe_dispatch(topk_d, 0, off_d, row_token, slot_row, ws),
+                 0, dispatch_bytes(Tt, k, rows, G), "hbm"),
+                ("act_quant_rows", lambda: bfp8.bfp8_act_quant_rows(x, row_token, nrows, q, qs),
+                 0, act_quant_bytes(rows, K) + 4 * rows, "hbm"),
+                ("fp8_gemm_grouped", lambda: bfp8.bfp8_gemm_grouped(q, qs, b, bs, h, off_d),
+                 2 * rows * N * K, gemm_bytes(rows, N, K, G), "hbm"),
+                ("moe_combine", lambda: bfp8.bfp8_moe_combine(h, slot_row, w_d, y),
+                 0, combine_bytes(Tt, k, rows, N), "hbm"),
+            ]
+            counts = (off[1:] - off[:-1]).tolist()
+            self.shape = dict(tokens=Tt, top_k=k, local_experts=G, rows=rows, row_capacity=cap,
+                              N=N, K=K, tokens_per_expert_min=min(counts),
+                              tokens_per_expert_max=max(counts))
+            self.dominant, self.dominant_kernel = ["fp8_gemm_grouped"], "gemm_grouped"
         else:
             raise ValueError(c)
 
@@ -149,7 +195,7 @@ class Step:
 
 # ------------------------------------------------------------------ CPU oracle leg
 
-def cpu_baseline(wl, target_s=12.0):
+def cpu_baseline(wl, target_s=12.0, kind=None):
     """Time the CPU oracle on a proportional sample of one step: a fraction f of the
     rows of every stage (activation rows, and weight rows for dequant)."""
     import oracle
@@ -176,6 +222,21 @@ def cpu_baseline(wl, target_s=12.0):
             if c == 3:
                 wrows = max(1, int(round(t["w1"].shape[0] * rows / wl.meta["M"])))
                 oracle.weight_dequant(t["w1"].numpy()[:wrows], t["s1"].numpy()[:-(-wrows // BLOCK)])
+        elif kind == "moe-layer":
+            # rows = sampled tokens: dispatch of the whole batch, then every later stage
+            # for the sampled tokens' local slots only
+            G = wl.meta["G"]
+            off, rt, sr = oracle.moe_dispatch(t["topk"].numpy(), 0, G)
+            mine = np.unique(sr[:rows][sr[:rows] >= 0])
+            q, s = oracle.act_quant(x_bits[rt[mine]])
+            grp = np.searchsorted(off, mine, side="right") - 1
+            c_off = np.concatenate([[0], np.cumsum(np.bincount(grp, minlength=G))]).astype(np.int32)
+            h = oracle.gemm_grouped(q, s, t["w1"].numpy(), t["s1"].numpy(), c_off, threads=threads)
+            pos = np.full(int(off[-1]), -1, np.int64)
+            pos[mine] = np.arange(mine.size)
+            sub = np.where(sr[:rows] >= 0, pos[np.maximum(sr[:rows], 0)], -1).astype(np.int32)
+            oracle.moe_combine(oracle.f32_to_bf16(h.astype(np.float32)), sub, t["weights"].numpy()[:rows])
+            done = 2.0 * mine.size * wl.meta["N"] * wl.meta["K"]
         else:
             ids, off = t["token_ids"].numpy(), t["offsets"].numpy()
             xg = x_bits[ids[:rows]]
@@ -188,13 +249,14 @@ def cpu_baseline(wl, target_s=12.0):
             done = 2.0 * rows * wl.meta["N"] * wl.meta["K"]
         return time.perf_counter() - t0, done
 
-    M = wl.meta.get("M", wl.meta.get("T"))
+    M = wl.meta["tokens"] if kind == "moe-layer" else wl.meta.get("M", wl.meta.get("T"))
     probe = min(M, max(1, threads))
     dt, _ = run(probe)
     rows = int(min(M, max(probe, probe * target_s / max(dt, 1e-6))))
     dt, flop = run(rows)
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{rows} of {M} rows of every stage of one step ({dt:.1f} s of CPU work)"}
+            "sample": (f"{rows} of {M} {'tokens' if kind == 'moe-layer' else 'rows'} of every stage "
+                       f"of one step ({dt:.1f} s of CPU work)")}
 
 
 # ------------------------------------------------------------------ traffic
@@ -255,7 +317,7 @@ def main():
 
     t0 = time.time()
     wl = synth.make(WORKLOADS[args.workload])
-    step = Step(wl, dev)
+    step = Step(wl, dev, args.workload)
     gen_s = time.time() - t0
     print(f"# workload {wl.name}: inputs built in {gen_s:.1f}s; launches "
           f"{[l[0] for l in step.launches]}", file=sys.stderr, flush=True)
@@ -306,9 +368,10 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, args.cpu_seconds)
+        cpu = cpu_baseline(wl, args.cpu_seconds, args.workload)
 
-    config = {"workload": wl.name, "shape": step.shape,
+    wl_name = f"moe-layer-{wl.name}" if args.workload == "moe-layer" else wl.name
+    config = {"workload": wl_name, "shape": step.shape,
               "step": " -> ".join(l[0] for l in step.launches),
               "value_definition": "GEMM FLOP per step / wall time per step",
               "input_sha256_16": step.hashes, "seeds": "1000*config+tensor_id",

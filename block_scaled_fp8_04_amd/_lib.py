@@ -28,7 +28,8 @@ BFP8_ERR_ARG = 7
 
 EXPORTS = ("bfp8_act_quant", "bfp8_weight_dequant", "bfp8_gemm", "bfp8_gemm_workspace_size",
            "bfp8_gemm_grouped", "bfp8_e4m3_encode_range", "bfp8_bf16_round_range",
-           "bfp8_gemm_kernel_name",
+           "bfp8_gemm_kernel_name", "bfp8_moe_dispatch_workspace_size", "bfp8_moe_dispatch",
+           "bfp8_act_quant_rows", "bfp8_moe_combine",
            "bfp8_status_string", "bfp8_version")
 
 _lib = None
@@ -66,6 +67,14 @@ def library():
     lib.bfp8_bf16_round_range.restype = ctypes.c_int
     lib.bfp8_gemm_kernel_name.argtypes = [I64, I64, I64]
     lib.bfp8_gemm_kernel_name.restype = ctypes.c_char_p
+    lib.bfp8_moe_dispatch_workspace_size.argtypes = [I64, I32, I32]
+    lib.bfp8_moe_dispatch_workspace_size.restype = ctypes.c_size_t
+    lib.bfp8_moe_dispatch.argtypes = [P, I64, I32, I32, I32, P, P, P, P, ctypes.c_size_t, P]
+    lib.bfp8_moe_dispatch.restype = ctypes.c_int
+    lib.bfp8_act_quant_rows.argtypes = [P, I64, P, P, P, P, I64, I64, P]
+    lib.bfp8_act_quant_rows.restype = ctypes.c_int
+    lib.bfp8_moe_combine.argtypes = [P, I64, P, P, P, I64, I32, I64, P]
+    lib.bfp8_moe_combine.restype = ctypes.c_int
     lib.bfp8_status_string.argtypes = [ctypes.c_int]
     lib.bfp8_status_string.restype = ctypes.c_char_p
     lib.bfp8_version.argtypes = []
@@ -209,6 +218,60 @@ def bfp8_bf16_round_range(first, count, out, variant=0, stream=None):
         int(first), int(count), _ptr(out), int(variant), _stream(stream, out.device)))
 
 
+def bfp8_moe_dispatch_workspace_size(T, k, G) -> int:
+    return int(library().bfp8_moe_dispatch_workspace_size(int(T), int(k), int(G)))
+
+
+def bfp8_moe_dispatch(topk_idx, expert_lo, group_offsets, row_token, slot_row, workspace,
+                      stream=None):
+    """Stable sort of the (token, slot) pairs of topk_idx int32 [T, k] by local expert.
+
+    Local experts are expert_lo .. expert_lo + G - 1 with G = group_offsets.numel() - 1.
+    Writes group_offsets int32 [G+1], row_token int32 [T*k], slot_row int32 [T, k].
+    """
+    _cuda_contig(topk_idx, group_offsets, row_token, slot_row, workspace)
+    for t in (topk_idx, group_offsets, row_token, slot_row):
+        _need(t.dtype == torch.int32, "index tensors must be int32")
+    _need(topk_idx.dim() == 2, "topk_idx must be [T, k]")
+    T, k = topk_idx.shape
+    G = group_offsets.numel() - 1
+    _need(row_token.numel() >= T * k and slot_row.shape == (T, k), "row_token [T*k], slot_row [T, k]")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("bfp8_moe_dispatch", library().bfp8_moe_dispatch(
+        _ptr(topk_idx), T, k, int(expert_lo), G, _ptr(group_offsets), _ptr(row_token),
+        _ptr(slot_row), _ptr(workspace), ws_bytes, _stream(stream, group_offsets.device)))
+
+
+def bfp8_act_quant_rows(x, row_token, num_rows, q, scales, stream=None):
+    """q[r], scales[r] = act_quant(x[row_token[r]]) for r < min(num_rows[0], M)."""
+    q = _bytes_view(q)
+    _cuda_contig(x, row_token, num_rows, q, scales)
+    _need(x.dtype == torch.bfloat16 and scales.dtype == torch.float32, "x must be bf16, scales fp32")
+    _need(row_token.dtype == torch.int32 and (num_rows is None or num_rows.dtype == torch.int32),
+          "row_token and num_rows must be int32")
+    T, K = x.shape
+    M = q.shape[0]
+    _need(q.shape == (M, K) and scales.shape == (M, K // BLOCK) and row_token.numel() >= M,
+          "q [M, K], scales [M, K/128], row_token [M]")
+    _check("bfp8_act_quant_rows", library().bfp8_act_quant_rows(
+        _ptr(x), T, _ptr(row_token), _ptr(num_rows), _ptr(q), _ptr(scales), M, K,
+        _stream(stream, x.device)))
+
+
+def bfp8_moe_combine(expert_out, slot_row, weights, y, stream=None):
+    """y bf16 [T, N] = sum over local slots of weights[t, j] * expert_out[slot_row[t, j]]."""
+    _cuda_contig(expert_out, slot_row, weights, y)
+    _need(expert_out.dtype == torch.bfloat16 and y.dtype == torch.bfloat16, "bf16 expert_out and y")
+    _need(slot_row.dtype == torch.int32 and weights.dtype == torch.float32,
+          "slot_row int32, weights fp32")
+    rows, N = expert_out.shape
+    T, k = slot_row.shape
+    _need(weights.shape == (T, k) and y.shape == (T, N), "weights [T, k], y [T, N]")
+    _check("bfp8_moe_combine", library().bfp8_moe_combine(
+        _ptr(expert_out), rows, _ptr(slot_row), _ptr(weights), _ptr(y), T, k, N,
+        _stream(stream, y.device)))
+
+
 # ------------------------------------------------------- allocating conveniences
 
 def act_quant(x, stream=None):
@@ -242,3 +305,44 @@ def linear_fp8(x, w, w_s, workspace=None, stream=None):
     """The FP8 branch of linear(): act_quant(x) then the block-scaled GEMM with (w, w.scale)."""
     q, s = act_quant(x, stream)
     return gemm(q, s, w, w_s, workspace, stream)
+
+
+def moe_dispatch(topk_idx, expert_lo, G, stream=None):
+    """(group_offsets [G+1], row_token [T*k], slot_row [T, k]) for local experts expert_lo..+G-1."""
+    T, k = topk_idx.shape
+    dev = topk_idx.device
+    off = torch.empty(G + 1, dtype=torch.int32, device=dev)
+    row_token = torch.empty(max(1, T * k), dtype=torch.int32, device=dev)
+    slot_row = torch.empty((T, k), dtype=torch.int32, device=dev)
+    ws = torch.empty(max(1, bfp8_moe_dispatch_workspace_size(T, k, G) // 4), dtype=torch.int32,
+                     device=dev)
+    bfp8_moe_dispatch(topk_idx, expert_lo, off, row_token, slot_row, ws, stream)
+    return off, row_token, slot_row
+
+
+def moe_combine(expert_out, slot_row, weights, stream=None):
+    y = torch.empty((slot_row.shape[0], expert_out.shape[1]), dtype=torch.bfloat16,
+                    device=expert_out.device)
+    bfp8_moe_combine(expert_out, slot_row, weights, y, stream)
+    return y
+
+
+def moe_experts_fp8(x, topk_idx, weights, w, w_s, expert_lo, stream=None):
+    """Routed experts of one GPU, one block-scaled GEMM each, fully on the device.
+
+    dispatch -> act_quant of the gathered rows -> grouped GEMM -> weighted combine.
+    x bf16 [T, K]; topk_idx int32 [T, k]; weights fp32 [T, k]; w e4m3 [G, N, K] with
+    scales w_s [G, ceil(N/128), K/128].  Returns y bf16 [T, N].  Row buffers are sized
+    for the worst case T*k rows; only the first group_offsets[G] are touched.
+    """
+    T, K = x.shape
+    k = topk_idx.shape[1]
+    G, N, _ = w.shape
+    off, row_token, slot_row = moe_dispatch(topk_idx, expert_lo, G, stream)
+    cap = T * k
+    q = torch.empty((cap, K), dtype=torch.uint8, device=x.device)
+    qs = torch.empty((cap, K // BLOCK), dtype=torch.float32, device=x.device)
+    bfp8_act_quant_rows(x, row_token[:cap], off[G:], q, qs, stream)
+    out = torch.empty((cap, N), dtype=torch.bfloat16, device=x.device)
+    bfp8_gemm_grouped(q, qs, w, w_s, out, off, stream)
+    return moe_combine(out, slot_row, weights, stream)

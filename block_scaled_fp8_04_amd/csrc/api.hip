@@ -44,8 +44,8 @@ const char* bfp8_status_string(int status) {
         case BFP8_ERR_NULL: return "a required pointer is NULL";
         case BFP8_ERR_SHAPE: return "invalid shape (negative size, or K not a multiple of 128)";
         case BFP8_ERR_ALIGN: return "pointer misaligned";
-        case BFP8_ERR_WORKSPACE: return "workspace smaller than bfp8_gemm_workspace_size()";
-        case BFP8_ERR_GROUPS: return "group count must be at least 1";
+        case BFP8_ERR_WORKSPACE: return "workspace smaller than the matching *_workspace_size() call";
+        case BFP8_ERR_GROUPS: return "group count out of range (below 1, or above the dispatch limit)";
         case BFP8_ERR_HIP: return "HIP runtime error at launch";
         case BFP8_ERR_ARG: return "invalid argument";
         default: return "unknown status";
@@ -104,6 +104,58 @@ int bfp8_gemm_grouped(const void* a, const float* a_s, const void* b, const floa
         return BFP8_ERR_ALIGN;
     return from_hip(bfp8::launch_gemm_grouped(a, a_s, b, b_s, c_bf16, group_offsets, G, total_M,
                                               N, K, (hipStream_t)stream));
+}
+
+size_t bfp8_moe_dispatch_workspace_size(int64_t T, int32_t k, int32_t G) {
+    if (T <= 0 || k < 1 || G < 1 || G > BFP8_MOE_MAX_GROUPS || T * (int64_t)k >= ((int64_t)1 << 31))
+        return 0;
+    return bfp8::moe_dispatch_workspace_bytes(T, k, G);
+}
+
+int bfp8_moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32_t expert_lo,
+                      int32_t G, int32_t* group_offsets, int32_t* row_token, int32_t* slot_row,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+    static_assert(BFP8_MOE_MAX_GROUPS == bfp8::kMoeMaxGroups, "dispatch group limit");
+    if (T < 0 || k < 1 || T * (int64_t)k >= ((int64_t)1 << 31)) return BFP8_ERR_SHAPE;
+    if (G < 1 || G > BFP8_MOE_MAX_GROUPS) return BFP8_ERR_GROUPS;
+    const size_t need = T > 0 ? bfp8::moe_dispatch_workspace_bytes(T, k, G) : 0;
+    if (!group_offsets) return BFP8_ERR_NULL;
+    if (T > 0 && (!topk_idx || !row_token || !slot_row || !workspace)) return BFP8_ERR_NULL;
+    if (!aligned(group_offsets, 4) || !aligned(topk_idx, 4) || !aligned(row_token, 4) ||
+        !aligned(slot_row, 4) || !aligned(workspace, 4))
+        return BFP8_ERR_ALIGN;
+    if (workspace_bytes < need) return BFP8_ERR_WORKSPACE;
+    return from_hip(bfp8::launch_moe_dispatch(topk_idx, T, k, expert_lo, G, group_offsets,
+                                              row_token, slot_row, workspace,
+                                              (hipStream_t)stream));
+}
+
+int bfp8_act_quant_rows(const void* x_bf16, int64_t T, const int32_t* row_token,
+                        const int32_t* num_rows, void* q_e4m3, float* scales, int64_t M,
+                        int64_t K, void* stream) {
+    if (T < 0 || M < 0 || K <= 0 || K % BFP8_BLOCK != 0) return BFP8_ERR_SHAPE;
+    if (M == 0) return BFP8_OK;
+    if ((T > 0 && !x_bf16) || !row_token || !q_e4m3 || !scales) return BFP8_ERR_NULL;
+    if (!aligned(x_bf16, 16) || !aligned(q_e4m3, 16) || !aligned(scales, 4) ||
+        !aligned(row_token, 4) || !aligned(num_rows, 4))
+        return BFP8_ERR_ALIGN;
+    return from_hip(bfp8::launch_act_quant_rows(x_bf16, T, row_token, num_rows, q_e4m3, scales, M,
+                                                K, (hipStream_t)stream));
+}
+
+int bfp8_moe_combine(const void* expert_out_bf16, int64_t rows, const int32_t* slot_row,
+                     const float* weights, void* y_bf16, int64_t T, int32_t k, int64_t N,
+                     void* stream) {
+    if (T < 0 || k < 1 || N < 0 || rows < 0 || T > ((int64_t)1 << 24) ||
+        T * (int64_t)k >= ((int64_t)1 << 31) || (N + 2047) / 2048 > 65535)
+        return BFP8_ERR_SHAPE;
+    if (T == 0 || N == 0) return BFP8_OK;
+    if ((rows > 0 && !expert_out_bf16) || !slot_row || !weights || !y_bf16) return BFP8_ERR_NULL;
+    if (!aligned(expert_out_bf16, 2) || !aligned(y_bf16, 2) || !aligned(slot_row, 4) ||
+        !aligned(weights, 4))
+        return BFP8_ERR_ALIGN;
+    return from_hip(bfp8::launch_moe_combine(expert_out_bf16, rows, slot_row, weights, y_bf16, T,
+                                             k, N, (hipStream_t)stream));
 }
 
 const char* bfp8_gemm_kernel_name(int64_t M, int64_t N, int64_t K) {

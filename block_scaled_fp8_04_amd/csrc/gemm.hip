@@ -662,17 +662,31 @@ __device__ __forceinline__ GroupTiles group_tiles(int64_t rows) {
     return t;
 }
 
+// Rows of group g: the device offsets clamped into [0, total_M] (and the end
+// to at least the start), so offsets produced on the device can never send a
+// tile outside the caller's buffers.
+__device__ __forceinline__ void group_rows(const int32_t* __restrict__ off, int g,
+                                           int64_t total_M, int64_t& lo, int64_t& hi) {
+    int64_t a = off[g], b = off[g + 1];
+    a = a < 0 ? 0 : (a > total_M ? total_M : a);
+    b = b < a ? a : (b > total_M ? total_M : b);
+    lo = a;
+    hi = b;
+}
+
 template <class T, bool kLight>
 __global__ __launch_bounds__(T::THREADS, 1) void gemm_grouped_big_kernel(
     const uint8_t* __restrict__ a, const float* __restrict__ as, const uint8_t* __restrict__ b,
     const float* __restrict__ bs, uint16_t* __restrict__ c, const int32_t* __restrict__ off,
-    int G, int64_t N, int64_t K, int nt) {
+    int G, int64_t total_M, int64_t N, int64_t K, int nt) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[T::NSTAGE * T::STAGE];
     const int64_t KB = K / kBlock;
     const int64_t NB = (N + kBlock - 1) / kBlock;
     int64_t total = 0;
     for (int g = 0; g < G; ++g) {
-        const GroupTiles gt = group_tiles<T::BM>((int64_t)off[g + 1] - off[g]);
+        int64_t lo, hi;
+        group_rows(off, g, total_M, lo, hi);
+        const GroupTiles gt = group_tiles<T::BM>(hi - lo);
         total += (kLight ? gt.m_light : gt.m_heavy) * nt;
     }
     const int nwg = gridDim.x;                    // a multiple of 8
@@ -683,9 +697,10 @@ __global__ __launch_bounds__(T::THREADS, 1) void gemm_grouped_big_kernel(
         if (t >= total) continue;
         int64_t rest = t;
         int g = 0;
-        int64_t tm = 0, tn = 0;
+        int64_t tm = 0, tn = 0, g_lo = 0, g_hi = 0;
         for (; g < G; ++g) {
-            const GroupTiles gt = group_tiles<T::BM>((int64_t)off[g + 1] - off[g]);
+            group_rows(off, g, total_M, g_lo, g_hi);
+            const GroupTiles gt = group_tiles<T::BM>(g_hi - g_lo);
             const int64_t mcount = kLight ? gt.m_light : gt.m_heavy;
             if (rest < mcount * nt) {
                 tm = (kLight ? gt.m_heavy : 0) + rest % mcount;
@@ -694,7 +709,7 @@ __global__ __launch_bounds__(T::THREADS, 1) void gemm_grouped_big_kernel(
             }
             rest -= mcount * nt;
         }
-        const int64_t m0 = (int64_t)off[g] + tm * T::BM, m_end = off[g + 1];
+        const int64_t m0 = g_lo + tm * T::BM, m_end = g_hi;
         gemm_tile_big<T, kLight>(a, as, b + (int64_t)g * N * K, bs + (int64_t)g * NB * KB, c, m0,
                                  m_end, tn * T::BN, N, K, lds);
     }
@@ -943,12 +958,12 @@ hipError_t launch_gemm_grouped(const void* a, const float* as, const void* b, co
     grid_l = (grid_l + 7) / 8 * 8;
     hipLaunchKernelGGL((gemm_grouped_big_kernel<T, false>), dim3((unsigned)grid_h),
                        dim3(T::THREADS), 0, stream, (const uint8_t*)a, as, (const uint8_t*)b, bs,
-                       (uint16_t*)c, off, (int)G, N, K, nt);
+                       (uint16_t*)c, off, (int)G, total_M, N, K, nt);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((gemm_grouped_big_kernel<T, true>), dim3((unsigned)grid_l),
                        dim3(T::THREADS), 0, stream, (const uint8_t*)a, as, (const uint8_t*)b, bs,
-                       (uint16_t*)c, off, (int)G, N, K, nt);
+                       (uint16_t*)c, off, (int)G, total_M, N, K, nt);
     return hipGetLastError();
 }
 

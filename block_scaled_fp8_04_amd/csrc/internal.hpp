@@ -9,11 +9,17 @@
 
 namespace bfp8 {
 
+// Largest number of local experts the MoE dispatch handles (LDS counters).
+constexpr int kMoeMaxGroups = 1024;
+
 // Compute units of the current device (cached per device).
 int device_cu_count();
 
 hipError_t launch_act_quant(const void* x, void* q, float* s, int64_t M, int64_t K,
                             hipStream_t stream);
+hipError_t launch_act_quant_rows(const void* x, int64_t T, const int32_t* row_token,
+                                 const int32_t* num_rows, void* q, float* s, int64_t M, int64_t K,
+                                 hipStream_t stream);
 hipError_t launch_encode_range(uint32_t first, int64_t count, void* out, int variant,
                                hipStream_t stream);
 hipError_t launch_bf16_round_range(uint32_t first, int64_t count, void* out, int variant,
@@ -31,5 +37,13 @@ hipError_t launch_gemm(const void* a, const float* as, const void* b, const floa
 hipError_t launch_gemm_grouped(const void* a, const float* as, const void* b, const float* bs,
                                void* c, const int32_t* off, int32_t G, int64_t total_M,
                                int64_t N, int64_t K, hipStream_t stream);
+
+size_t moe_dispatch_workspace_bytes(int64_t T, int32_t k, int32_t G);
+hipError_t launch_moe_dispatch(const int32_t* topk, int64_t T, int32_t k, int32_t lo, int32_t G,
+                               int32_t* off, int32_t* row_token, int32_t* slot_row, void* ws,
+                               hipStream_t stream);
+hipError_t launch_moe_combine(const void* out, int64_t rows_cap, const int32_t* slot_row,
+                              const float* weight, void* y, int64_t T, int32_t k, int64_t N,
+                              hipStream_t stream);
 
 }  // namespace bfp8

@@ -108,6 +108,78 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint4* __restrict_
     }
 }
 
+// act_quant of gathered rows: output row r is the quantization of input row
+// row_token[r], for r < min(*num_rows, M); rows past that, and rows whose
+// token lies outside [0, T), are not written.  Quantization is row-local, so
+// this equals gathering rows of act_quant(x).  Same mapping as
+// act_quant_kernel (eight lanes per 128-element block, two blocks per lane
+// per iteration); the block index splits into (output row, k-block) and the
+// source block is (row_token[row], k-block).
+__device__ __forceinline__ bool rows_source(const uint4* __restrict__ x,
+                                            const int32_t* __restrict__ row_token, int64_t T,
+                                            int64_t KB, int64_t blk, const uint4*& src) {
+    const int64_t r = blk / KB;
+    const int64_t kb = blk - r * KB;
+    const int64_t tok = row_token[r];
+    if (tok < 0 || tok >= T) return false;
+    src = x + (tok * KB + kb) * 16;
+    return true;
+}
+
+template <bool kHw>
+__global__ __launch_bounds__(256) void act_quant_rows_kernel(
+    const uint4* __restrict__ x, int64_t T, const int32_t* __restrict__ row_token,
+    const int32_t* __restrict__ num_rows, uint4* __restrict__ q, float* __restrict__ s, int64_t M,
+    int64_t KB) {
+    int64_t rows = M;
+    if (num_rows) {
+        const int64_t nr = *num_rows;
+        rows = nr < 0 ? 0 : (nr < M ? nr : M);
+    }
+    const int64_t nblocks = rows * KB;
+    const int lane8 = threadIdx.x & 7;
+    const int64_t groups = ((int64_t)gridDim.x * blockDim.x) >> 3;
+    int64_t blk = (((int64_t)blockIdx.x * blockDim.x) + threadIdx.x) >> 3;
+    for (; blk + groups < nblocks; blk += 2 * groups) {
+        const uint4 *pa = nullptr, *pb = nullptr;
+        const bool va = rows_source(x, row_token, T, KB, blk, pa);
+        const bool vb = rows_source(x, row_token, T, KB, blk + groups, pb);
+        uint4 a0{}, a1{}, b0{}, b1{};
+        if (va) {
+            a0 = load_nt(pa + lane8 * 2);
+            a1 = load_nt(pa + lane8 * 2 + 1);
+        }
+        if (vb) {
+            b0 = load_nt(pb + lane8 * 2);
+            b1 = load_nt(pb + lane8 * 2 + 1);
+        }
+        uint4 qa, qb;
+        float sa, sb;
+        if (va) {
+            quant_block_part<kHw>(a0, a1, lane8, qa, sa);
+            q[blk * 8 + lane8] = qa;
+            if (lane8 == 0) s[blk] = sa;
+        }
+        if (vb) {
+            quant_block_part<kHw>(b0, b1, lane8, qb, sb);
+            q[(blk + groups) * 8 + lane8] = qb;
+            if (lane8 == 0) s[blk + groups] = sb;
+        }
+    }
+    if (blk < nblocks) {
+        const uint4* pa = nullptr;
+        if (rows_source(x, row_token, T, KB, blk, pa)) {
+            const uint4 a0 = load_nt(pa + lane8 * 2);
+            const uint4 a1 = load_nt(pa + lane8 * 2 + 1);
+            uint4 qa;
+            float sa;
+            quant_block_part<kHw>(a0, a1, lane8, qa, sa);
+            q[blk * 8 + lane8] = qa;
+            if (lane8 == 0) s[blk] = sa;
+        }
+    }
+}
+
 // Encodes the fp32 bit patterns first .. first+count-1 (test helper).
 template <bool kHw>
 __global__ __launch_bounds__(256) void encode_range_kernel(uint32_t first, int64_t count,
@@ -163,6 +235,19 @@ hipError_t launch_act_quant(const void* x, void* q, float* s, int64_t M, int64_t
     const int grid = (int)(wg_needed < wg_cap ? (wg_needed > 0 ? wg_needed : 1) : wg_cap);
     hipLaunchKernelGGL(act_quant_kernel<kActQuantHwEncode>, dim3(grid), dim3(256), 0, stream,
                        (const uint4*)x, (uint4*)q, s, nblocks);
+    return hipGetLastError();
+}
+
+hipError_t launch_act_quant_rows(const void* x, int64_t T, const int32_t* row_token,
+                                 const int32_t* num_rows, void* q, float* s, int64_t M, int64_t K,
+                                 hipStream_t stream) {
+    const int64_t KB = K / kBlock;
+    const int64_t nblocks = M * KB;                            // upper bound: *num_rows may be less
+    const int64_t wg_needed = (nblocks + 63) / 64;
+    const int64_t wg_cap = (int64_t)device_cu_count() * 8;
+    const int grid = (int)(wg_needed < wg_cap ? (wg_needed > 0 ? wg_needed : 1) : wg_cap);
+    hipLaunchKernelGGL(act_quant_rows_kernel<kActQuantHwEncode>, dim3(grid), dim3(256), 0, stream,
+                       (const uint4*)x, T, row_token, num_rows, (uint4*)q, s, M, KB);
     return hipGetLastError();
 }
 

@@ -17,7 +17,8 @@ Recipe (each choice is also listed in the design notes):
   torch's own ``float8_e4m3fn`` cast of ``N(0,1) / scale`` clamped to +-448
   (torch's cast rounds to nearest-even; the clamp makes it saturate);
 * routing: per token, 256 uniform scores; a stable descending sort picks the
-  top 8 (ties to the lower expert id); experts 0..31 are kept, each with its
+  top 8 (ties to the lower expert id); the routing weights are the chosen
+  scores over their sum; experts 0..31 are the local ones, each with its
   tokens in ascending order.
 """
 from dataclasses import dataclass, field
@@ -80,11 +81,25 @@ def weight(N: int, K: int, value_seed: int, scale_seed: int, lo: float = -8.0,
     return weight_codes(N, K, S, value_seed), S
 
 
+def routing_table(tokens: int, seed: int, n_experts: int = N_ROUTED, top_k: int = TOP_K):
+    """(topk int32 [tokens, top_k], weights fp32 [tokens, top_k]).
+
+    Per token, n_experts uniform scores stand in for the gate's sigmoid scores;
+    a stable descending sort picks the top_k experts (ties to the lower id), and
+    the weights are the chosen scores divided by their sum (route scale 1).
+    """
+    scores = torch.rand(tokens, n_experts, generator=_gen(seed), dtype=torch.float32)
+    top = torch.sort(scores, dim=1, descending=True, stable=True)
+    idx = top.indices[:, :top_k].to(torch.int32).contiguous()
+    val = top.values[:, :top_k]
+    weights = (val / val.sum(dim=1, keepdim=True)).to(torch.float32).contiguous()
+    return idx, weights
+
+
 def routing(tokens: int, seed: int, n_experts: int = N_ROUTED, top_k: int = TOP_K,
             local: int = LOCAL_EXPERTS):
-    """Token ids grouped by local expert, and int32 offsets [local+1]."""
-    scores = torch.rand(tokens, n_experts, generator=_gen(seed), dtype=torch.float32)
-    order = torch.sort(scores, dim=1, descending=True, stable=True).indices[:, :top_k]
+    """Token ids grouped by local expert (experts 0 .. local-1), and int32 offsets [local+1]."""
+    order, _ = routing_table(tokens, seed, n_experts, top_k)
     ids: List[torch.Tensor] = []
     counts = []
     for e in range(local):
@@ -147,6 +162,7 @@ def make(config: int, scale: float = 1.0) -> Workload:
         t["x"] = activations(tokens, DIM, seed_of(4, 0))
         token_ids, offsets = routing(tokens, seed_of(4, 6))
         t["token_ids"], t["offsets"] = token_ids, offsets
+        t["topk"], t["weights"] = routing_table(tokens, seed_of(4, 6))
         G = LOCAL_EXPERTS
         codes = torch.empty(G, MOE_INTER, DIM, dtype=torch.uint8)
         scales = torch.empty(G, MOE_INTER // BLOCK, DIM // BLOCK, dtype=torch.float32)

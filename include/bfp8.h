@@ -44,15 +44,16 @@ extern "C" {
 #endif
 
 #define BFP8_BLOCK 128
-#define BFP8_VERSION 1
+#define BFP8_VERSION 2
+#define BFP8_MOE_MAX_GROUPS 1024
 
 typedef enum bfp8_status {
     BFP8_OK = 0,
     BFP8_ERR_NULL = 1,      /* a required pointer is NULL */
     BFP8_ERR_SHAPE = 2,     /* a size is negative, or K is not a multiple of 128 where required */
     BFP8_ERR_ALIGN = 3,     /* a pointer is not aligned as documented */
-    BFP8_ERR_WORKSPACE = 4, /* workspace given but smaller than bfp8_gemm_workspace_size() */
-    BFP8_ERR_GROUPS = 5,    /* G < 1 (grouped GEMM) */
+    BFP8_ERR_WORKSPACE = 4, /* workspace smaller than the matching *_workspace_size() */
+    BFP8_ERR_GROUPS = 5,    /* G < 1, or G > BFP8_MOE_MAX_GROUPS (MoE dispatch) */
     BFP8_ERR_HIP = 6,       /* the HIP runtime reported an error at launch */
     BFP8_ERR_ARG = 7        /* any other invalid argument */
 } bfp8_status;
@@ -118,14 +119,91 @@ size_t bfp8_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
  *   a     : e4m3 [total_M, K] rows sorted by group       a_s : fp32 [total_M, K/128]
  *   b     : e4m3 [G, N, K]                               b_s : fp32 [G, ceil(N/128), K/128]
  *   c_bf16: bf16 [total_M, N] output
- *   group_offsets : DEVICE int32 [G+1]; must satisfy off[0] = 0,
- *     off[g] <= off[g+1], off[G] = total_M.  Empty groups are allowed.  The
- *     kernel trusts the offsets (they live on the device); rows outside every
- *     group are never written.
+ *   group_offsets : DEVICE int32 [G+1], normally off[0] = 0 and
+ *     off[g] <= off[g+1] <= total_M.  Empty groups are allowed, and off[G] may
+ *     be less than total_M, so total_M can be a capacity (e.g. the offsets
+ *     written by bfp8_moe_dispatch, read by the kernel without a host copy).
+ *     The kernel clamps every offset into [0, total_M] and each group's end to
+ *     at least its start, so no offset value makes it read or write outside
+ *     the buffers.  Rows outside every group are never written.
  * Errors: as bfp8_gemm, plus BFP8_ERR_GROUPS if G < 1. */
 int bfp8_gemm_grouped(const void* a, const float* a_s, const void* b, const float* b_s,
                       void* c_bf16, const int32_t* group_offsets, int32_t G,
                       int64_t total_M, int64_t N, int64_t K, void* stream);
+
+/* ----------------------------------------------------------------------
+ * MoE dispatch and combine around the grouped GEMM ([BT] "MoE trace": per
+ * expert counts; for each local expert with tokens, the tokens routed to it,
+ * in ascending order, go through the expert, and y[idx] gains the expert's
+ * output times the routing weight, y starting at zero; [DF] expert sharding:
+ * a GPU holds the contiguous expert range expert_lo .. expert_lo + G - 1).
+ * Together: bfp8_moe_dispatch -> bfp8_act_quant_rows -> bfp8_gemm_grouped ->
+ * bfp8_moe_combine, all on the device, with no host synchronization.
+ * ---------------------------------------------------------------------- */
+
+/* Bytes of int32 workspace bfp8_moe_dispatch needs (a multiple of 16; 0 when
+ * T * k == 0).  Pure host function. */
+size_t bfp8_moe_dispatch_workspace_size(int64_t T, int32_t k, int32_t G);
+
+/* Stable counting sort of the routed (token, slot) pairs by local expert.
+ *   topk_idx      : DEVICE int32 [T, k] expert id of each (token, slot); ids
+ *                   outside expert_lo .. expert_lo + G - 1 are not local
+ *   group_offsets : DEVICE int32 [G+1] output: rows of local expert g are
+ *                   off[g] .. off[g+1]; off[0] = 0, off[G] = local pairs
+ *   row_token     : DEVICE int32 [T * k] output: row_token[r] = token of row r
+ *                   for r < off[G] (entries past off[G] are not written)
+ *   slot_row      : DEVICE int32 [T, k] output: the row of each (token, slot),
+ *                   or -1 when the slot's expert is not local
+ * Inside one expert, rows follow (token, slot) order, so tokens ascend, as in
+ * the pages' per-expert selection.  Deterministic.
+ *   workspace     : DEVICE, at least bfp8_moe_dispatch_workspace_size(T, k, G)
+ *                   bytes, 4-byte aligned; contents on entry are ignored.
+ * T == 0 still writes group_offsets (all zero).
+ * Errors: BFP8_ERR_SHAPE if T < 0, k < 1 or T * k >= 2^31; BFP8_ERR_GROUPS if
+ * G < 1 or G > BFP8_MOE_MAX_GROUPS; BFP8_ERR_NULL for a NULL pointer that the
+ * call needs; BFP8_ERR_ALIGN if an int32 array or the workspace is not 4-byte
+ * aligned; BFP8_ERR_WORKSPACE if workspace_bytes is too small. */
+int bfp8_moe_dispatch(const int32_t* topk_idx, int64_t T, int32_t k, int32_t expert_lo,
+                      int32_t G, int32_t* group_offsets, int32_t* row_token, int32_t* slot_row,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* act_quant of gathered rows: for r < min(*num_rows, M) output row r is
+ * act_quant of input row row_token[r] (same arithmetic as bfp8_act_quant,
+ * bit for bit; quantization is row-local, so this equals gathering rows of
+ * act_quant(x)).  Rows past min(*num_rows, M), and rows whose token is
+ * outside [0, T), are not written.
+ *   x_bf16    : bf16 [T, K], 16-byte aligned
+ *   row_token : DEVICE int32 [M]
+ *   num_rows  : DEVICE int32 [1], e.g. group_offsets + G of bfp8_moe_dispatch;
+ *               NULL means M rows
+ *   q_e4m3    : e4m3 [M, K] output, 16-byte aligned
+ *   scales    : fp32 [M, K/128] output
+ * Errors: BFP8_ERR_SHAPE if T < 0, M < 0, K <= 0 or K % 128 != 0;
+ * BFP8_ERR_NULL; BFP8_ERR_ALIGN. */
+int bfp8_act_quant_rows(const void* x_bf16, int64_t T, const int32_t* row_token,
+                        const int32_t* num_rows, void* q_e4m3, float* scales, int64_t M,
+                        int64_t K, void* stream);
+
+/* Weighted combine of the expert outputs back to token order:
+ *     y[t, n] = bf16_rne( sum_{j < k, 0 <= slot_row[t,j] < rows} weights[t, j] *
+ *                         expert_out[slot_row[t, j], n] )
+ * summed in fp32 in slot order (fused multiply-adds); a token with no local
+ * slot gets zeros.  This is the pages' y[idx] += expert(x[idx]) * weight over
+ * the local experts, with one rounding to bf16 at the end instead of one per
+ * expert.
+ *   expert_out_bf16 : bf16 [rows, N] (the grouped GEMM's output)
+ *   slot_row        : DEVICE int32 [T, k] (from bfp8_moe_dispatch)
+ *   weights         : DEVICE fp32 [T, k] routing weights
+ *   y_bf16          : bf16 [T, N] output (every element written)
+ * A 16-byte vector kernel runs when N % 8 == 0 and expert_out and y are
+ * 16-byte aligned; a scalar one otherwise.
+ * Errors: BFP8_ERR_SHAPE if T < 0, k < 1, N < 0, rows < 0, T > 2^24,
+ * T * k >= 2^31 or N > 65535 * 2048; BFP8_ERR_NULL;
+ * BFP8_ERR_ALIGN if a bf16 pointer is not 2-byte or an int32/fp32 pointer not
+ * 4-byte aligned. */
+int bfp8_moe_combine(const void* expert_out_bf16, int64_t rows, const int32_t* slot_row,
+                     const float* weights, void* y_bf16, int64_t T, int32_t k, int64_t N,
+                     void* stream);
 
 /* Test helper: encodes the 2^32 float32 bit patterns first .. first+count-1
  * to e4m3 codes with the same device routine act_quant uses (variant 0), or

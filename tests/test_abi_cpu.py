@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert bfp8.bfp8_version() == 1
+    assert bfp8.bfp8_version() == 2
     for code in range(8):
         assert bfp8.bfp8_status_string(code)
     assert bfp8.bfp8_status_string(0) == "ok"
@@ -127,6 +127,64 @@ def test_gemm_grouped_validation(lib):
     assert call(off=ctypes.c_void_p(0x10002)) == _lib.BFP8_ERR_ALIGN
     assert call(a=ODD) == _lib.BFP8_ERR_ALIGN
     assert call(a=None, T=0) == _lib.BFP8_OK
+
+
+def test_moe_dispatch_validation(lib):
+    f = lib.bfp8_moe_dispatch
+    need = bfp8.bfp8_moe_dispatch_workspace_size(100, 8, 32)
+    assert need > 0 and need % 16 == 0
+    assert bfp8.bfp8_moe_dispatch_workspace_size(0, 8, 32) == 0
+    assert bfp8.bfp8_moe_dispatch_workspace_size(100, 8, 2000) == 0
+
+    def call(topk=FAKE, T=100, k=8, lo=0, G=32, off=FAKE, rt=FAKE, sr=FAKE, ws=FAKE, wsb=need):
+        return f(topk, T, k, lo, G, off, rt, sr, ws, wsb, None)
+
+    assert call(T=-1) == _lib.BFP8_ERR_SHAPE
+    assert call(k=0) == _lib.BFP8_ERR_SHAPE
+    assert call(T=1 << 28, k=8) == _lib.BFP8_ERR_SHAPE          # T*k reaches 2^31
+    assert call(G=0) == _lib.BFP8_ERR_GROUPS
+    assert call(G=1025) == _lib.BFP8_ERR_GROUPS
+    for name in ("topk", "off", "rt", "sr", "ws"):
+        assert call(**{name: None}) == _lib.BFP8_ERR_NULL, name
+    assert call(off=ctypes.c_void_p(0x10002)) == _lib.BFP8_ERR_ALIGN
+    assert call(ws=ctypes.c_void_p(0x10001)) == _lib.BFP8_ERR_ALIGN
+    assert call(wsb=need - 16) == _lib.BFP8_ERR_WORKSPACE
+    assert call(T=0, off=None) == _lib.BFP8_ERR_NULL             # offsets are written even for T=0
+
+
+def test_act_quant_rows_validation(lib):
+    f = lib.bfp8_act_quant_rows
+
+    def call(x=FAKE, T=10, rt=FAKE, nr=FAKE, q=FAKE, s=FAKE, M=20, K=256):
+        return f(x, T, rt, nr, q, s, M, K, None)
+
+    assert call(K=100) == _lib.BFP8_ERR_SHAPE
+    assert call(T=-1) == _lib.BFP8_ERR_SHAPE
+    assert call(M=-1) == _lib.BFP8_ERR_SHAPE
+    for name in ("x", "rt", "q", "s"):
+        assert call(**{name: None}) == _lib.BFP8_ERR_NULL, name
+    assert call(x=ODD) == _lib.BFP8_ERR_ALIGN
+    assert call(q=ctypes.c_void_p(0x10008)) == _lib.BFP8_ERR_ALIGN
+    assert call(nr=ctypes.c_void_p(0x10002)) == _lib.BFP8_ERR_ALIGN
+    assert call(M=0, x=None, rt=None) == _lib.BFP8_OK
+
+
+def test_moe_combine_validation(lib):
+    f = lib.bfp8_moe_combine
+
+    def call(o=FAKE, rows=50, sr=FAKE, w=FAKE, y=FAKE, T=10, k=8, N=64):
+        return f(o, rows, sr, w, y, T, k, N, None)
+
+    assert call(T=-1) == _lib.BFP8_ERR_SHAPE
+    assert call(k=0) == _lib.BFP8_ERR_SHAPE
+    assert call(rows=-1) == _lib.BFP8_ERR_SHAPE
+    assert call(T=(1 << 24) + 1, k=1) == _lib.BFP8_ERR_SHAPE
+    for name in ("o", "sr", "w", "y"):
+        assert call(**{name: None}) == _lib.BFP8_ERR_NULL, name
+    assert call(o=ODD) == _lib.BFP8_ERR_ALIGN
+    assert call(sr=ctypes.c_void_p(0x10002)) == _lib.BFP8_ERR_ALIGN
+    assert call(T=0) == _lib.BFP8_OK
+    assert call(o=None, rows=0, T=0) == _lib.BFP8_OK
 
 
 def test_encode_range_validation(lib):
