@@ -273,15 +273,17 @@ struct BigTile {
     // Row scales of one K block, permuted for the fragment layout: row 16 i + t
     // sits at float t * SPITCH + i.  SPITCH = BM/16 + 4 keeps the 16 lanes of a
     // read on distinct bank groups and each lane's TM values 16-byte aligned.
-    // The weight scale of the tile's n-th 128-column block sits in the first
-    // pad slot of line n, at float n * SPITCH + BM/16.
     static constexpr int SPITCH = BM / 16 + 4;
     static constexpr int S_FLOATS = 16 * SPITCH;
     static constexpr int S_INSTR = (S_FLOATS + 63) / 64;   // 256-byte scale instructions
-    // every wave issues one scale instruction (waves past S_INSTR fill unused
-    // slots), so all waves have the same number of loads in flight per stage
-    static constexpr int S_BYTES = (WAVES * 256 + 1023) / 1024 * 1024;
-    static constexpr int LOADS_PER_STAGE = BM / 8 / WAVES + BN / 8 / WAVES + 1;
+    // Every wave issues one row-scale instruction into its own 256-byte slot
+    // (waves past S_INSTR fill slots nobody reads) and one weight-scale
+    // instruction into the shared 256-byte weight-scale line (float t = the
+    // weight scale of the tile's 128-column block t; every wave writes the
+    // same values there), so all waves have the same loads in flight.
+    static constexpr int SB_OFF = WAVES * 256;
+    static constexpr int S_BYTES = (WAVES * 256 + 256 + 1023) / 1024 * 1024;
+    static constexpr int LOADS_PER_STAGE = BM / 8 / WAVES + BN / 8 / WAVES + 2;
 
     static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
     static constexpr int A_INSTR = BM / 8 / WAVES;          // 1 KB instructions per wave for A
@@ -290,9 +292,24 @@ struct BigTile {
     static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns must share one scale block");
     static_assert(S_INSTR <= WAVES, "one scale instruction per wave at most");
     static_assert(TM % 4 == 0, "scales are read four at a time");
-    static_assert(BN / 128 <= 16 || BN < 128, "weight scales use one pad slot per line");
+    static_assert(BN / 128 <= 64, "weight scales fit one 64-float line");
     static_assert(STAGE % 1024 == 0, "stages stay 1 KB aligned");
-    static_assert(NSTAGE >= 2 && NSTAGE * STAGE <= 160 * 1024, "stages must fit in LDS");
+    static_assert(NSTAGE >= 2 && NSTAGE <= 4 && NSTAGE * STAGE <= 158 * 1024, "stages must fit in LDS");
+};
+
+// The LDS stages of a large tile are distinct __shared__ arrays, and the K
+// loop is unrolled by the stage count, so every read and every
+// direct-to-LDS fill names its stage at compile time.  The compiler can then
+// see that a fill of one stage never aliases the reads of another, and it
+// waits on LDS reads only for the reads it needs (with one shared array it
+// drains every outstanding LDS read before each use).
+template <class T>
+struct Stages {
+    uint8_t* p[4];
+};
+template <int S>
+struct StageId {
+    static constexpr int value = S;
 };
 
 typedef __attribute__((address_space(3))) void* lds_void_t;
@@ -319,6 +336,22 @@ __device__ __forceinline__ void barrier_lds() {
     asm volatile("" ::: "memory");
 }
 
+// Direct-to-LDS loads through a buffer resource (MUBUF).  Unlike the flat
+// global form, the compiler tracks these only with the vector-memory
+// counter, so LDS reads that follow them keep precise LDS waits.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes) {
+    const int num = (int)(bytes < 0xFFFFFFFFull ? bytes : 0xFFFFFFFFull);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, num, 0x00020000);
+}
+__device__ __forceinline__ void buf_lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                          void* lds_dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t)lds_dst, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void buf_lds4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                         void* lds_dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t)lds_dst, 4, voff, soff, 0, 0);
+}
+
 __device__ __forceinline__ void load_lds16(const void* src, void* lds_dst) {
     __builtin_amdgcn_global_load_lds((gbl_void_t)src, (lds_void_t)lds_dst, 16, 0, 0);
 }
@@ -341,72 +374,96 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
                                               const uint8_t* __restrict__ b,
                                               const float* __restrict__ bs,
                                               uint16_t* __restrict__ c, int64_t m0, int64_t m_end,
-                                              int64_t n0, int64_t N, int64_t K, uint8_t* lds) {
+                                              int64_t n0, int64_t N, int64_t K,
+                                              const Stages<T>& st) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm0 = (wave / T::WAVES_N) * T::WM;
     const int wn0 = (wave % T::WAVES_N) * T::WN;
     const int64_t KB = K / kBlock;
+    const int64_t NBK = (N + kBlock - 1) / kBlock;
+    const int64_t rows_a = (m_end - m0) < T::BM ? (m_end - m0) : T::BM;     // >= 1
+    const int64_t rows_b = (N - n0) < T::BN ? (N - n0) : T::BN;            // >= 1
+
+    // Buffer resources cover exactly the tile's valid rows (and the scale
+    // rows), and every offset below stays inside them: rows past the end
+    // read the last valid row and are never stored.
+    const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(a + m0 * K, (uint64_t)rows_a * K);
+    const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(b + n0 * K, (uint64_t)rows_b * K);
+    const __amdgpu_buffer_rsrc_t rs_as = make_rsrc(as + m0 * KB, (uint64_t)rows_a * KB * 4);
+    const __amdgpu_buffer_rsrc_t rs_bs = make_rsrc(bs, (uint64_t)NBK * KB * 4);
 
     // Direct-load sources.  Instruction i of this wave fills LDS rows
     // r0 .. r0+7 (r0 = 8 * (wave * INSTR + i)); lane l writes physical chunk
     // l & 7 of row r0 + (l >> 3), which must hold logical chunk
-    // (l & 7) ^ swz(row).  Offsets are 32-bit, relative to the tile's
-    // first row, so the K-block step is one scalar add on the base pointer.
+    // (l & 7) ^ swz(row).  Offsets are relative to the tile's first row; the
+    // K block enters as the scalar offset.
     const int lrow = lane >> 3;
     uint32_t a_off[T::A_INSTR], b_off[T::B_INSTR];
 #pragma unroll
     for (int i = 0; i < T::A_INSTR; ++i) {
-        const int row = (wave * T::A_INSTR + i) * 8 + lrow;
+        int row = (wave * T::A_INSTR + i) * 8 + lrow;
         const int chunk = (lane & 7) ^ swz(row);
-        int64_t grow = m0 + row;
-        grow = grow < m_end ? grow : m_end - 1;
-        a_off[i] = (uint32_t)((grow - m0) * K) + chunk * 16;
+        row = row < rows_a ? row : (int)rows_a - 1;
+        a_off[i] = (uint32_t)(row * K) + chunk * 16;
     }
 #pragma unroll
     for (int i = 0; i < T::B_INSTR; ++i) {
-        const int row = (wave * T::B_INSTR + i) * 8 + lrow;
+        int row = (wave * T::B_INSTR + i) * 8 + lrow;
         const int chunk = (lane & 7) ^ swz(row);
-        int64_t gcol = n0 + row;
-        gcol = gcol < N ? gcol : N - 1;
-        b_off[i] = (uint32_t)((gcol - n0) * K) + chunk * 16;
+        row = row < rows_b ? row : (int)rows_b - 1;
+        b_off[i] = (uint32_t)(row * K) + chunk * 16;
     }
-    // scale slot p = t * SPITCH + i holds the activation scale of row 16 i + t;
-    // slot t * SPITCH + BM/16 holds the weight scale of the tile's 128-column
-    // block t; other pad slots load row 0's scale (never read)
-    const int64_t NBK = (N + kBlock - 1) / kBlock;
-    const float* s_src;
+    // row-scale slot p = t * SPITCH + i holds the activation scale of row
+    // 16 i + t; other slots load row 0's scale (never read)
+    uint32_t as_off;
     {
         const int p = wave * 64 + lane;
         const int t = p / T::SPITCH, i = p % T::SPITCH;
-        if (i == T::BM / 16 && t < (T::BN + 127) / 128) {
-            int64_t nb = (n0 >> 7) + t;
-            nb = nb < NBK ? nb : NBK - 1;
-            s_src = bs + nb * KB;
-        } else {
-            const int row = (t < 16 && i < T::BM / 16) ? 16 * i + t : 0;
-            int64_t grow = m0 + row;
-            grow = grow < m_end ? grow : m_end - 1;
-            s_src = as + grow * KB;
-        }
+        int row = (t < 16 && i < T::BM / 16) ? 16 * i + t : 0;
+        row = row < rows_a ? row : (int)rows_a - 1;
+        as_off = (uint32_t)(row * KB * 4);
     }
-    const uint8_t* a_tile = a + m0 * K;
-    const uint8_t* b_tile = b + n0 * K;
-    const int sb_slot = ((wn0 >> 7) * T::SPITCH + T::BM / 16);   // this wave's weight scale
+    // weight-scale line: float l = scale of 128-column block (n0 / 128 + l)
+    uint32_t bs_off;
+    {
+        int64_t nb = (n0 >> 7) + lane;
+        nb = nb < NBK ? nb : NBK - 1;
+        bs_off = (uint32_t)(nb * KB * 4);
+    }
 
-    auto issue = [&](int64_t kb, int stage) {
-        uint8_t* base = lds + stage * T::STAGE;
-        const uint8_t* ak = a_tile + kb * kBlock;
-        const uint8_t* bk = b_tile + kb * kBlock;
+    auto issue = [&](int64_t kb, uint8_t* base) __attribute__((always_inline)) {
+        const uint32_t ko = (uint32_t)(kb * kBlock);
 #pragma unroll
         for (int i = 0; i < T::A_INSTR; ++i)
-            load_lds16(ak + a_off[i], base + (wave * T::A_INSTR + i) * 1024);
+            buf_lds16(rs_a, a_off[i], ko, base + (wave * T::A_INSTR + i) * 1024);
 #pragma unroll
         for (int i = 0; i < T::B_INSTR; ++i)
-            load_lds16(bk + b_off[i], base + T::A_BYTES + (wave * T::B_INSTR + i) * 1024);
-        load_lds4(s_src + kb, base + T::A_BYTES + T::B_BYTES + wave * 256);
+            buf_lds16(rs_b, b_off[i], ko, base + T::A_BYTES + (wave * T::B_INSTR + i) * 1024);
+        const uint32_t so = (uint32_t)(kb * 4);
+        buf_lds4(rs_as, as_off, so, base + T::A_BYTES + T::B_BYTES + wave * 256);
+        buf_lds4(rs_bs, bs_off, so, base + T::A_BYTES + T::B_BYTES + T::SB_OFF);
     };
+    // load q of a stage, in issue()'s order: A rows, B rows, row scales, weight scales
+    auto issue_one = [&](int q, int64_t kb, uint8_t* base) __attribute__((always_inline)) {
+        const uint32_t ko = (uint32_t)(kb * kBlock);
+        const uint32_t so = (uint32_t)(kb * 4);
+        if (q < T::A_INSTR)
+            buf_lds16(rs_a, a_off[q], ko, base + (wave * T::A_INSTR + q) * 1024);
+        else if (q < T::A_INSTR + T::B_INSTR)
+            buf_lds16(rs_b, b_off[q - T::A_INSTR], ko,
+                      base + T::A_BYTES + (wave * T::B_INSTR + q - T::A_INSTR) * 1024);
+        else if (q == T::A_INSTR + T::B_INSTR)
+            buf_lds4(rs_as, as_off, so, base + T::A_BYTES + T::B_BYTES + wave * 256);
+        else
+            buf_lds4(rs_bs, bs_off, so, base + T::A_BYTES + T::B_BYTES + T::SB_OFF);
+    };
+    // With two stages the next block's loads go out right after the barrier
+    // (they get one block of lead); with three or more they are spread over
+    // the first rows' MFMAs of the full-tile loop, so no wave stalls on a long
+    // burst of load issues while its MFMAs wait.
+    constexpr bool kSpread = T::NSTAGE > 2;
 
     v4f acc[T::TM][T::TN];
 #pragma unroll
@@ -415,7 +472,9 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
         for (int j = 0; j < T::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
     // a workgroup that walks several tiles must not refill a stage that a
-    // slower wave still reads for the previous tile
+    // slower wave still reads for the previous tile, and every wave's loads
+    // of the previous tile have landed (all waves write the weight-scale line)
+    wait_vmcnt<0>();
     barrier_lds();
     int tm_valid = T::TM;
     if (kGuard) {
@@ -424,38 +483,39 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
         tm_valid = __builtin_amdgcn_readfirstlane(tm_valid);
     }
 
-    // prologue: K blocks 0 .. NSTAGE-2 in flight
-#pragma unroll
-    for (int st = 0; st + 1 < T::NSTAGE; ++st)
-        if (st < KB) issue(st, st);
+    // prologue: K blocks 0 .. NSTAGE-2 in flight, block s in stage s
+    issue(0, st.p[0]);
+    if (T::NSTAGE > 2 && 1 < KB) issue(1, st.p[1]);
+    if (T::NSTAGE > 3 && 2 < KB) issue(2, st.p[2]);
 
     const int lr = lane & 15;
     const int lk = (lane >> 4) * 2;
     const int off0 = ((lk ^ swz(lr)) << 4);
     const int off1 = (((lk + 1) ^ swz(lr)) << 4);
     const int sread = lr * T::SPITCH + wm0 / 16;
+    const int sb_slot = wn0 >> 7;                      // this wave's weight-scale float
 
-    int cur = 0;
-    for (int64_t kb = 0; kb < KB; ++kb) {
-        // this wave's loads of block kb are done once at most the later
-        // blocks' loads are outstanding; the barrier then makes every wave's
-        // loads visible and guarantees stage (kb-1) is no longer being read
-        // loads complete in issue order; after block kb's loads, at most the
-        // loads of blocks kb+1 .. kb+NSTAGE-2 may be outstanding
+    // One K block from stage S; block kb + NSTAGE - 1 goes to the stage that
+    // block kb - 1 used.
+    auto step = [&](int64_t kb, auto S_) __attribute__((always_inline)) {
+        constexpr int S = decltype(S_)::value;
+        constexpr int SF = (S + T::NSTAGE - 1) % T::NSTAGE;
+        // this wave's loads of block kb are done once at most the loads of
+        // blocks kb+1 .. kb+NSTAGE-2 are outstanding (loads complete in issue
+        // order); the barrier then makes every wave's loads visible and
+        // guarantees stage SF (block kb - 1) is no longer being read
         if (kb + T::NSTAGE - 2 < KB)
             wait_vmcnt<T::LOADS_PER_STAGE * (T::NSTAGE - 2)>();
         else
             wait_vmcnt<0>();
         barrier_lds();
-        if (kb + T::NSTAGE - 1 < KB) {
-            int st = cur + T::NSTAGE - 1;
-            st = st >= T::NSTAGE ? st - T::NSTAGE : st;
-            issue(kb + T::NSTAGE - 1, st);
-        }
+        const bool more = kb + T::NSTAGE - 1 < KB;
+        if ((kGuard || !kSpread) && more) issue(kb + T::NSTAGE - 1, st.p[SF]);
 
-        const uint8_t* As = lds + cur * T::STAGE;
+        const uint8_t* As = st.p[S];
         const uint8_t* Bs = As + T::A_BYTES;
         const float* Ss = (const float*)(Bs + T::B_BYTES);
+        const float* Sb = (const float*)(Bs + T::B_BYTES + T::SB_OFF);
         if (!kGuard) {
             // The K block as a fixed sequence of small scheduling regions
             // (sched_barrier keeps the compiler from reordering across them):
@@ -485,7 +545,7 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
                 } else {
 #pragma unroll
                     for (int i = 0; i < T::TM; i += 4) s4[i / 4] = *(const v4f*)(Ss + sread + i);
-                    sbv = Ss[sb_slot];
+                    sbv = Sb[sb_slot];
                 }
                 cur_p[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                     fb[j], fa_cur, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
@@ -505,6 +565,17 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 1; i < T::TM; ++i) {
+                if (kSpread && more) {
+                    constexpr int NQ = T::LOADS_PER_STAGE;
+                    const int q0 = 2 * (i - 1);
+                    if (q0 < NQ) issue_one(q0, kb + T::NSTAGE - 1, st.p[SF]);
+                    if (q0 + 1 < NQ) issue_one(q0 + 1, kb + T::NSTAGE - 1, st.p[SF]);
+                    if (i == T::TM - 1) {
+#pragma unroll
+                        for (int q = q0 + 2; q < NQ; ++q) issue_one(q, kb + T::NSTAGE - 1, st.p[SF]);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
                 fa_cur = fa_nxt;
                 if (i + 1 < T::TM) {
                     const uint8_t* r = As + (wm0 + 16 * (i + 1) + lr) * kBlock;
@@ -536,7 +607,7 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
                 const uint8_t* q = Bs + (wn0 + 16 * j + lr) * kBlock;
                 fb[j] = frag_from(*(const uint4*)(q + off0), *(const uint4*)(q + off1));
             }
-            const float sbv = Ss[sb_slot];
+            const float sbv = Sb[sb_slot];
             float sc[T::TM];
 #pragma unroll
             for (int i = 0; i < T::TM; i += 4) {
@@ -558,7 +629,17 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
                 }
             }
         }
-        cur = cur + 1 == T::NSTAGE ? 0 : cur + 1;
+    };
+
+    for (int64_t kb0 = 0; kb0 < KB; kb0 += T::NSTAGE) {
+        step(kb0, StageId<0>{});
+        if (kb0 + 1 < KB) step(kb0 + 1, StageId<1>{});
+        if constexpr (T::NSTAGE > 2) {
+            if (kb0 + 2 < KB) step(kb0 + 2, StageId<2>{});
+        }
+        if constexpr (T::NSTAGE > 3) {
+            if (kb0 + 3 < KB) step(kb0 + 3, StageId<3>{});
+        }
     }
 
     // epilogue: lane holds row m0 + wm0 + 16 i + lr, columns n0 + wn0 + 16 j + 4 (lane >> 4) + 0..3
@@ -594,6 +675,14 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
     }
 }
 
+// The stage arrays of a large-tile kernel (unused ones are 16 bytes).
+#define BIG_TILE_STAGES(T, st)                                                            \
+    __shared__ __attribute__((aligned(1024))) uint8_t st##_0[T::STAGE];                    \
+    __shared__ __attribute__((aligned(1024))) uint8_t st##_1[T::STAGE];                    \
+    __shared__ __attribute__((aligned(1024))) uint8_t st##_2[T::NSTAGE > 2 ? T::STAGE : 16]; \
+    __shared__ __attribute__((aligned(1024))) uint8_t st##_3[T::NSTAGE > 3 ? T::STAGE : 16]; \
+    const Stages<T> st = {{st##_0, st##_1, st##_2, st##_3}}
+
 // Maps a workgroup id to a tile so that the workgroups resident on one XCD
 // (ids are dealt round-robin over the 8 XCDs) work on a compact block of
 // tiles: ids are first regrouped XCD by XCD, then walked in bands of GM
@@ -619,7 +708,7 @@ __global__ __launch_bounds__(T::THREADS, 1) void gemm_big_kernel(const uint8_t* 
                                                                  uint16_t* __restrict__ c,
                                                                  int64_t M, int64_t N, int64_t K,
                                                                  int mt, int nt) {
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[T::NSTAGE * T::STAGE];
+    BIG_TILE_STAGES(T, lds);
     int tm, tn;
     tile_of(blockIdx.x, gridDim.x, mt, nt, tm, tn);
     const int64_t m0 = (int64_t)tm * T::BM;
@@ -679,7 +768,7 @@ __global__ __launch_bounds__(T::THREADS, 1) void gemm_grouped_big_kernel(
     const uint8_t* __restrict__ a, const float* __restrict__ as, const uint8_t* __restrict__ b,
     const float* __restrict__ bs, uint16_t* __restrict__ c, const int32_t* __restrict__ off,
     int G, int64_t total_M, int64_t N, int64_t K, int nt) {
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[T::NSTAGE * T::STAGE];
+    BIG_TILE_STAGES(T, lds);
     const int64_t KB = K / kBlock;
     const int64_t NB = (N + kBlock - 1) / kBlock;
     int64_t total = 0;
