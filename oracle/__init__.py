@@ -55,6 +55,8 @@ class Oracle:
         lib.oracle_gemm_grouped_rows.argtypes = [P, P, P, P, P, ctypes.c_int32, I64, I64, I64,
                                                  P, I64, P, ctypes.c_int]
         lib.oracle_gemm_grouped_rows.restype = ctypes.c_int
+        lib.oracle_gemm_bf16_rows.argtypes = [P, P, I64, I64, I64, P, I64, P, ctypes.c_int]
+        lib.oracle_gemm_bf16_rows.restype = ctypes.c_int
         lib.oracle_moe_dispatch.argtypes = [P, I64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                             P, P, P]
         lib.oracle_moe_combine.argtypes = [P, P, P, I64, ctypes.c_int32, I64, P]
@@ -171,6 +173,21 @@ class Oracle:
         return out
 
 
+    def gemm_bf16(self, a_bits, b_bits, rows=None, threads=None) -> np.ndarray:
+        """fp64 reference of C = A * B^T for bf16 A [M,K] and B [N,K] (bit patterns), given rows."""
+        a = _c(a_bits, np.uint16); b = _c(b_bits, np.uint16)
+        M, K = a.shape
+        N = b.shape[0]
+        if b.shape[1] != K:
+            raise ValueError("gemm_bf16 operand shapes do not agree")
+        r = _rows(rows, M)
+        out = np.empty((r.size, N), np.float64)
+        rc = self.lib.oracle_gemm_bf16_rows(_ptr(a), _ptr(b), M, N, K, _ptr(r), r.size, _ptr(out),
+                                            threads or default_threads())
+        if rc:
+            raise ValueError(f"oracle_gemm_bf16_rows failed ({rc})")
+        return out
+
     # ---------------------------------------------------------------- MoE
 
     def moe_dispatch(self, topk, expert_lo, G):
@@ -267,6 +284,10 @@ def gemm(a, sa, b, sb, rows=None, threads=None):
 
 def gemm_grouped(a, sa, b, sb, offsets, rows=None, threads=None):
     return default().gemm_grouped(a, sa, b, sb, offsets, rows, threads)
+
+
+def gemm_bf16(a_bits, b_bits, rows=None, threads=None):
+    return default().gemm_bf16(a_bits, b_bits, rows, threads)
 
 
 def moe_dispatch(topk, expert_lo, G):

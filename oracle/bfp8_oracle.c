@@ -26,6 +26,8 @@
  *     selected in ascending order, run through the expert, and added into a
  *     zero-initialised y after multiplication by their routing weight.
  *     "Data flow" (codevetter): a GPU holds a contiguous range of experts.
+ *   - pyshine tour, "FP8 with per-block scales": the second branch of
+ *     linear() dequantizes the weight and runs an ordinary BF16 matmul.
  * The e4m3 format itself is the OCP 8-bit floating point E4M3 encoding
  * (torch.float8_e4m3fn): bias 7, no infinities, NaN only at S.1111.111,
  * largest finite value 448.
@@ -296,6 +298,69 @@ int oracle_gemm_grouped_rows(const uint8_t* a, const float* sa, const uint8_t* b
     for (int64_t i = 0; i < nrows; ++i)
         if (rows[i] < 0 || rows[i] >= total_M) return -1;
     return run_gemm_rows(a, sa, b, sb, off, G, N, K, rows, nrows, out, nthreads);
+}
+
+/* --------------------------------------------------------- BF16 branch GEMM */
+
+/* The other branch of linear(): the weight is first expanded to bf16
+ * (weight_dequant) and multiplied with the bf16 activations by an ordinary
+ * BF16 matmul (pyshine tour, "FP8 with per-block scales").  Reference:
+ *     out[i, n] = sum_k a[rows[i], k] * b[n, k]   in fp64,
+ * a bf16 [M,K], b bf16 [N,K] (bit patterns), C = A * B^T.  Each product of
+ * two bf16 values is exact in fp64; only the sum rounds. */
+typedef struct {
+    const uint16_t *a, *b;
+    int64_t N, K;
+    const int64_t* rows;
+    int64_t nrows;
+    double* out;
+    int tid, nthreads;
+} gemm_bf16_job;
+
+static void* gemm_bf16_worker(void* arg) {
+    gemm_bf16_job* J = (gemm_bf16_job*)arg;
+    double* arow = (double*)malloc((size_t)J->K * sizeof(double));
+    if (!arow) return NULL;
+    for (int64_t i = J->tid; i < J->nrows; i += J->nthreads) {
+        const uint16_t* a = J->a + J->rows[i] * J->K;
+        for (int64_t k = 0; k < J->K; ++k) arow[k] = (double)oracle_bf16_to_f32(a[k]);
+        for (int64_t n = 0; n < J->N; ++n) {
+            const uint16_t* b = J->b + n * J->K;
+            double sum = 0.0;
+            for (int64_t k = 0; k < J->K; ++k) sum += arow[k] * (double)oracle_bf16_to_f32(b[k]);
+            J->out[i * J->N + n] = sum;
+        }
+    }
+    free(arow);
+    return NULL;
+}
+
+int oracle_gemm_bf16_rows(const uint16_t* a, const uint16_t* b, int64_t M, int64_t N, int64_t K,
+                          const int64_t* rows, int64_t nrows, double* out, int nthreads) {
+    if (M < 0 || N < 0 || K < 0) return -1;
+    for (int64_t i = 0; i < nrows; ++i)
+        if (rows[i] < 0 || rows[i] >= M) return -1;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    gemm_bf16_job* jobs = (gemm_bf16_job*)calloc((size_t)nthreads, sizeof(gemm_bf16_job));
+    pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+    if (!jobs || !th) { free(jobs); free(th); return -2; }
+    for (int t = 0; t < nthreads; ++t) {
+        gemm_bf16_job* J = &jobs[t];
+        J->a = a; J->b = b; J->N = N; J->K = K;
+        J->rows = rows; J->nrows = nrows; J->out = out;
+        J->tid = t; J->nthreads = nthreads;
+    }
+    int started = 0;
+    for (int t = 1; t < nthreads; ++t) {
+        if (pthread_create(&th[t], NULL, gemm_bf16_worker, &jobs[t]) != 0) break;
+        started = t;
+    }
+    for (int t = started + 1; t < nthreads; ++t) gemm_bf16_worker(&jobs[t]);
+    gemm_bf16_worker(&jobs[0]);
+    for (int t = 1; t <= started; ++t) pthread_join(th[t], NULL);
+    free(jobs); free(th);
+    return 0;
 }
 
 /* ------------------------------------------------- MoE dispatch and combine */

@@ -521,6 +521,58 @@ def pin_grouped_reduces_to_gemm(orc):
     assert np.all(np.isnan(partial[4:])) and not np.any(np.isnan(partial[:4]))
 
 
+# ------------------------------------------------------------- BF16 branch pins
+#
+# Source: pyshine "DeepSeek-V3" tour, "FP8 with per-block scales": the other
+# branch of linear() dequantizes the weight and runs an ordinary BF16 matmul.
+
+def _rand_bf16_bits(shape, seed, scale=1.0):
+    rng = np.random.default_rng(seed)
+    return torch_bf16((rng.standard_normal(shape) * scale).astype(np.float32)).reshape(shape)
+
+
+def pin_gemm_bf16_exact_rational(orc):
+    """B1: bf16 GEMM == the exact rational sum (fractions), up to one fp64 rounding per term."""
+    a = _rand_bf16_bits((3, 40), 1001)
+    b = _rand_bf16_bits((5, 40), 1002, 3.0)
+    got = orc.gemm_bf16(a, b)
+    av, bv = bf16_bits_to_f32(a).astype(np.float64), bf16_bits_to_f32(b).astype(np.float64)
+    for i in range(3):
+        for n in range(5):
+            exact = sum(Fraction(float(av[i, k])) * Fraction(float(bv[n, k])) for k in range(40))
+            bound = 1e-15 * float(np.sum(np.abs(av[i] * bv[n])))
+            assert abs(got[i, n] - float(exact)) <= bound, (i, n)
+
+
+def pin_gemm_bf16_identity_and_integers(orc):
+    """B2: identity weight returns A exactly; integer-valued operands give exact integer sums."""
+    a = _rand_bf16_bits((6, 32), 1003)
+    eye = torch_bf16(np.eye(32, dtype=np.float32))
+    assert np.array_equal(orc.gemm_bf16(a, eye), bf16_bits_to_f32(a).astype(np.float64))
+    rng = np.random.default_rng(1004)
+    ai = rng.integers(-100, 100, size=(4, 96)).astype(np.float32)
+    bi = rng.integers(-100, 100, size=(9, 96)).astype(np.float32)
+    got = orc.gemm_bf16(torch_bf16(ai).reshape(4, 96), torch_bf16(bi).reshape(9, 96))
+    assert np.array_equal(got, ai.astype(np.int64) @ bi.astype(np.int64).T)
+
+
+def pin_bf16_branch_vs_torch(orc):
+    """B3: x @ dequant(W)^T through the oracle == torch float64 matmul of the same bf16 values
+    (ragged N and K, several rows), and the row subset computes the same rows."""
+    N, K, M = 200, 320, 7
+    w = _rand_codes((N, K), 1005)
+    S = _rand_scales((-(-N // BLOCK), -(-K // BLOCK)), 1006)
+    wd = orc.weight_dequant(w, S)                          # bf16 bits [N, K]
+    x = _rand_bf16_bits((M, K), 1007)
+    got = orc.gemm_bf16(x, wd)
+    ref = (torch.from_numpy(bf16_bits_to_f32(x).astype(np.float64)) @
+           torch.from_numpy(bf16_bits_to_f32(wd).astype(np.float64)).T).numpy()
+    tol = 1e-13 * (np.abs(bf16_bits_to_f32(x)).astype(np.float64) @ np.abs(bf16_bits_to_f32(wd)).astype(np.float64).T)
+    assert np.all(np.abs(got - ref) <= tol)
+    rows = np.array([6, 0, 3])
+    assert np.array_equal(orc.gemm_bf16(x, wd, rows=rows), got[rows])
+
+
 # ------------------------------------------------------ MoE dispatch / combine pins
 #
 # Source: "Behavior traces - deepseek-ai/DeepSeek-V3" (codevetter), MoE trace

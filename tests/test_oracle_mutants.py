@@ -16,6 +16,13 @@ import pins
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "bfp8_oracle.c")
 
 MUTANTS = {
+    # bf16 GEMM: weight row stride lost
+    "bf16_gemm_row_stride": ("const uint16_t* b = J->b + n * J->K;", "const uint16_t* b = J->b + n;"),
+    # bf16 GEMM: fp32 accumulation
+    "bf16_gemm_float_sum": ("double sum = 0.0;\n            for (int64_t k = 0; k < J->K; ++k) sum += arow[k]",
+                            "float sum = 0.0f;\n            for (int64_t k = 0; k < J->K; ++k) sum += arow[k]"),
+    # bf16 GEMM: last K element dropped
+    "bf16_gemm_short_k": ("for (int64_t k = 0; k < J->K; ++k) sum += arow[k]", "for (int64_t k = 0; k + 1 < J->K; ++k) sum += arow[k]"),
     # dispatch: slots ordered slot-major instead of token-major inside an expert
     "dispatch_slot_major": ("for (int64_t t = 0; t < T; ++t)\n            for (int32_t j = 0; j < k; ++j)\n                if (topk",
                             "for (int32_t j = 0; j < k; ++j)\n            for (int64_t t = 0; t < T; ++t)\n                if (topk"),
