@@ -40,8 +40,10 @@ from block_scaled_fp8_04_amd import synth  # noqa: E402
 BLOCK = 128
 PEAK_FP8_TFLOPS = 5000.0          # MI355X dense fp8 MFMA (no sparsity)
 PEAK_HBM_GBS = 8000.0             # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0         # MI355X dense bf16 MFMA (no sparsity)
 
-WORKLOADS = {"tiny": 0, "decode": 1, "moe-pair": 2, "dense-mlp": 3, "grouped": 4, "moe-layer": 4}
+WORKLOADS = {"tiny": 0, "decode": 1, "moe-pair": 2, "dense-mlp": 3, "grouped": 4, "moe-layer": 4,
+             "bf16-branch": 3}
 
 
 # ------------------------------------------------------------------ accounting
@@ -80,8 +82,8 @@ class Step:
         self.dev = dev
         t = wl.tensors
         c = wl.config
-        if kind == "moe-layer":
-            c = "moe-layer"
+        if kind in ("moe-layer", "bf16-branch"):
+            c = kind
         self.launches = []            # (name, callable, flops, bytes, bound)
         self.hashes = {}
         for k, v in t.items():
@@ -148,6 +150,27 @@ class Step:
             self.shape = dict(T=T, G=G, N=N, K=K, tokens_per_expert_min=min(counts),
                               tokens_per_expert_max=max(counts))
             self.dominant, self.dominant_kernel = ["fp8_gemm_grouped"], "gemm_grouped"
+        elif c == "bf16-branch":
+            M, N1, K1, N2, K2 = (wl.meta[k] for k in ("M", "N1", "K1", "N2", "K2"))
+            x = t["x"].to(dev)
+            w1, s1 = t["w1"].to(dev), t["s1"].to(dev)
+            w2, s2 = t["w2"].to(dev), t["s2"].to(dev)
+            w1d = torch.empty(N1, K1, dtype=torch.bfloat16, device=dev)
+            w2d = torch.empty(N2, K2, dtype=torch.bfloat16, device=dev)
+            h = torch.empty(M, N1, dtype=torch.bfloat16, device=dev)
+            y = torch.empty(M, N2, dtype=torch.bfloat16, device=dev)
+            self.launches += [
+                ("weight_dequant_1", lambda: bfp8.bfp8_weight_dequant(w1, s1, w1d), 0,
+                 dequant_bytes(N1, K1), "hbm"),
+                ("bf16_gemm_1", lambda: bfp8.bfp8_gemm_bf16(x, w1d, h), 2 * M * N1 * K1,
+                 2 * M * K1 + 2 * N1 * K1 + 2 * M * N1, "mfma_bf16"),
+                ("weight_dequant_2", lambda: bfp8.bfp8_weight_dequant(w2, s2, w2d), 0,
+                 dequant_bytes(N2, K2), "hbm"),
+                ("bf16_gemm_2", lambda: bfp8.bfp8_gemm_bf16(h, w2d, y), 2 * M * N2 * K2,
+                 2 * M * K2 + 2 * N2 * K2 + 2 * M * N2, "mfma_bf16"),
+            ]
+            self.shape = dict(M=M, N1=N1, K1=K1, N2=N2, K2=K2)
+            self.dominant, self.dominant_kernel = ["bf16_gemm_1", "bf16_gemm_2"], "gemm_bf16"
         elif c == "moe-layer":
             topk, wts, off = t["topk"], t["weights"], t["offsets"]
             Tt, k = topk.shape
@@ -222,6 +245,13 @@ def cpu_baseline(wl, target_s=12.0, kind=None):
             if c == 3:
                 wrows = max(1, int(round(t["w1"].shape[0] * rows / wl.meta["M"])))
                 oracle.weight_dequant(t["w1"].numpy()[:wrows], t["s1"].numpy()[:-(-wrows // BLOCK)])
+        elif kind == "bf16-branch":
+            w1d = oracle.weight_dequant(t["w1"].numpy(), t["s1"].numpy())
+            h = oracle.gemm_bf16(x_bits, w1d, rows=np.arange(rows), threads=threads)
+            hb = oracle.f32_to_bf16(h.astype(np.float32))
+            w2d = oracle.weight_dequant(t["w2"].numpy(), t["s2"].numpy())
+            oracle.gemm_bf16(hb, w2d, threads=threads)
+            done = 2.0 * rows * (wl.meta["N1"] * wl.meta["K1"] + wl.meta["N2"] * wl.meta["K2"])
         elif kind == "moe-layer":
             # rows = sampled tokens: dispatch of the whole batch, then every later stage
             # for the sampled tokens' local slots only
@@ -308,10 +338,15 @@ def main():
         src = torch.ones(n, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
         for _ in range(3):
             dst.copy_(src)
+        e1.record()
         torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
+        ms = e0.elapsed_time(e1) / 3
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 3, "copy_ms": ms,
+                          "copy_gbs": 2 * n / (ms * 1e-3) / 1e9}), flush=True)
         return
     bfp8.library()
 
@@ -343,7 +378,12 @@ def main():
         if flop:
             entry["tflops"] = flop / (ms * 1e-3) / 1e12
         entry["gbs"] = nbytes / (ms * 1e-3) / 1e9
-        entry["frac"] = (entry["tflops"] / PEAK_FP8_TFLOPS) if bound == "mfma" else (entry["gbs"] / PEAK_HBM_GBS)
+        if bound == "mfma":
+            entry["frac"] = entry["tflops"] / PEAK_FP8_TFLOPS
+        elif bound == "mfma_bf16":
+            entry["frac"] = entry["tflops"] / PEAK_BF16_TFLOPS
+        else:
+            entry["frac"] = entry["gbs"] / PEAK_HBM_GBS
         kernels[name] = entry
 
     gemm_flop = sum(l[2] for l in step.launches)
@@ -354,10 +394,11 @@ def main():
     avg_us = float(np.mean([kernels[n]["avg_us"] for n in dom]))
     d = kernels[dom[0]]
     traffic = read_traffic(step.dominant_kernel)
-    if d["bound"] == "mfma":
+    if d["bound"] in ("mfma", "mfma_bf16"):
+        peak = PEAK_FP8_TFLOPS if d["bound"] == "mfma" else PEAK_BF16_TFLOPS
         ach = d["flop"] / (avg_us * 1e-6) / 1e12
-        roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                "frac": ach / PEAK_FP8_TFLOPS, "traffic": traffic, "kernel": step.dominant_kernel,
+        roof = {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
+                "frac": ach / peak, "traffic": traffic, "kernel": step.dominant_kernel,
                 "launches": dom, "avg_us": avg_us}
     else:
         nbytes = float(np.mean([kernels[n]["bytes"] for n in dom]))
@@ -370,16 +411,18 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, args.cpu_seconds, args.workload)
 
-    wl_name = f"moe-layer-{wl.name}" if args.workload == "moe-layer" else wl.name
+    wl_name = f"{args.workload}-{wl.name}" if args.workload in ("moe-layer", "bf16-branch") else wl.name
     config = {"workload": wl_name, "shape": step.shape,
               "step": " -> ".join(l[0] for l in step.launches),
               "value_definition": "GEMM FLOP per step / wall time per step",
               "input_sha256_16": step.hashes, "seeds": "1000*config+tensor_id",
               "parallelism": "single-gpu"}
+    dtype = ("bf16 (fp32 accumulate, bf16 out; fp8_e4m3 weights dequantized)"
+             if args.workload == "bf16-branch" else "fp8_e4m3 (fp32 accumulate, bf16 out)")
     out = {"metric": "block-FP8 GEMM TFLOP/s & % of fp8 MFMA peak; act_quant/dequant HBM GB/s",
            "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
-           "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3 (fp32 accumulate, bf16 out)",
+           "scaling": "weak", "vs_baseline": None, "dtype": dtype,
            "data": "synthetic (seeded; DeepSeek-V3 projection shapes, random-init)",
            "config": config, "kernels": kernels, "roofline": roof, "cpu_baseline": cpu}
     print(json.dumps(out), flush=True)

@@ -29,7 +29,7 @@ BFP8_ERR_ARG = 7
 EXPORTS = ("bfp8_act_quant", "bfp8_weight_dequant", "bfp8_gemm", "bfp8_gemm_workspace_size",
            "bfp8_gemm_grouped", "bfp8_e4m3_encode_range", "bfp8_bf16_round_range",
            "bfp8_gemm_kernel_name", "bfp8_moe_dispatch_workspace_size", "bfp8_moe_dispatch",
-           "bfp8_act_quant_rows", "bfp8_moe_combine",
+           "bfp8_act_quant_rows", "bfp8_moe_combine", "bfp8_gemm_bf16",
            "bfp8_status_string", "bfp8_version")
 
 _lib = None
@@ -75,6 +75,8 @@ def library():
     lib.bfp8_act_quant_rows.restype = ctypes.c_int
     lib.bfp8_moe_combine.argtypes = [P, I64, P, P, P, I64, I32, I64, P]
     lib.bfp8_moe_combine.restype = ctypes.c_int
+    lib.bfp8_gemm_bf16.argtypes = [P, P, P, I64, I64, I64, P]
+    lib.bfp8_gemm_bf16.restype = ctypes.c_int
     lib.bfp8_status_string.argtypes = [ctypes.c_int]
     lib.bfp8_status_string.restype = ctypes.c_char_p
     lib.bfp8_version.argtypes = []
@@ -202,6 +204,18 @@ def bfp8_gemm_grouped(a, a_s, b, b_s, c, group_offsets, stream=None):
         _stream(stream, a.device)))
 
 
+def bfp8_gemm_bf16(a, b, c, stream=None):
+    """c bf16 [M,N] = a bf16 [M,K] x b bf16 [N,K]^T (the BF16 branch's matmul)."""
+    _cuda_contig(a, b, c)
+    _need(a.dtype == torch.bfloat16 and b.dtype == torch.bfloat16 and c.dtype == torch.bfloat16,
+          "a, b and c must be bf16")
+    M, K = a.shape
+    N = b.shape[0]
+    _need(b.shape[1] == K and c.shape == (M, N), "shapes must be a [M,K], b [N,K], c [M,N]")
+    _check("bfp8_gemm_bf16", library().bfp8_gemm_bf16(_ptr(a), _ptr(b), _ptr(c), M, N, K,
+                                                      _stream(stream, a.device)))
+
+
 def bfp8_e4m3_encode_range(first, count, out, variant=0, stream=None):
     """Device encode of the fp32 bit patterns first .. first+count-1 into out (uint8)."""
     _cuda_contig(out)
@@ -299,6 +313,17 @@ def gemm_grouped(a, a_s, b, b_s, group_offsets, stream=None):
     c = torch.empty((a.shape[0], b.shape[1]), dtype=torch.bfloat16, device=a.device)
     bfp8_gemm_grouped(a, a_s, b, b_s, c, group_offsets, stream)
     return c
+
+
+def gemm_bf16(a, b, stream=None):
+    c = torch.empty((a.shape[0], b.shape[0]), dtype=torch.bfloat16, device=a.device)
+    bfp8_gemm_bf16(a, b, c, stream)
+    return c
+
+
+def linear_bf16(x, w, w_s, stream=None):
+    """The BF16 branch of linear(): weight_dequant(w, w.scale) then the bf16 matmul."""
+    return gemm_bf16(x, weight_dequant(w, w_s, stream), stream)
 
 
 def linear_fp8(x, w, w_s, workspace=None, stream=None):

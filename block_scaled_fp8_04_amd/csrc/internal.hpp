@@ -38,6 +38,10 @@ hipError_t launch_gemm_grouped(const void* a, const float* as, const void* b, co
                                void* c, const int32_t* off, int32_t G, int64_t total_M,
                                int64_t N, int64_t K, hipStream_t stream);
 
+hipError_t launch_gemm_bf16(const void* a, const void* b, void* c, int64_t M, int64_t N, int64_t K,
+                            hipStream_t stream);
+const char* gemm_bf16_config_name(int64_t M, int64_t N, int64_t K);
+
 size_t moe_dispatch_workspace_bytes(int64_t T, int32_t k, int32_t G);
 hipError_t launch_moe_dispatch(const int32_t* topk, int64_t T, int32_t k, int32_t lo, int32_t G,
                                int32_t* off, int32_t* row_token, int32_t* slot_row, void* ws,

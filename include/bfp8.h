@@ -44,7 +44,7 @@ extern "C" {
 #endif
 
 #define BFP8_BLOCK 128
-#define BFP8_VERSION 2
+#define BFP8_VERSION 3
 #define BFP8_MOE_MAX_GROUPS 1024
 
 typedef enum bfp8_status {
@@ -130,6 +130,18 @@ size_t bfp8_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
 int bfp8_gemm_grouped(const void* a, const float* a_s, const void* b, const float* b_s,
                       void* c_bf16, const int32_t* group_offsets, int32_t G,
                       int64_t total_M, int64_t N, int64_t K, void* stream);
+
+/* The BF16 branch of linear() ([PY] "FP8 with per-block scales": the weight
+ * is expanded to bf16 by weight_dequant and multiplied by an ordinary BF16
+ * matmul).  C = A * B^T with B a Linear weight (out_features x in_features):
+ *     c[m, n] = bf16_rne( sum_k a[m, k] * b[n, k] )      (fp32 accumulation)
+ *   a_bf16 : bf16 [M, K], 16-byte aligned
+ *   b_bf16 : bf16 [N, K], 16-byte aligned (e.g. bfp8_weight_dequant's output)
+ *   c_bf16 : bf16 [M, N] output, 2-byte aligned
+ * Errors: BFP8_ERR_SHAPE if M < 0, N < 0, K <= 0, K % 64 != 0 or K >= 2^22;
+ * BFP8_ERR_NULL; BFP8_ERR_ALIGN. */
+int bfp8_gemm_bf16(const void* a_bf16, const void* b_bf16, void* c_bf16, int64_t M, int64_t N,
+                   int64_t K, void* stream);
 
 /* ----------------------------------------------------------------------
  * MoE dispatch and combine around the grouped GEMM ([BT] "MoE trace": per

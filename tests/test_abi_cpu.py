@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert bfp8.bfp8_version() == 2
+    assert bfp8.bfp8_version() == 3
     for code in range(8):
         assert bfp8.bfp8_status_string(code)
     assert bfp8.bfp8_status_string(0) == "ok"
@@ -127,6 +127,23 @@ def test_gemm_grouped_validation(lib):
     assert call(off=ctypes.c_void_p(0x10002)) == _lib.BFP8_ERR_ALIGN
     assert call(a=ODD) == _lib.BFP8_ERR_ALIGN
     assert call(a=None, T=0) == _lib.BFP8_OK
+
+
+def test_gemm_bf16_validation(lib):
+    f = lib.bfp8_gemm_bf16
+
+    def call(a=FAKE, b=FAKE, c=FAKE, M=64, N=64, K=128):
+        return f(a, b, c, M, N, K, None)
+
+    assert call(K=100) == _lib.BFP8_ERR_SHAPE
+    assert call(K=0) == _lib.BFP8_ERR_SHAPE
+    assert call(K=1 << 22) == _lib.BFP8_ERR_SHAPE
+    assert call(M=-1) == _lib.BFP8_ERR_SHAPE
+    for name in ("a", "b", "c"):
+        assert call(**{name: None}) == _lib.BFP8_ERR_NULL, name
+    assert call(a=ctypes.c_void_p(0x10008)) == _lib.BFP8_ERR_ALIGN
+    assert call(c=ODD) == _lib.BFP8_ERR_ALIGN
+    assert call(a=None, M=0) == _lib.BFP8_OK
 
 
 def test_moe_dispatch_validation(lib):
