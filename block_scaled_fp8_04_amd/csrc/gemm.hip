@@ -15,18 +15,22 @@
 //    per element: acc += P * (a_s[row] * b_s).  The weight-scale block is the
 //    same for all of a wave's columns (a wave's N range lies inside one
 //    128-column block), so the fold needs one scale per row.
-//  * A workgroup is 4 waves in a 2 x 2 layout over a BM x BN tile.  A and B
-//    tiles of one K block (BM x 128 and BN x 128 bytes) are staged through LDS,
-//    double buffered: while the waves multiply stage s, the next K block's
-//    global loads are in flight in registers and are written to stage s^1.
-//    One barrier per K block.
+//  * Large tiles (BigTile): 256x256 (8 waves of 128x64, 2 LDS stages),
+//    256x128 (8 waves of 64x64, 3 stages) and 128x128 (4 waves of 64x64,
+//    3 stages).  A and B rows of one K block go straight from global memory
+//    into LDS with buffer loads; the stages are distinct LDS arrays and the K
+//    loop is unrolled by the stage count, so every stage is named at compile
+//    time.  A vmcnt-counted wait and one barrier open each K block.
 //  * LDS rows are 128 bytes; the eight 16-byte chunks of row r are stored at
 //    chunk position (chunk ^ swz(r)) (see swz below), so the 16 rows read
 //    together by a fragment load (same logical chunk) hit no bank twice.
 //  * MFMA operand layout: lane l supplies row (l & 15) of the sub-tile and the
 //    32 K-bytes starting at 32 * (l >> 4), for A and B alike, so each K index
-//    pairs the same position of A and B.  The accumulator layout of a 16x16
-//    fp32 result is: lane l holds column (l & 15), rows 4*(l >> 4) + 0..3.
+//    pairs the same position of A and B.  Operands go weight-first, so the
+//    16x16 result is C^T: lane l holds output row (l & 15) and the four
+//    consecutive columns 4 (l >> 4) + 0..3.
+//  * Skinny problems (M <= 64) with a workspace use split-K (gemm_skinny_kernel
+//    and a fixed-order reduction).
 //  * Rows past M (or past a group's end) and columns past N read a clamped,
 //    valid row and are never stored.
 #include "device_codec.hpp"
@@ -36,21 +40,6 @@ namespace bfp8 {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
-
-template <int BM_, int BN_>
-struct Tile {
-    static constexpr int BM = BM_, BN = BN_;
-    static constexpr int WM = BM / 2, WN = BN / 2;      // per-wave extent (2 x 2 waves)
-    static constexpr int TM = WM / 16, TN = WN / 16;    // 16 x 16 sub-tiles per wave
-    static constexpr int A_BYTES = BM * kBlock;
-    static constexpr int B_BYTES = BN * kBlock;
-    static constexpr int A_LOADS = A_BYTES / (256 * 16);
-    static constexpr int B_LOADS = B_BYTES / (256 * 16);
-    static constexpr int STAGE = A_BYTES + B_BYTES + BM * 4;
-    static_assert(A_LOADS >= 1 && B_LOADS >= 1, "tile too small for 256 threads");
-    static_assert(TM >= 1 && TN >= 1, "wave tile must hold a 16x16 sub-tile");
-    static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns must share one scale block");
-};
 
 // LDS chunk swizzle of a 128-byte row: logical 16-byte chunk c of row r is
 // stored at chunk position c ^ swz(r).  Measured on MI355X with the fragment
@@ -64,168 +53,6 @@ __device__ __forceinline__ v8i frag_from(const uint4 x0, const uint4 x1) {
     f[0] = (int)x0.x; f[1] = (int)x0.y; f[2] = (int)x0.z; f[3] = (int)x0.w;
     f[4] = (int)x1.x; f[5] = (int)x1.y; f[6] = (int)x1.z; f[7] = (int)x1.w;
     return f;
-}
-
-// Computes rows [m0, min(m0 + BM, m_end)) x columns [n0, min(n0 + BN, N)),
-// summing K blocks [kb_begin, kb_end).  With partial == nullptr the result is
-// rounded to bf16 into c; otherwise the fp32 partial sum goes to
-// partial[row * N + col] (split-K).
-template <class T>
-__device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ a,
-                                          const float* __restrict__ as,
-                                          const uint8_t* __restrict__ b,
-                                          const float* __restrict__ bs,
-                                          uint16_t* __restrict__ c, int64_t m0, int64_t m_end,
-                                          int64_t n0, int64_t N, int64_t K, uint8_t* lds,
-                                          int64_t kb_begin, int64_t kb_end,
-                                          float* __restrict__ partial) {
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm0 = (wave >> 1) * T::WM;
-    const int wn0 = (wave & 1) * T::WN;
-    const int64_t KB = K / kBlock;
-    const int64_t NB = (N + kBlock - 1) / kBlock;
-
-    // global sources and LDS destinations of this thread's 16-byte chunks
-    const uint8_t* a_src[T::A_LOADS];
-    const uint8_t* b_src[T::B_LOADS];
-    int a_dst[T::A_LOADS], b_dst[T::B_LOADS];
-#pragma unroll
-    for (int i = 0; i < T::A_LOADS; ++i) {
-        const int ch = tid + 256 * i, row = ch >> 3, col = ch & 7;
-        int64_t grow = m0 + row;
-        grow = grow < m_end ? grow : m_end - 1;
-        a_src[i] = a + grow * K + col * 16;
-        a_dst[i] = row * kBlock + ((col ^ swz(row)) << 4);
-    }
-#pragma unroll
-    for (int i = 0; i < T::B_LOADS; ++i) {
-        const int ch = tid + 256 * i, row = ch >> 3, col = ch & 7;
-        int64_t gcol = n0 + row;
-        gcol = gcol < N ? gcol : N - 1;
-        b_src[i] = b + gcol * K + col * 16;
-        b_dst[i] = T::A_BYTES + row * kBlock + ((col ^ swz(row)) << 4);
-    }
-    const float* sa_src = nullptr;
-    if (tid < T::BM) {
-        int64_t grow = m0 + tid;
-        grow = grow < m_end ? grow : m_end - 1;
-        sa_src = as + grow * KB;
-    }
-    int64_t nblk = (n0 + wn0) >> 7;
-    nblk = nblk < NB ? nblk : NB - 1;
-    const float* sb_src = bs + nblk * KB;
-
-    v4f acc[T::TM][T::TN];
-#pragma unroll
-    for (int i = 0; i < T::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < T::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    uint4 ra[T::A_LOADS], rb[T::B_LOADS];
-    float rsa = 0.f;
-
-    auto load_regs = [&](int64_t kb) {
-#pragma unroll
-        for (int i = 0; i < T::A_LOADS; ++i) ra[i] = *(const uint4*)(a_src[i] + kb * kBlock);
-#pragma unroll
-        for (int i = 0; i < T::B_LOADS; ++i) rb[i] = *(const uint4*)(b_src[i] + kb * kBlock);
-        if (tid < T::BM) rsa = sa_src[kb];
-    };
-    auto store_lds = [&](int stage) {
-        uint8_t* base = lds + stage * T::STAGE;
-#pragma unroll
-        for (int i = 0; i < T::A_LOADS; ++i) *(uint4*)(base + a_dst[i]) = ra[i];
-#pragma unroll
-        for (int i = 0; i < T::B_LOADS; ++i) *(uint4*)(base + b_dst[i]) = rb[i];
-        if (tid < T::BM) ((float*)(base + T::A_BYTES + T::B_BYTES))[tid] = rsa;
-    };
-
-    load_regs(kb_begin);
-    store_lds(0);
-    __syncthreads();
-
-    const int lr = lane & 15;
-    const int lk = (lane >> 4) * 2;               // first of this lane's two 16-byte chunks
-    const int off0 = ((lk ^ swz(lr)) << 4);
-    const int off1 = (((lk + 1) ^ swz(lr)) << 4);
-    const int srow = 4 * (lane >> 4);
-
-    for (int64_t kb = kb_begin; kb < kb_end; ++kb) {
-        const int cur = (int)((kb - kb_begin) & 1);
-        const bool more = kb + 1 < kb_end;
-        if (more) load_regs(kb + 1);
-
-        const uint8_t* As = lds + cur * T::STAGE;
-        const uint8_t* Bs = As + T::A_BYTES;
-        const float* Ss = (const float*)(Bs + T::B_BYTES);
-        v8i fa[T::TM], fb[T::TN];
-#pragma unroll
-        for (int i = 0; i < T::TM; ++i) {
-            const uint8_t* r = As + (wm0 + 16 * i + lr) * kBlock;
-            fa[i] = frag_from(*(const uint4*)(r + off0), *(const uint4*)(r + off1));
-        }
-#pragma unroll
-        for (int j = 0; j < T::TN; ++j) {
-            const uint8_t* r = Bs + (wn0 + 16 * j + lr) * kBlock;
-            fb[j] = frag_from(*(const uint4*)(r + off0), *(const uint4*)(r + off1));
-        }
-        const float sbv = sb_src[kb];
-#pragma unroll
-        for (int i = 0; i < T::TM; ++i) {
-            const v4f sa4 = *(const v4f*)(Ss + wm0 + 16 * i + srow);
-            const v4f sc = sa4 * sbv;
-#pragma unroll
-            for (int j = 0; j < T::TN; ++j) {
-                const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    fa[i], fb[j], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-                acc[i][j] = p * sc + acc[i][j];
-            }
-        }
-        if (more) store_lds(cur ^ 1);
-        __syncthreads();
-    }
-
-    // epilogue: fp32 -> bf16 (nearest even) or the fp32 partial, masked to
-    // the valid rows / columns
-#pragma unroll
-    for (int i = 0; i < T::TM; ++i) {
-#pragma unroll
-        for (int j = 0; j < T::TN; ++j) {
-            const int64_t col = n0 + wn0 + 16 * j + lr;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t row = m0 + wm0 + 16 * i + srow + r;
-                if (row < m_end && col < N) {
-                    if (partial) partial[row * N + col] = acc[i][j][r];
-                    else c[row * N + col] = (uint16_t)bf16_rne_bits(acc[i][j][r]);
-                }
-            }
-        }
-    }
-}
-
-template <class T>
-__global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t* __restrict__ a,
-                                                      const float* __restrict__ as,
-                                                      const uint8_t* __restrict__ b,
-                                                      const float* __restrict__ bs,
-                                                      uint16_t* __restrict__ c, int64_t M,
-                                                      int64_t N, int64_t K, int mt, int nt) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * T::STAGE];
-    // bands of 8 M-tiles: within a band, consecutive workgroups walk down the
-    // band's M-tiles for one N-tile, then move to the next N-tile.
-    constexpr int GM = 8;
-    const int id = blockIdx.x;
-    const int band = id / (GM * nt);
-    const int first_m = band * GM;
-    const int rows_in_band = (mt - first_m) < GM ? (mt - first_m) : GM;
-    const int in_band = id - band * GM * nt;
-    const int tm = first_m + in_band % rows_in_band;
-    const int tn = in_band / rows_in_band;
-    gemm_tile<T>(a, as, b, bs, c, (int64_t)tm * T::BM, M, (int64_t)tn * T::BN, N, K, lds, 0,
-                 K / kBlock, nullptr);
 }
 
 // Adds the split-K partial sums ws[0..splits)[M][N] in index order (a fixed
@@ -627,6 +454,8 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
                         acc[i][j] = p * sc[i] + acc[i][j];
                     }
                 }
+                // one row at a time: hoisting every row's A reads spills registers
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     };
@@ -919,8 +748,6 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint8_t* __restr
     }
 }
 
-using TileLarge = Tile<128, 128>;
-using TileSmall = Tile<64, 64>;
 
 // Split-K plan for skinny problems (M <= 64): enough (tile, split) pairs for
 // about 512 workgroups, at least 2 K blocks per split.  Host-only arithmetic,
@@ -953,6 +780,7 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 using BigSquare = BigTile<256, 256, 2, 4, 2>;   // 8 waves of 128 x 64, 2 stages
 
 using BigWide = BigTile<256, 128, 4, 2, 3>;     // 8 waves of 64 x 64, 3 stages
+using BigMid = BigTile<128, 128, 2, 2, 3>;      // 4 waves of 64 x 64, 3 stages
 
 template <class T>
 static void launch_big(const void* a, const float* as, const void* b, const float* bs, void* c,
@@ -969,16 +797,14 @@ GemmConfig gemm_config(int64_t M, int64_t N, int64_t /*K*/) {
     const int64_t tiles_wide = ((M + 255) / 256) * ((N + 127) / 128);
     if (M > 128 && tiles_sq >= 2 * cus) return GemmConfig::kBig256x256;
     if (M > 128 && tiles_wide >= cus / 2) return GemmConfig::kBig256x128;
-    if (M <= 64) return GemmConfig::kReg64x64;
-    return GemmConfig::kReg128x128;
+    return GemmConfig::kBig128x128;
 }
 
 const char* gemm_config_name(GemmConfig cfg) {
     switch (cfg) {
         case GemmConfig::kBig256x256: return "lds-direct 256x256, 8 waves of 128x64";
         case GemmConfig::kBig256x128: return "lds-direct 256x128, 8 waves of 64x64";
-        case GemmConfig::kReg64x64: return "register-staged 64x64, 4 waves of 32x32";
-        case GemmConfig::kReg128x128: return "register-staged 128x128, 4 waves of 64x64";
+        case GemmConfig::kBig128x128: return "lds-direct 128x128, 4 waves of 64x64";
     }
     return "unknown";
 }
@@ -1012,22 +838,9 @@ hipError_t launch_gemm(const void* a, const float* as, const void* b, const floa
         case GemmConfig::kBig256x128:
             launch_big<BigWide>(a, as, b, bs, c, M, N, K, stream);
             break;
-        case GemmConfig::kReg64x64: {
-            using T = TileSmall;
-            const int mt = (int)((M + T::BM - 1) / T::BM), nt = (int)((N + T::BN - 1) / T::BN);
-            hipLaunchKernelGGL(gemm_kernel<T>, dim3(mt * nt), dim3(256), 0, stream,
-                               (const uint8_t*)a, as, (const uint8_t*)b, bs, (uint16_t*)c, M, N, K,
-                               mt, nt);
+        case GemmConfig::kBig128x128:
+            launch_big<BigMid>(a, as, b, bs, c, M, N, K, stream);
             break;
-        }
-        case GemmConfig::kReg128x128: {
-            using T = TileLarge;
-            const int mt = (int)((M + T::BM - 1) / T::BM), nt = (int)((N + T::BN - 1) / T::BN);
-            hipLaunchKernelGGL(gemm_kernel<T>, dim3(mt * nt), dim3(256), 0, stream,
-                               (const uint8_t*)a, as, (const uint8_t*)b, bs, (uint16_t*)c, M, N, K,
-                               mt, nt);
-            break;
-        }
     }
     return hipGetLastError();
 }

@@ -28,7 +28,7 @@ hipError_t launch_weight_dequant(const void* w, const float* s, void* out, int64
                                  hipStream_t stream);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
-enum class GemmConfig { kBig256x256, kBig256x128, kReg64x64, kReg128x128 };
+enum class GemmConfig { kBig256x256, kBig256x128, kBig128x128 };
 GemmConfig gemm_config(int64_t M, int64_t N, int64_t K);
 const char* gemm_config_name(GemmConfig cfg);
 hipError_t launch_gemm(const void* a, const float* as, const void* b, const float* bs, void* c,
