@@ -5,7 +5,11 @@ input already resident in HBM.  For the default workload (the dense MLP
 layer-0 shape of DeepSeek-V3: x [8192, 7168], W_up [18432, 7168],
 W_down [7168, 18432]) a step is
 
-    act_quant(x) -> fp8 GEMM up -> act_quant(H) -> fp8 GEMM down -> weight_dequant(W_up)
+    act_quant(x) -> fp8 GEMM up with act_quant(H) in its epilogue -> fp8 GEMM down
+    -> weight_dequant(W_up)
+
+(--workload dense-mlp-unfused runs act_quant(H) as its own kernel after a bf16 H;
+the codes and scales are the same bits either way).
 
 Printed: one JSON line.  `value` is the step's GEMM FLOP divided by the step's
 wall time (TFLOP/s); `kernels` gives each kernel's average duration from HIP
@@ -15,7 +19,7 @@ bounds it; `roofline` repeats that for the dominant kernel; `cpu_baseline`
 times the CPU oracle on a bounded, proportional sample of the same step.
 
 Other workloads (parity-test shapes, measured on demand): --workload tiny |
-decode | moe-pair | dense-mlp | grouped | moe-layer.  moe-layer is the routed
+decode | moe-pair | dense-mlp-unfused | grouped | moe-layer | bf16-branch.  moe-layer is the routed
 experts of one GPU end to end on the device: moe_dispatch(topk) ->
 act_quant_rows(x, row_token) -> grouped GEMM (row buffers sized for T*k rows)
 -> moe_combine (weighted sum back to token order).
@@ -43,7 +47,7 @@ PEAK_HBM_GBS = 8000.0             # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0         # MI355X dense bf16 MFMA (no sparsity)
 
 WORKLOADS = {"tiny": 0, "decode": 1, "moe-pair": 2, "dense-mlp": 3, "grouped": 4, "moe-layer": 4,
-             "bf16-branch": 3}
+             "bf16-branch": 3, "dense-mlp-unfused": 3}
 
 
 # ------------------------------------------------------------------ accounting
@@ -82,7 +86,7 @@ class Step:
         self.dev = dev
         t = wl.tensors
         c = wl.config
-        if kind in ("moe-layer", "bf16-branch"):
+        if kind in ("moe-layer", "bf16-branch", "dense-mlp"):
             c = kind
         self.launches = []            # (name, callable, flops, bytes, bound)
         self.hashes = {}
@@ -150,6 +154,30 @@ class Step:
             self.shape = dict(T=T, G=G, N=N, K=K, tokens_per_expert_min=min(counts),
                               tokens_per_expert_max=max(counts))
             self.dominant, self.dominant_kernel = ["fp8_gemm_grouped"], "gemm_grouped"
+        elif c == "dense-mlp":
+            # the dense chain with act_quant of H fused into the up projection's epilogue
+            # (bit-identical codes and scales to act_quant of the stored bf16 H)
+            M, N1, K1, N2, K2 = (wl.meta[k] for k in ("M", "N1", "K1", "N2", "K2"))
+            x = t["x"].to(dev)
+            w1, s1 = t["w1"].to(dev), t["s1"].to(dev)
+            w2, s2 = t["w2"].to(dev), t["s2"].to(dev)
+            q = torch.empty(M, K1, dtype=torch.uint8, device=dev)
+            qs = torch.empty(M, K1 // BLOCK, dtype=torch.float32, device=dev)
+            qh = torch.empty(M, K2, dtype=torch.uint8, device=dev)
+            qhs = torch.empty(M, K2 // BLOCK, dtype=torch.float32, device=dev)
+            y = torch.empty(M, N2, dtype=torch.bfloat16, device=dev)
+            wd = torch.empty(N1, K1, dtype=torch.bfloat16, device=dev)
+            self.launches += [
+                ("act_quant_x", lambda: bfp8.bfp8_act_quant(x, q, qs), 0, act_quant_bytes(M, K1), "hbm"),
+                ("fp8_gemm_1_quant", lambda: bfp8.bfp8_gemm_act_quant(q, qs, w1, s1, qh, qhs),
+                 2 * M * N1 * K1, M * K1 + N1 * K1 + M * N1 + 4 * M * (N1 // BLOCK), "mfma"),
+                ("fp8_gemm_2", lambda: bfp8.bfp8_gemm(qh, qhs, w2, s2, y), 2 * M * N2 * K2,
+                 gemm_bytes(M, N2, K2), "mfma"),
+                ("weight_dequant", lambda: bfp8.bfp8_weight_dequant(w1, s1, wd), 0,
+                 dequant_bytes(N1, K1), "hbm"),
+            ]
+            self.shape = dict(M=M, N1=N1, K1=K1, N2=N2, K2=K2)
+            self.dominant, self.dominant_kernel = ["fp8_gemm_1_quant", "fp8_gemm_2"], "gemm"
         elif c == "bf16-branch":
             M, N1, K1, N2, K2 = (wl.meta[k] for k in ("M", "N1", "K1", "N2", "K2"))
             x = t["x"].to(dev)
@@ -231,7 +259,15 @@ def cpu_baseline(wl, target_s=12.0, kind=None):
     def run(rows):
         done = 0.0
         t0 = time.perf_counter()
-        if c in (0, 1):
+        if kind == "bf16-branch":
+            # the weights are dequantized whole (a fixed cost), the GEMMs on the sampled rows
+            w1d = oracle.weight_dequant(t["w1"].numpy(), t["s1"].numpy())
+            h = oracle.gemm_bf16(x_bits, w1d, rows=np.arange(rows), threads=threads)
+            hb = oracle.f32_to_bf16(h.astype(np.float32))
+            w2d = oracle.weight_dequant(t["w2"].numpy(), t["s2"].numpy())
+            oracle.gemm_bf16(hb, w2d, threads=threads)
+            done = 2.0 * rows * (wl.meta["N1"] * wl.meta["K1"] + wl.meta["N2"] * wl.meta["K2"])
+        elif c in (0, 1):
             q, s = oracle.act_quant(x_bits[:rows])
             oracle.gemm(q, s, t["w1"].numpy(), t["s1"].numpy(), threads=threads)
             done = 2.0 * rows * wl.meta["N"] * wl.meta["K"]
@@ -245,13 +281,6 @@ def cpu_baseline(wl, target_s=12.0, kind=None):
             if c == 3:
                 wrows = max(1, int(round(t["w1"].shape[0] * rows / wl.meta["M"])))
                 oracle.weight_dequant(t["w1"].numpy()[:wrows], t["s1"].numpy()[:-(-wrows // BLOCK)])
-        elif kind == "bf16-branch":
-            w1d = oracle.weight_dequant(t["w1"].numpy(), t["s1"].numpy())
-            h = oracle.gemm_bf16(x_bits, w1d, rows=np.arange(rows), threads=threads)
-            hb = oracle.f32_to_bf16(h.astype(np.float32))
-            w2d = oracle.weight_dequant(t["w2"].numpy(), t["s2"].numpy())
-            oracle.gemm_bf16(hb, w2d, threads=threads)
-            done = 2.0 * rows * (wl.meta["N1"] * wl.meta["K1"] + wl.meta["N2"] * wl.meta["K2"])
         elif kind == "moe-layer":
             # rows = sampled tokens: dispatch of the whole batch, then every later stage
             # for the sampled tokens' local slots only
@@ -411,7 +440,8 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, args.cpu_seconds, args.workload)
 
-    wl_name = f"{args.workload}-{wl.name}" if args.workload in ("moe-layer", "bf16-branch") else wl.name
+    wl_name = (f"{args.workload}-{wl.name}" if args.workload in ("moe-layer", "bf16-branch", "dense-mlp-unfused")
+               else wl.name)
     config = {"workload": wl_name, "shape": step.shape,
               "step": " -> ".join(l[0] for l in step.launches),
               "value_definition": "GEMM FLOP per step / wall time per step",

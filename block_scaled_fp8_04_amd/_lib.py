@@ -30,6 +30,7 @@ EXPORTS = ("bfp8_act_quant", "bfp8_weight_dequant", "bfp8_gemm", "bfp8_gemm_work
            "bfp8_gemm_grouped", "bfp8_e4m3_encode_range", "bfp8_bf16_round_range",
            "bfp8_gemm_kernel_name", "bfp8_moe_dispatch_workspace_size", "bfp8_moe_dispatch",
            "bfp8_act_quant_rows", "bfp8_moe_combine", "bfp8_gemm_bf16",
+           "bfp8_gemm_act_quant",
            "bfp8_status_string", "bfp8_version")
 
 _lib = None
@@ -75,6 +76,8 @@ def library():
     lib.bfp8_act_quant_rows.restype = ctypes.c_int
     lib.bfp8_moe_combine.argtypes = [P, I64, P, P, P, I64, I32, I64, P]
     lib.bfp8_moe_combine.restype = ctypes.c_int
+    lib.bfp8_gemm_act_quant.argtypes = [P, P, P, P, P, P, I64, I64, I64, P]
+    lib.bfp8_gemm_act_quant.restype = ctypes.c_int
     lib.bfp8_gemm_bf16.argtypes = [P, P, P, I64, I64, I64, P]
     lib.bfp8_gemm_bf16.restype = ctypes.c_int
     lib.bfp8_status_string.argtypes = [ctypes.c_int]
@@ -185,6 +188,23 @@ def bfp8_gemm(a, a_s, b, b_s, c, workspace=None, stream=None):
     _check("bfp8_gemm", library().bfp8_gemm(_ptr(a), _ptr(a_s), _ptr(b), _ptr(b_s), _ptr(c),
                                             M, N, K, _ptr(workspace), ws_bytes,
                                             _stream(stream, a.device)))
+
+
+def bfp8_gemm_act_quant(a, a_s, b, b_s, q, q_scales, stream=None):
+    """q e4m3 [M,N], q_scales [M,N/128] = act_quant(bf16(a x b^T)) in one kernel (N % 128 == 0)."""
+    a, b, q = _bytes_view(a), _bytes_view(b), _bytes_view(q)
+    _cuda_contig(a, a_s, b, b_s, q, q_scales)
+    M, K = a.shape
+    N = b.shape[0]
+    _need(b.shape[1] == K, "a and b must share K")
+    _need(a_s.dtype == torch.float32 and b_s.dtype == torch.float32 and q_scales.dtype == torch.float32,
+          "scales must be fp32")
+    _need(a_s.shape == (M, K // BLOCK) and b_s.shape == (-(-N // BLOCK), K // BLOCK),
+          "a_s [M, K/128], b_s [ceil(N/128), K/128]")
+    _need(q.shape == (M, N) and q_scales.shape == (M, N // BLOCK), "q [M, N], q_scales [M, N/128]")
+    _check("bfp8_gemm_act_quant", library().bfp8_gemm_act_quant(
+        _ptr(a), _ptr(a_s), _ptr(b), _ptr(b_s), _ptr(q), _ptr(q_scales), M, N, K,
+        _stream(stream, a.device)))
 
 
 def bfp8_gemm_grouped(a, a_s, b, b_s, c, group_offsets, stream=None):
@@ -324,6 +344,14 @@ def gemm_bf16(a, b, stream=None):
 def linear_bf16(x, w, w_s, stream=None):
     """The BF16 branch of linear(): weight_dequant(w, w.scale) then the bf16 matmul."""
     return gemm_bf16(x, weight_dequant(w, w_s, stream), stream)
+
+
+def gemm_act_quant(a, a_s, b, b_s, stream=None):
+    M, N = a.shape[0], b.shape[0]
+    q = torch.empty((M, N), dtype=torch.uint8, device=a.device)
+    qs = torch.empty((M, N // BLOCK), dtype=torch.float32, device=a.device)
+    bfp8_gemm_act_quant(a, a_s, b, b_s, q, qs, stream)
+    return q, qs
 
 
 def linear_fp8(x, w, w_s, workspace=None, stream=None):

@@ -115,4 +115,25 @@ __device__ __forceinline__ void store_nt(uint4* p, const uint4 v) {
     __builtin_nontemporal_store(w, (u32x4*)p);
 }
 
+// Correctly rounded fp32 quotient x / s from the correctly rounded reciprocal
+// r = fl(1 / s): y0 = fl(x r) is within one ulp of x / s, the remainder
+// x - y0 s is exact as one fused multiply-add, and one more fused step
+// y0 + (x - y0 s) r rounds to fl(x / s) (Markstein's correction step).  The
+// GPU tests check the kernel against the oracle's fp32 division on every pair
+// of bf16 block maximum and bf16 element.
+// The correction step turns a quotient of -0 into +0 (-0 + +0 rounds to +0),
+// so the sign of x is put back; for x != 0 it is already the quotient's sign
+// because s > 0.
+__device__ __forceinline__ float quotient(float x, float s, float r) {
+    const float y0 = x * r;
+    const float e = __builtin_fmaf(-y0, s, x);
+    return __builtin_copysignf(__builtin_fmaf(e, r, y0), x);
+}
+
+// An fp32 value rounded to bf16 (nearest even, the conversion every bf16
+// output uses) and widened back.
+__device__ __forceinline__ float bf16_round_f32(float x) {
+    return __uint_as_float((pack_bf16x2(x, x) & 0xFFFFu) << 16);
+}
+
 }  // namespace bfp8

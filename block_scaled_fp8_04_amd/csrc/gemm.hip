@@ -195,14 +195,84 @@ __device__ __forceinline__ void load_lds4(const void* src, void* lds_dst) {
 // MFMAs and folds of its 16-row sub-tile rows that lie entirely past m_end
 // (a wave-uniform test); full tiles run the unguarded, explicitly scheduled
 // loop.
-template <class T, bool kGuard>
+// Where the tile's result goes: bf16 into c, or (kQuant) act_quant of the
+// bf16-rounded result into e4m3 codes q [M, N] and scales qs [M, N/128].
+struct QuantOut {
+    uint8_t* q;
+    float* qs;
+};
+
+// act_quant fused into the GEMM epilogue ("Data flow", FP8 quantization
+// bullet: the next linear() quantizes this output in 128-element blocks).
+// Each result is first rounded to bf16 (the unfused path's stored output),
+// so the codes and scales equal act_quant of the bf16 result bit for bit:
+// the same block max, scale = max(amax, floor) / 448, correctly rounded
+// quotient and e4m3 conversion.  A 128-column block of a row spans the 64
+// columns of two neighbouring waves (wave and wave ^ 1): each wave reduces its
+// part over its lanes, the two halves meet in LDS, and each wave writes its
+// own 64 codes per row (4 bytes per lane and sub-tile); the even wave writes
+// the row's scale.  Requires N % 128 == 0, so blocks past N are whole and
+// skipped.
+template <class T>
+__device__ __forceinline__ void quant_epilogue(v4f (&acc)[T::TM][T::TN], const QuantOut& qo,
+                                               int64_t m0, int64_t m_end, int64_t n0, int64_t N,
+                                               int wave, int wm0, int wn0, int lane,
+                                               uint8_t* lds_scratch) {
+    static_assert(T::WN == 64, "a 128-column block spans two waves of 64 columns");
+    const int lr = lane & 15, g = lane >> 4;
+    float pm[T::TM];
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i) {
+        float m = 0.f;
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                acc[i][j][r] = bf16_round_f32(acc[i][j][r]);
+                m = fmaxf(m, fabsf(acc[i][j][r]));
+            }
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        pm[i] = m;
+    }
+    // the stages are free once every wave has left the K loop
+    float* part = (float*)lds_scratch;            // [WAVES][WM] partial row maxima
+    __syncthreads();
+    if (g == 0) {
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i) part[wave * T::WM + 16 * i + lr] = pm[i];
+    }
+    __syncthreads();
+    const bool block_valid = n0 + wn0 < N;          // N % 128 == 0: the whole block or none
+    const int64_t nbq = N / kBlock;
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i) {
+        const float amax = fmaxf(pm[i], part[(wave ^ 1) * T::WM + 16 * i + lr]);
+        const float s = fmaxf(amax, kAmaxFloor) / kE4m3Max;
+        const float rcp = 1.0f / s;
+        const int64_t row = m0 + wm0 + 16 * i + lr;
+        if (row < m_end && block_valid) {
+            uint8_t* qrow = qo.q + row * N + n0 + wn0 + 4 * g;
+#pragma unroll
+            for (int j = 0; j < T::TN; ++j) {
+                const uint32_t codes = e4m3_encode4<true>(
+                    quotient(acc[i][j][0], s, rcp), quotient(acc[i][j][1], s, rcp),
+                    quotient(acc[i][j][2], s, rcp), quotient(acc[i][j][3], s, rcp));
+                *(uint32_t*)(qrow + 16 * j) = codes;
+            }
+            if (g == 0 && (wn0 & 127) == 0) qo.qs[row * nbq + ((n0 + wn0) >> 7)] = s;
+        }
+    }
+}
+
+template <class T, bool kGuard, bool kQuant = false>
 __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
                                               const float* __restrict__ as,
                                               const uint8_t* __restrict__ b,
                                               const float* __restrict__ bs,
                                               uint16_t* __restrict__ c, int64_t m0, int64_t m_end,
                                               int64_t n0, int64_t N, int64_t K,
-                                              const Stages<T>& st) {
+                                              const Stages<T>& st, QuantOut qo = QuantOut{}) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -472,6 +542,10 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
     }
 
     // epilogue: lane holds row m0 + wm0 + 16 i + lr, columns n0 + wn0 + 16 j + 4 (lane >> 4) + 0..3
+    if constexpr (kQuant) {
+        quant_epilogue<T>(acc, qo, m0, m_end, n0, N, wave, wm0, wn0, lane, st.p[0]);
+        return;
+    }
     const int cq = 4 * (lane >> 4);
     const bool interior = (m0 + T::BM <= m_end) && (n0 + T::BN <= N);
     const bool vec = interior && (N % 4 == 0) && (((uintptr_t)c & 7u) == 0);
@@ -545,6 +619,23 @@ __global__ __launch_bounds__(T::THREADS, 1) void gemm_big_kernel(const uint8_t* 
         gemm_tile_big<T, false>(a, as, b, bs, c, m0, M, (int64_t)tn * T::BN, N, K, lds);
     else
         gemm_tile_big<T, true>(a, as, b, bs, c, m0, M, (int64_t)tn * T::BN, N, K, lds);
+}
+
+// The same GEMM with act_quant of its output fused into the epilogue.
+template <class T>
+__global__ __launch_bounds__(T::THREADS, 1) void gemm_quant_kernel(
+    const uint8_t* __restrict__ a, const float* __restrict__ as, const uint8_t* __restrict__ b,
+    const float* __restrict__ bs, uint8_t* __restrict__ q, float* __restrict__ qs, int64_t M,
+    int64_t N, int64_t K, int mt, int nt) {
+    BIG_TILE_STAGES(T, lds);
+    int tm, tn;
+    tile_of(blockIdx.x, gridDim.x, mt, nt, tm, tn);
+    const int64_t m0 = (int64_t)tm * T::BM;
+    const QuantOut qo{q, qs};
+    if (m0 + T::BM <= M)
+        gemm_tile_big<T, false, true>(a, as, b, bs, nullptr, m0, M, (int64_t)tn * T::BN, N, K, lds, qo);
+    else
+        gemm_tile_big<T, true, true>(a, as, b, bs, nullptr, m0, M, (int64_t)tn * T::BN, N, K, lds, qo);
 }
 
 // Persistent grouped kernel on the large tiles.
@@ -790,6 +881,17 @@ static void launch_big(const void* a, const float* as, const void* b, const floa
                        (const uint8_t*)a, as, (const uint8_t*)b, bs, (uint16_t*)c, M, N, K, mt, nt);
 }
 
+template <class T>
+static hipError_t launch_quant(const void* a, const float* as, const void* b, const float* bs,
+                               void* q, float* qs, int64_t M, int64_t N, int64_t K,
+                               hipStream_t stream) {
+    const int mt = (int)((M + T::BM - 1) / T::BM), nt = (int)((N + T::BN - 1) / T::BN);
+    hipLaunchKernelGGL(gemm_quant_kernel<T>, dim3(mt * nt), dim3(T::THREADS), 0, stream,
+                       (const uint8_t*)a, as, (const uint8_t*)b, bs, (uint8_t*)q, qs, M, N, K, mt,
+                       nt);
+    return hipGetLastError();
+}
+
 // Which kernel configuration serves an M x N x K problem (the tile table).
 GemmConfig gemm_config(int64_t M, int64_t N, int64_t /*K*/) {
     const int64_t cus = device_cu_count();
@@ -843,6 +945,20 @@ hipError_t launch_gemm(const void* a, const float* as, const void* b, const floa
             break;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_gemm_quant(const void* a, const float* as, const void* b, const float* bs,
+                             void* q, float* qs, int64_t M, int64_t N, int64_t K,
+                             hipStream_t stream) {
+    switch (gemm_config(M, N, K)) {
+        case GemmConfig::kBig256x256:
+            return launch_quant<BigSquare>(a, as, b, bs, q, qs, M, N, K, stream);
+        case GemmConfig::kBig256x128:
+            return launch_quant<BigWide>(a, as, b, bs, q, qs, M, N, K, stream);
+        case GemmConfig::kBig128x128:
+            return launch_quant<BigMid>(a, as, b, bs, q, qs, M, N, K, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm_grouped(const void* a, const float* as, const void* b, const float* bs,

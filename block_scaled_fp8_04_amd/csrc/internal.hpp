@@ -34,6 +34,9 @@ const char* gemm_config_name(GemmConfig cfg);
 hipError_t launch_gemm(const void* a, const float* as, const void* b, const float* bs, void* c,
                        int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
                        hipStream_t stream);
+hipError_t launch_gemm_quant(const void* a, const float* as, const void* b, const float* bs,
+                             void* q, float* qs, int64_t M, int64_t N, int64_t K,
+                             hipStream_t stream);
 hipError_t launch_gemm_grouped(const void* a, const float* as, const void* b, const float* bs,
                                void* c, const int32_t* off, int32_t G, int64_t total_M,
                                int64_t N, int64_t K, hipStream_t stream);

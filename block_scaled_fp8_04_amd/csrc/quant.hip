@@ -24,21 +24,6 @@
 
 namespace bfp8 {
 
-// Correctly rounded fp32 quotient x / s from the correctly rounded reciprocal
-// r = fl(1 / s): y0 = fl(x r) is within one ulp of x / s, the remainder
-// x - y0 s is exact as one fused multiply-add, and one more fused step
-// y0 + (x - y0 s) r rounds to fl(x / s) (Markstein's correction step).  The
-// GPU tests check the kernel against the oracle's fp32 division on every pair
-// of bf16 block maximum and bf16 element.
-// The correction step turns a quotient of -0 into +0 (-0 + +0 rounds to +0),
-// so the sign of x is put back; for x != 0 it is already the quotient's sign
-// because s > 0.
-__device__ __forceinline__ float quotient(float x, float s, float r) {
-    const float y0 = x * r;
-    const float e = __builtin_fmaf(-y0, s, x);
-    return __builtin_copysignf(__builtin_fmaf(e, r, y0), x);
-}
-
 template <bool kHw>
 __device__ __forceinline__ void quant_block_part(const uint4 v0, const uint4 v1, int lane8,
                                                  uint4& out, float& scale) {

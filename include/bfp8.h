@@ -44,7 +44,7 @@ extern "C" {
 #endif
 
 #define BFP8_BLOCK 128
-#define BFP8_VERSION 3
+#define BFP8_VERSION 4
 #define BFP8_MOE_MAX_GROUPS 1024
 
 typedef enum bfp8_status {
@@ -105,6 +105,21 @@ int bfp8_weight_dequant(const void* w_e4m3, const float* s, void* out_bf16,
 int bfp8_gemm(const void* a, const float* a_s, const void* b, const float* b_s,
               void* c_bf16, int64_t M, int64_t N, int64_t K,
               void* workspace, size_t workspace_bytes, void* stream);
+
+/* fp8_gemm with the next linear()'s act_quant fused into its epilogue ([DF]
+ * FP8 bullet: a linear() output is quantized in 128-element blocks before the
+ * next fp8_gemm; the dense chain's "act_quant of W1 output before the second
+ * GEMM").  Same product as bfp8_gemm, but instead of bf16 C it writes
+ *     q, qs = act_quant( bf16_rne(C) )
+ * i.e. exactly what bfp8_act_quant would write for bfp8_gemm's output, bit for
+ * bit, without storing or re-reading C.
+ *   a, a_s, b, b_s : as bfp8_gemm
+ *   q_e4m3  : e4m3 [M, N] output, 4-byte aligned
+ *   q_scales: fp32 [M, N/128] output
+ * Errors: as bfp8_gemm, and BFP8_ERR_SHAPE if N % 128 != 0. */
+int bfp8_gemm_act_quant(const void* a, const float* a_s, const void* b, const float* b_s,
+                        void* q_e4m3, float* q_scales, int64_t M, int64_t N, int64_t K,
+                        void* stream);
 
 /* Bytes of fp32 workspace bfp8_gemm would use for split-K at this shape
  * (0 when the shape does not use split-K).  Pure host function. */

@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert bfp8.bfp8_version() == 3
+    assert bfp8.bfp8_version() == 4
     for code in range(8):
         assert bfp8.bfp8_status_string(code)
     assert bfp8.bfp8_status_string(0) == "ok"
@@ -127,6 +127,22 @@ def test_gemm_grouped_validation(lib):
     assert call(off=ctypes.c_void_p(0x10002)) == _lib.BFP8_ERR_ALIGN
     assert call(a=ODD) == _lib.BFP8_ERR_ALIGN
     assert call(a=None, T=0) == _lib.BFP8_OK
+
+
+def test_gemm_act_quant_validation(lib):
+    f = lib.bfp8_gemm_act_quant
+
+    def call(a=FAKE, a_s=FAKE, b=FAKE, b_s=FAKE, q=FAKE, qs=FAKE, M=64, N=256, K=256):
+        return f(a, a_s, b, b_s, q, qs, M, N, K, None)
+
+    assert call(N=200) == _lib.BFP8_ERR_SHAPE          # N % 128
+    assert call(K=100) == _lib.BFP8_ERR_SHAPE
+    assert call(M=-1) == _lib.BFP8_ERR_SHAPE
+    for name in ("a", "a_s", "b", "b_s", "q", "qs"):
+        assert call(**{name: None}) == _lib.BFP8_ERR_NULL, name
+    assert call(q=ctypes.c_void_p(0x10002)) == _lib.BFP8_ERR_ALIGN
+    assert call(a=ODD) == _lib.BFP8_ERR_ALIGN
+    assert call(a=None, M=0) == _lib.BFP8_OK
 
 
 def test_gemm_bf16_validation(lib):

@@ -1,0 +1,97 @@
+"""GPU parity of the fp8 GEMM with act_quant fused into its epilogue.
+
+Two checks per case:
+  * consistency: the fused kernel's codes and scales equal bfp8_act_quant of
+    bfp8_gemm's bf16 output, bit for bit (both on the GPU; the fused epilogue
+    rounds to bf16 first exactly as the stored output is rounded);
+  * parity with the oracle on sampled rows: the dequantized codes
+    deq(q) * s approximate the oracle's fp64 product C within the GEMM
+    tolerance plus what the bf16 rounding and the e4m3 quantization may add:
+        |deq - C| <= tol_gemm + 2^-8 |C| + 2^-4 (|C| + tol_gemm) + 2^-10 s,
+    (half an e4m3 ulp is at most 2^-4 of a normal value and 2^-10 s in the
+    subnormal range), and the scales match max(amax, 1e-4) / 448 of the
+    oracle's row blocks within the same GEMM tolerance on the block maximum.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import block_scaled_fp8_04_amd as bfp8
+from block_scaled_fp8_04_amd import synth
+from gpu_helpers import GEMM_REL, GEMM_RMS, announce, dev, sample_rows, u8, workload
+
+pytestmark = pytest.mark.gpu
+BLOCK = 128
+
+
+def _e4m3_values():
+    return torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _check(q, qs, ref, what):
+    """q uint8 [r, N], qs [r, N/128] (numpy) against the oracle's fp64 rows ref [r, N]."""
+    vals = _e4m3_values()
+    deq = vals[q] * np.repeat(qs.astype(np.float64), BLOCK, axis=1)
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    tol = GEMM_REL * np.abs(ref) + GEMM_RMS * rms
+    s_col = np.repeat(qs.astype(np.float64), BLOCK, axis=1)
+    bound = tol + 2.0 ** -8 * np.abs(ref) + 2.0 ** -4 * (np.abs(ref) + tol) + 2.0 ** -10 * s_col
+    err = np.abs(deq - ref)
+    assert np.all(err <= bound), f"{what}: {int((err > bound).sum())} elements outside the bound"
+    amax = np.abs(ref).reshape(ref.shape[0], -1, BLOCK).max(axis=2)
+    tol_a = (GEMM_REL + 2.0 ** -8) * amax + GEMM_RMS * rms
+    s_ref = np.maximum(amax, 1e-4) / 448.0
+    assert np.all(np.abs(qs - s_ref) <= tol_a / 448.0 + 1e-12), f"{what}: scales outside tolerance"
+    announce(f"{what}: worst err/bound {float(np.max(err / bound)):.3f}")
+
+
+def _case(q_a, s_a, w, s_w, what, rows=None):
+    M, N = q_a.shape[0], w.shape[0]
+    announce(f"gemm_act_quant {what} M={M} N={N} K={q_a.shape[1]} via {bfp8.bfp8_gemm_kernel_name(M, N, q_a.shape[1])}")
+    q = torch.full((M, N), 0x33, dtype=torch.uint8, device=dev())
+    qs = torch.full((M, N // BLOCK), -1.0, dtype=torch.float32, device=dev())
+    bfp8.bfp8_gemm_act_quant(q_a, s_a, w, s_w, q, qs)
+    c = bfp8.gemm(q_a, s_a, w, s_w)
+    q2, qs2 = bfp8.act_quant(c)
+    torch.cuda.synchronize()
+    assert torch.equal(q, q2), f"{what}: codes differ from act_quant(gemm)"
+    assert torch.equal(qs, qs2), f"{what}: scales differ from act_quant(gemm)"
+    r = np.arange(M) if rows is None else rows
+    ref = oracle.gemm(u8(q_a), s_a.cpu().numpy(), u8(w), s_w.cpu().numpy(), rows=r)
+    rt = torch.from_numpy(np.asarray(r)).to(dev())
+    _check(u8(q[rt]), qs[rt].cpu().numpy(), ref, what)
+
+
+def test_fused_quant_shapes():
+    g = torch.Generator().manual_seed(61)
+    for i, (M, N, K) in enumerate([(16, 256, 256), (1, 128, 128), (130, 384, 384), (300, 1280, 256),
+                                    (2000, 4096, 256), (4100, 8192, 128), (257, 640, 512)]):
+        x = (torch.randn(M, K, generator=g) * (1 + i)).to(torch.bfloat16).to(dev())
+        q_a, s_a = bfp8.act_quant(x)
+        w, s_w = synth.weight(N, K, 620 + i, 640 + i)
+        rows = None if M <= 300 else sample_rows(M, 16, 660 + i)
+        _case(q_a, s_a, w.to(dev()), s_w.to(dev()), f"shape {i}", rows)
+
+
+def test_fused_quant_zero_rows():
+    """A zero activation row gives a zero output row: codes 0 and the floor scale."""
+    K, N = 256, 512
+    x = torch.randn(64, K).to(torch.bfloat16)
+    x[5] = 0
+    q_a, s_a = bfp8.act_quant(x.to(dev()))
+    w, s_w = synth.weight(N, K, 670, 671)
+    q, qs = bfp8.gemm_act_quant(q_a, s_a, w.to(dev()), s_w.to(dev()))
+    torch.cuda.synchronize()
+    assert torch.all(q[5] == 0)
+    assert torch.all(qs[5] == torch.tensor(1e-4, dtype=torch.float32) / 448.0)
+
+
+def test_fused_quant_dense_chain_full_size():
+    """The dense MLP up projection with H quantized in the epilogue, then the down GEMM on it."""
+    wl = workload(3)
+    x = wl.tensors["x"].to(dev())
+    w1, s1 = wl.tensors["w1"].to(dev()), wl.tensors["s1"].to(dev())
+    q_a, s_a = bfp8.act_quant(x)
+    rows = np.array([0, 1, 2047, 2048, 6000, 8191], np.int64)
+    _case(q_a, s_a, w1, s1, "dense-mlp up 8192x18432x7168", rows)
