@@ -57,6 +57,7 @@ class Oracle:
         lib.oracle_gemm_grouped_rows.restype = ctypes.c_int
         lib.oracle_gemm_bf16_rows.argtypes = [P, P, I64, I64, I64, P, I64, P, ctypes.c_int]
         lib.oracle_gemm_bf16_rows.restype = ctypes.c_int
+        lib.oracle_swiglu_bf16.argtypes = [P, P, I64, P]
         lib.oracle_moe_dispatch.argtypes = [P, I64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                             P, P, P]
         lib.oracle_moe_combine.argtypes = [P, P, P, I64, ctypes.c_int32, I64, P]
@@ -188,6 +189,15 @@ class Oracle:
             raise ValueError(f"oracle_gemm_bf16_rows failed ({rc})")
         return out
 
+    def swiglu_bf16(self, g, u) -> np.ndarray:
+        """bf16 bits of bf16(bf16(silu(bf16(g))) * bf16(u)) for fp64 arrays g, u of one shape."""
+        g = _c(g, np.float64); u = _c(u, np.float64)
+        if g.shape != u.shape:
+            raise ValueError("g and u must have one shape")
+        h = np.empty(g.shape, np.uint16)
+        self.lib.oracle_swiglu_bf16(_ptr(g), _ptr(u), g.size, _ptr(h))
+        return h
+
     # ---------------------------------------------------------------- MoE
 
     def moe_dispatch(self, topk, expert_lo, G):
@@ -288,6 +298,10 @@ def gemm_grouped(a, sa, b, sb, offsets, rows=None, threads=None):
 
 def gemm_bf16(a_bits, b_bits, rows=None, threads=None):
     return default().gemm_bf16(a_bits, b_bits, rows, threads)
+
+
+def swiglu_bf16(g, u):
+    return default().swiglu_bf16(g, u)
 
 
 def moe_dispatch(topk, expert_lo, G):

@@ -28,6 +28,9 @@
  *     "Data flow" (codevetter): a GPU holds a contiguous range of experts.
  *   - pyshine tour, "FP8 with per-block scales": the second branch of
  *     linear() dequantizes the weight and runs an ordinary BF16 matmul.
+ *   - the gated FFN (w1, w3 -> activation * up -> w2) of the MLP/Expert
+ *     modules ("Data flow", MLP and Expert projections); the activation is
+ *     this oracle's stated reading (SiLU), the pages do not print it.
  * The e4m3 format itself is the OCP 8-bit floating point E4M3 encoding
  * (torch.float8_e4m3fn): bias 7, no infinities, NaN only at S.1111.111,
  * largest finite value 448.
@@ -361,6 +364,28 @@ int oracle_gemm_bf16_rows(const uint16_t* a, const uint16_t* b, int64_t M, int64
     for (int t = 1; t <= started; ++t) pthread_join(th[t], NULL);
     free(jobs); free(th);
     return 0;
+}
+
+/* ------------------------------------------------------- gated FFN activation */
+
+/* The gated FFN between the first and the second projection of an expert
+ * or the dense MLP: h = silu(w1 x) * (w3 x).  The pages name w1/w2/w3
+ * ("gate_proj -> w1") but never print the activation; this oracle takes
+ * SiLU, silu(x) = x / (1 + e^-x), as DeepSeek-V3's model code uses.  The
+ * steps follow a bf16 model: g and u are the projections' bf16 outputs,
+ * silu(g) is evaluated in floating point and rounded to bf16, and the product
+ * of the two bf16 values (exact) is rounded to bf16:
+ *     h = bf16( bf16( silu( bf16(g) ) ) * bf16(u) ).
+ * g and u arrive as fp64 GEMM results and are rounded to bf16 through fp32.
+ * Output: bf16 bit patterns. */
+void oracle_swiglu_bf16(const double* g, const double* u, int64_t n, uint16_t* h) {
+    for (int64_t i = 0; i < n; ++i) {
+        const double gb = (double)oracle_bf16_to_f32(oracle_f32_to_bf16((float)g[i]));
+        const double ub = (double)oracle_bf16_to_f32(oracle_f32_to_bf16((float)u[i]));
+        const double sg = gb / (1.0 + exp(-gb));
+        const double sgb = (double)oracle_bf16_to_f32(oracle_f32_to_bf16((float)sg));
+        h[i] = oracle_f32_to_bf16((float)(sgb * ub));
+    }
 }
 
 /* ------------------------------------------------- MoE dispatch and combine */

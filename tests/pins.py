@@ -573,6 +573,51 @@ def pin_bf16_branch_vs_torch(orc):
     assert np.array_equal(orc.gemm_bf16(x, wd, rows=rows), got[rows])
 
 
+# ------------------------------------------------------------ gated FFN pins
+#
+# The gated FFN's activation is not printed on the pages; the oracle's reading
+# is SiLU (pinned here against torch's own silu), with the bf16 rounding steps
+# of a bf16 model.
+
+def pin_swiglu_vs_torch_silu(orc):
+    """G1: with u = 1 the gate output is bf16(silu(bf16 g)), torch's float64 silu rounded by torch."""
+    rng = np.random.default_rng(1100)
+    g = np.concatenate([rng.standard_normal(4000) * 4, [0.0, -0.0, 30.0, -30.0, 1e-3, -1e-3]])
+    h = orc.swiglu_bf16(g, np.ones_like(g))
+    gb = torch.from_numpy(g.astype(np.float32)).to(torch.bfloat16).double()
+    ref = torch.nn.functional.silu(gb).float().to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(h, ref)
+
+
+def pin_swiglu_bf16_model_steps(orc):
+    """G3: random g, u through torch's bf16 ops: silu(bf16 g) rounded to bf16 by torch, times
+    bf16 u (exact in fp32), rounded to bf16 by torch."""
+    rng = np.random.default_rng(1102)
+    g, u = rng.standard_normal(5000) * 3, rng.standard_normal(5000) * 2
+    h = orc.swiglu_bf16(g, u)
+    gb = torch.from_numpy(g.astype(np.float32)).to(torch.bfloat16)
+    ub = torch.from_numpy(u.astype(np.float32)).to(torch.bfloat16)
+    sg = torch.nn.functional.silu(gb.double()).float().to(torch.bfloat16)
+    ref = (sg.float() * ub.float()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(h, ref)
+
+
+def pin_swiglu_identities(orc):
+    """G2: silu(x) - silu(-x) = x within the roundings; zero gate or zero up gives 0; the
+    product with an exact power-of-two u is exact."""
+    rng = np.random.default_rng(1101)
+    x = rng.standard_normal(2000) * 3
+    hp = bf16_bits_to_f32(orc.swiglu_bf16(x, np.ones_like(x))).astype(np.float64)
+    hm = bf16_bits_to_f32(orc.swiglu_bf16(-x, np.ones_like(x))).astype(np.float64)
+    xb = bf16_bits_to_f32(torch_bf16(x.astype(np.float32))).astype(np.float64)
+    assert np.all(np.abs((hp - hm) - xb) <= 2.0 ** -7 * (np.abs(hp) + np.abs(hm)) + 1e-30)
+    assert np.all(orc.swiglu_bf16(np.zeros(5), rng.standard_normal(5)) & 0x7FFF == 0)
+    assert np.all(orc.swiglu_bf16(rng.standard_normal(5), np.zeros(5)) & 0x7FFF == 0)
+    h1 = bf16_bits_to_f32(orc.swiglu_bf16(x, np.ones_like(x))).astype(np.float64)
+    h4 = bf16_bits_to_f32(orc.swiglu_bf16(x, np.full_like(x, 4.0))).astype(np.float64)
+    assert np.array_equal(h4, 4.0 * h1)
+
+
 # ------------------------------------------------------ MoE dispatch / combine pins
 #
 # Source: "Behavior traces - deepseek-ai/DeepSeek-V3" (codevetter), MoE trace

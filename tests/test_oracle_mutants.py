@@ -16,6 +16,10 @@ import pins
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "bfp8_oracle.c")
 
 MUTANTS = {
+    # gated FFN: sigmoid of the wrong sign
+    "swiglu_sign": ("const double sg = gb / (1.0 + exp(-gb));", "const double sg = gb / (1.0 + exp(gb));"),
+    # gated FFN: the activation's bf16 rounding skipped
+    "swiglu_no_round": ("h[i] = oracle_f32_to_bf16((float)(sgb * ub));", "h[i] = oracle_f32_to_bf16((float)(sg * ub));"),
     # bf16 GEMM: weight row stride lost
     "bf16_gemm_row_stride": ("const uint16_t* b = J->b + n * J->K;", "const uint16_t* b = J->b + n;"),
     # bf16 GEMM: fp32 accumulation
