@@ -19,7 +19,9 @@ bounds it; `roofline` repeats that for the dominant kernel; `cpu_baseline`
 times the CPU oracle on a bounded, proportional sample of the same step.
 
 Other workloads (parity-test shapes, measured on demand): --workload tiny |
-decode | moe-pair | dense-mlp-unfused | grouped | moe-layer | bf16-branch.  moe-layer is the routed
+decode | moe-pair | dense-mlp-unfused | grouped | moe-layer | bf16-branch |
+expert-ffn (one expert's gated FFN with the SiLU gate and act_quant fused into the
+[w1; w3] GEMM's epilogue).  moe-layer is the routed
 experts of one GPU end to end on the device: moe_dispatch(topk) ->
 act_quant_rows(x, row_token) -> grouped GEMM (row buffers sized for T*k rows)
 -> moe_combine (weighted sum back to token order).
@@ -47,7 +49,7 @@ PEAK_HBM_GBS = 8000.0             # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0         # MI355X dense bf16 MFMA (no sparsity)
 
 WORKLOADS = {"tiny": 0, "decode": 1, "moe-pair": 2, "dense-mlp": 3, "grouped": 4, "moe-layer": 4,
-             "bf16-branch": 3, "dense-mlp-unfused": 3}
+             "bf16-branch": 3, "dense-mlp-unfused": 3, "expert-ffn": 2}
 
 
 # ------------------------------------------------------------------ accounting
@@ -86,7 +88,7 @@ class Step:
         self.dev = dev
         t = wl.tensors
         c = wl.config
-        if kind in ("moe-layer", "bf16-branch", "dense-mlp"):
+        if kind in ("moe-layer", "bf16-branch", "dense-mlp", "expert-ffn"):
             c = kind
         self.launches = []            # (name, callable, flops, bytes, bound)
         self.hashes = {}
@@ -178,6 +180,28 @@ class Step:
             ]
             self.shape = dict(M=M, N1=N1, K1=K1, N2=N2, K2=K2)
             self.dominant, self.dominant_kernel = ["fp8_gemm_1_quant", "fp8_gemm_2"], "gemm"
+        elif c == "expert-ffn":
+            # one routed expert's gated FFN: act_quant(x) -> [w1; w3] GEMM with silu(g) * u and
+            # act_quant in the epilogue -> w2 GEMM
+            M, N1, K1, N2, K2 = (wl.meta[k] for k in ("M", "N1", "K1", "N2", "K2"))
+            x = t["x"].to(dev)
+            w13, s13 = bfp8.interleave_w13(t["w1"], t["s1"], t["w3"], t["s3"])
+            w13, s13 = w13.to(dev), s13.to(dev)
+            w2, s2 = t["w2"].to(dev), t["s2"].to(dev)
+            q = torch.empty(M, K1, dtype=torch.uint8, device=dev)
+            qs = torch.empty(M, K1 // BLOCK, dtype=torch.float32, device=dev)
+            qh = torch.empty(M, K2, dtype=torch.uint8, device=dev)
+            qhs = torch.empty(M, K2 // BLOCK, dtype=torch.float32, device=dev)
+            y = torch.empty(M, N2, dtype=torch.bfloat16, device=dev)
+            self.launches += [
+                ("act_quant_x", lambda: bfp8.bfp8_act_quant(x, q, qs), 0, act_quant_bytes(M, K1), "hbm"),
+                ("fp8_gemm_w13_swiglu_quant", lambda: bfp8.bfp8_gemm_swiglu_act_quant(q, qs, w13, s13, qh, qhs),
+                 2 * M * 2 * N1 * K1, M * K1 + 2 * N1 * K1 + M * N1 + 4 * M * (N1 // BLOCK), "mfma"),
+                ("fp8_gemm_w2", lambda: bfp8.bfp8_gemm(qh, qhs, w2, s2, y), 2 * M * N2 * K2,
+                 gemm_bytes(M, N2, K2), "mfma"),
+            ]
+            self.shape = dict(M=M, N_gate_up=2 * N1, N_out=N1, K1=K1, N2=N2, K2=K2, activation="silu (stated reading)")
+            self.dominant, self.dominant_kernel = ["fp8_gemm_w13_swiglu_quant"], "gemm"
         elif c == "bf16-branch":
             M, N1, K1, N2, K2 = (wl.meta[k] for k in ("M", "N1", "K1", "N2", "K2"))
             x = t["x"].to(dev)
@@ -440,8 +464,8 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, args.cpu_seconds, args.workload)
 
-    wl_name = (f"{args.workload}-{wl.name}" if args.workload in ("moe-layer", "bf16-branch", "dense-mlp-unfused")
-               else wl.name)
+    wl_name = (f"{args.workload}-{wl.name}"
+               if args.workload in ("moe-layer", "bf16-branch", "dense-mlp-unfused", "expert-ffn") else wl.name)
     config = {"workload": wl_name, "shape": step.shape,
               "step": " -> ".join(l[0] for l in step.launches),
               "value_definition": "GEMM FLOP per step / wall time per step",

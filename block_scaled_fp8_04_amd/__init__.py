@@ -12,5 +12,6 @@ from ._lib import (  # noqa: F401
     bfp8_weight_dequant, gemm, gemm_grouped, library, linear_fp8, status_string, weight_dequant,
     bfp8_act_quant_rows, bfp8_moe_combine, bfp8_moe_dispatch, bfp8_moe_dispatch_workspace_size,
     moe_combine, moe_dispatch, moe_experts_fp8, bfp8_gemm_bf16, gemm_bf16, linear_bf16,
-    bfp8_gemm_act_quant, gemm_act_quant,
+    bfp8_gemm_act_quant, gemm_act_quant, bfp8_gemm_swiglu_act_quant, gemm_swiglu_act_quant,
+    interleave_w13,
 )

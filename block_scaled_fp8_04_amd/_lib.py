@@ -30,7 +30,7 @@ EXPORTS = ("bfp8_act_quant", "bfp8_weight_dequant", "bfp8_gemm", "bfp8_gemm_work
            "bfp8_gemm_grouped", "bfp8_e4m3_encode_range", "bfp8_bf16_round_range",
            "bfp8_gemm_kernel_name", "bfp8_moe_dispatch_workspace_size", "bfp8_moe_dispatch",
            "bfp8_act_quant_rows", "bfp8_moe_combine", "bfp8_gemm_bf16",
-           "bfp8_gemm_act_quant",
+           "bfp8_gemm_act_quant", "bfp8_gemm_swiglu_act_quant",
            "bfp8_status_string", "bfp8_version")
 
 _lib = None
@@ -78,6 +78,8 @@ def library():
     lib.bfp8_moe_combine.restype = ctypes.c_int
     lib.bfp8_gemm_act_quant.argtypes = [P, P, P, P, P, P, I64, I64, I64, P]
     lib.bfp8_gemm_act_quant.restype = ctypes.c_int
+    lib.bfp8_gemm_swiglu_act_quant.argtypes = [P, P, P, P, P, P, I64, I64, I64, P]
+    lib.bfp8_gemm_swiglu_act_quant.restype = ctypes.c_int
     lib.bfp8_gemm_bf16.argtypes = [P, P, P, I64, I64, I64, P]
     lib.bfp8_gemm_bf16.restype = ctypes.c_int
     lib.bfp8_status_string.argtypes = [ctypes.c_int]
@@ -205,6 +207,36 @@ def bfp8_gemm_act_quant(a, a_s, b, b_s, q, q_scales, stream=None):
     _check("bfp8_gemm_act_quant", library().bfp8_gemm_act_quant(
         _ptr(a), _ptr(a_s), _ptr(b), _ptr(b_s), _ptr(q), _ptr(q_scales), M, N, K,
         _stream(stream, a.device)))
+
+
+def bfp8_gemm_swiglu_act_quant(a, a_s, w13, s13, q, q_scales, stream=None):
+    """q, q_scales = act_quant(bf16(bf16(silu(bf16(a w1^T))) * bf16(a w3^T))) for the 64-row
+    interleaved w13 [2N, K] (see interleave_w13) with its per-64-row scales s13 [2N/64, K/128]."""
+    a, w13, q = _bytes_view(a), _bytes_view(w13), _bytes_view(q)
+    _cuda_contig(a, a_s, w13, s13, q, q_scales)
+    M, K = a.shape
+    N2 = w13.shape[0]
+    _need(w13.shape[1] == K and N2 % 256 == 0, "w13 must be [2N, K] with N % 128 == 0")
+    N = N2 // 2
+    _need(a_s.shape == (M, K // BLOCK) and s13.shape == (N2 // 64, K // BLOCK),
+          "a_s [M, K/128], s13 [2N/64, K/128]")
+    _need(q.shape == (M, N) and q_scales.shape == (M, N // BLOCK), "q [M, N], q_scales [M, N/128]")
+    _check("bfp8_gemm_swiglu_act_quant", library().bfp8_gemm_swiglu_act_quant(
+        _ptr(a), _ptr(a_s), _ptr(w13), _ptr(s13), _ptr(q), _ptr(q_scales), M, N, K,
+        _stream(stream, a.device)))
+
+
+def interleave_w13(w1, s1, w3, s3):
+    """One-time weight preparation (data movement only) for bfp8_gemm_swiglu_act_quant:
+    w1, w3 e4m3 [N, K] with 128x128 scale grids s1, s3 [N/128, K/128] ->
+    w13 [2N, K] (64-row groups alternating w1, w3) and s13 [2N/64, K/128]."""
+    N, K = w1.shape
+    _need(w3.shape == (N, K) and N % 128 == 0, "w1 and w3 must be [N, K] with N % 128 == 0")
+    w13 = torch.stack([w1.reshape(N // 64, 64, K), w3.reshape(N // 64, 64, K)], dim=1).reshape(2 * N, K)
+    g1 = s1.repeat_interleave(2, dim=0)                  # scale of each 64-row group of w1
+    g3 = s3.repeat_interleave(2, dim=0)
+    s13 = torch.stack([g1, g3], dim=1).reshape(2 * N // 64, -1)
+    return w13.contiguous(), s13.contiguous()
 
 
 def bfp8_gemm_grouped(a, a_s, b, b_s, c, group_offsets, stream=None):
@@ -351,6 +383,14 @@ def gemm_act_quant(a, a_s, b, b_s, stream=None):
     q = torch.empty((M, N), dtype=torch.uint8, device=a.device)
     qs = torch.empty((M, N // BLOCK), dtype=torch.float32, device=a.device)
     bfp8_gemm_act_quant(a, a_s, b, b_s, q, qs, stream)
+    return q, qs
+
+
+def gemm_swiglu_act_quant(a, a_s, w13, s13, stream=None):
+    M, N = a.shape[0], w13.shape[0] // 2
+    q = torch.empty((M, N), dtype=torch.uint8, device=a.device)
+    qs = torch.empty((M, N // BLOCK), dtype=torch.float32, device=a.device)
+    bfp8_gemm_swiglu_act_quant(a, a_s, w13, s13, q, qs, stream)
     return q, qs
 
 

@@ -106,6 +106,20 @@ int bfp8_gemm_act_quant(const void* a, const float* a_s, const void* b, const fl
                                             (hipStream_t)stream));
 }
 
+int bfp8_gemm_swiglu_act_quant(const void* a, const float* a_s, const void* w13,
+                               const float* s13, void* q_e4m3, float* q_scales, int64_t M,
+                               int64_t N, int64_t K, void* stream) {
+    if (M < 0 || N < 0 || K <= 0 || K % BFP8_BLOCK != 0 || N % BFP8_BLOCK != 0)
+        return BFP8_ERR_SHAPE;
+    if (M == 0 || N == 0) return BFP8_OK;
+    if (!a || !a_s || !w13 || !s13 || !q_e4m3 || !q_scales) return BFP8_ERR_NULL;
+    if (!aligned(a, 16) || !aligned(w13, 16) || !aligned(a_s, 4) || !aligned(s13, 4) ||
+        !aligned(q_e4m3, 4) || !aligned(q_scales, 4))
+        return BFP8_ERR_ALIGN;
+    return from_hip(bfp8::launch_gemm_swiglu_quant(a, a_s, w13, s13, q_e4m3, q_scales, M, N, K,
+                                                   (hipStream_t)stream));
+}
+
 int bfp8_gemm_grouped(const void* a, const float* a_s, const void* b, const float* b_s,
                       void* c_bf16, const int32_t* group_offsets, int32_t G, int64_t total_M,
                       int64_t N, int64_t K, void* stream) {

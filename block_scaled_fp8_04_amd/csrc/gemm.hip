@@ -195,12 +195,15 @@ __device__ __forceinline__ void load_lds4(const void* src, void* lds_dst) {
 // MFMAs and folds of its 16-row sub-tile rows that lie entirely past m_end
 // (a wave-uniform test); full tiles run the unguarded, explicitly scheduled
 // loop.
-// Where the tile's result goes: bf16 into c, or (kQuant) act_quant of the
-// bf16-rounded result into e4m3 codes q [M, N] and scales qs [M, N/128].
+// Where the tile's result goes (the epilogue mode): kEpiBf16 stores bf16 C;
+// kEpiQuant writes act_quant of the bf16-rounded result, e4m3 codes q [M, N]
+// and scales qs [M, N/128]; kEpiSwiglu multiplies a 64-row-interleaved
+// [w1; w3] weight and writes act_quant of silu(w1 x) * (w3 x), q [M, N/2].
 struct QuantOut {
     uint8_t* q;
     float* qs;
 };
+constexpr int kEpiBf16 = 0, kEpiQuant = 1, kEpiSwiglu = 2;
 
 // act_quant fused into the GEMM epilogue ("Data flow", FP8 quantization
 // bullet: the next linear() quantizes this output in 128-element blocks).
@@ -265,7 +268,96 @@ __device__ __forceinline__ void quant_epilogue(v4f (&acc)[T::TM][T::TN], const Q
     }
 }
 
-template <class T, bool kGuard, bool kQuant = false>
+// The gated FFN's first GEMM with its activation and act_quant in the
+// epilogue.  The weight is [w1; w3] interleaved by 64 rows (rows 128 t ..
+// 128 t + 63 are w1 rows 64 t .., the next 64 are the matching w3 rows), so in
+// a 256-column tile of the 2 x 4 wave layout, waves wn = 0, 2 hold w1 x (the
+// gate g) and waves wn = 1, 3 hold w3 x (the up value u) for the same 128
+// output columns, each lane at the same (row, column) as its partner's lane.
+// Output: h = bf16( bf16( silu(g) ) * u ), the operations a bf16 model does
+// on bf16 g and u (silu(x) = x / (1 + e^-x), evaluated in fp32 and rounded
+// once); then act_quant of h's 128-column block exactly as quant_epilogue.
+// The u waves hand their values to the g waves through LDS (lane-major, no
+// bank conflicts); the two g waves of a row meet in LDS for the block max.
+template <class T>
+__device__ __forceinline__ void swiglu_quant_epilogue(v4f (&acc)[T::TM][T::TN], const QuantOut& qo,
+                                                      int64_t m0, int64_t m_end, int64_t n0,
+                                                      int64_t N, int wave, int wm0, int wn0,
+                                                      int lane, const Stages<T>& st) {
+    static_assert(T::WN == 64 && T::WAVES_N == 4 && T::BN == 256 && T::WAVES_M == 2,
+                  "the gated epilogue runs on the 256 x 256 tile");
+    constexpr int PER_LANE = T::TM * T::TN * 4;
+    static_assert(2 * PER_LANE * 64 * 4 <= T::A_BYTES + T::B_BYTES, "u hand-off fits one stage");
+    const int lr = lane & 15, g = lane >> 4;
+    const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
+    const bool is_up = (wn & 1) != 0;
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[i][j][r] = bf16_round_f32(acc[i][j][r]);
+    // stage wm carries the u values of the two column groups of wave row wm
+    float* xu = (float*)(wm == 0 ? st.p[0] : st.p[1]) + (wn >> 1) * PER_LANE * 64;
+    float* part = (float*)(st.p[0] + T::A_BYTES + T::B_BYTES);     // [2 x 2 waves][WM] maxima
+    __syncthreads();                                               // every wave left the K loop
+    if (is_up) {
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+            for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) xu[((i * T::TN + j) * 4 + r) * 64 + lane] = acc[i][j][r];
+    }
+    __syncthreads();
+    float pm[T::TM];
+    if (!is_up) {
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i) {
+            float m = 0.f;
+#pragma unroll
+            for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float gv = acc[i][j][r];
+                    const float u = xu[((i * T::TN + j) * 4 + r) * 64 + lane];
+                    const float sg = bf16_round_f32(gv / (1.0f + expf(-gv)));
+                    const float h = bf16_round_f32(sg * u);
+                    acc[i][j][r] = h;
+                    m = fmaxf(m, fabsf(h));
+                }
+            m = fmaxf(m, __shfl_xor(m, 16));
+            m = fmaxf(m, __shfl_xor(m, 32));
+            pm[i] = m;
+            if (g == 0) part[(wm * 2 + (wn >> 1)) * T::WM + 16 * i + lr] = m;
+        }
+    }
+    __syncthreads();
+    if (is_up) return;
+    const int64_t nout = N / 2;
+    const int64_t nbq = nout / kBlock;
+    const int64_t h0 = n0 / 2 + (wn >> 1) * 64;                  // this wave's first h column
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i) {
+        const float amax = fmaxf(pm[i], part[(wm * 2 + ((wn >> 1) ^ 1)) * T::WM + 16 * i + lr]);
+        const float s = fmaxf(amax, kAmaxFloor) / kE4m3Max;
+        const float rcp = 1.0f / s;
+        const int64_t row = m0 + wm0 + 16 * i + lr;
+        if (row < m_end) {
+            uint8_t* qrow = qo.q + row * nout + h0 + 4 * g;
+#pragma unroll
+            for (int j = 0; j < T::TN; ++j) {
+                const uint32_t codes = e4m3_encode4<true>(
+                    quotient(acc[i][j][0], s, rcp), quotient(acc[i][j][1], s, rcp),
+                    quotient(acc[i][j][2], s, rcp), quotient(acc[i][j][3], s, rcp));
+                *(uint32_t*)(qrow + 16 * j) = codes;
+            }
+            if (g == 0 && wn == 0) qo.qs[row * nbq + (n0 >> 8)] = s;
+        }
+    }
+}
+
+template <class T, bool kGuard, int kEpi = kEpiBf16>
 __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
                                               const float* __restrict__ as,
                                               const uint8_t* __restrict__ b,
@@ -289,7 +381,8 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
     const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(a + m0 * K, (uint64_t)rows_a * K);
     const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(b + n0 * K, (uint64_t)rows_b * K);
     const __amdgpu_buffer_rsrc_t rs_as = make_rsrc(as + m0 * KB, (uint64_t)rows_a * KB * 4);
-    const __amdgpu_buffer_rsrc_t rs_bs = make_rsrc(bs, (uint64_t)NBK * KB * 4);
+    const __amdgpu_buffer_rsrc_t rs_bs =
+        make_rsrc(bs, (uint64_t)((kEpi == kEpiSwiglu) ? (N + 63) / 64 : NBK) * KB * 4);
 
     // Direct-load sources.  Instruction i of this wave fills LDS rows
     // r0 .. r0+7 (r0 = 8 * (wave * INSTR + i)); lane l writes physical chunk
@@ -323,10 +416,14 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
         as_off = (uint32_t)(row * KB * 4);
     }
     // weight-scale line: float l = scale of 128-column block (n0 / 128 + l)
+    // weight scales: one per 128 weight rows, or per 64 rows for the
+    // interleaved [w1; w3] weight (each 64-row group keeps its own block scale)
+    constexpr int kSgShift = (kEpi == kEpiSwiglu) ? 6 : 7;
+    const int64_t NBS = (kEpi == kEpiSwiglu) ? (N + 63) / 64 : NBK;
     uint32_t bs_off;
     {
-        int64_t nb = (n0 >> 7) + lane;
-        nb = nb < NBK ? nb : NBK - 1;
+        int64_t nb = (n0 >> kSgShift) + lane;
+        nb = nb < NBS ? nb : NBS - 1;
         bs_off = (uint32_t)(nb * KB * 4);
     }
 
@@ -390,7 +487,7 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
     const int off0 = ((lk ^ swz(lr)) << 4);
     const int off1 = (((lk + 1) ^ swz(lr)) << 4);
     const int sread = lr * T::SPITCH + wm0 / 16;
-    const int sb_slot = wn0 >> 7;                      // this wave's weight-scale float
+    const int sb_slot = wn0 >> kSgShift;               // this wave's weight-scale float
 
     // One K block from stage S; block kb + NSTAGE - 1 goes to the stage that
     // block kb - 1 used.
@@ -542,8 +639,12 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
     }
 
     // epilogue: lane holds row m0 + wm0 + 16 i + lr, columns n0 + wn0 + 16 j + 4 (lane >> 4) + 0..3
-    if constexpr (kQuant) {
+    if constexpr (kEpi == kEpiQuant) {
         quant_epilogue<T>(acc, qo, m0, m_end, n0, N, wave, wm0, wn0, lane, st.p[0]);
+        return;
+    }
+    if constexpr (kEpi == kEpiSwiglu) {
+        swiglu_quant_epilogue<T>(acc, qo, m0, m_end, n0, N, wave, wm0, wn0, lane, st);
         return;
     }
     const int cq = 4 * (lane >> 4);
@@ -621,8 +722,10 @@ __global__ __launch_bounds__(T::THREADS, 1) void gemm_big_kernel(const uint8_t* 
         gemm_tile_big<T, true>(a, as, b, bs, c, m0, M, (int64_t)tn * T::BN, N, K, lds);
 }
 
-// The same GEMM with act_quant of its output fused into the epilogue.
-template <class T>
+// The same GEMM with act_quant of its output (kEpi = kEpiQuant), or of the
+// gated activation of an interleaved [w1; w3] product (kEpiSwiglu), fused
+// into the epilogue.
+template <class T, int kEpi>
 __global__ __launch_bounds__(T::THREADS, 1) void gemm_quant_kernel(
     const uint8_t* __restrict__ a, const float* __restrict__ as, const uint8_t* __restrict__ b,
     const float* __restrict__ bs, uint8_t* __restrict__ q, float* __restrict__ qs, int64_t M,
@@ -633,9 +736,9 @@ __global__ __launch_bounds__(T::THREADS, 1) void gemm_quant_kernel(
     const int64_t m0 = (int64_t)tm * T::BM;
     const QuantOut qo{q, qs};
     if (m0 + T::BM <= M)
-        gemm_tile_big<T, false, true>(a, as, b, bs, nullptr, m0, M, (int64_t)tn * T::BN, N, K, lds, qo);
+        gemm_tile_big<T, false, kEpi>(a, as, b, bs, nullptr, m0, M, (int64_t)tn * T::BN, N, K, lds, qo);
     else
-        gemm_tile_big<T, true, true>(a, as, b, bs, nullptr, m0, M, (int64_t)tn * T::BN, N, K, lds, qo);
+        gemm_tile_big<T, true, kEpi>(a, as, b, bs, nullptr, m0, M, (int64_t)tn * T::BN, N, K, lds, qo);
 }
 
 // Persistent grouped kernel on the large tiles.
@@ -881,12 +984,12 @@ static void launch_big(const void* a, const float* as, const void* b, const floa
                        (const uint8_t*)a, as, (const uint8_t*)b, bs, (uint16_t*)c, M, N, K, mt, nt);
 }
 
-template <class T>
+template <class T, int kEpi = kEpiQuant>
 static hipError_t launch_quant(const void* a, const float* as, const void* b, const float* bs,
                                void* q, float* qs, int64_t M, int64_t N, int64_t K,
                                hipStream_t stream) {
     const int mt = (int)((M + T::BM - 1) / T::BM), nt = (int)((N + T::BN - 1) / T::BN);
-    hipLaunchKernelGGL(gemm_quant_kernel<T>, dim3(mt * nt), dim3(T::THREADS), 0, stream,
+    hipLaunchKernelGGL((gemm_quant_kernel<T, kEpi>), dim3(mt * nt), dim3(T::THREADS), 0, stream,
                        (const uint8_t*)a, as, (const uint8_t*)b, bs, (uint8_t*)q, qs, M, N, K, mt,
                        nt);
     return hipGetLastError();
@@ -959,6 +1062,12 @@ hipError_t launch_gemm_quant(const void* a, const float* as, const void* b, cons
             return launch_quant<BigMid>(a, as, b, bs, q, qs, M, N, K, stream);
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_swiglu_quant(const void* a, const float* as, const void* w13,
+                                    const float* s13, void* q, float* qs, int64_t M, int64_t n_out,
+                                    int64_t K, hipStream_t stream) {
+    return launch_quant<BigSquare, kEpiSwiglu>(a, as, w13, s13, q, qs, M, 2 * n_out, K, stream);
 }
 
 hipError_t launch_gemm_grouped(const void* a, const float* as, const void* b, const float* bs,

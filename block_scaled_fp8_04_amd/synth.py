@@ -8,7 +8,7 @@ Recipe (each choice is also listed in the design notes):
 
 * seeds: ``1000 * config + tensor_id`` on a CPU ``torch.Generator``; tensor ids
   0 = x, 1 = W1 values, 2 = W1 scales, 3 = W2 values, 4 = W2 scales,
-  5 = outlier mask, 6 = routing scores;
+  5 = outlier mask, 6 = routing scores, 7 = W3 values, 8 = W3 scales;
 * activations: float32 N(0,1), optionally with a Bernoulli(p) mask of entries
   multiplied by an outlier factor, then rounded to bf16 by torch;
 * weight scales: ``2**U`` with U uniform on ``[lo, hi]`` (log-uniform), fp32,
@@ -150,6 +150,8 @@ def make(config: int, scale: float = 1.0) -> Workload:
         t["x"] = activations(M, DIM, seed_of(2, 0))
         t["w1"], t["s1"] = weight(MOE_INTER, DIM, seed_of(2, 1), seed_of(2, 2))
         t["w2"], t["s2"] = weight(DIM, MOE_INTER, seed_of(2, 3), seed_of(2, 4))
+        # the gated expert's third projection (w3), for the fused gated-FFN step
+        t["w3"], t["s3"] = weight(MOE_INTER, DIM, seed_of(2, 7), seed_of(2, 8))
         wl.meta.update(M=M, N1=MOE_INTER, K1=DIM, N2=DIM, K2=MOE_INTER)
     elif config == 3:
         M = max(1, int(8192 * scale))

@@ -44,7 +44,7 @@ extern "C" {
 #endif
 
 #define BFP8_BLOCK 128
-#define BFP8_VERSION 4
+#define BFP8_VERSION 5
 #define BFP8_MOE_MAX_GROUPS 1024
 
 typedef enum bfp8_status {
@@ -120,6 +120,27 @@ int bfp8_gemm(const void* a, const float* a_s, const void* b, const float* b_s,
 int bfp8_gemm_act_quant(const void* a, const float* a_s, const void* b, const float* b_s,
                         void* q_e4m3, float* q_scales, int64_t M, int64_t N, int64_t K,
                         void* stream);
+
+/* The gated FFN's first projection with its activation and act_quant fused
+ * into the epilogue (the MLP/Expert modules' w1 and w3 ([DF]), then the next
+ * linear()'s act_quant).  The pages do not print the activation; this
+ * library reads it as SiLU, silu(x) = x / (1 + e^-x), with the rounding steps
+ * of a bf16 model:
+ *     g = bf16(x w1^T),  u = bf16(x w3^T)          (block-scaled fp8 GEMMs)
+ *     h = bf16( bf16( silu(g) ) * u )              (silu in fp32)
+ *     q, q_scales = act_quant(h)                   (128-element blocks)
+ * The weight is w1 and w3 interleaved by 64 rows: rows 128 t .. 128 t + 63
+ * of w13 are w1 rows 64 t .., rows 128 t + 64 .. 128 t + 127 are w3 rows
+ * 64 t .. (bfp8.interleave_w13 builds it once from w1, w3 and their scale
+ * grids).  Its scales are one per 64 weight rows: s13[2 t + 0, kb] =
+ * w1_s[t / 2, kb], s13[2 t + 1, kb] = w3_s[t / 2, kb].
+ *   a, a_s   : as bfp8_gemm (x quantized by act_quant)
+ *   w13      : e4m3 [2 N, K], 16-byte aligned     s13 : fp32 [2 N / 64, K/128]
+ *   q_e4m3   : e4m3 [M, N] output, 4-byte aligned q_scales : fp32 [M, N/128]
+ * Errors: as bfp8_gemm, and BFP8_ERR_SHAPE if N % 128 != 0. */
+int bfp8_gemm_swiglu_act_quant(const void* a, const float* a_s, const void* w13,
+                               const float* s13, void* q_e4m3, float* q_scales, int64_t M,
+                               int64_t N, int64_t K, void* stream);
 
 /* Bytes of fp32 workspace bfp8_gemm would use for split-K at this shape
  * (0 when the shape does not use split-K).  Pure host function. */

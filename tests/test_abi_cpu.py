@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert bfp8.bfp8_version() == 4
+    assert bfp8.bfp8_version() == 5
     for code in range(8):
         assert bfp8.bfp8_status_string(code)
     assert bfp8.bfp8_status_string(0) == "ok"
@@ -143,6 +143,35 @@ def test_gemm_act_quant_validation(lib):
     assert call(q=ctypes.c_void_p(0x10002)) == _lib.BFP8_ERR_ALIGN
     assert call(a=ODD) == _lib.BFP8_ERR_ALIGN
     assert call(a=None, M=0) == _lib.BFP8_OK
+
+
+def test_gemm_swiglu_act_quant_validation(lib):
+    f = lib.bfp8_gemm_swiglu_act_quant
+
+    def call(a=FAKE, a_s=FAKE, w=FAKE, s=FAKE, q=FAKE, qs=FAKE, M=64, N=256, K=256):
+        return f(a, a_s, w, s, q, qs, M, N, K, None)
+
+    assert call(N=192) == _lib.BFP8_ERR_SHAPE
+    assert call(K=64) == _lib.BFP8_ERR_SHAPE
+    for name in ("a", "a_s", "w", "s", "q", "qs"):
+        assert call(**{name: None}) == _lib.BFP8_ERR_NULL, name
+    assert call(q=ctypes.c_void_p(0x10002)) == _lib.BFP8_ERR_ALIGN
+    assert call(a=None, M=0) == _lib.BFP8_OK
+
+
+def test_interleave_w13_layout():
+    """The interleaved weight puts w1 and w3 in alternating 64-row groups, scales per group."""
+    import torch
+    N, K = 256, 256
+    w1 = torch.arange(N * K, dtype=torch.int64).reshape(N, K) % 251
+    w3 = (torch.arange(N * K, dtype=torch.int64).reshape(N, K) * 7 + 3) % 253
+    s1 = torch.arange(4, dtype=torch.float32).reshape(2, 2)
+    s3 = 10 + torch.arange(4, dtype=torch.float32).reshape(2, 2)
+    w13, s13 = bfp8.interleave_w13(w1, s1, w3, s3)
+    for t in range(N // 64):
+        assert torch.equal(w13[128 * t:128 * t + 64], w1[64 * t:64 * t + 64])
+        assert torch.equal(w13[128 * t + 64:128 * t + 128], w3[64 * t:64 * t + 64])
+        assert torch.equal(s13[2 * t], s1[t // 2]) and torch.equal(s13[2 * t + 1], s3[t // 2])
 
 
 def test_gemm_bf16_validation(lib):

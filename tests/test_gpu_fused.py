@@ -95,3 +95,53 @@ def test_fused_quant_dense_chain_full_size():
     q_a, s_a = bfp8.act_quant(x)
     rows = np.array([0, 1, 2047, 2048, 6000, 8191], np.int64)
     _case(q_a, s_a, w1, s1, "dense-mlp up 8192x18432x7168", rows)
+
+
+# ------------------------------------------------------------------- gated FFN
+
+def _swiglu_case(M, N, K, seed, what, rows=None):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(M, K, generator=g).to(torch.bfloat16).to(dev())
+    q_a, s_a = bfp8.act_quant(x)
+    w1, s1 = synth.weight(N, K, seed + 1, seed + 2)
+    w3, s3 = synth.weight(N, K, seed + 3, seed + 4)
+    w13, s13 = bfp8.interleave_w13(w1, s1, w3, s3)
+    announce(f"gemm_swiglu_act_quant {what} M={M} N={N} K={K}")
+    q = torch.full((M, N), 0x33, dtype=torch.uint8, device=dev())
+    qs = torch.full((M, N // BLOCK), -1.0, dtype=torch.float32, device=dev())
+    bfp8.bfp8_gemm_swiglu_act_quant(q_a, s_a, w13.to(dev()), s13.to(dev()), q, qs)
+    torch.cuda.synchronize()
+    r = np.arange(M) if rows is None else rows
+    qa, sa = u8(q_a), s_a.cpu().numpy()
+    c1 = oracle.gemm(qa, sa, w1.numpy(), s1.numpy(), rows=r)
+    c3 = oracle.gemm(qa, sa, w3.numpy(), s3.numpy(), rows=r)
+    h = oracle.bf16_to_f32(oracle.swiglu_bf16(c1, c3)).astype(np.float64)
+    # bound: the GEMM tolerance of g and u carried through silu(g) * u (|silu'| < 1.1),
+    # three bf16 roundings, then the e4m3 quantization of the block
+    tol1 = GEMM_REL * np.abs(c1) + GEMM_RMS * float(np.sqrt(np.mean(c1 ** 2)))
+    tol3 = GEMM_REL * np.abs(c3) + GEMM_RMS * float(np.sqrt(np.mean(c3 ** 2)))
+    silu = c1 / (1.0 + np.exp(-c1))
+    bh = 1.1 * np.abs(c3) * tol1 + np.abs(silu) * tol3 + 2.0 ** -6 * np.abs(h) + 1e-30
+    rt = torch.from_numpy(np.asarray(r)).to(dev())
+    qn, qsn = u8(q[rt]), qs[rt].cpu().numpy()
+    s_col = np.repeat(qsn.astype(np.float64), BLOCK, axis=1)
+    deq = _e4m3_values()[qn] * s_col
+    bound = bh + 2.0 ** -4 * (np.abs(h) + bh) + 2.0 ** -10 * s_col
+    err = np.abs(deq - h)
+    assert np.all(err <= bound), f"{what}: {int((err > bound).sum())} elements outside the bound"
+    amax = np.abs(h).reshape(len(r), -1, BLOCK).max(axis=2)
+    bmax = bh.reshape(len(r), -1, BLOCK).max(axis=2)
+    s_ref = np.maximum(amax, 1e-4) / 448.0
+    assert np.all(np.abs(qsn - s_ref) <= bmax / 448.0 + 1e-12), f"{what}: scales outside tolerance"
+    announce(f"{what}: worst err/bound {float(np.max(err / bound)):.3f}")
+
+
+def test_swiglu_quant_shapes():
+    _swiglu_case(256, 256, 256, 1200, "one tile")
+    _swiglu_case(300, 640, 512, 1210, "ragged M, five tiles")
+    _swiglu_case(1, 128, 128, 1220, "single row")
+
+
+def test_swiglu_quant_expert_shape():
+    """One routed expert's gated FFN input projection at its real shape: 4096 x (2 x 2048) x 7168."""
+    _swiglu_case(4096, 2048, 7168, 1230, "expert 4096x2048x7168", rows=sample_rows(4096, 12, 1231))
