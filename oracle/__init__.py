@@ -58,6 +58,8 @@ class Oracle:
         lib.oracle_gemm_bf16_rows.argtypes = [P, P, I64, I64, I64, P, I64, P, ctypes.c_int]
         lib.oracle_gemm_bf16_rows.restype = ctypes.c_int
         lib.oracle_swiglu_bf16.argtypes = [P, P, I64, P]
+        lib.oracle_act_quant_pow2.argtypes = [P, P, P, I64, I64]
+        lib.oracle_act_quant_pow2.restype = ctypes.c_int
         lib.oracle_moe_dispatch.argtypes = [P, I64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                             P, P, P]
         lib.oracle_moe_combine.argtypes = [P, P, P, I64, ctypes.c_int32, I64, P]
@@ -189,6 +191,16 @@ class Oracle:
             raise ValueError(f"oracle_gemm_bf16_rows failed ({rc})")
         return out
 
+    def act_quant_pow2(self, x_bits):
+        """act_quant with scales rounded up to powers of two (the e8m0 reading of scale_fmt)."""
+        x = _c(x_bits, np.uint16)
+        M, K = x.shape
+        q = np.empty((M, K), np.uint8)
+        s = np.empty((M, K // BLOCK), np.float32)
+        if self.lib.oracle_act_quant_pow2(_ptr(x), _ptr(q), _ptr(s), M, K):
+            raise ValueError("K must be a positive multiple of 128")
+        return q, s
+
     def swiglu_bf16(self, g, u) -> np.ndarray:
         """bf16 bits of bf16(bf16(silu(bf16(g))) * bf16(u)) for fp64 arrays g, u of one shape."""
         g = _c(g, np.float64); u = _c(u, np.float64)
@@ -298,6 +310,10 @@ def gemm_grouped(a, sa, b, sb, offsets, rows=None, threads=None):
 
 def gemm_bf16(a_bits, b_bits, rows=None, threads=None):
     return default().gemm_bf16(a_bits, b_bits, rows, threads)
+
+
+def act_quant_pow2(x_bits):
+    return default().act_quant_pow2(x_bits)
 
 
 def swiglu_bf16(g, u):

@@ -168,6 +168,41 @@ int oracle_act_quant(const uint16_t* x, uint8_t* q, float* s, int64_t M, int64_t
     return 0;
 }
 
+/* act_quant with power-of-two scales: the reading of the model's scale_fmt
+ * field ("Data flow", config data flows: scale_fmt is a ModelArgs field; its
+ * meaning is not on the pages).  Reading: the block scale max(amax, floor)/448
+ * (an fp32 division, as above) is rounded UP to the next power of two, so
+ * every quotient still fits the e4m3 range; the scale is then exactly
+ * representable as an unsigned 8-bit exponent (e8m0).  The power is found
+ * with frexp: y = f 2^e with f in [0.5, 1), so 2^e is the smallest power of
+ * two >= y unless f == 0.5 (y itself a power of two). */
+int oracle_act_quant_pow2(const uint16_t* x, uint8_t* q, float* s, int64_t M, int64_t K) {
+    if (K <= 0 || K % ORACLE_BLOCK != 0 || M < 0) return -1;
+    int64_t KB = K / ORACLE_BLOCK;
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t kb = 0; kb < KB; ++kb) {
+            const uint16_t* xb = x + m * K + kb * ORACLE_BLOCK;
+            uint8_t* qb = q + m * K + kb * ORACLE_BLOCK;
+            float amax = 0.0f;
+            for (int j = 0; j < ORACLE_BLOCK; ++j) {
+                float a = fabsf(oracle_bf16_to_f32(xb[j]));
+                if (a > amax) amax = a;
+            }
+            float clamped = amax < ORACLE_AMAX_FLOOR ? ORACLE_AMAX_FLOOR : amax;
+            float y = clamped / ORACLE_E4M3_MAX;
+            int e;
+            double f = frexp((double)y, &e);
+            float scale = (float)ldexp(1.0, f == 0.5 ? e - 1 : e);
+            for (int j = 0; j < ORACLE_BLOCK; ++j) {
+                float quotient = oracle_bf16_to_f32(xb[j]) / scale;
+                qb[j] = oracle_e4m3_encode(quotient);
+            }
+            s[m * KB + kb] = scale;
+        }
+    }
+    return 0;
+}
+
 /* -------------------------------------------------------- weight_dequant */
 
 /* out[n,k] = bf16( e4m3_value(w[n,k]) * S[n/128][k/128] ), the product

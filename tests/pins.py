@@ -618,6 +618,45 @@ def pin_swiglu_identities(orc):
     assert np.array_equal(h4, 4.0 * h1)
 
 
+# ------------------------------------------------------- power-of-two scale pins
+#
+# scale_fmt is a ModelArgs field whose meaning the pages do not give; the
+# oracle's reading is "scale rounded up to a power of two".  These pins tie the
+# oracle to that reading through independent numpy/torch arithmetic.
+
+def pin_act_quant_pow2_vs_numpy(orc):
+    """P1: scale = 2^ceil(log2(fl32(max(amax, 1e-4) / 448))) (numpy), codes = torch's e4m3 cast
+    of x / scale (exact: a power-of-two division), with outliers, tiny and zero blocks."""
+    rng = np.random.default_rng(1300)
+    x = rng.standard_normal((12, 640)).astype(np.float32) * np.exp2(rng.integers(-20, 20, (12, 1)))
+    x[3, :128] = 0.0
+    x[4, 128:256] = 1e-6
+    x[5, 5] = 3e4
+    xb = torch_bf16(x).reshape(x.shape)
+    q, s = orc.act_quant_pow2(xb)
+    xf = bf16_bits_to_f32(xb).reshape(12, 5, 128)
+    amax = np.abs(xf).max(axis=2)
+    y = (np.maximum(amax, np.float32(1e-4)) / np.float32(448.0)).astype(np.float32)
+    s_ref = np.exp2(np.ceil(np.log2(y.astype(np.float64)))).astype(np.float32)
+    assert np.array_equal(s, s_ref)
+    codes = torch_e4m3_cast((xf / s_ref[:, :, None]).reshape(12, 640))
+    assert np.array_equal(q, codes.reshape(12, 640))
+
+
+def pin_act_quant_pow2_bounds(orc):
+    """P2: the power-of-two scale is within [y, 2y) of the plain scale y, and no code
+    saturates below the block max (max |code value| <= 448, > 224)."""
+    x = _rand_bf16(20, 384, 1301)
+    q, s = orc.act_quant_pow2(x)
+    q0, s0 = orc.act_quant(x)
+    assert np.all(s >= s0) and np.all(s < 2 * s0)
+    m, e = np.frexp(s.astype(np.float64))
+    assert np.all(m == 0.5)
+    vals = torch_e4m3_values()[q].reshape(20, 3, 128)
+    mx = np.abs(vals).max(axis=2)
+    assert np.all(mx <= 448.0) and np.all(mx > 224.0 - 1e-9)
+
+
 # ------------------------------------------------------ MoE dispatch / combine pins
 #
 # Source: "Behavior traces - deepseek-ai/DeepSeek-V3" (codevetter), MoE trace

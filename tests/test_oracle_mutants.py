@@ -16,6 +16,10 @@ import pins
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "bfp8_oracle.c")
 
 MUTANTS = {
+    # power-of-two scale rounded down instead of up
+    "pow2_round_down": ("float scale = (float)ldexp(1.0, f == 0.5 ? e - 1 : e);", "float scale = (float)ldexp(1.0, e - 1);"),
+    # power-of-two scale one octave too large for exact powers
+    "pow2_exact_power": ("float scale = (float)ldexp(1.0, f == 0.5 ? e - 1 : e);", "float scale = (float)ldexp(1.0, e);"),
     # gated FFN: sigmoid of the wrong sign
     "swiglu_sign": ("const double sg = gb / (1.0 + exp(-gb));", "const double sg = gb / (1.0 + exp(gb));"),
     # gated FFN: the activation's bf16 rounding skipped
