@@ -21,7 +21,7 @@ times the CPU oracle on a bounded, proportional sample of the same step.
 Other workloads (parity-test shapes, measured on demand): --workload tiny |
 decode | moe-pair | dense-mlp-unfused | grouped | moe-layer | bf16-branch |
 expert-ffn (one expert's gated FFN with the SiLU gate and act_quant fused into the
-[w1; w3] GEMM's epilogue).  moe-layer is the routed
+[w1; w3] GEMM's epilogue) | dense-mlp-ue8m0 (power-of-two scales applied by the MFMA).  moe-layer is the routed
 experts of one GPU end to end on the device: moe_dispatch(topk) ->
 act_quant_rows(x, row_token) -> grouped GEMM (row buffers sized for T*k rows)
 -> moe_combine (weighted sum back to token order).
@@ -49,7 +49,7 @@ PEAK_HBM_GBS = 8000.0             # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0         # MI355X dense bf16 MFMA (no sparsity)
 
 WORKLOADS = {"tiny": 0, "decode": 1, "moe-pair": 2, "dense-mlp": 3, "grouped": 4, "moe-layer": 4,
-             "bf16-branch": 3, "dense-mlp-unfused": 3, "expert-ffn": 2}
+             "bf16-branch": 3, "dense-mlp-unfused": 3, "expert-ffn": 2, "dense-mlp-ue8m0": 3}
 
 
 # ------------------------------------------------------------------ accounting
@@ -88,7 +88,7 @@ class Step:
         self.dev = dev
         t = wl.tensors
         c = wl.config
-        if kind in ("moe-layer", "bf16-branch", "dense-mlp", "expert-ffn"):
+        if kind in ("moe-layer", "bf16-branch", "dense-mlp", "expert-ffn", "dense-mlp-ue8m0"):
             c = kind
         self.launches = []            # (name, callable, flops, bytes, bound)
         self.hashes = {}
@@ -202,6 +202,33 @@ class Step:
             ]
             self.shape = dict(M=M, N_gate_up=2 * N1, N_out=N1, K1=K1, N2=N2, K2=K2, activation="silu (stated reading)")
             self.dominant, self.dominant_kernel = ["fp8_gemm_w13_swiglu_quant"], "gemm"
+        elif c == "dense-mlp-ue8m0":
+            # the dense chain with power-of-two scales (weights re-drawn from the same seeds with
+            # their block scales rounded to powers of two), scales applied by the MFMA
+            M, N1, K1, N2, K2 = (wl.meta[k] for k in ("M", "N1", "K1", "N2", "K2"))
+            w1, s1 = synth.weight(N1, K1, synth.seed_of(3, 1), synth.seed_of(3, 2), pow2=True)
+            w2, s2 = synth.weight(N2, K2, synth.seed_of(3, 3), synth.seed_of(3, 4), pow2=True)
+            self.hashes.update(w1_pow2=sha_of(w1), s1_pow2=sha_of(s1), w2_pow2=sha_of(w2), s2_pow2=sha_of(s2))
+            x = t["x"].to(dev)
+            w1, s1, w2, s2 = w1.to(dev), s1.to(dev), w2.to(dev), s2.to(dev)
+            q = torch.empty(M, K1, dtype=torch.uint8, device=dev)
+            qs = torch.empty(M, K1 // BLOCK, dtype=torch.float32, device=dev)
+            h = torch.empty(M, N1, dtype=torch.bfloat16, device=dev)
+            qh = torch.empty(M, K2, dtype=torch.uint8, device=dev)
+            qhs = torch.empty(M, K2 // BLOCK, dtype=torch.float32, device=dev)
+            y = torch.empty(M, N2, dtype=torch.bfloat16, device=dev)
+            self.launches += [
+                ("act_quant_ue8m0_x", lambda: bfp8.bfp8_act_quant_ue8m0(x, q, qs), 0,
+                 act_quant_bytes(M, K1), "hbm"),
+                ("fp8_gemm_ue8m0_1", lambda: bfp8.bfp8_gemm_ue8m0(q, qs, w1, s1, h), 2 * M * N1 * K1,
+                 gemm_bytes(M, N1, K1), "mfma"),
+                ("act_quant_ue8m0_h", lambda: bfp8.bfp8_act_quant_ue8m0(h, qh, qhs), 0,
+                 act_quant_bytes(M, K2), "hbm"),
+                ("fp8_gemm_ue8m0_2", lambda: bfp8.bfp8_gemm_ue8m0(qh, qhs, w2, s2, y), 2 * M * N2 * K2,
+                 gemm_bytes(M, N2, K2), "mfma"),
+            ]
+            self.shape = dict(M=M, N1=N1, K1=K1, N2=N2, K2=K2, scales="powers of two (e8m0)")
+            self.dominant, self.dominant_kernel = ["fp8_gemm_ue8m0_1", "fp8_gemm_ue8m0_2"], "gemm_ue8m0"
         elif c == "bf16-branch":
             M, N1, K1, N2, K2 = (wl.meta[k] for k in ("M", "N1", "K1", "N2", "K2"))
             x = t["x"].to(dev)
@@ -465,7 +492,8 @@ def main():
         cpu = cpu_baseline(wl, args.cpu_seconds, args.workload)
 
     wl_name = (f"{args.workload}-{wl.name}"
-               if args.workload in ("moe-layer", "bf16-branch", "dense-mlp-unfused", "expert-ffn") else wl.name)
+               if args.workload in ("moe-layer", "bf16-branch", "dense-mlp-unfused", "expert-ffn",
+                                    "dense-mlp-ue8m0") else wl.name)
     config = {"workload": wl_name, "shape": step.shape,
               "step": " -> ".join(l[0] for l in step.launches),
               "value_definition": "GEMM FLOP per step / wall time per step",

@@ -30,7 +30,8 @@ EXPORTS = ("bfp8_act_quant", "bfp8_weight_dequant", "bfp8_gemm", "bfp8_gemm_work
            "bfp8_gemm_grouped", "bfp8_e4m3_encode_range", "bfp8_bf16_round_range",
            "bfp8_gemm_kernel_name", "bfp8_moe_dispatch_workspace_size", "bfp8_moe_dispatch",
            "bfp8_act_quant_rows", "bfp8_moe_combine", "bfp8_gemm_bf16",
-           "bfp8_gemm_act_quant", "bfp8_gemm_swiglu_act_quant",
+           "bfp8_gemm_act_quant", "bfp8_gemm_swiglu_act_quant", "bfp8_act_quant_ue8m0",
+           "bfp8_gemm_ue8m0",
            "bfp8_status_string", "bfp8_version")
 
 _lib = None
@@ -80,6 +81,10 @@ def library():
     lib.bfp8_gemm_act_quant.restype = ctypes.c_int
     lib.bfp8_gemm_swiglu_act_quant.argtypes = [P, P, P, P, P, P, I64, I64, I64, P]
     lib.bfp8_gemm_swiglu_act_quant.restype = ctypes.c_int
+    lib.bfp8_act_quant_ue8m0.argtypes = [P, P, P, I64, I64, P]
+    lib.bfp8_act_quant_ue8m0.restype = ctypes.c_int
+    lib.bfp8_gemm_ue8m0.argtypes = [P, P, P, P, P, I64, I64, I64, P]
+    lib.bfp8_gemm_ue8m0.restype = ctypes.c_int
     lib.bfp8_gemm_bf16.argtypes = [P, P, P, I64, I64, I64, P]
     lib.bfp8_gemm_bf16.restype = ctypes.c_int
     lib.bfp8_status_string.argtypes = [ctypes.c_int]
@@ -157,6 +162,31 @@ def bfp8_act_quant(x, q, scales, stream=None):
     _need(q.shape == (M, K) and scales.shape == (M, K // BLOCK), "output shapes do not match x")
     _check("bfp8_act_quant", library().bfp8_act_quant(_ptr(x), _ptr(q), _ptr(scales), M, K,
                                                       _stream(stream, x.device)))
+
+
+def bfp8_act_quant_ue8m0(x, q, scales, stream=None):
+    """act_quant with power-of-two scales (the e8m0 reading of scale_fmt)."""
+    q = _bytes_view(q)
+    _cuda_contig(x, q, scales)
+    _need(x.dtype == torch.bfloat16 and scales.dtype == torch.float32, "x must be bf16, scales fp32")
+    M, K = x.shape
+    _need(q.shape == (M, K) and scales.shape == (M, K // BLOCK), "output shapes do not match x")
+    _check("bfp8_act_quant_ue8m0", library().bfp8_act_quant_ue8m0(_ptr(x), _ptr(q), _ptr(scales), M, K,
+                                                                  _stream(stream, x.device)))
+
+
+def bfp8_gemm_ue8m0(a, a_s, b, b_s, c, stream=None):
+    """bfp8_gemm for power-of-two scales, applied by the MFMA itself."""
+    a, b = _bytes_view(a), _bytes_view(b)
+    _cuda_contig(a, a_s, b, b_s, c)
+    M, K = a.shape
+    N = b.shape[0]
+    _need(b.shape[1] == K, "a and b must share K")
+    _need(a_s.shape == (M, K // BLOCK) and b_s.shape == (-(-N // BLOCK), K // BLOCK),
+          "a_s [M, K/128], b_s [ceil(N/128), K/128]")
+    _need(c.dtype == torch.bfloat16 and c.shape == (M, N), "c must be bf16 [M, N]")
+    _check("bfp8_gemm_ue8m0", library().bfp8_gemm_ue8m0(_ptr(a), _ptr(a_s), _ptr(b), _ptr(b_s), _ptr(c),
+                                                        M, N, K, _stream(stream, a.device)))
 
 
 def bfp8_weight_dequant(w, s, out, stream=None):
@@ -392,6 +422,20 @@ def gemm_swiglu_act_quant(a, a_s, w13, s13, stream=None):
     qs = torch.empty((M, N // BLOCK), dtype=torch.float32, device=a.device)
     bfp8_gemm_swiglu_act_quant(a, a_s, w13, s13, q, qs, stream)
     return q, qs
+
+
+def act_quant_ue8m0(x, stream=None):
+    M, K = x.shape
+    q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    s = torch.empty((M, K // BLOCK), dtype=torch.float32, device=x.device)
+    bfp8_act_quant_ue8m0(x, q, s, stream)
+    return q, s
+
+
+def gemm_ue8m0(a, a_s, b, b_s, stream=None):
+    c = torch.empty((a.shape[0], b.shape[0]), dtype=torch.bfloat16, device=a.device)
+    bfp8_gemm_ue8m0(a, a_s, b, b_s, c, stream)
+    return c
 
 
 def linear_fp8(x, w, w_s, workspace=None, stream=None):

@@ -357,7 +357,10 @@ __device__ __forceinline__ void swiglu_quant_epilogue(v4f (&acc)[T::TM][T::TN], 
     }
 }
 
-template <class T, bool kGuard, int kEpi = kEpiBf16>
+// kHwScale: every activation and weight scale is a power of two (the e8m0
+// reading of scale_fmt), so the MFMA applies them itself (its per-row e8m0
+// scale operands) and accumulates across K blocks with no fold.
+template <class T, bool kGuard, int kEpi = kEpiBf16, bool kHwScale = false>
 __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
                                               const float* __restrict__ as,
                                               const uint8_t* __restrict__ b,
@@ -504,13 +507,53 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
             wait_vmcnt<0>();
         barrier_lds();
         const bool more = kb + T::NSTAGE - 1 < KB;
-        if ((kGuard || !kSpread) && more) issue(kb + T::NSTAGE - 1, st.p[SF]);
+        // (the spread issue lives in the full-tile fold loop; other loops issue here)
+        if ((kGuard || !kSpread || kHwScale) && more) issue(kb + T::NSTAGE - 1, st.p[SF]);
 
         const uint8_t* As = st.p[S];
         const uint8_t* Bs = As + T::A_BYTES;
         const float* Ss = (const float*)(Bs + T::B_BYTES);
         const float* Sb = (const float*)(Bs + T::B_BYTES + T::SB_OFF);
-        if (!kGuard) {
+        if constexpr (kHwScale) {
+            // scale operands: the weight first (uniform over the wave's columns), the
+            // activation second (lane l: row 16 i + (l & 15)); e8m0 byte = fp32 exponent
+            v8i fb[T::TN];
+#pragma unroll
+            for (int j = 0; j < T::TN; ++j) {
+                const uint8_t* q = Bs + (wn0 + 16 * j + lr) * kBlock;
+                fb[j] = frag_from(*(const uint4*)(q + off0), *(const uint4*)(q + off1));
+            }
+            const int eb = (int)(__float_as_uint(Sb[sb_slot]) >> 23);
+            int ea[T::TM];
+#pragma unroll
+            for (int i = 0; i < T::TM; i += 4) {
+                const v4f s4 = *(const v4f*)(Ss + sread + i);
+                ea[i] = (int)(__float_as_uint(s4[0]) >> 23);
+                ea[i + 1] = (int)(__float_as_uint(s4[1]) >> 23);
+                ea[i + 2] = (int)(__float_as_uint(s4[2]) >> 23);
+                ea[i + 3] = (int)(__float_as_uint(s4[3]) >> 23);
+            }
+            v8i fa_nxt;
+            {
+                const uint8_t* r = As + (wm0 + lr) * kBlock;
+                fa_nxt = frag_from(*(const uint4*)(r + off0), *(const uint4*)(r + off1));
+            }
+#pragma unroll
+            for (int i = 0; i < T::TM; ++i) {
+                const v8i fa = fa_nxt;
+                if (i + 1 < T::TM) {
+                    const uint8_t* r = As + (wm0 + 16 * (i + 1) + lr) * kBlock;
+                    fa_nxt = frag_from(*(const uint4*)(r + off0), *(const uint4*)(r + off1));
+                }
+                if (!kGuard || i < tm_valid) {
+#pragma unroll
+                    for (int j = 0; j < T::TN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            fb[j], fa, acc[i][j], 0, 0, 0, eb, 0, ea[i]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else if (!kGuard) {
             // The K block as a fixed sequence of small scheduling regions
             // (sched_barrier keeps the compiler from reordering across them):
             // a wave starts multiplying once A row 0 and B fragment 0 are in
@@ -720,6 +763,22 @@ __global__ __launch_bounds__(T::THREADS, 1) void gemm_big_kernel(const uint8_t* 
         gemm_tile_big<T, false>(a, as, b, bs, c, m0, M, (int64_t)tn * T::BN, N, K, lds);
     else
         gemm_tile_big<T, true>(a, as, b, bs, c, m0, M, (int64_t)tn * T::BN, N, K, lds);
+}
+
+// The GEMM with power-of-two scales applied by the MFMA (kHwScale).
+template <class T>
+__global__ __launch_bounds__(T::THREADS, 1) void gemm_ue8m0_kernel(
+    const uint8_t* __restrict__ a, const float* __restrict__ as, const uint8_t* __restrict__ b,
+    const float* __restrict__ bs, uint16_t* __restrict__ c, int64_t M, int64_t N, int64_t K, int mt,
+    int nt) {
+    BIG_TILE_STAGES(T, lds);
+    int tm, tn;
+    tile_of(blockIdx.x, gridDim.x, mt, nt, tm, tn);
+    const int64_t m0 = (int64_t)tm * T::BM;
+    if (m0 + T::BM <= M)
+        gemm_tile_big<T, false, kEpiBf16, true>(a, as, b, bs, c, m0, M, (int64_t)tn * T::BN, N, K, lds);
+    else
+        gemm_tile_big<T, true, kEpiBf16, true>(a, as, b, bs, c, m0, M, (int64_t)tn * T::BN, N, K, lds);
 }
 
 // The same GEMM with act_quant of its output (kEpi = kEpiQuant), or of the
@@ -1060,6 +1119,25 @@ hipError_t launch_gemm_quant(const void* a, const float* as, const void* b, cons
             return launch_quant<BigWide>(a, as, b, bs, q, qs, M, N, K, stream);
         case GemmConfig::kBig128x128:
             return launch_quant<BigMid>(a, as, b, bs, q, qs, M, N, K, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <class T>
+static hipError_t launch_ue8m0(const void* a, const float* as, const void* b, const float* bs,
+                               void* c, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+    const int mt = (int)((M + T::BM - 1) / T::BM), nt = (int)((N + T::BN - 1) / T::BN);
+    hipLaunchKernelGGL(gemm_ue8m0_kernel<T>, dim3(mt * nt), dim3(T::THREADS), 0, stream,
+                       (const uint8_t*)a, as, (const uint8_t*)b, bs, (uint16_t*)c, M, N, K, mt, nt);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_ue8m0(const void* a, const float* as, const void* b, const float* bs,
+                             void* c, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+    switch (gemm_config(M, N, K)) {
+        case GemmConfig::kBig256x256: return launch_ue8m0<BigSquare>(a, as, b, bs, c, M, N, K, stream);
+        case GemmConfig::kBig256x128: return launch_ue8m0<BigWide>(a, as, b, bs, c, M, N, K, stream);
+        case GemmConfig::kBig128x128: return launch_ue8m0<BigMid>(a, as, b, bs, c, M, N, K, stream);
     }
     return hipErrorInvalidValue;
 }

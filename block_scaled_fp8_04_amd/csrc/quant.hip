@@ -24,7 +24,17 @@
 
 namespace bfp8 {
 
-template <bool kHw>
+// Power-of-two scale (the e8m0 reading of the model's scale_fmt): the scale
+// max(amax, floor) / 448 rounded up to the next power of two, taken from its
+// fp32 bits (biased exponent, plus one when any mantissa bit is set).  The
+// quotient by it is then an exact scaling.
+__device__ __forceinline__ float pow2_ceil(float y) {
+    uint32_t e = __float_as_uint(y) >> 23;
+    if (__float_as_uint(y) & 0x7FFFFFu) e += 1;
+    return __uint_as_float(e << 23);
+}
+
+template <bool kHw, bool kPow2 = false>
 __device__ __forceinline__ void quant_block_part(const uint4 v0, const uint4 v1, int lane8,
                                                  uint4& out, float& scale) {
     float f[16];
@@ -40,7 +50,8 @@ __device__ __forceinline__ void quant_block_part(const uint4 v0, const uint4 v1,
     amax = fmaxf(amax, __shfl_xor(amax, 1, 8));
     amax = fmaxf(amax, __shfl_xor(amax, 2, 8));
     amax = fmaxf(amax, __shfl_xor(amax, 4, 8));
-    const float s = fmaxf(amax, kAmaxFloor) / kE4m3Max;  // correctly rounded
+    float s = fmaxf(amax, kAmaxFloor) / kE4m3Max;        // correctly rounded
+    if (kPow2) s = pow2_ceil(s);
     const float r = 1.0f / s;
     float y[16];
 #pragma unroll
@@ -54,7 +65,7 @@ __device__ __forceinline__ void quant_block_part(const uint4 v0, const uint4 v1,
 }
 
 // x: nblocks * 16 uint4 (256 B per block); q: nblocks * 8 uint4; s: nblocks floats.
-template <bool kHw>
+template <bool kHw, bool kPow2 = false>
 __global__ __launch_bounds__(256) void act_quant_kernel(const uint4* __restrict__ x,
                                                         uint4* __restrict__ q,
                                                         float* __restrict__ s,
@@ -72,8 +83,8 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint4* __restrict_
         const uint4 b1 = load_nt(p1 + 1);
         uint4 qa, qb;
         float sa, sb;
-        quant_block_part<kHw>(a0, a1, lane8, qa, sa);
-        quant_block_part<kHw>(b0, b1, lane8, qb, sb);
+        quant_block_part<kHw, kPow2>(a0, a1, lane8, qa, sa);
+        quant_block_part<kHw, kPow2>(b0, b1, lane8, qb, sb);
         q[blk * 8 + lane8] = qa;
         q[(blk + groups) * 8 + lane8] = qb;
         if (lane8 == 0) {
@@ -87,7 +98,7 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint4* __restrict_
         const uint4 a1 = load_nt(p0 + 1);
         uint4 qa;
         float sa;
-        quant_block_part<kHw>(a0, a1, lane8, qa, sa);
+        quant_block_part<kHw, kPow2>(a0, a1, lane8, qa, sa);
         q[blk * 8 + lane8] = qa;
         if (lane8 == 0) s[blk] = sa;
     }
@@ -233,6 +244,17 @@ hipError_t launch_act_quant_rows(const void* x, int64_t T, const int32_t* row_to
     const int grid = (int)(wg_needed < wg_cap ? (wg_needed > 0 ? wg_needed : 1) : wg_cap);
     hipLaunchKernelGGL(act_quant_rows_kernel<kActQuantHwEncode>, dim3(grid), dim3(256), 0, stream,
                        (const uint4*)x, T, row_token, num_rows, (uint4*)q, s, M, KB);
+    return hipGetLastError();
+}
+
+hipError_t launch_act_quant_pow2(const void* x, void* q, float* s, int64_t M, int64_t K,
+                                 hipStream_t stream) {
+    const int64_t nblocks = M * (K / kBlock);
+    const int64_t wg_needed = (nblocks + 63) / 64;
+    const int64_t wg_cap = (int64_t)device_cu_count() * 8;
+    const int grid = (int)(wg_needed < wg_cap ? (wg_needed > 0 ? wg_needed : 1) : wg_cap);
+    hipLaunchKernelGGL((act_quant_kernel<kActQuantHwEncode, true>), dim3(grid), dim3(256), 0, stream,
+                       (const uint4*)x, (uint4*)q, s, nblocks);
     return hipGetLastError();
 }
 

@@ -75,9 +75,14 @@ def weight_codes(N: int, K: int, scales: torch.Tensor, seed: int) -> torch.Tenso
 
 
 def weight(N: int, K: int, value_seed: int, scale_seed: int, lo: float = -8.0,
-           hi: float = -2.0):
-    """(codes uint8 [N,K], scales fp32 [ceil(N/128), ceil(K/128)])."""
+           hi: float = -2.0, pow2: bool = False):
+    """(codes uint8 [N,K], scales fp32 [ceil(N/128), ceil(K/128)]).
+
+    pow2: the scales are rounded to the nearest power of two (a checkpoint with
+    power-of-two block scales)."""
     S = block_scales(-(-N // BLOCK), -(-K // BLOCK), scale_seed, lo, hi)
+    if pow2:
+        S = torch.exp2(torch.round(torch.log2(S.double()))).to(torch.float32)
     return weight_codes(N, K, S, value_seed), S
 
 

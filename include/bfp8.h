@@ -44,7 +44,7 @@ extern "C" {
 #endif
 
 #define BFP8_BLOCK 128
-#define BFP8_VERSION 5
+#define BFP8_VERSION 6
 #define BFP8_MOE_MAX_GROUPS 1024
 
 typedef enum bfp8_status {
@@ -141,6 +141,29 @@ int bfp8_gemm_act_quant(const void* a, const float* a_s, const void* b, const fl
 int bfp8_gemm_swiglu_act_quant(const void* a, const float* a_s, const void* w13,
                                const float* s13, void* q_e4m3, float* q_scales, int64_t M,
                                int64_t N, int64_t K, void* stream);
+
+/* Power-of-two scales: the library's reading of the model's scale_fmt field
+ * ([DF] config data flows: scale_fmt is a ModelArgs field; the pages do not
+ * say what it means).  Reading: each block scale is rounded UP to a power of
+ * two (an unsigned 8-bit exponent, "ue8m0"), so every quotient stays in the
+ * e4m3 range and the scales can be applied by the hardware.
+ *
+ * bfp8_act_quant_ue8m0: as bfp8_act_quant, but
+ *     s = 2^ceil(log2( max(amax, 1e-4f) / 448 ))   (the fp32 quotient rounded up
+ *                                                   to a power of two, exactly)
+ * Same arguments, layouts and errors as bfp8_act_quant. */
+int bfp8_act_quant_ue8m0(const void* x_bf16, void* q_e4m3, float* scales, int64_t M, int64_t K,
+                         void* stream);
+
+/* bfp8_gemm_ue8m0: fp8_gemm for power-of-two activation and weight scales.
+ * The MFMA applies the scales (its e8m0 scale operands) and accumulates the
+ * scaled block products directly, with no per-block fold:
+ *     c[m, n] = bf16_rne( sum_kb P_kb[m, n] * a_s[m, kb] * b_s[n/128, kb] )
+ * Every scale must be a power of two in [2^-127, 2^127] stored as fp32 (as
+ * bfp8_act_quant_ue8m0 writes); for any other value only its exponent is used.
+ * Same arguments, layouts and errors as bfp8_gemm without a workspace. */
+int bfp8_gemm_ue8m0(const void* a, const float* a_s, const void* b, const float* b_s,
+                    void* c_bf16, int64_t M, int64_t N, int64_t K, void* stream);
 
 /* Bytes of fp32 workspace bfp8_gemm would use for split-K at this shape
  * (0 when the shape does not use split-K).  Pure host function. */

@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert bfp8.bfp8_version() == 5
+    assert bfp8.bfp8_version() == 6
     for code in range(8):
         assert bfp8.bfp8_status_string(code)
     assert bfp8.bfp8_status_string(0) == "ok"
@@ -172,6 +172,19 @@ def test_interleave_w13_layout():
         assert torch.equal(w13[128 * t:128 * t + 64], w1[64 * t:64 * t + 64])
         assert torch.equal(w13[128 * t + 64:128 * t + 128], w3[64 * t:64 * t + 64])
         assert torch.equal(s13[2 * t], s1[t // 2]) and torch.equal(s13[2 * t + 1], s3[t // 2])
+
+
+def test_ue8m0_validation(lib):
+    f = lib.bfp8_act_quant_ue8m0
+    assert f(FAKE, FAKE, FAKE, 4, 100, None) == _lib.BFP8_ERR_SHAPE
+    assert f(None, FAKE, FAKE, 4, 128, None) == _lib.BFP8_ERR_NULL
+    assert f(ODD, FAKE, FAKE, 4, 128, None) == _lib.BFP8_ERR_ALIGN
+    assert f(None, None, None, 0, 128, None) == _lib.BFP8_OK
+    g = lib.bfp8_gemm_ue8m0
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 64, 200, None) == _lib.BFP8_ERR_SHAPE
+    assert g(FAKE, None, FAKE, FAKE, FAKE, 64, 64, 256, None) == _lib.BFP8_ERR_NULL
+    assert g(ODD, FAKE, FAKE, FAKE, FAKE, 64, 64, 256, None) == _lib.BFP8_ERR_ALIGN
+    assert g(None, FAKE, FAKE, FAKE, FAKE, 0, 64, 256, None) == _lib.BFP8_OK
 
 
 def test_gemm_bf16_validation(lib):

@@ -1,0 +1,77 @@
+"""GPU parity of the power-of-two-scale path (the e8m0 reading of scale_fmt).
+
+act_quant_ue8m0 is bit-exact against the oracle; the hardware-scaled GEMM is
+within the path's GEMM tolerance of the oracle's fp64 product on the same
+codes and (power-of-two) scales.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import block_scaled_fp8_04_amd as bfp8
+from block_scaled_fp8_04_amd import synth
+from gpu_helpers import announce, bits16, dev, gemm_check, sample_rows, u8, workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _aq_case(x, what):
+    announce(f"act_quant_ue8m0 {what} {tuple(x.shape)}")
+    q, s = bfp8.act_quant_ue8m0(x.to(dev()))
+    torch.cuda.synchronize()
+    rq, rs = oracle.act_quant_pow2(bits16(x))
+    assert np.array_equal(u8(q), rq), f"{what}: codes differ"
+    assert np.array_equal(s.cpu().numpy(), rs), f"{what}: scales differ"
+    m, _ = np.frexp(rs.astype(np.float64))
+    assert np.all(m == 0.5), f"{what}: a scale is not a power of two"
+
+
+def test_act_quant_ue8m0_workloads():
+    for cfg in (0, 1):
+        _aq_case(workload(cfg).tensors["x"], f"config {cfg}")
+    _aq_case(workload(3).tensors["x"][:1024], "dense x, first 1024 rows")
+
+
+def test_act_quant_ue8m0_edge_cases():
+    K = 128 * 6
+    x = torch.randn(8, K, generator=torch.Generator().manual_seed(5)).float()
+    x[0] = 0.0                                     # zero row: floor scale
+    x[1] = 1e-7                                    # below the floor
+    x[2, :128] = 448.0 * 2.0 ** -3                 # block max a power of two times 448
+    x[2, 128:256] = 448.0 * 2.0 ** -3 * (1 + 2 ** -7)   # just above it: next octave
+    x[3] *= 2.0 ** 40                              # large
+    x[4] *= 2.0 ** -60                             # tiny (below the floor)
+    x[5, 7] = -3.0e38                              # near the bf16 maximum
+    x[6] = -0.0
+    x[7, ::2] = 1.0
+    _aq_case(x.to(torch.bfloat16), "edge cases")
+
+
+def _gemm_case(M, N, K, seed, what, rows=None):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(M, K, generator=g).to(torch.bfloat16).to(dev())
+    q, s = bfp8.act_quant_ue8m0(x)
+    w, ws = synth.weight(N, K, seed + 1, seed + 2, pow2=True)
+    wd, wsd = w.to(dev()), ws.to(dev())
+    announce(f"gemm_ue8m0 {what} M={M} N={N} K={K} via {bfp8.bfp8_gemm_kernel_name(M, N, K)}")
+    c = bfp8.gemm_ue8m0(q, s, wd, wsd)
+    c_fold = bfp8.gemm(q, s, wd, wsd)
+    torch.cuda.synchronize()
+    r = np.arange(M) if rows is None else rows
+    ref = oracle.gemm(u8(q), s.cpu().numpy(), u8(w), ws.numpy(), rows=r)
+    rt = torch.from_numpy(np.asarray(r)).to(dev())
+    worst = gemm_check(c[rt], ref, what)
+    gemm_check(c_fold[rt], ref, what + " (fold path)")
+    announce(f"gemm_ue8m0 {what}: worst err/bound {worst:.3f}")
+
+
+def test_gemm_ue8m0_shapes():
+    for i, (M, N, K) in enumerate([(16, 256, 256), (130, 300, 384), (300, 1000, 640),
+                                    (2000, 4096, 256), (4096, 8192, 256)]):
+        rows = None if M <= 300 else sample_rows(M, 16, 900 + i)
+        _gemm_case(M, N, K, 910 + 10 * i, f"shape {i}", rows)
+
+
+def test_gemm_ue8m0_dense_full_size():
+    _gemm_case(8192, 18432, 7168, 990, "dense-mlp up", rows=np.array([0, 1, 4095, 8191]))
