@@ -845,7 +845,7 @@ __device__ __forceinline__ void group_rows(const int32_t* __restrict__ off, int 
     hi = b;
 }
 
-template <class T, bool kLight>
+template <class T, bool kLight, int HBM>
 __global__ __launch_bounds__(T::THREADS, 1) void gemm_grouped_big_kernel(
     const uint8_t* __restrict__ a, const float* __restrict__ as, const uint8_t* __restrict__ b,
     const float* __restrict__ bs, uint16_t* __restrict__ c, const int32_t* __restrict__ off,
@@ -857,7 +857,7 @@ __global__ __launch_bounds__(T::THREADS, 1) void gemm_grouped_big_kernel(
     for (int g = 0; g < G; ++g) {
         int64_t lo, hi;
         group_rows(off, g, total_M, lo, hi);
-        const GroupTiles gt = group_tiles<T::BM>(hi - lo);
+        const GroupTiles gt = group_tiles<HBM>(hi - lo);
         total += (kLight ? gt.m_light : gt.m_heavy) * nt;
     }
     const int nwg = gridDim.x;                    // a multiple of 8
@@ -871,16 +871,18 @@ __global__ __launch_bounds__(T::THREADS, 1) void gemm_grouped_big_kernel(
         int64_t tm = 0, tn = 0, g_lo = 0, g_hi = 0;
         for (; g < G; ++g) {
             group_rows(off, g, total_M, g_lo, g_hi);
-            const GroupTiles gt = group_tiles<T::BM>(g_hi - g_lo);
+            const GroupTiles gt = group_tiles<HBM>(g_hi - g_lo);
             const int64_t mcount = kLight ? gt.m_light : gt.m_heavy;
             if (rest < mcount * nt) {
-                tm = (kLight ? gt.m_heavy : 0) + rest % mcount;
+                // a light tile starts after the group's heavy tiles (it holds fewer
+                // than HBM / 2 rows, so one tile of T::BM >= HBM / 2 rows covers them)
+                tm = kLight ? gt.m_heavy : rest % mcount;
                 tn = rest / mcount;
                 break;
             }
             rest -= mcount * nt;
         }
-        const int64_t m0 = g_lo + tm * T::BM, m_end = g_hi;
+        const int64_t m0 = g_lo + tm * (kLight ? HBM : T::BM), m_end = g_hi;
         gemm_tile_big<T, kLight>(a, as, b + (int64_t)g * N * K, bs + (int64_t)g * NB * KB, c, m0,
                                  m_end, tn * T::BN, N, K, lds);
     }
@@ -1148,28 +1150,43 @@ hipError_t launch_gemm_swiglu_quant(const void* a, const float* as, const void* 
     return launch_quant<BigSquare, kEpiSwiglu>(a, as, w13, s13, q, qs, M, 2 * n_out, K, stream);
 }
 
-hipError_t launch_gemm_grouped(const void* a, const float* as, const void* b, const float* bs,
-                               void* c, const int32_t* off, int32_t G, int64_t total_M,
-                               int64_t N, int64_t K, hipStream_t stream) {
-    using T = BigWide;
-    const int nt = (int)((N + T::BN - 1) / T::BN);
+// Heavy tiles on TH, light tiles (the remainder rows of a group, fewer than
+// TH::BM / 2) on the smaller TL, whose narrower N tiles spread the light pass
+// over more workgroups.
+template <class TH, class TL>
+static hipError_t launch_grouped_pair(const void* a, const float* as, const void* b,
+                                      const float* bs, void* c, const int32_t* off, int32_t G,
+                                      int64_t total_M, int64_t N, int64_t K, hipStream_t stream) {
+    static_assert(TL::BM >= TH::BM / 2, "a light tile must hold every remainder row");
+    const int nt_h = (int)((N + TH::BN - 1) / TH::BN);
+    const int nt_l = (int)((N + TL::BN - 1) / TL::BN);
     // upper bounds of the tile counts (the exact ones depend on the device offsets)
-    const int64_t max_heavy = ((total_M + T::BM / 2 - 1) / (T::BM / 2)) * (int64_t)nt;
-    const int64_t max_light = (int64_t)G * nt;
+    const int64_t max_heavy = ((total_M + TH::BM / 2 - 1) / (TH::BM / 2)) * (int64_t)nt_h;
+    const int64_t max_light = (int64_t)G * nt_l;
     const int64_t cus = device_cu_count();
     int64_t grid_h = max_heavy < cus ? max_heavy : cus;
     int64_t grid_l = max_light < cus ? max_light : cus;
     grid_h = (grid_h + 7) / 8 * 8;
     grid_l = (grid_l + 7) / 8 * 8;
-    hipLaunchKernelGGL((gemm_grouped_big_kernel<T, false>), dim3((unsigned)grid_h),
-                       dim3(T::THREADS), 0, stream, (const uint8_t*)a, as, (const uint8_t*)b, bs,
-                       (uint16_t*)c, off, (int)G, total_M, N, K, nt);
+    hipLaunchKernelGGL((gemm_grouped_big_kernel<TH, false, TH::BM>), dim3((unsigned)grid_h),
+                       dim3(TH::THREADS), 0, stream, (const uint8_t*)a, as, (const uint8_t*)b, bs,
+                       (uint16_t*)c, off, (int)G, total_M, N, K, nt_h);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gemm_grouped_big_kernel<T, true>), dim3((unsigned)grid_l),
-                       dim3(T::THREADS), 0, stream, (const uint8_t*)a, as, (const uint8_t*)b, bs,
-                       (uint16_t*)c, off, (int)G, total_M, N, K, nt);
+    hipLaunchKernelGGL((gemm_grouped_big_kernel<TL, true, TH::BM>), dim3((unsigned)grid_l),
+                       dim3(TL::THREADS), 0, stream, (const uint8_t*)a, as, (const uint8_t*)b, bs,
+                       (uint16_t*)c, off, (int)G, total_M, N, K, nt_l);
     return hipGetLastError();
+}
+
+#ifndef BFP8_GROUPED_PAIR
+#define BFP8_GROUPED_PAIR BigSquare, BigMid
+#endif
+
+hipError_t launch_gemm_grouped(const void* a, const float* as, const void* b, const float* bs,
+                               void* c, const int32_t* off, int32_t G, int64_t total_M,
+                               int64_t N, int64_t K, hipStream_t stream) {
+    return launch_grouped_pair<BFP8_GROUPED_PAIR>(a, as, b, bs, c, off, G, total_M, N, K, stream);
 }
 
 }  // namespace bfp8
