@@ -1,0 +1,84 @@
+"""The library's calls inside a captured HIP graph: the decode-shaped linear (act_quant and
+the split-K GEMM over a caller workspace) and the MoE chain are captured once and replayed
+several times, with eager work and synchronizations in between; every replay must equal the
+eager result bit for bit (the kernels are deterministic and enqueue no memset or allocation).
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp8_04_amd as bfp8
+from gpu_helpers import announce, dev, workload
+
+pytestmark = pytest.mark.gpu
+
+
+def test_decode_linear_graph_replays():
+    wl = workload(1)
+    x = wl.tensors["x"].to(dev())
+    w, s = wl.tensors["w1"].to(dev()), wl.tensors["s1"].to(dev())
+    M, K = x.shape
+    N = w.shape[0]
+    ws = torch.empty(max(1, bfp8.bfp8_gemm_workspace_size(M, N, K) // 4), dtype=torch.float32, device=dev())
+    q = torch.empty(M, K, dtype=torch.uint8, device=dev())
+    qs = torch.empty(M, K // 128, dtype=torch.float32, device=dev())
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=dev())
+
+    def step():
+        bfp8.bfp8_act_quant(x, q, qs)
+        bfp8.bfp8_gemm(q, qs, w, s, y, ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = y.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(4):
+        y.zero_()
+        ws.fill_(float("nan"))                     # stale workspace must not leak into the result
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        announce(f"decode graph replay {r}")
+        assert torch.equal(y, ref), f"replay {r} differs from the eager result"
+        _ = (x.float() * 2).sum()                  # eager work between replays
+        torch.cuda.synchronize()
+
+
+def test_moe_chain_graph_replays():
+    wl = workload(4, 0.25)
+    x, topk, wts = wl.tensors["x"].to(dev()), wl.tensors["topk"].to(dev()), wl.tensors["weights"].to(dev())
+    W, S = wl.tensors["w1"].to(dev()), wl.tensors["s1"].to(dev())
+    T, k = topk.shape
+    G, N, K = W.shape
+    cap = T * k
+    off = torch.empty(G + 1, dtype=torch.int32, device=dev())
+    row_token = torch.empty(cap, dtype=torch.int32, device=dev())
+    slot_row = torch.empty(T, k, dtype=torch.int32, device=dev())
+    dws = torch.empty(max(1, bfp8.bfp8_moe_dispatch_workspace_size(T, k, G) // 4), dtype=torch.int32, device=dev())
+    q = torch.empty(cap, K, dtype=torch.uint8, device=dev())
+    qs = torch.empty(cap, K // 128, dtype=torch.float32, device=dev())
+    h = torch.empty(cap, N, dtype=torch.bfloat16, device=dev())
+    y = torch.empty(T, N, dtype=torch.bfloat16, device=dev())
+
+    def step():
+        bfp8.bfp8_moe_dispatch(topk, 0, off, row_token, slot_row, dws)
+        bfp8.bfp8_act_quant_rows(x, row_token, off[G:], q, qs)
+        bfp8.bfp8_gemm_grouped(q, qs, W, S, h, off)
+        bfp8.bfp8_moe_combine(h, slot_row, wts, y)
+
+    step()
+    torch.cuda.synchronize()
+    ref = y.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(3):
+        y.zero_()
+        off.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        announce(f"moe graph replay {r}")
+        assert torch.equal(y, ref), f"replay {r} differs from the eager result"
