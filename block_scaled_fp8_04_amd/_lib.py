@@ -31,7 +31,7 @@ EXPORTS = ("bfp8_act_quant", "bfp8_weight_dequant", "bfp8_gemm", "bfp8_gemm_work
            "bfp8_gemm_kernel_name", "bfp8_moe_dispatch_workspace_size", "bfp8_moe_dispatch",
            "bfp8_act_quant_rows", "bfp8_moe_combine", "bfp8_gemm_bf16",
            "bfp8_gemm_act_quant", "bfp8_gemm_swiglu_act_quant", "bfp8_act_quant_ue8m0",
-           "bfp8_gemm_ue8m0",
+           "bfp8_gemm_ue8m0", "bfp8_linear_fp8_workspace_size", "bfp8_linear_fp8",
            "bfp8_status_string", "bfp8_version")
 
 _lib = None
@@ -85,6 +85,10 @@ def library():
     lib.bfp8_act_quant_ue8m0.restype = ctypes.c_int
     lib.bfp8_gemm_ue8m0.argtypes = [P, P, P, P, P, I64, I64, I64, P]
     lib.bfp8_gemm_ue8m0.restype = ctypes.c_int
+    lib.bfp8_linear_fp8_workspace_size.argtypes = [I64, I64, I64]
+    lib.bfp8_linear_fp8_workspace_size.restype = ctypes.c_size_t
+    lib.bfp8_linear_fp8.argtypes = [P, P, P, P, I64, I64, I64, P, ctypes.c_size_t, P]
+    lib.bfp8_linear_fp8.restype = ctypes.c_int
     lib.bfp8_gemm_bf16.argtypes = [P, P, P, I64, I64, I64, P]
     lib.bfp8_gemm_bf16.restype = ctypes.c_int
     lib.bfp8_status_string.argtypes = [ctypes.c_int]
@@ -267,6 +271,34 @@ def interleave_w13(w1, s1, w3, s3):
     g3 = s3.repeat_interleave(2, dim=0)
     s13 = torch.stack([g1, g3], dim=1).reshape(2 * N // 64, -1)
     return w13.contiguous(), s13.contiguous()
+
+
+def bfp8_linear_fp8_workspace_size(M, N, K) -> int:
+    return int(library().bfp8_linear_fp8_workspace_size(int(M), int(N), int(K)))
+
+
+def bfp8_linear_fp8(x, w, w_s, y, workspace, stream=None):
+    """y bf16 [M,N] = fp8_gemm(act_quant(x bf16 [M,K]), w, w_s) in one call (see include/bfp8.h).
+
+    workspace: a device tensor of at least bfp8_linear_fp8_workspace_size(M, N, K) bytes
+    (linear_workspace() allocates one)."""
+    w = _bytes_view(w)
+    _cuda_contig(x, w, w_s, y, workspace)
+    _need(x.dtype == torch.bfloat16 and y.dtype == torch.bfloat16, "x and y must be bf16")
+    M, K = x.shape
+    N = w.shape[0]
+    _need(w.shape[1] == K and w_s.shape == (-(-N // BLOCK), K // BLOCK) and y.shape == (M, N),
+          "w [N, K], w_s [ceil(N/128), K/128], y [M, N]")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check("bfp8_linear_fp8", library().bfp8_linear_fp8(_ptr(x), _ptr(w), _ptr(w_s), _ptr(y), M, N, K,
+                                                        _ptr(workspace), nbytes,
+                                                        _stream(stream, x.device)))
+
+
+def linear_workspace(M, N, K, device):
+    """A workspace for bfp8_linear_fp8 at this shape."""
+    n = max(256, bfp8_linear_fp8_workspace_size(M, N, K))
+    return torch.empty((n + 255) // 256 * 256, dtype=torch.uint8, device=device)
 
 
 def bfp8_gemm_grouped(a, a_s, b, b_s, c, group_offsets, stream=None):

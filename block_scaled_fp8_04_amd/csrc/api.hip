@@ -140,6 +140,24 @@ int bfp8_gemm_swiglu_act_quant(const void* a, const float* a_s, const void* w13,
                                                    (hipStream_t)stream));
 }
 
+size_t bfp8_linear_fp8_workspace_size(int64_t M, int64_t N, int64_t K) {
+    if (M <= 0 || N <= 0 || K <= 0 || K % BFP8_BLOCK != 0) return 0;
+    return bfp8::linear_workspace_bytes(M, N, K);
+}
+
+int bfp8_linear_fp8(const void* x_bf16, const void* w, const float* w_s, void* y_bf16, int64_t M,
+                    int64_t N, int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
+    if (M < 0 || N < 0 || K <= 0 || K % BFP8_BLOCK != 0) return BFP8_ERR_SHAPE;
+    if (M == 0 || N == 0) return BFP8_OK;
+    if (!x_bf16 || !w || !w_s || !y_bf16 || !workspace) return BFP8_ERR_NULL;
+    if (!aligned(x_bf16, 16) || !aligned(w, 16) || !aligned(w_s, 4) || !aligned(y_bf16, 2) ||
+        !aligned(workspace, 256))
+        return BFP8_ERR_ALIGN;
+    if (workspace_bytes < bfp8::linear_workspace_bytes(M, N, K)) return BFP8_ERR_WORKSPACE;
+    return from_hip(bfp8::launch_linear_fp8(x_bf16, w, w_s, y_bf16, M, N, K, workspace,
+                                            (hipStream_t)stream));
+}
+
 int bfp8_gemm_grouped(const void* a, const float* a_s, const void* b, const float* b_s,
                       void* c_bf16, const int32_t* group_offsets, int32_t G, int64_t total_M,
                       int64_t N, int64_t K, void* stream) {

@@ -1026,6 +1026,29 @@ static SplitPlan split_plan(int64_t M, int64_t N, int64_t K) {
     return p;
 }
 
+static size_t round256(size_t v) { return (v + 255) / 256 * 256; }
+
+// The FP8 branch of linear(): act_quant of x into the workspace, then the
+// GEMM, split over K (partials after the codes) where split_plan splits.
+// A single kernel that also reduces the splits (the last workgroup of a tile
+// adding them) was slower on this chip: publishing partials across XCDs costs
+// an L2 write-back per workgroup and an invalidate per tile, more than the two
+// extra launches.
+size_t linear_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    return round256((size_t)M * K) + round256((size_t)M * (K / kBlock) * 4) +
+           round256(gemm_workspace_bytes(M, N, K));
+}
+
+hipError_t launch_linear_fp8(const void* x, const void* b, const float* bs, void* c, int64_t M,
+                             int64_t N, int64_t K, void* workspace, hipStream_t stream) {
+    uint8_t* q = (uint8_t*)workspace;
+    float* qs = (float*)(q + round256((size_t)M * K));
+    uint8_t* part = (uint8_t*)qs + round256((size_t)M * (K / kBlock) * 4);
+    hipError_t e = launch_act_quant(x, q, qs, M, K, stream);
+    if (e != hipSuccess) return e;
+    return launch_gemm(q, qs, b, bs, c, M, N, K, part, gemm_workspace_bytes(M, N, K), stream);
+}
+
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     const SplitPlan p = split_plan(M, N, K);
     if (p.splits < 2) return 0;

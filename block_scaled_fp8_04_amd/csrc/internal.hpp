@@ -44,6 +44,9 @@ hipError_t launch_gemm_quant(const void* a, const float* as, const void* b, cons
 hipError_t launch_gemm_swiglu_quant(const void* a, const float* as, const void* w13,
                                     const float* s13, void* q, float* qs, int64_t M, int64_t n_out,
                                     int64_t K, hipStream_t stream);
+size_t linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_linear_fp8(const void* x, const void* b, const float* bs, void* c, int64_t M,
+                             int64_t N, int64_t K, void* workspace, hipStream_t stream);
 hipError_t launch_gemm_grouped(const void* a, const float* as, const void* b, const float* bs,
                                void* c, const int32_t* off, int32_t G, int64_t total_M,
                                int64_t N, int64_t K, hipStream_t stream);

@@ -44,7 +44,7 @@ extern "C" {
 #endif
 
 #define BFP8_BLOCK 128
-#define BFP8_VERSION 6
+#define BFP8_VERSION 7
 #define BFP8_MOE_MAX_GROUPS 1024
 
 typedef enum bfp8_status {
@@ -164,6 +164,24 @@ int bfp8_act_quant_ue8m0(const void* x_bf16, void* q_e4m3, float* scales, int64_
  * Same arguments, layouts and errors as bfp8_gemm without a workspace. */
 int bfp8_gemm_ue8m0(const void* a, const float* a_s, const void* b, const float* b_s,
                     void* c_bf16, int64_t M, int64_t N, int64_t K, void* stream);
+
+/* The FP8 branch of linear() in one call ([DF] FP8 bullet: act_quant of the
+ * input, then fp8_gemm with the weight and its scale):
+ *     y = bf16( fp8_gemm( act_quant(x), w, w_s ) )
+ * It runs bfp8_act_quant into the workspace, then bfp8_gemm with the rest of
+ * the workspace as its split-K partials, so y is bit-identical to those two
+ * calls (with a split-K workspace where bfp8_gemm would split).
+ *   x_bf16 : bf16 [M, K], 16-byte aligned;  w, w_s : as bfp8_gemm's b, b_s
+ *   y_bf16 : bf16 [M, N] output
+ *   workspace : DEVICE, at least bfp8_linear_fp8_workspace_size(M, N, K)
+ *     bytes, 256-byte aligned, owned by the caller, any contents; it holds the
+ *     codes, the scales and the split partials of the call.  Calls that share
+ *     a workspace must not overlap in time.
+ * Errors: as bfp8_gemm; BFP8_ERR_NULL if the workspace is NULL;
+ * BFP8_ERR_WORKSPACE if it is too small. */
+size_t bfp8_linear_fp8_workspace_size(int64_t M, int64_t N, int64_t K);
+int bfp8_linear_fp8(const void* x_bf16, const void* w, const float* w_s, void* y_bf16, int64_t M,
+                    int64_t N, int64_t K, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of fp32 workspace bfp8_gemm would use for split-K at this shape
  * (0 when the shape does not use split-K).  Pure host function. */

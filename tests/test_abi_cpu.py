@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert bfp8.bfp8_version() == 6
+    assert bfp8.bfp8_version() == 7
     for code in range(8):
         assert bfp8.bfp8_status_string(code)
     assert bfp8.bfp8_status_string(0) == "ok"
@@ -185,6 +185,24 @@ def test_ue8m0_validation(lib):
     assert g(FAKE, None, FAKE, FAKE, FAKE, 64, 64, 256, None) == _lib.BFP8_ERR_NULL
     assert g(ODD, FAKE, FAKE, FAKE, FAKE, 64, 64, 256, None) == _lib.BFP8_ERR_ALIGN
     assert g(None, FAKE, FAKE, FAKE, FAKE, 0, 64, 256, None) == _lib.BFP8_OK
+
+
+def test_linear_fp8_validation(lib):
+    f = lib.bfp8_linear_fp8
+    need = bfp8.bfp8_linear_fp8_workspace_size(64, 1536, 7168)
+    assert need > 0 and need % 256 == 0
+    assert bfp8.bfp8_linear_fp8_workspace_size(4096, 2048, 7168) >= 4096 * 7168
+    WS = ctypes.c_void_p(0x100000)
+
+    def call(x=FAKE, w=FAKE, s=FAKE, y=FAKE, M=64, N=1536, K=7168, ws=WS, wsb=need):
+        return f(x, w, s, y, M, N, K, ws, wsb, None)
+
+    assert call(K=100) == _lib.BFP8_ERR_SHAPE
+    for name in ("x", "w", "s", "y", "ws"):
+        assert call(**{name: None}) == _lib.BFP8_ERR_NULL, name
+    assert call(ws=ctypes.c_void_p(0x100010)) == _lib.BFP8_ERR_ALIGN
+    assert call(wsb=need - 256) == _lib.BFP8_ERR_WORKSPACE
+    assert call(x=None, M=0) == _lib.BFP8_OK
 
 
 def test_gemm_bf16_validation(lib):

@@ -1,0 +1,141 @@
+"""GPU parity of bfp8_linear_fp8, the FP8 branch of linear() in one call
+(act_quant into the workspace, then the GEMM with split-K partials after it).
+Checks:
+  * bit-identity with bfp8_act_quant + bfp8_gemm (with a split-K workspace
+    where the GEMM would split);
+  * parity with the oracle (act_quant then the fp64 GEMM of the codes) within
+    the GEMM tolerance |err| <= 2^-7 |ref| + 1e-3 rms(ref);
+  * one workspace serving a sequence of shapes (larger, smaller, split and
+    unsplit) whatever it held before;
+  * no write outside the output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import block_scaled_fp8_04_amd as bfp8
+from block_scaled_fp8_04_amd import synth
+from gpu_helpers import announce, bits16, canary_intact, dev, gemm_check, u8, with_canary, workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _two_step(x, w, w_s):
+    """bfp8_act_quant then bfp8_gemm, with a split-K workspace where it splits."""
+    q, s = bfp8.act_quant(x)
+    M, K = x.shape
+    need = bfp8.bfp8_gemm_workspace_size(M, w.shape[0], K)
+    work = torch.empty(max(need, 4) // 4, dtype=torch.float32, device=dev()) if need else None
+    return q, s, bfp8.gemm(q, s, w, w_s, workspace=work)
+
+
+def _linear(x, w, w_s, work):
+    M, N = x.shape[0], w.shape[0]
+    raw, y, pad = with_canary((M, N), torch.bfloat16)
+    bfp8.bfp8_linear_fp8(x, w, w_s, y, work)
+    torch.cuda.synchronize()
+    assert canary_intact(raw, pad), "wrote outside the output"
+    return y
+
+
+def _case(M, N, K, seed, work=None, oracle_rows=None):
+    g = torch.Generator().manual_seed(seed)
+    x = (torch.randn(M, K, generator=g) * (1 + 3 * torch.rand(M, 1, generator=g))).to(torch.bfloat16)
+    w, w_s = synth.weight(N, K, 1100 + seed, 1200 + seed)
+    x, w, w_s = x.to(dev()), w.to(dev()), w_s.to(dev())
+    if work is None:
+        work = bfp8.linear_workspace(M, N, K, dev())
+    announce(f"linear_fp8 M={M} N={N} K={K} seed={seed} workspace={work.numel()} B")
+    y = _linear(x, w, w_s, work)
+    q, s, ref2 = _two_step(x, w, w_s)
+    torch.cuda.synchronize()
+    diff = int((bits16(y) != bits16(ref2)).sum())
+    assert diff == 0, f"[{M},{N},{K}]: {diff} outputs differ from act_quant + gemm"
+    rows = np.arange(M) if oracle_rows is None else oracle_rows
+    qo, so = oracle.act_quant(bits16(x))
+    assert np.array_equal(qo, u8(q)), "act_quant codes differ from the oracle"
+    ref = oracle.gemm(qo, so, u8(w), w_s.cpu().numpy(), rows=rows)
+    worst = gemm_check(y[torch.from_numpy(rows).to(dev())], ref, f"linear[{M},{N},{K}]")
+    announce(f"linear_fp8 [{M},{N},{K}] bit-identical to act_quant+gemm; oracle worst err/bound {worst:.3f}")
+    return y
+
+
+def test_linear_decode_config():
+    """The decode workload's shapes (x [64, 7168], up-projection [1536, 7168])."""
+    wl = workload(1)
+    x = wl.tensors["x"].to(dev())
+    w, w_s = wl.tensors["w1"].to(dev()), wl.tensors["s1"].to(dev())
+    M, K = x.shape
+    N = w.shape[0]
+    work = bfp8.linear_workspace(M, N, K, dev())
+    announce(f"linear_fp8 decode M={M} N={N} K={K}")
+    y = _linear(x, w, w_s, work)
+    _, _, ref2 = _two_step(x, w, w_s)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), ref2.view(torch.int16))
+    qo, so = oracle.act_quant(bits16(x))
+    ref = oracle.gemm(qo, so, u8(w), w_s.cpu().numpy())
+    gemm_check(y, ref, "decode linear")
+
+
+@pytest.mark.parametrize("shape", [
+    (1, 256, 512),        # one row, two splits of two K blocks
+    (37, 300, 1152),      # ragged rows and columns
+    (64, 1536, 7168),     # the decode up-projection
+    (64, 7168, 2048),     # the decode down-projection shape of an expert
+    (50, 129, 640),       # a ragged column tail in a one-tile-wide problem
+    (8, 4096, 7168),
+])
+def test_linear_split_k_shapes(shape):
+    M, N, K = shape
+    _case(M, N, K, seed=M + N)
+
+
+@pytest.mark.parametrize("shape", [
+    (16, 128, 256),       # two K blocks: no split
+    (65, 300, 1152),      # M > 64
+    (8, 24576, 1024),     # 384 tiles: no split
+    (200, 2048, 7168),
+])
+def test_linear_unsplit_shapes(shape):
+    M, N, K = shape
+    rows = None if M <= 64 else np.array([0, 1, M // 2, M - 2, M - 1])
+    _case(M, N, K, seed=3 * M + N, oracle_rows=rows)
+
+
+def test_linear_shared_workspace_sequence():
+    """One workspace, sized for the largest shape and filled with NaN bytes
+    first, serves calls at several shapes in a row; each result is
+    bit-identical to act_quant + gemm."""
+    shapes = [(64, 1536, 7168), (5, 300, 1152), (200, 2048, 7168), (64, 1536, 7168), (33, 7168, 2048)]
+    need = max(bfp8.bfp8_linear_fp8_workspace_size(*s) for s in shapes)
+    work = torch.full(((need + 255) // 256 * 256,), 0xFF, dtype=torch.uint8, device=dev())
+    for i, (M, N, K) in enumerate(shapes):
+        rows = None if M <= 64 else np.array([0, M - 1])
+        _case(M, N, K, seed=40 + i, work=work, oracle_rows=rows)
+
+
+def test_linear_repeat_deterministic():
+    """Repeated calls give the same bits (the split partials are added in a fixed order)."""
+    M, N, K = 64, 1536, 7168
+    g = torch.Generator().manual_seed(77)
+    x = torch.randn(M, K, generator=g).to(torch.bfloat16).to(dev())
+    w, w_s = synth.weight(N, K, 1300, 1301)
+    w, w_s = w.to(dev()), w_s.to(dev())
+    work = bfp8.linear_workspace(M, N, K, dev())
+    y0 = _linear(x, w, w_s, work)
+    for _ in range(5):
+        y = _linear(x, w, w_s, work)
+        assert torch.equal(y.view(torch.int16), y0.view(torch.int16))
+
+
+def test_linear_rejects_small_workspace():
+    M, N, K = 64, 1536, 7168
+    x = torch.zeros(M, K, dtype=torch.bfloat16, device=dev())
+    w, w_s = synth.weight(N, K, 1, 2)
+    need = bfp8.bfp8_linear_fp8_workspace_size(M, N, K)
+    work = torch.empty(need - 256, dtype=torch.uint8, device=dev())
+    with pytest.raises(bfp8.Bfp8Error):
+        bfp8.bfp8_linear_fp8(x, w.to(dev()), w_s.to(dev()), torch.empty(M, N, dtype=torch.bfloat16,
+                                                                          device=dev()), work)
