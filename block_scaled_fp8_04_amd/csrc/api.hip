@@ -38,11 +38,15 @@ extern "C" {
 
 int bfp8_version(void) { return BFP8_VERSION; }
 
+// The fp8 GEMM tiles address a tile's rows with 32-bit byte offsets (row * K,
+// row < 256), so K stays below 2^22 (the bf16 GEMM's limit too).
+static bool gemm_k_ok(int64_t K) { return K > 0 && K % BFP8_BLOCK == 0 && K < ((int64_t)1 << 22); }
+
 const char* bfp8_status_string(int status) {
     switch (status) {
         case BFP8_OK: return "ok";
         case BFP8_ERR_NULL: return "a required pointer is NULL";
-        case BFP8_ERR_SHAPE: return "invalid shape (negative size, or K not a multiple of 128)";
+        case BFP8_ERR_SHAPE: return "invalid shape (negative size, K not a multiple of 128, or a size past its stated limit)";
         case BFP8_ERR_ALIGN: return "pointer misaligned";
         case BFP8_ERR_WORKSPACE: return "workspace smaller than the matching *_workspace_size() call";
         case BFP8_ERR_GROUPS: return "group count out of range (below 1, or above the dispatch limit)";
@@ -72,7 +76,7 @@ int bfp8_act_quant_ue8m0(const void* x_bf16, void* q_e4m3, float* scales, int64_
 
 int bfp8_gemm_ue8m0(const void* a, const float* a_s, const void* b, const float* b_s, void* c_bf16,
                     int64_t M, int64_t N, int64_t K, void* stream) {
-    if (M < 0 || N < 0 || K <= 0 || K % BFP8_BLOCK != 0) return BFP8_ERR_SHAPE;
+    if (M < 0 || N < 0 || !gemm_k_ok(K)) return BFP8_ERR_SHAPE;
     if (M == 0 || N == 0) return BFP8_OK;
     if (!a || !a_s || !b || !b_s || !c_bf16) return BFP8_ERR_NULL;
     if (!aligned(a, 16) || !aligned(b, 16) || !aligned(a_s, 4) || !aligned(b_s, 4) ||
@@ -98,7 +102,7 @@ size_t bfp8_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
 int bfp8_gemm(const void* a, const float* a_s, const void* b, const float* b_s, void* c_bf16,
               int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
               void* stream) {
-    if (M < 0 || N < 0 || K <= 0 || K % BFP8_BLOCK != 0) return BFP8_ERR_SHAPE;
+    if (M < 0 || N < 0 || !gemm_k_ok(K)) return BFP8_ERR_SHAPE;
     if (M == 0 || N == 0) return BFP8_OK;
     if (!a || !a_s || !b || !b_s || !c_bf16) return BFP8_ERR_NULL;
     if (!aligned(a, 16) || !aligned(b, 16) || !aligned(a_s, 4) || !aligned(b_s, 4) ||
@@ -115,7 +119,7 @@ int bfp8_gemm(const void* a, const float* a_s, const void* b, const float* b_s, 
 int bfp8_gemm_act_quant(const void* a, const float* a_s, const void* b, const float* b_s,
                         void* q_e4m3, float* q_scales, int64_t M, int64_t N, int64_t K,
                         void* stream) {
-    if (M < 0 || N < 0 || K <= 0 || K % BFP8_BLOCK != 0 || N % BFP8_BLOCK != 0)
+    if (M < 0 || N < 0 || !gemm_k_ok(K) || N % BFP8_BLOCK != 0)
         return BFP8_ERR_SHAPE;
     if (M == 0 || N == 0) return BFP8_OK;
     if (!a || !a_s || !b || !b_s || !q_e4m3 || !q_scales) return BFP8_ERR_NULL;
@@ -129,7 +133,7 @@ int bfp8_gemm_act_quant(const void* a, const float* a_s, const void* b, const fl
 int bfp8_gemm_swiglu_act_quant(const void* a, const float* a_s, const void* w13,
                                const float* s13, void* q_e4m3, float* q_scales, int64_t M,
                                int64_t N, int64_t K, void* stream) {
-    if (M < 0 || N < 0 || K <= 0 || K % BFP8_BLOCK != 0 || N % BFP8_BLOCK != 0)
+    if (M < 0 || N < 0 || !gemm_k_ok(K) || N % BFP8_BLOCK != 0)
         return BFP8_ERR_SHAPE;
     if (M == 0 || N == 0) return BFP8_OK;
     if (!a || !a_s || !w13 || !s13 || !q_e4m3 || !q_scales) return BFP8_ERR_NULL;
@@ -147,7 +151,7 @@ size_t bfp8_linear_fp8_workspace_size(int64_t M, int64_t N, int64_t K) {
 
 int bfp8_linear_fp8(const void* x_bf16, const void* w, const float* w_s, void* y_bf16, int64_t M,
                     int64_t N, int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
-    if (M < 0 || N < 0 || K <= 0 || K % BFP8_BLOCK != 0) return BFP8_ERR_SHAPE;
+    if (M < 0 || N < 0 || !gemm_k_ok(K)) return BFP8_ERR_SHAPE;
     if (M == 0 || N == 0) return BFP8_OK;
     if (!x_bf16 || !w || !w_s || !y_bf16 || !workspace) return BFP8_ERR_NULL;
     if (!aligned(x_bf16, 16) || !aligned(w, 16) || !aligned(w_s, 4) || !aligned(y_bf16, 2) ||
@@ -161,7 +165,7 @@ int bfp8_linear_fp8(const void* x_bf16, const void* w, const float* w_s, void* y
 int bfp8_gemm_grouped(const void* a, const float* a_s, const void* b, const float* b_s,
                       void* c_bf16, const int32_t* group_offsets, int32_t G, int64_t total_M,
                       int64_t N, int64_t K, void* stream) {
-    if (total_M < 0 || N < 0 || K <= 0 || K % BFP8_BLOCK != 0) return BFP8_ERR_SHAPE;
+    if (total_M < 0 || N < 0 || !gemm_k_ok(K)) return BFP8_ERR_SHAPE;
     if (G < 1) return BFP8_ERR_GROUPS;
     if (total_M == 0 || N == 0) return BFP8_OK;
     if (!a || !a_s || !b || !b_s || !c_bf16 || !group_offsets) return BFP8_ERR_NULL;

@@ -50,7 +50,8 @@ extern "C" {
 typedef enum bfp8_status {
     BFP8_OK = 0,
     BFP8_ERR_NULL = 1,      /* a required pointer is NULL */
-    BFP8_ERR_SHAPE = 2,     /* a size is negative, or K is not a multiple of 128 where required */
+    BFP8_ERR_SHAPE = 2,     /* a size is negative, K is not a multiple of 128 where required,
+                               or a size is past the limit its call states */
     BFP8_ERR_ALIGN = 3,     /* a pointer is not aligned as documented */
     BFP8_ERR_WORKSPACE = 4, /* workspace smaller than the matching *_workspace_size() */
     BFP8_ERR_GROUPS = 5,    /* G < 1, or G > BFP8_MOE_MAX_GROUPS (MoE dispatch) */
@@ -100,8 +101,9 @@ int bfp8_weight_dequant(const void* w_e4m3, const float* s, void* out_bf16,
  *   workspace : optional fp32 scratch for split-K on skinny problems; NULL
  *     disables split-K.  If non-NULL it must hold at least
  *     bfp8_gemm_workspace_size(M, N, K) bytes and be 16-byte aligned.
- * Errors: BFP8_ERR_SHAPE if M, N < 0 or K <= 0 or K % 128 != 0; BFP8_ERR_NULL;
- * BFP8_ERR_ALIGN; BFP8_ERR_WORKSPACE if workspace_bytes is too small. */
+ * Errors: BFP8_ERR_SHAPE if M, N < 0, K <= 0, K % 128 != 0 or K >= 2^22 (the
+ * tiles address rows with 32-bit byte offsets); BFP8_ERR_NULL; BFP8_ERR_ALIGN;
+ * BFP8_ERR_WORKSPACE if workspace_bytes is too small. */
 int bfp8_gemm(const void* a, const float* a_s, const void* b, const float* b_s,
               void* c_bf16, int64_t M, int64_t N, int64_t K,
               void* workspace, size_t workspace_bytes, void* stream);

@@ -187,6 +187,20 @@ def test_ue8m0_validation(lib):
     assert g(None, FAKE, FAKE, FAKE, FAKE, 0, 64, 256, None) == _lib.BFP8_OK
 
 
+def test_gemm_k_limit(lib):
+    """Every fp8 GEMM entry point rejects K >= 2^22 (32-bit tile row offsets) before any launch."""
+    K = 1 << 22
+    big = ctypes.c_void_p(0x100000)
+    assert lib.bfp8_gemm(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, K, None, 0, None) == _lib.BFP8_ERR_SHAPE
+    assert lib.bfp8_gemm(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0, K - 128, None, 0, None) == _lib.BFP8_OK
+    assert lib.bfp8_gemm_act_quant(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 128, K, None) == _lib.BFP8_ERR_SHAPE
+    assert lib.bfp8_gemm_swiglu_act_quant(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 256, K, None) == _lib.BFP8_ERR_SHAPE
+    assert lib.bfp8_gemm_ue8m0(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, K, None) == _lib.BFP8_ERR_SHAPE
+    assert lib.bfp8_linear_fp8(FAKE, FAKE, FAKE, FAKE, 1, 1, K, big, 1 << 30, None) == _lib.BFP8_ERR_SHAPE
+    off = ctypes.c_void_p(0x200000)
+    assert lib.bfp8_gemm_grouped(FAKE, FAKE, FAKE, FAKE, FAKE, off, 1, 1, 1, K, None) == _lib.BFP8_ERR_SHAPE
+
+
 def test_linear_fp8_validation(lib):
     f = lib.bfp8_linear_fp8
     need = bfp8.bfp8_linear_fp8_workspace_size(64, 1536, 7168)
