@@ -83,7 +83,7 @@ def sha_of(t: torch.Tensor) -> str:
 class Step:
     """Device buffers and the ordered launches of one step; every launch is named."""
 
-    def __init__(self, wl, dev, kind=None):
+    def __init__(self, wl, dev, kind=None, cold=False):
         self.wl = wl
         self.dev = dev
         t = wl.tensors
@@ -104,9 +104,21 @@ class Step:
             y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
             ws_bytes = bfp8.bfp8_gemm_workspace_size(M, N, K)
             work = torch.empty(max(1, ws_bytes // 4), dtype=torch.float32, device=dev) if ws_bytes else None
+            # cold: successive steps read different copies of the weight, more than 512 MB in
+            # all, so no step finds its weight in the 256 MB Infinity Cache or in L2
+            copies = [(w, s)]
+            if cold:
+                n_copies = -(-(512 << 20) // (w.numel() + 4 * s.numel()))
+                copies = [(w.clone(), s.clone()) for _ in range(n_copies)]
+            self.copies, self.turn = copies, 0
+
+            def gemm_step():
+                wc, sc = self.copies[self.turn % len(self.copies)]
+                self.turn += 1
+                bfp8.bfp8_gemm(q, qs, wc, sc, y, work)
             self.launches += [
                 ("act_quant", lambda: bfp8.bfp8_act_quant(x, q, qs), 0, act_quant_bytes(M, K), "hbm"),
-                ("fp8_gemm", lambda: bfp8.bfp8_gemm(q, qs, w, s, y, work), 2 * M * N * K,
+                ("fp8_gemm", gemm_step, 2 * M * N * K,
                  gemm_bytes(M, N, K), "mfma" if c == 0 else "hbm"),
             ]
             self.shape = dict(M=M, N=N, K=K)
@@ -402,6 +414,9 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="time the step as replays of one captured HIP graph (launch-bound shapes); "
                          "the per-kernel table still comes from an eager pass with events")
+    ap.add_argument("--cold", action="store_true",
+                    help="decode: rotate over weight copies totalling > 512 MB so every step "
+                         "reads its weight from HBM (eager launches only)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy three times (reference for the "
@@ -435,7 +450,9 @@ def main():
 
     t0 = time.time()
     wl = synth.make(WORKLOADS[args.workload])
-    step = Step(wl, dev, args.workload)
+    if args.cold and (args.workload != "decode" or args.graph):
+        sys.exit("--cold applies to the decode workload with eager launches")
+    step = Step(wl, dev, args.workload, cold=args.cold)
     gen_s = time.time() - t0
     print(f"# workload {wl.name}: inputs built in {gen_s:.1f}s; launches "
           f"{[l[0] for l in step.launches]}", file=sys.stderr, flush=True)
@@ -518,7 +535,8 @@ def main():
               "step": " -> ".join(l[0] for l in step.launches),
               "value_definition": "GEMM FLOP per step / wall time per step",
               "input_sha256_16": step.hashes, "seeds": "1000*config+tensor_id",
-              "parallelism": "single-gpu", "launch": launch_mode}
+              "parallelism": "single-gpu", "launch": launch_mode,
+              "caches": "cold (weight copies > 512 MB rotated)" if args.cold else "no flush between steps"}
     dtype = ("bf16 (fp32 accumulate, bf16 out; fp8_e4m3 weights dequantized)"
              if args.workload == "bf16-branch" else "fp8_e4m3 (fp32 accumulate, bf16 out)")
     out = {"metric": "block-FP8 GEMM TFLOP/s & % of fp8 MFMA peak; act_quant/dequant HBM GB/s",
