@@ -424,9 +424,11 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build runs the path on a single MI355X "
-              "(multi-GPU sharding is a design note, not measured). Use --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the path runs on a single MI355X "
+              "(sharding across GPUs is described, not measured). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.cold and (args.workload != "decode" or args.graph):
+        sys.exit("--cold applies to the decode workload with eager launches")
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
@@ -450,8 +452,6 @@ def main():
 
     t0 = time.time()
     wl = synth.make(WORKLOADS[args.workload])
-    if args.cold and (args.workload != "decode" or args.graph):
-        sys.exit("--cold applies to the decode workload with eager launches")
     step = Step(wl, dev, args.workload, cold=args.cold)
     gen_s = time.time() - t0
     print(f"# workload {wl.name}: inputs built in {gen_s:.1f}s; launches "
