@@ -383,8 +383,9 @@ def cpu_baseline(wl, target_s=12.0, kind=None):
 
 # ------------------------------------------------------------------ traffic
 
-def read_traffic(kernel_name):
-    """HBM bytes per launch measured by rocprofv3 counters, if the kernel source is unchanged."""
+def read_traffic(kernel_name, workload):
+    """HBM bytes per launch measured by rocprofv3 counters on this workload, if the kernel
+    source is unchanged since (else None)."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel_name}.txt")
     if not os.path.exists(path):
         return None
@@ -393,6 +394,8 @@ def read_traffic(kernel_name):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
+    if kv.get("workload") != workload:
+        return None
     src = os.path.join(ROOT, "block_scaled_fp8_04_amd", "csrc", kv.get("source", "gemm.hip"))
     if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != kv.get("source_sha256"):
         return None
@@ -510,7 +513,7 @@ def main():
     dom = step.dominant
     avg_us = float(np.mean([kernels[n]["avg_us"] for n in dom]))
     d = kernels[dom[0]]
-    traffic = read_traffic(step.dominant_kernel)
+    traffic = read_traffic(step.dominant_kernel, args.workload)
     if d["bound"] in ("mfma", "mfma_bf16"):
         peak = PEAK_FP8_TFLOPS if d["bound"] == "mfma" else PEAK_BF16_TFLOPS
         ach = d["flop"] / (avg_us * 1e-6) / 1e12

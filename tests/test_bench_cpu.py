@@ -89,3 +89,11 @@ def test_package_never_imports_the_oracle():
             if f.endswith((".hip", ".hpp", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "bfp8_oracle" not in text and "oracle/" not in text, f
+
+
+def test_traffic_is_tied_to_its_workload(bench):
+    """Counter-measured HBM bytes are reported only for the workload they were measured on."""
+    assert bench.read_traffic("gemm", "decode") is None
+    assert bench.read_traffic("gemm", "moe-pair") is None
+    assert bench.read_traffic("gemm_grouped", "moe-layer") is None
+    assert bench.read_traffic("no_such_kernel", "dense-mlp") is None
