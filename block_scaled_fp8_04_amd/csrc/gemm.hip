@@ -1005,7 +1005,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint8_t* __restr
 
 
 // Split-K plan for skinny problems (M <= 64): enough (tile, split) pairs for
-// about 512 workgroups, at least 2 K blocks per split.  Host-only arithmetic,
+// about 384 workgroups, at least 2 K blocks per split.  Host-only arithmetic,
 // so bfp8_gemm_workspace_size needs no device.
 struct SplitPlan {
     int splits, kb_per;
@@ -1084,7 +1084,10 @@ GemmConfig gemm_config(int64_t M, int64_t N, int64_t /*K*/) {
     const int64_t cus = device_cu_count();
     const int64_t tiles_sq = ((M + 255) / 256) * ((N + 255) / 256);
     const int64_t tiles_wide = ((M + 255) / 256) * ((N + 127) / 128);
-    if (M > 128 && tiles_sq >= 2 * cus) return GemmConfig::kBig256x256;
+    // 256 x 256 from 5/8 of a tile per CU up: at 160-288 tiles it beat 256 x 128 by 6-30%
+    // (one round of the more efficient tile against several of the smaller one); at 128
+    // tiles, half the CUs idle and 256 x 128 is 25% faster
+    if (M > 128 && tiles_sq >= cus * 5 / 8) return GemmConfig::kBig256x256;
     if (M > 128 && tiles_wide >= cus / 2) return GemmConfig::kBig256x128;
     return GemmConfig::kBig128x128;
 }
