@@ -98,9 +98,10 @@ struct BigTile {
     static constexpr int TM = WM / 16, TN = WN / 16;
     static constexpr int A_BYTES = BM * kBlock, B_BYTES = BN * kBlock;
     // Row scales of one K block, permuted for the fragment layout: row 16 i + t
-    // sits at float t * SPITCH + i.  SPITCH = BM/16 + 4 keeps the 16 lanes of a
-    // read on distinct bank groups and each lane's TM values 16-byte aligned.
-    static constexpr int SPITCH = BM / 16 + 4;
+    // sits at float t * SPITCH + i.  SPITCH is a multiple of 4 floats (each
+    // lane's TM values 16-byte aligned) and an odd number of 16-byte units, so
+    // the 16 lanes of a read fall on 16 distinct groups of 4 banks.
+    static constexpr int SPITCH = ((BM / 16 + 4) / 4) % 2 == 1 ? BM / 16 + 4 : BM / 16 + 8;
     static constexpr int S_FLOATS = 16 * SPITCH;
     static constexpr int S_INSTR = (S_FLOATS + 63) / 64;   // 256-byte scale instructions
     // Every wave issues one row-scale instruction into its own 256-byte slot
@@ -802,11 +803,12 @@ __global__ __launch_bounds__(T::THREADS, 1) void gemm_quant_kernel(
 
 // Persistent grouped kernel on the large tiles.
 //
-// Tiles.  Group g (rows off[g] .. off[g+1]) has n_g / BM full M-tiles and,
-// when BM does not divide n_g, one partial M-tile.  A tile is "heavy" when
-// at least half of its rows exist, "light" otherwise; routed experts hold a
-// few rows more or fewer than a multiple of the tile height, so a light tile
-// is typically a handful of rows.  The heavy tiles and the light tiles are
+// Tiles.  Group g (rows off[g] .. off[g+1]) has n_g / HBM full heavy M-tiles
+// and, when HBM does not divide n_g, a remainder.  A remainder of at least LBM
+// rows (the light tile's height) takes one more, partial, heavy tile; a
+// smaller one takes a light tile.  Routed experts hold a few rows more or
+// fewer than a multiple of the heavy height, so a light tile is typically a
+// handful of rows.  The heavy tiles and the light tiles are
 // two launches of this kernel (kLight): heavy tiles run the full-tile loop
 // (rows past the group's end are computed on clamped inputs and not
 // stored), light tiles the guarded loop that skips sub-tile rows past the
@@ -823,13 +825,13 @@ struct GroupTiles {
     int64_t m_heavy, m_light;   // M-tiles of one group by kind
 };
 
-template <int BM>
+template <int HBM, int LBM>
 __device__ __forceinline__ GroupTiles group_tiles(int64_t rows) {
-    const int64_t full = rows / BM;
-    const int64_t rem = rows - full * BM;
+    const int64_t full = rows / HBM;
+    const int64_t rem = rows - full * HBM;
     GroupTiles t;
-    t.m_heavy = full + (rem >= BM / 2 ? 1 : 0);
-    t.m_light = (rem > 0 && rem < BM / 2) ? 1 : 0;
+    t.m_heavy = full + (rem >= LBM ? 1 : 0);
+    t.m_light = (rem > 0 && rem < LBM) ? 1 : 0;
     return t;
 }
 
@@ -845,7 +847,7 @@ __device__ __forceinline__ void group_rows(const int32_t* __restrict__ off, int 
     hi = b;
 }
 
-template <class T, bool kLight, int HBM>
+template <class T, bool kLight, int HBM, int LBM>
 __global__ __launch_bounds__(T::THREADS, 1) void gemm_grouped_big_kernel(
     const uint8_t* __restrict__ a, const float* __restrict__ as, const uint8_t* __restrict__ b,
     const float* __restrict__ bs, uint16_t* __restrict__ c, const int32_t* __restrict__ off,
@@ -857,7 +859,7 @@ __global__ __launch_bounds__(T::THREADS, 1) void gemm_grouped_big_kernel(
     for (int g = 0; g < G; ++g) {
         int64_t lo, hi;
         group_rows(off, g, total_M, lo, hi);
-        const GroupTiles gt = group_tiles<HBM>(hi - lo);
+        const GroupTiles gt = group_tiles<HBM, LBM>(hi - lo);
         total += (kLight ? gt.m_light : gt.m_heavy) * nt;
     }
     const int nwg = gridDim.x;                    // a multiple of 8
@@ -871,11 +873,11 @@ __global__ __launch_bounds__(T::THREADS, 1) void gemm_grouped_big_kernel(
         int64_t tm = 0, tn = 0, g_lo = 0, g_hi = 0;
         for (; g < G; ++g) {
             group_rows(off, g, total_M, g_lo, g_hi);
-            const GroupTiles gt = group_tiles<HBM>(g_hi - g_lo);
+            const GroupTiles gt = group_tiles<HBM, LBM>(g_hi - g_lo);
             const int64_t mcount = kLight ? gt.m_light : gt.m_heavy;
             if (rest < mcount * nt) {
                 // a light tile starts after the group's heavy tiles (it holds fewer
-                // than HBM / 2 rows, so one tile of T::BM >= HBM / 2 rows covers them)
+                // than LBM = T::BM rows, so one tile covers them)
                 tm = kLight ? gt.m_heavy : rest % mcount;
                 tn = rest / mcount;
                 break;
@@ -1059,6 +1061,7 @@ using BigSquare = BigTile<256, 256, 2, 4, 2>;   // 8 waves of 128 x 64, 2 stages
 
 using BigWide = BigTile<256, 128, 4, 2, 3>;     // 8 waves of 64 x 64, 3 stages
 using BigMid = BigTile<128, 128, 2, 2, 3>;      // 4 waves of 64 x 64, 3 stages
+using BigLight = BigTile<64, 128, 1, 4, 4>;     // 4 waves of 64 x 32, 4 stages (grouped light tiles)
 
 template <class T>
 static void launch_big(const void* a, const float* as, const void* b, const float* bs, void* c,
@@ -1177,36 +1180,37 @@ hipError_t launch_gemm_swiglu_quant(const void* a, const float* as, const void* 
 }
 
 // Heavy tiles on TH, light tiles (the remainder rows of a group, fewer than
-// TH::BM / 2) on the smaller TL, whose narrower N tiles spread the light pass
-// over more workgroups.
+// TL::BM) on the smaller TL.  The light pass streams the weights of the
+// groups with a remainder for a few rows each, so TL is short (64 rows) with
+// four stages: three K blocks of weight loads in flight per workgroup.
 template <class TH, class TL>
 static hipError_t launch_grouped_pair(const void* a, const float* as, const void* b,
                                       const float* bs, void* c, const int32_t* off, int32_t G,
                                       int64_t total_M, int64_t N, int64_t K, hipStream_t stream) {
-    static_assert(TL::BM >= TH::BM / 2, "a light tile must hold every remainder row");
+    static_assert(TL::BM <= TH::BM, "light tiles hold the remainders below TL::BM rows");
     const int nt_h = (int)((N + TH::BN - 1) / TH::BN);
     const int nt_l = (int)((N + TL::BN - 1) / TL::BN);
     // upper bounds of the tile counts (the exact ones depend on the device offsets)
-    const int64_t max_heavy = ((total_M + TH::BM / 2 - 1) / (TH::BM / 2)) * (int64_t)nt_h;
+    const int64_t max_heavy = ((total_M + TL::BM - 1) / TL::BM) * (int64_t)nt_h;
     const int64_t max_light = (int64_t)G * nt_l;
     const int64_t cus = device_cu_count();
     int64_t grid_h = max_heavy < cus ? max_heavy : cus;
     int64_t grid_l = max_light < cus ? max_light : cus;
     grid_h = (grid_h + 7) / 8 * 8;
     grid_l = (grid_l + 7) / 8 * 8;
-    hipLaunchKernelGGL((gemm_grouped_big_kernel<TH, false, TH::BM>), dim3((unsigned)grid_h),
+    hipLaunchKernelGGL((gemm_grouped_big_kernel<TH, false, TH::BM, TL::BM>), dim3((unsigned)grid_h),
                        dim3(TH::THREADS), 0, stream, (const uint8_t*)a, as, (const uint8_t*)b, bs,
                        (uint16_t*)c, off, (int)G, total_M, N, K, nt_h);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gemm_grouped_big_kernel<TL, true, TH::BM>), dim3((unsigned)grid_l),
+    hipLaunchKernelGGL((gemm_grouped_big_kernel<TL, true, TH::BM, TL::BM>), dim3((unsigned)grid_l),
                        dim3(TL::THREADS), 0, stream, (const uint8_t*)a, as, (const uint8_t*)b, bs,
                        (uint16_t*)c, off, (int)G, total_M, N, K, nt_l);
     return hipGetLastError();
 }
 
 #ifndef BFP8_GROUPED_PAIR
-#define BFP8_GROUPED_PAIR BigSquare, BigMid
+#define BFP8_GROUPED_PAIR BigSquare, BigLight
 #endif
 
 hipError_t launch_gemm_grouped(const void* a, const float* as, const void* b, const float* bs,

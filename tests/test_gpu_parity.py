@@ -394,7 +394,9 @@ def test_grouped_small_cases():
     from block_scaled_fp8_04_amd import synth
     g = torch.Generator().manual_seed(41)
     K, N = 256, 300
-    for counts in ([3, 0, 5, 1, 0, 4], [0, 0, 130], [129], [1] * 9, [0, 257, 0, 0, 64, 1]):
+    # light tiles hold remainders below 64 rows; 64 and more take a partial heavy tile
+    for counts in ([3, 0, 5, 1, 0, 4], [0, 0, 130], [129], [1] * 9, [0, 257, 0, 0, 64, 1],
+                   [63, 100, 326, 191]):
         counts = np.array(counts)
         G = len(counts)
         off = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32))
