@@ -16,8 +16,9 @@
 //    same for all of a wave's columns (a wave's N range lies inside one
 //    128-column block), so the fold needs one scale per row.
 //  * Large tiles (BigTile): 256x256 (8 waves of 128x64, 2 LDS stages),
-//    256x128 (8 waves of 64x64, 3 stages) and 128x128 (4 waves of 64x64,
-//    3 stages).  A and B rows of one K block go straight from global memory
+//    256x128 (8 waves of 64x64, 3 stages), 128x128 (4 waves of 64x64,
+//    3 stages) and, for the grouped GEMM's remainder rows, 64x128 (4 waves of
+//    64x32, 4 stages).  A and B rows of one K block go straight from global memory
 //    into LDS with buffer loads; the stages are distinct LDS arrays and the K
 //    loop is unrolled by the stage count, so every stage is named at compile
 //    time.  A vmcnt-counted wait and one barrier open each K block.
