@@ -66,7 +66,9 @@ typedef enum bfp8_status {
  *     q[..] = e4m3_rne_saturating( x[..] / s )            (fp32 quotient, correctly rounded)
  *     scales[m, kb] = s
  * The floor 1e-4 on amax is this library's reading of "clamping each tile's
- * max" (it only matters for blocks whose max |x| is below 1e-4).
+ * max" (it only matters for blocks whose max |x| is below 1e-4).  Inputs are
+ * finite: a block holding a NaN or an infinity gets unspecified codes and
+ * scale (the call itself still succeeds and writes only its outputs).
  *   x_bf16 : bf16 [M, K], 16-byte aligned
  *   q_e4m3 : e4m3 [M, K] output, 16-byte aligned
  *   scales : fp32 [M, K/128] output, 4-byte aligned
