@@ -1,5 +1,6 @@
 """The library's calls inside a captured HIP graph: the decode-shaped linear (act_quant and
-the split-K GEMM over a caller workspace) and the MoE chain are captured once and replayed
+the split-K GEMM over a caller workspace, and the same as one bfp8_linear_fp8 call) and the
+MoE chain are captured once and replayed
 several times, with eager work and synchronizations in between; every replay must equal the
 eager result bit for bit (the kernels are deterministic and enqueue no memset or allocation).
 """
@@ -43,6 +44,33 @@ def test_decode_linear_graph_replays():
         announce(f"decode graph replay {r}")
         assert torch.equal(y, ref), f"replay {r} differs from the eager result"
         _ = (x.float() * 2).sum()                  # eager work between replays
+        torch.cuda.synchronize()
+
+
+def test_linear_fp8_graph_replays():
+    """bfp8_linear_fp8 (act_quant into its workspace, then the split-K GEMM) captured once."""
+    wl = workload(1)
+    x = wl.tensors["x"].to(dev())
+    w, s = wl.tensors["w1"].to(dev()), wl.tensors["s1"].to(dev())
+    M, K = x.shape
+    N = w.shape[0]
+    work = bfp8.linear_workspace(M, N, K, dev())
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=dev())
+    bfp8.bfp8_linear_fp8(x, w, s, y, work)
+    torch.cuda.synchronize()
+    ref = y.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        bfp8.bfp8_linear_fp8(x, w, s, y, work)
+    for r in range(4):
+        y.zero_()
+        work.fill_(0xFF)                           # stale workspace must not leak into the result
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        announce(f"linear_fp8 graph replay {r}")
+        assert torch.equal(y, ref), f"replay {r} differs from the eager result"
+        _ = (x.float() * 2).sum()
         torch.cuda.synchronize()
 
 
