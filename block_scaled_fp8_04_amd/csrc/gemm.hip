@@ -470,6 +470,15 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
     constexpr bool kSpread = T::NSTAGE > 2;
 
     v4f acc[T::TM][T::TN];
+    // The unguarded fold loop folds the last sub-tile row of block kb during
+    // the first row's MFMAs of block kb + 1 (so no wave ends a block with folds
+    // that no MFMA hides): prev holds that row's block products, sc_last its
+    // scale.  Each sum still takes its block terms in order, so the results
+    // are the same bits.
+    v4f prev[T::TN];
+    float sc_last = 0.f;
+#pragma unroll
+    for (int j = 0; j < T::TN; ++j) prev[j] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < T::TM; ++i)
 #pragma unroll
@@ -570,7 +579,7 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
             // the previous row while the next A row is read.
             v8i fb[T::TN];
             v8i fa_cur, fa_nxt;
-            v4f cur_p[T::TN], prev[T::TN];
+            v4f cur_p[T::TN];
             float sc[T::TM];
             {
                 const uint8_t* r = As + (wm0 + lr) * kBlock;
@@ -593,6 +602,7 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
                 }
                 cur_p[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                     fb[j], fa_cur, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                acc[T::TM - 1][j] = prev[j] * sc_last + acc[T::TM - 1][j];
                 __builtin_amdgcn_sched_barrier(0);
             }
             {
@@ -633,17 +643,17 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
                 }
 #pragma unroll
                 for (int j = 0; j < T::TN; ++j) prev[j] = cur_p[j];
-                if (i + 1 < T::TM) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                // per MFMA four folds of the previous row; the next row's A reads go out
+                // after the first MFMA (about 1% faster than before it)
 #pragma unroll
                 for (int j = 0; j < T::TN; ++j) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if (j == 0 && i + 1 < T::TM) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
                     __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
-#pragma unroll
-            for (int j = 0; j < T::TN; ++j)
-                acc[T::TM - 1][j] = prev[j] * sc[T::TM - 1] + acc[T::TM - 1][j];
+            sc_last = sc[T::TM - 1];
         } else {
             v8i fb[T::TN];
 #pragma unroll
@@ -688,6 +698,11 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
         }
     }
 
+    // the last block's last row (the unguarded fold loop carries it into the next block)
+    if constexpr (!kGuard && !kHwScale) {
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j) acc[T::TM - 1][j] = prev[j] * sc_last + acc[T::TM - 1][j];
+    }
     // epilogue: lane holds row m0 + wm0 + 16 i + lr, columns n0 + wn0 + 16 j + 4 (lane >> 4) + 0..3
     if constexpr (kEpi == kEpiQuant) {
         quant_epilogue<T>(acc, qo, m0, m_end, n0, N, wave, wm0, wn0, lane, st.p[0]);
