@@ -491,20 +491,22 @@ def main():
 
     launch_mode = "eager"
     if args.graph:
-        # one step captured into a graph (the library only enqueues kernels on the
-        # current stream, with no allocation or memset), then timed as replays
+        # the K timed steps captured into one graph (the library only enqueues
+        # kernels on the current stream, with no allocation or memset), so the
+        # host's cost of a replay is not paid per step; warmup replays the same
+        # graph, then one timed replay runs exactly K steps
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            step.run()
-        for _ in range(max(1, args.warmup)):
+            for _ in range(args.steps):
+                step.run()
+        for _ in range(max(1, -(-args.warmup // args.steps))):
             graph.replay()
         torch.cuda.synchronize()
         t_start = time.perf_counter()
-        for _ in range(args.steps):
-            graph.replay()
+        graph.replay()
         torch.cuda.synchronize()
         ms_per_step = (time.perf_counter() - t_start) * 1e3 / args.steps
-        launch_mode = "hip-graph replay"
+        launch_mode = f"hip-graph replay ({args.steps} steps in one graph)"
 
     gemm_flop = sum(l[2] for l in step.launches)
     value = gemm_flop / (ms_per_step * 1e-3) / 1e12
