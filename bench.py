@@ -54,6 +54,13 @@ WORKLOADS = {"tiny": 0, "decode": 1, "moe-pair": 2, "dense-mlp": 3, "grouped": 4
 
 # ------------------------------------------------------------------ accounting
 
+def gemm_workspace(M, N, K, dev):
+    """The fp32 workspace bfp8_gemm uses at this shape (split-K of skinny problems, or the
+    split last round of large ones), or None when it uses none."""
+    n = bfp8.bfp8_gemm_workspace_size(M, N, K)
+    return torch.empty(max(1, n // 4), dtype=torch.float32, device=dev) if n else None
+
+
 def act_quant_bytes(M, K):
     return 2 * M * K + M * K + 4 * M * (K // BLOCK)
 
@@ -134,12 +141,13 @@ class Step:
             qh = torch.empty(M, K2, dtype=torch.uint8, device=dev)
             qhs = torch.empty(M, K2 // BLOCK, dtype=torch.float32, device=dev)
             y = torch.empty(M, N2, dtype=torch.bfloat16, device=dev)
+            work1, work2 = gemm_workspace(M, N1, K1, dev), gemm_workspace(M, N2, K2, dev)
             self.launches += [
                 ("act_quant_x", lambda: bfp8.bfp8_act_quant(x, q, qs), 0, act_quant_bytes(M, K1), "hbm"),
-                ("fp8_gemm_1", lambda: bfp8.bfp8_gemm(q, qs, w1, s1, h), 2 * M * N1 * K1,
+                ("fp8_gemm_1", lambda: bfp8.bfp8_gemm(q, qs, w1, s1, h, work1), 2 * M * N1 * K1,
                  gemm_bytes(M, N1, K1), "mfma"),
                 ("act_quant_h", lambda: bfp8.bfp8_act_quant(h, qh, qhs), 0, act_quant_bytes(M, K2), "hbm"),
-                ("fp8_gemm_2", lambda: bfp8.bfp8_gemm(qh, qhs, w2, s2, y), 2 * M * N2 * K2,
+                ("fp8_gemm_2", lambda: bfp8.bfp8_gemm(qh, qhs, w2, s2, y, work2), 2 * M * N2 * K2,
                  gemm_bytes(M, N2, K2), "mfma"),
             ]
             if c == 3:
@@ -181,11 +189,12 @@ class Step:
             qhs = torch.empty(M, K2 // BLOCK, dtype=torch.float32, device=dev)
             y = torch.empty(M, N2, dtype=torch.bfloat16, device=dev)
             wd = torch.empty(N1, K1, dtype=torch.bfloat16, device=dev)
+            work2 = gemm_workspace(M, N2, K2, dev)
             self.launches += [
                 ("act_quant_x", lambda: bfp8.bfp8_act_quant(x, q, qs), 0, act_quant_bytes(M, K1), "hbm"),
                 ("fp8_gemm_1_quant", lambda: bfp8.bfp8_gemm_act_quant(q, qs, w1, s1, qh, qhs),
                  2 * M * N1 * K1, M * K1 + N1 * K1 + M * N1 + 4 * M * (N1 // BLOCK), "mfma"),
-                ("fp8_gemm_2", lambda: bfp8.bfp8_gemm(qh, qhs, w2, s2, y), 2 * M * N2 * K2,
+                ("fp8_gemm_2", lambda: bfp8.bfp8_gemm(qh, qhs, w2, s2, y, work2), 2 * M * N2 * K2,
                  gemm_bytes(M, N2, K2), "mfma"),
                 ("weight_dequant", lambda: bfp8.bfp8_weight_dequant(w1, s1, wd), 0,
                  dequant_bytes(N1, K1), "hbm"),

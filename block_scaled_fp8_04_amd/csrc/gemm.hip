@@ -90,6 +90,24 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
     }
 }
 
+// Adds the tail's split partial sums ws[s][M][W] (W = N - n1) in split order
+// and writes bf16 columns [n1, N) of c (row stride N).  W % 4 == 0.
+__global__ __launch_bounds__(256) void tail_reduce_kernel(const float* __restrict__ ws,
+                                                          uint16_t* __restrict__ c, int64_t M,
+                                                          int64_t N, int64_t n1, int splits) {
+    const int64_t W = N - n1, W4 = W / 4, total = M * W4;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+        const int64_t row = i / W4, c4 = i - row * W4;
+        v4f sum = ((const v4f*)ws)[i];
+        for (int sp = 1; sp < splits; ++sp) sum = sum + ((const v4f*)(ws + (int64_t)sp * M * W))[i];
+        uint2 o;
+        o.x = pack_bf16x2(sum[0], sum[1]);
+        o.y = pack_bf16x2(sum[2], sum[3]);
+        *(uint2*)(c + row * N + n1 + 4 * c4) = o;
+    }
+}
+
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int NSTAGE_>
 struct BigTile {
     static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
@@ -208,7 +226,14 @@ struct QuantOut {
     uint8_t* q;
     float* qs;
 };
-constexpr int kEpiBf16 = 0, kEpiQuant = 1, kEpiSwiglu = 2;
+// kEpiF32: the tile multiplies K blocks [kb_lo, kb_hi) only and stores its
+// fp32 partial sums, row r and column n at ws[r * ldw + n - n_base].
+struct PartialOut {
+    int64_t kb_lo = 0, kb_hi = -1;      // kb_hi < 0: all K blocks
+    float* ws = nullptr;
+    int64_t ldw = 0, n_base = 0;
+};
+constexpr int kEpiBf16 = 0, kEpiQuant = 1, kEpiSwiglu = 2, kEpiF32 = 3;
 
 // act_quant fused into the GEMM epilogue ("Data flow", FP8 quantization
 // bullet: the next linear() quantizes this output in 128-element blocks).
@@ -372,13 +397,16 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
                                               const float* __restrict__ bs,
                                               uint16_t* __restrict__ c, int64_t m0, int64_t m_end,
                                               int64_t n0, int64_t N, int64_t K,
-                                              const Stages<T>& st, QuantOut qo = QuantOut{}) {
+                                              const Stages<T>& st, QuantOut qo = QuantOut{},
+                                              PartialOut po = PartialOut{}) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm0 = (wave / T::WAVES_N) * T::WM;
     const int wn0 = (wave % T::WAVES_N) * T::WN;
     const int64_t KB = K / kBlock;
+    // the K blocks this tile multiplies: [K0, KE)
+    const int64_t K0 = po.kb_lo, KE = po.kb_hi < 0 ? KB : po.kb_hi;
     const int64_t NBK = (N + kBlock - 1) / kBlock;
     const int64_t rows_a = (m_end - m0) < T::BM ? (m_end - m0) : T::BM;     // >= 1
     const int64_t rows_b = (N - n0) < T::BN ? (N - n0) : T::BN;            // >= 1
@@ -497,9 +525,9 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
     }
 
     // prologue: K blocks 0 .. NSTAGE-2 in flight, block s in stage s
-    issue(0, st.p[0]);
-    if (T::NSTAGE > 2 && 1 < KB) issue(1, st.p[1]);
-    if (T::NSTAGE > 3 && 2 < KB) issue(2, st.p[2]);
+    issue(K0, st.p[0]);
+    if (T::NSTAGE > 2 && K0 + 1 < KE) issue(K0 + 1, st.p[1]);
+    if (T::NSTAGE > 3 && K0 + 2 < KE) issue(K0 + 2, st.p[2]);
 
     const int lr = lane & 15;
     const int lk = (lane >> 4) * 2;
@@ -517,12 +545,12 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
         // blocks kb+1 .. kb+NSTAGE-2 are outstanding (loads complete in issue
         // order); the barrier then makes every wave's loads visible and
         // guarantees stage SF (block kb - 1) is no longer being read
-        if (kb + T::NSTAGE - 2 < KB)
+        if (kb + T::NSTAGE - 2 < KE)
             wait_vmcnt<T::LOADS_PER_STAGE * (T::NSTAGE - 2)>();
         else
             wait_vmcnt<0>();
         barrier_lds();
-        const bool more = kb + T::NSTAGE - 1 < KB;
+        const bool more = kb + T::NSTAGE - 1 < KE;
         // (the spread issue lives in the full-tile fold loop; other loops issue here)
         if ((kGuard || !kSpread || kHwScale) && more) issue(kb + T::NSTAGE - 1, st.p[SF]);
 
@@ -687,14 +715,14 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
         }
     };
 
-    for (int64_t kb0 = 0; kb0 < KB; kb0 += T::NSTAGE) {
+    for (int64_t kb0 = K0; kb0 < KE; kb0 += T::NSTAGE) {
         step(kb0, StageId<0>{});
-        if (kb0 + 1 < KB) step(kb0 + 1, StageId<1>{});
+        if (kb0 + 1 < KE) step(kb0 + 1, StageId<1>{});
         if constexpr (T::NSTAGE > 2) {
-            if (kb0 + 2 < KB) step(kb0 + 2, StageId<2>{});
+            if (kb0 + 2 < KE) step(kb0 + 2, StageId<2>{});
         }
         if constexpr (T::NSTAGE > 3) {
-            if (kb0 + 3 < KB) step(kb0 + 3, StageId<3>{});
+            if (kb0 + 3 < KE) step(kb0 + 3, StageId<3>{});
         }
     }
 
@@ -710,6 +738,20 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
     }
     if constexpr (kEpi == kEpiSwiglu) {
         swiglu_quant_epilogue<T>(acc, qo, m0, m_end, n0, N, wave, wm0, wn0, lane, st);
+        return;
+    }
+    if constexpr (kEpi == kEpiF32) {
+        const int cq = 4 * (lane >> 4);
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i) {
+            const int64_t row = m0 + wm0 + 16 * i + lr;
+#pragma unroll
+            for (int j = 0; j < T::TN; ++j) {
+                const int64_t col = n0 + wn0 + 16 * j + cq;
+                if (row < m_end && col + 3 < N)
+                    *(v4f*)(po.ws + row * po.ldw + (col - po.n_base)) = acc[i][j];
+            }
+        }
         return;
     }
     const int cq = 4 * (lane >> 4);
@@ -785,6 +827,33 @@ __global__ __launch_bounds__(T::THREADS, 1) void gemm_big_kernel(const uint8_t* 
         gemm_tile_big<T, false>(a, as, b, bs, c, m0, M, (int64_t)tn * T::BN, N, K, lds);
     else
         gemm_tile_big<T, true>(a, as, b, bs, c, m0, M, (int64_t)tn * T::BN, N, K, lds);
+}
+
+// The last, partly filled round of a large GEMM ("tail"): columns
+// [n1, N) in full 256-column tiles, each tile's K blocks split in `splits`
+// runs of kb_per blocks, so twice as many workgroups fill the round.  Split s
+// writes its fp32 partial sums to ws[s][M][N - n1]; tail_reduce_kernel adds
+// them in split order.  Workgroup id = s * tiles + tile, the tiles of one
+// split laid out over the XCDs as in gemm_big_kernel.
+template <class T>
+__global__ __launch_bounds__(T::THREADS, 1) void gemm_tail_kernel(
+    const uint8_t* __restrict__ a, const float* __restrict__ as, const uint8_t* __restrict__ b,
+    const float* __restrict__ bs, float* __restrict__ ws, int64_t M, int64_t N, int64_t K, int mt,
+    int nt_tail, int64_t n1, int64_t kb_per) {
+    BIG_TILE_STAGES(T, lds);
+    const int tiles = mt * nt_tail;
+    const int split = blockIdx.x / tiles;
+    int tm, tn;
+    tile_of(blockIdx.x - split * tiles, tiles, mt, nt_tail, tm, tn);
+    const int64_t KB = K / kBlock;
+    PartialOut po;
+    po.kb_lo = split * kb_per;
+    po.kb_hi = po.kb_lo + kb_per < KB ? po.kb_lo + kb_per : KB;
+    po.ldw = N - n1;
+    po.ws = ws + (int64_t)split * M * po.ldw;
+    po.n_base = n1;
+    gemm_tile_big<T, false, kEpiF32>(a, as, b, bs, nullptr, (int64_t)tm * T::BM, M,
+                                     n1 + (int64_t)tn * T::BN, N, K, lds, QuantOut{}, po);
 }
 
 // The GEMM with power-of-two scales applied by the MFMA (kHwScale).
@@ -1049,6 +1118,38 @@ static SplitPlan split_plan(int64_t M, int64_t N, int64_t K) {
     return p;
 }
 
+// Tail plan for large GEMMs on 256 x 256 tiles: when the tiles fill a few
+// whole rounds of the chip's 256 CUs and a last round at most half full, and
+// that last round is whole columns of tiles (rem = mt * nt_tail), the tail
+// columns run as two K halves (twice the workgroups) into an fp32 workspace,
+// then one reduction.  Measured on 8192 x 7168 x 18432 (3.5 rounds): the half
+// round cost 0.79 of a full round before.  Host-only arithmetic, planned for
+// 256 CUs, so bfp8_gemm_workspace_size needs no device.
+struct TailPlan {
+    int nt_main = 0, nt_tail = 0, splits = 0;
+    int64_t kb_per = 0;
+};
+
+static TailPlan tail_plan(int64_t M, int64_t N, int64_t K) {
+    TailPlan p;
+    constexpr int64_t kCUs = 256;
+    if (M <= 128 || M % 256 != 0 || N % 256 != 0) return p;
+    const int64_t mt = M / 256, nt = N / 256, tiles = mt * nt, KB = K / kBlock;
+    const int64_t rem = tiles % kCUs;
+    if (tiles < kCUs || rem == 0 || rem % mt != 0 || 2 * rem > kCUs || KB < 8) return p;
+    p.nt_tail = (int)(rem / mt);
+    p.nt_main = (int)(nt - p.nt_tail);
+    p.splits = 2;
+    p.kb_per = (KB + 1) / 2;
+    return p;
+}
+
+static size_t tail_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    const TailPlan p = tail_plan(M, N, K);
+    if (p.splits == 0) return 0;
+    return (size_t)p.splits * (size_t)M * (size_t)p.nt_tail * 256 * sizeof(float);
+}
+
 static size_t round256(size_t v) { return (v + 255) / 256 * 256; }
 
 // The FP8 branch of linear(): act_quant of x into the workspace, then the
@@ -1074,7 +1175,7 @@ hipError_t launch_linear_fp8(const void* x, const void* b, const float* bs, void
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     const SplitPlan p = split_plan(M, N, K);
-    if (p.splits < 2) return 0;
+    if (p.splits < 2) return tail_workspace_bytes(M, N, K);
     return (size_t)p.splits * (size_t)M * (size_t)N * sizeof(float);
 }
 
@@ -1147,7 +1248,33 @@ hipError_t launch_gemm(const void* a, const float* as, const void* b, const floa
                            (const float*)workspace, (uint16_t*)c, MN, plan.splits);
         return hipGetLastError();
     }
-    switch (gemm_config(M, N, K)) {
+    const GemmConfig cfg = gemm_config(M, N, K);
+    const TailPlan tp = tail_plan(M, N, K);
+    if (cfg == GemmConfig::kBig256x256 && workspace && tp.splits > 0 &&
+        workspace_bytes >= tail_workspace_bytes(M, N, K) && ((uintptr_t)c & 7u) == 0) {
+        // whole rounds of 256 x 256 tiles over columns [0, n1), then the tail
+        const int mt = (int)(M / 256);
+        const int64_t n1 = (int64_t)tp.nt_main * 256;
+        hipLaunchKernelGGL(gemm_big_kernel<BigSquare>, dim3(mt * tp.nt_main), dim3(BigSquare::THREADS),
+                           0, stream, (const uint8_t*)a, as, (const uint8_t*)b, bs, (uint16_t*)c, M,
+                           N, K, mt, tp.nt_main);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(gemm_tail_kernel<BigSquare>, dim3(mt * tp.nt_tail * tp.splits),
+                           dim3(BigSquare::THREADS), 0, stream, (const uint8_t*)a, as,
+                           (const uint8_t*)b, bs, (float*)workspace, M, N, K, mt, tp.nt_tail, n1,
+                           tp.kb_per);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int64_t quads = M * (N - n1) / 4;
+        int64_t grid = (quads + 255) / 256;
+        const int64_t cap = (int64_t)device_cu_count() * 8;
+        grid = grid < cap ? grid : cap;
+        hipLaunchKernelGGL(tail_reduce_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                           (const float*)workspace, (uint16_t*)c, M, N, n1, tp.splits);
+        return hipGetLastError();
+    }
+    switch (cfg) {
         case GemmConfig::kBig256x256:
             launch_big<BigSquare>(a, as, b, bs, c, M, N, K, stream);
             break;

@@ -100,9 +100,12 @@ int bfp8_weight_dequant(const void* w_e4m3, const float* s, void* out_bf16,
  *   a   : e4m3 [M, K], 16-byte aligned         a_s : fp32 [M, K/128]
  *   b   : e4m3 [N, K], 16-byte aligned         b_s : fp32 [ceil(N/128), K/128]
  *   c_bf16 : bf16 [M, N] output, 4-byte aligned (N odd: 2-byte)
- *   workspace : optional fp32 scratch for split-K on skinny problems; NULL
- *     disables split-K.  If non-NULL it must hold at least
- *     bfp8_gemm_workspace_size(M, N, K) bytes and be 16-byte aligned.
+ *   workspace : optional fp32 scratch: split-K partial sums on skinny problems
+ *     (M <= 64), and on large problems whose last round of 256 x 256 tiles is
+ *     at most half full, the partial sums of those tiles' two K halves.  NULL
+ *     disables both (one pass over K per tile).  If non-NULL it must hold at
+ *     least bfp8_gemm_workspace_size(M, N, K) bytes and be 16-byte aligned;
+ *     its contents on entry do not matter.
  * Errors: BFP8_ERR_SHAPE if M, N < 0, K <= 0, K % 128 != 0 or K >= 2^22 (the
  * tiles address rows with 32-bit byte offsets); BFP8_ERR_NULL; BFP8_ERR_ALIGN;
  * BFP8_ERR_WORKSPACE if workspace_bytes is too small. */
@@ -187,8 +190,9 @@ size_t bfp8_linear_fp8_workspace_size(int64_t M, int64_t N, int64_t K);
 int bfp8_linear_fp8(const void* x_bf16, const void* w, const float* w_s, void* y_bf16, int64_t M,
                     int64_t N, int64_t K, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of fp32 workspace bfp8_gemm would use for split-K at this shape
- * (0 when the shape does not use split-K).  Pure host function. */
+/* Bytes of fp32 workspace bfp8_gemm would use at this shape: split-K of a
+ * skinny problem, or the split last round of a large one (0 when neither
+ * applies).  Pure host function (the plan assumes the 256 CUs of MI355X). */
 size_t bfp8_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
 
 /* Grouped fp8_gemm over one GPU's share of routed experts ([BT] "MoE trace":

@@ -243,6 +243,11 @@ def test_gemm_chain_full_size(config):
     h = _gemm_case(q, s, w1, s1, f"{wl.name}:gemm1", rows=rows)
     qh, sh = _act_quant_case(h.cpu(), f"{wl.name}:act_quant(H)")
     _gemm_case(qh, sh, w2, s2, f"{wl.name}:gemm2", rows=rows)
+    need = bfp8.bfp8_gemm_workspace_size(qh.shape[0], w2.shape[0], qh.shape[1])
+    if need:
+        # with a workspace (as the benchmark runs it) the last round of tiles is split over K
+        work = torch.empty(need // 4, dtype=torch.float32, device=dev())
+        _gemm_case(qh, sh, w2, s2, f"{wl.name}:gemm2+workspace", rows=rows, workspace=work)
 
 
 def test_gemm_ragged_shapes():
@@ -281,6 +286,31 @@ def test_gemm_split_k_workspace():
         c2 = bfp8.gemm(q, s, w, ws, workspace=work)
         torch.cuda.synchronize()
         assert torch.equal(c1, c2), "split-K result depends on the workspace contents"
+        with pytest.raises(bfp8.Bfp8Error):
+            bfp8.bfp8_gemm(q, s, w, ws, torch.empty_like(c1), work[: need // 4 - 4])
+
+
+def test_gemm_tail_split_workspace():
+    """Large shapes whose last round of 256 x 256 tiles is at most half full and whole
+    columns of tiles run those columns as two K halves into the workspace: same tolerance,
+    canaries intact, independent of what the workspace held, too small a workspace refused."""
+    from block_scaled_fp8_04_amd import synth
+    g = torch.Generator().manual_seed(8)
+    # (M, N, K): 2 x 129 tiles (2 in the tail), 4 x 65 tiles (4), 8 x 33 tiles (8, odd K blocks)
+    for (M, N, K) in ((512, 33024, 1024), (1024, 16640, 2048), (2048, 8448, 1152)):
+        need = bfp8.bfp8_gemm_workspace_size(M, N, K)
+        assert need > 0, (M, N, K)
+        x = torch.randn(M, K, generator=g).to(torch.bfloat16).to(dev())
+        q, s = bfp8.act_quant(x)
+        w, ws = synth.weight(N, K, 1100 + M, 1200 + N)
+        w, ws = w.to(dev()), ws.to(dev())
+        rows = sample_rows(M, seed=M)
+        work = torch.full((need // 4,), float("nan"), dtype=torch.float32, device=dev())
+        c1 = _gemm_case(q, s, w, ws, f"tail-split[{M},{N},{K}]", rows=rows, workspace=work)
+        work.fill_(1e30)
+        c2 = bfp8.gemm(q, s, w, ws, workspace=work)
+        torch.cuda.synchronize()
+        assert torch.equal(c1, c2), "tail-split result depends on the workspace contents"
         with pytest.raises(bfp8.Bfp8Error):
             bfp8.bfp8_gemm(q, s, w, ws, torch.empty_like(c1), work[: need // 4 - 4])
 
