@@ -524,6 +524,13 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
         tm_valid = __builtin_amdgcn_readfirstlane(tm_valid);
     }
 
+    // Waves w and w + 4 share a SIMD.  Left alone, the scheduler favours the
+    // older of the two, which finishes its block early and waits at the barrier
+    // while the other runs alone; raising waves 4..7 one priority level keeps
+    // each pair even (2-6% faster on the eight-wave tiles, same bits; raising
+    // waves 0..3 instead, or alternating by block, measured no better).
+    if (T::WAVES == 8 && wave >= 4) __builtin_amdgcn_s_setprio(1);
+
     // prologue: K blocks 0 .. NSTAGE-2 in flight, block s in stage s
     issue(K0, st.p[0]);
     if (T::NSTAGE > 2 && K0 + 1 < KE) issue(K0 + 1, st.p[1]);
