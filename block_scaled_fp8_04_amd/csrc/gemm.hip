@@ -133,12 +133,20 @@ struct BigTile {
     // cost address-unit time (dropping them measured 4-6% faster).
     static constexpr int SB_OFF = WAVES * 256;
     static constexpr int S_BYTES = (WAVES * 256 + 256 + 1023) / 1024 * 1024;
-    static constexpr int LOADS_PER_STAGE = BM / 8 / WAVES + BN / 8 / WAVES + 2;
+    // Waves that issue the A and B row loads.  In the two-stage eight-wave
+    // tiles waves 0..3 issue all of them and waves 4..7 (which run one
+    // priority level up) only multiply: 3.5-4.6% faster on the dense shapes
+    // than every wave loading its share (loads from waves 4..7, or waves 0..3
+    // loading without the priority split, measured slower).  With more stages
+    // every wave loads its share (the waits count loads per wave).
+    static constexpr int LOADERS = (NSTAGE == 2 && WAVES == 8) ? 4 : WAVES;
+    static constexpr int A_INSTR = BM / 8 / LOADERS;        // 1 KB instructions per loading wave for A
+    static constexpr int B_INSTR = BN / 8 / LOADERS;
+    static constexpr int LOADS_PER_STAGE = A_INSTR + B_INSTR + 2;
 
     static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
-    static constexpr int A_INSTR = BM / 8 / WAVES;          // 1 KB instructions per wave for A
-    static constexpr int B_INSTR = BN / 8 / WAVES;
-    static_assert(BM % (8 * WAVES) == 0 && BN % (8 * WAVES) == 0, "tile rows must split over waves");
+    static_assert(BM % (8 * LOADERS) == 0 && BN % (8 * LOADERS) == 0,
+                  "tile rows must split over the loading waves");
     static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns must share one scale block");
     static_assert(S_INSTR <= WAVES, "one scale instruction per wave at most");
     static_assert(TM % 4 == 0, "scales are read four at a time");
@@ -420,7 +428,8 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
     const __amdgpu_buffer_rsrc_t rs_bs =
         make_rsrc(bs, (uint64_t)((kEpi == kEpiSwiglu) ? (N + 63) / 64 : NBK) * KB * 4);
 
-    // Direct-load sources.  Instruction i of this wave fills LDS rows
+    // Direct-load sources (used by the loading waves, wave < LOADERS).
+    // Instruction i of this wave fills LDS rows
     // r0 .. r0+7 (r0 = 8 * (wave * INSTR + i)); lane l writes physical chunk
     // l & 7 of row r0 + (l >> 3), which must hold logical chunk
     // (l & 7) ^ swz(row).  Offsets are relative to the tile's first row; the
@@ -465,12 +474,14 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
 
     auto issue = [&](int64_t kb, uint8_t* base) __attribute__((always_inline)) {
         const uint32_t ko = (uint32_t)(kb * kBlock);
+        if (T::LOADERS == T::WAVES || wave < T::LOADERS) {
 #pragma unroll
-        for (int i = 0; i < T::A_INSTR; ++i)
-            buf_lds16(rs_a, a_off[i], ko, base + (wave * T::A_INSTR + i) * 1024);
+            for (int i = 0; i < T::A_INSTR; ++i)
+                buf_lds16(rs_a, a_off[i], ko, base + (wave * T::A_INSTR + i) * 1024);
 #pragma unroll
-        for (int i = 0; i < T::B_INSTR; ++i)
-            buf_lds16(rs_b, b_off[i], ko, base + T::A_BYTES + (wave * T::B_INSTR + i) * 1024);
+            for (int i = 0; i < T::B_INSTR; ++i)
+                buf_lds16(rs_b, b_off[i], ko, base + T::A_BYTES + (wave * T::B_INSTR + i) * 1024);
+        }
         const uint32_t so = (uint32_t)(kb * 4);
         if (T::NSTAGE > 2 || wave < T::S_INSTR)
             buf_lds4(rs_as, as_off, so, base + T::A_BYTES + T::B_BYTES + wave * 256);
