@@ -112,6 +112,25 @@ def test_gemm_workspace_contract(lib):
     assert bfp8.bfp8_gemm_workspace_size(5, 5, 100) == 0
 
 
+def test_gemm_tail_split_plan():
+    """The workspace a large GEMM asks for: only when its 256 x 256 tiles leave a last round
+    (of 256 CUs) at most half full that is whole tile columns, and K has at least 8 blocks;
+    then 2 halves x M x (tail columns) fp32 partial sums."""
+    ws = bfp8.bfp8_gemm_workspace_size
+    # dense down projection: 32 x 28 tiles = 3.5 rounds, tail = 4 tile columns
+    assert ws(8192, 7168, 18432) == 2 * 8192 * 4 * 256 * 4
+    assert ws(8192, 5120, 18432) == 2 * 8192 * 4 * 256 * 4       # 2.5 rounds
+    assert ws(8192, 18432, 7168) == 0                               # 9 whole rounds
+    assert ws(8192, 6144, 18432) == 0                               # 3 whole rounds
+    assert ws(4096, 7168, 2048) == 0                                # 1.75 rounds: tail too full
+    assert ws(512, 33024, 1024) == 2 * 512 * 1 * 256 * 4            # 2 x 129 tiles
+    assert ws(2048, 8448, 1152) == 2 * 2048 * 1 * 256 * 4           # 8 x 33 tiles, 9 K blocks
+    assert ws(8192 + 128, 7168, 18432) == 0                         # M not a multiple of 256
+    assert ws(8192, 7168 + 128, 18432) == 0                         # N not a multiple of 256
+    assert ws(8192, 7168, 896) == 0                                 # fewer than 8 K blocks
+    assert ws(256, 256, 256) == 0                                   # less than one round
+
+
 def test_gemm_grouped_validation(lib):
     f = lib.bfp8_gemm_grouped
 
