@@ -22,6 +22,13 @@
 //    into LDS with buffer loads; the stages are distinct LDS arrays and the K
 //    loop is unrolled by the stage count, so every stage is named at compile
 //    time.  A vmcnt-counted wait and one barrier open each K block.
+//  * Wave roles in the eight-wave tiles: waves w and w + 4 share a SIMD, and
+//    waves 4..7 run one priority level up.  In the two-stage 256x256 tile
+//    waves 0..3 also issue all of the tile's A and B loads, so waves 4..7
+//    only multiply.
+//  * Large problems with a workspace whose last round of 256x256 tiles would
+//    run at most half full split those tiles over K into the workspace
+//    (gemm_tail_kernel) and add the halves in order (tail_reduce_kernel).
 //  * LDS rows are 128 bytes; the eight 16-byte chunks of row r are stored at
 //    chunk position (chunk ^ swz(r)) (see swz below), so the 16 rows read
 //    together by a fragment load (same logical chunk) hit no bank twice.
