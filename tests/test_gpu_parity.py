@@ -315,6 +315,39 @@ def test_gemm_tail_split_workspace():
             bfp8.bfp8_gemm(q, s, w, ws, torch.empty_like(c1), work[: need // 4 - 4])
 
 
+def test_gemm_workspace_paths_random_shapes():
+    """Seeded random shapes through both workspace paths: skinny problems (deep or shallow
+    split-K, whichever the plan picks) and large ones whose last round of tiles is split over
+    K.  Each runs with and without the workspace; both within tolerance of the oracle on
+    sampled rows, canaries intact."""
+    from block_scaled_fp8_04_amd import synth
+    rng = np.random.default_rng(11)
+    g = torch.Generator().manual_seed(12)
+    shapes = []
+    for _ in range(8):                                   # skinny: M <= 64
+        M = int(rng.integers(1, 65))
+        N = int(rng.integers(1, 40)) * 64 + int(rng.integers(0, 64))
+        K = int(rng.integers(9, 40)) * 128
+        shapes.append((M, N, K))
+    for mt, rem_cols in ((2, 1), (4, 2), (8, 1)):        # large: whole rounds + a short tail
+        nt = 256 // mt + rem_cols
+        K = int(rng.integers(8, 24)) * 128
+        shapes.append((mt * 256, nt * 256, K))
+    for (M, N, K) in shapes:
+        need = bfp8.bfp8_gemm_workspace_size(M, N, K)
+        x = torch.randn(M, K, generator=g).to(torch.bfloat16).to(dev())
+        q, s = bfp8.act_quant(x)
+        w, ws = synth.weight(N, K, 1300 + M, 1400 + N)
+        w, ws = w.to(dev()), ws.to(dev())
+        rows = None if M <= 64 else sample_rows(M, extra=8, seed=M)
+        _gemm_case(q, s, w, ws, f"random[{M},{N},{K}] no workspace", rows=rows)
+        if need:
+            work = torch.full((need // 4,), float("nan"), dtype=torch.float32, device=dev())
+            _gemm_case(q, s, w, ws, f"random[{M},{N},{K}] workspace {need} B", rows=rows,
+                       workspace=work)
+    assert sum(1 for (M, N, K) in shapes if M > 64 and bfp8.bfp8_gemm_workspace_size(M, N, K)) == 3
+
+
 def test_gemm_identity_bit_exact():
     """G3: W = I (code 0x38, scale 1) gives bf16(fl32(dec(q) * s)) exactly."""
     wl = workload(0)
