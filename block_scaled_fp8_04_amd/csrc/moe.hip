@@ -22,6 +22,13 @@
 //        (expert, block) pair; offsets[g] is the value at (g, 0).
 //     3. dispatch_place_kernel: row = ws[g * B + b] + rank; writes slot_row
 //        and row_token.
+//     When the count table is small (it fits 64 KB of LDS, and its size times
+//     the number of workgroups is at most kFusedScanReads), steps 2 and 3 are
+//     one kernel instead, dispatch_scan_place_kernel: every workgroup copies
+//     the table into LDS and sums it itself (per expert the count over all
+//     blocks and over the blocks before its own, then an exclusive scan over
+//     experts), which gives the same row for every entry without a
+//     single-workgroup pass between rank and place.
 //   combine: y[t, :] = bf16( sum over the token's local slots, in slot
 //     order, of weight * out[slot_row] ) accumulated in fp32.  One workgroup
 //     per (token, 2048-column chunk), tokens along grid x; a lane owns 8
@@ -141,6 +148,96 @@ __global__ __launch_bounds__(kDispatchBlock) void dispatch_place_kernel(
     row_token[row] = (int32_t)(i / k);
 }
 
+// Limits of the fused kernel: the count table fits its LDS, and the table
+// entries read by all its workgroups together stay bounded.
+constexpr int kFusedScanLds = 16384;                      // int32 entries (64 KB)
+constexpr int64_t kFusedScanReads = int64_t(1) << 22;
+
+// Steps 2 and 3 in one kernel (workgroup b = the rank kernel's workgroup b).
+// The workgroup copies the count table into LDS (all loads in flight at
+// once), then base[g] = (entries of experts before g) + (entries of expert g
+// in blocks before b), which is ws[g * nblk + b] after step 2's exclusive scan.
+__global__ __launch_bounds__(kDispatchBlock) void dispatch_scan_place_kernel(
+    int64_t n, int k, int G, int nblk, const int32_t* __restrict__ ws,
+    int32_t* __restrict__ slot_row, int32_t* __restrict__ row_token, int32_t* __restrict__ off) {
+    extern __shared__ int32_t tab[];                      // [G][nblk]
+    __shared__ int32_t tot[kMoeMaxGroups];
+    __shared__ int32_t base[kMoeMaxGroups];
+    constexpr int U = 32;                                 // loads per thread in flight
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int b = blockIdx.x;
+    const int64_t i = (int64_t)b * kDispatchBlock + tid;
+    const int32_t parked = i < n ? slot_row[i] : -1;
+    const int len = G * nblk;
+    for (int q0 = 0; q0 < len; q0 += U * kDispatchBlock) {
+        int32_t x[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int q = q0 + u * kDispatchBlock + tid;
+            x[u] = q < len ? ws[q] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int q = q0 + u * kDispatchBlock + tid;
+            if (q < len) tab[q] = x[u];
+        }
+    }
+    __syncthreads();
+    // tpr lanes (a power of two, inside one wave) sum one expert's row
+    int tpr = 64;
+    while (tpr > 1 && tpr * G > kDispatchBlock) tpr >>= 1;
+    const int rows_per_pass = kDispatchBlock / tpr;
+    const int sub = lane & (tpr - 1);
+    for (int g0 = 0; g0 < G; g0 += rows_per_pass) {
+        const int g = g0 + tid / tpr;
+        int32_t t = 0, below = 0;
+        if (g < G) {
+            const int32_t* row = tab + g * nblk;
+#pragma unroll 8
+            for (int j = sub; j < nblk; j += tpr) {
+                const int32_t v = row[j];
+                t += v;
+                below += j < b ? v : 0;
+            }
+        }
+        for (int d = 1; d < tpr; d <<= 1) {
+            t += __shfl_xor(t, d);
+            below += __shfl_xor(below, d);
+        }
+        if (g < G && sub == 0) {
+            tot[g] = t;
+            base[g] = below;
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {
+        int32_t carry = 0;
+        for (int g0 = 0; g0 < G; g0 += 64) {
+            const int g = g0 + lane;
+            const int32_t v = g < G ? tot[g] : 0;
+            int32_t incl = v;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int32_t y = __shfl_up(incl, d);
+                if (lane >= d) incl += y;
+            }
+            if (g < G) {
+                const int32_t excl = carry + incl - v;
+                base[g] += excl;
+                if (b == 0) off[g] = excl;
+            }
+            carry += __shfl(incl, 63);
+        }
+        if (b == 0 && lane == 0) off[G] = carry;
+    }
+    __syncthreads();
+    if (parked < 0) return;
+    const int e = parked >> 16, r = parked & 0xFFFF;
+    const int32_t row = base[e] + r;
+    slot_row[i] = row;
+    row_token[row] = (int32_t)(i / k);
+}
+
 size_t moe_dispatch_workspace_bytes(int64_t T, int32_t k, int32_t G) {
     const int64_t n = T * (int64_t)k;
     const int64_t nblk = (n + kDispatchBlock - 1) / kDispatchBlock;
@@ -158,6 +255,13 @@ hipError_t launch_moe_dispatch(const int32_t* topk, int64_t T, int32_t k, int32_
                            n, lo, (int)G, nblk, slot_row, w);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+        const int64_t len = (int64_t)G * nblk;
+        if (len <= kFusedScanLds && len * nblk <= kFusedScanReads) {
+            hipLaunchKernelGGL(dispatch_scan_place_kernel, dim3(nblk), dim3(kDispatchBlock),
+                               (size_t)len * 4, stream, n, (int)k, (int)G, nblk, w, slot_row,
+                               row_token, off);
+            return hipGetLastError();
+        }
     }
     hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, stream, w, (int)G, nblk, off);
     hipError_t e = hipGetLastError();

@@ -67,6 +67,11 @@ def test_dispatch_golden_and_random():
         (4096, 8, 256, 0, 1, True),      # single local expert
         (700, 8, 2048, 0, 1024, True),   # the largest group count
         (257, 64, 96, 0, 96, True),      # 64 slots per token
+        # G * nblk^2 (count-table entries read by the fused scan-and-place
+        # kernel over all workgroups, nblk = 256 here) at its limit of 2^22,
+        # then just above it (the separate single-workgroup scan)
+        (8192, 8, 256, 0, 64, True),
+        (8192, 8, 256, 0, 65, True),
     ]
     for i, (T, k, E, lo, G, distinct) in enumerate(cases):
         _dispatch_case(_topk(T, k, E, 2000 + i, distinct), lo, G, f"case {i}")
