@@ -240,6 +240,7 @@ def test_combine_vector_and_scalar_paths():
     _combine_case(90, 6, 32, 4, 12, 100, 3020, "scalar N=100")
     _combine_case(50, 4, 16, 0, 16, 2048, 3030, "scalar (unaligned y)", y_offset=1)
     _combine_case(70, 8, 256, 250, 6, 256, 3040, "mostly empty tokens")
+    _combine_case(100, 12, 32, 0, 32, 2048, 3050, "vector k=12 (every slot local, two slot groups)")
 
 
 def test_combine_skips_rows_past_capacity():
