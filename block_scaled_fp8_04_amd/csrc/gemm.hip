@@ -405,7 +405,11 @@ __device__ __forceinline__ void swiglu_quant_epilogue(v4f (&acc)[T::TM][T::TN], 
 // kHwScale: every activation and weight scale is a power of two (the e8m0
 // reading of scale_fmt), so the MFMA applies them itself (its per-row e8m0
 // scale operands) and accumulates across K blocks with no fold.
-template <class T, bool kGuard, int kEpi = kEpiBf16, bool kHwScale = false>
+// kStagedStore: interior bf16 tiles of the two-stage tile store through LDS
+// (whole 128-byte row pieces); the grouped kernel leaves it off, since the
+// extra epilogue path makes its heavy tile spill.
+template <class T, bool kGuard, int kEpi = kEpiBf16, bool kHwScale = false,
+          bool kStagedStore = true>
 __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
                                               const float* __restrict__ as,
                                               const uint8_t* __restrict__ b,
@@ -782,6 +786,45 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
     const int cq = 4 * (lane >> 4);
     const bool interior = (m0 + T::BM <= m_end) && (n0 + T::BN <= N);
     const bool vec = interior && (N % 4 == 0) && (((uintptr_t)c & 7u) == 0);
+    if constexpr (kStagedStore && T::NSTAGE == 2 && T::WN == 64 && T::TM % 4 == 0) {
+        // Two-stage tiles: after a barrier the first stage is free.  Each wave
+        // turns 64 of its rows at a time into bf16 rows of 128 bytes there
+        // (16-byte chunks XOR-swizzled by row), then stores whole 128-byte
+        // row pieces, 16 bytes per lane.
+        if (vec && (N % 8 == 0) && (((uintptr_t)c & 15u) == 0)) {
+            __syncthreads();                      // every wave is past its last LDS read
+            uint8_t* buf = st.p[0] + wave * 8192;
+#pragma unroll
+            for (int h = 0; h < T::TM / 4; ++h) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * i + lr;
+#pragma unroll
+                    for (int j = 0; j < T::TN; ++j) {
+                        const int byte = (16 * j + cq) * 2;
+                        uint2 v;
+                        v.x = pack_bf16x2(acc[4 * h + i][j][0], acc[4 * h + i][j][1]);
+                        v.y = pack_bf16x2(acc[4 * h + i][j][2], acc[4 * h + i][j][3]);
+                        *(uint2*)(buf + r * 128 + ((((byte >> 4) ^ (r & 7))) << 4) + (byte & 15)) = v;
+                    }
+                }
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                uint4 o[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const int r = 8 * q + (lane >> 3), ch = lane & 7;
+                    o[q] = *(const uint4*)(buf + r * 128 + ((ch ^ (r & 7)) << 4));
+                }
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const int r = 8 * q + (lane >> 3), ch = lane & 7;
+                    *(uint4*)(c + (m0 + wm0 + 64 * h + r) * N + n0 + wn0 + ch * 8) = o[q];
+                }
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            }
+            return;
+        }
+    }
     if (vec) {
 #pragma unroll
         for (int i = 0; i < T::TM; ++i) {
@@ -1000,8 +1043,9 @@ __global__ __launch_bounds__(T::THREADS, 1) void gemm_grouped_big_kernel(
             rest -= mcount * nt;
         }
         const int64_t m0 = g_lo + tm * (kLight ? HBM : T::BM), m_end = g_hi;
-        gemm_tile_big<T, kLight>(a, as, b + (int64_t)g * N * K, bs + (int64_t)g * NB * KB, c, m0,
-                                 m_end, tn * T::BN, N, K, lds);
+        gemm_tile_big<T, kLight, kEpiBf16, false, false>(a, as, b + (int64_t)g * N * K,
+                                                         bs + (int64_t)g * NB * KB, c, m0, m_end,
+                                                         tn * T::BN, N, K, lds);
     }
 }
 
