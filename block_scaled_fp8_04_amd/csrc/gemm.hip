@@ -258,15 +258,19 @@ constexpr int kEpiBf16 = 0, kEpiQuant = 1, kEpiSwiglu = 2, kEpiF32 = 3;
 // quotient and e4m3 conversion.  A 128-column block of a row spans the 64
 // columns of two neighbouring waves (wave and wave ^ 1): each wave reduces its
 // part over its lanes, the two halves meet in LDS, and each wave writes its
-// own 64 codes per row (4 bytes per lane and sub-tile); the even wave writes
-// the row's scale.  Requires N % 128 == 0, so blocks past N are whole and
-// skipped.
+// own 64 codes per row; the even wave writes the row's scale.  With a 16-byte
+// aligned q the codes go through LDS first (each wave's WM rows of 64 bytes
+// in the second stage, 16-byte chunks XOR-swizzled by row), so every store
+// writes a whole 64-byte row piece, 16 bytes per lane; otherwise each lane
+// stores its 4 bytes per sub-tile directly.  Requires N % 128 == 0, so
+// blocks past N are whole and skipped.
 template <class T>
 __device__ __forceinline__ void quant_epilogue(v4f (&acc)[T::TM][T::TN], const QuantOut& qo,
                                                int64_t m0, int64_t m_end, int64_t n0, int64_t N,
                                                int wave, int wm0, int wn0, int lane,
-                                               uint8_t* lds_scratch) {
+                                               uint8_t* lds_scratch, uint8_t* lds_codes) {
     static_assert(T::WN == 64, "a 128-column block spans two waves of 64 columns");
+    static_assert(T::WAVES * T::WM * 64 <= T::STAGE, "the staged codes fit one stage");
     const int lr = lane & 15, g = lane >> 4;
     float pm[T::TM];
 #pragma unroll
@@ -293,6 +297,8 @@ __device__ __forceinline__ void quant_epilogue(v4f (&acc)[T::TM][T::TN], const Q
     __syncthreads();
     const bool block_valid = n0 + wn0 < N;          // N % 128 == 0: the whole block or none
     const int64_t nbq = N / kBlock;
+    const bool staged = ((uintptr_t)qo.q & 15u) == 0;
+    uint8_t* cbuf = lds_codes + wave * (T::WM * 64);
 #pragma unroll
     for (int i = 0; i < T::TM; ++i) {
         const float amax = fmaxf(pm[i], part[(wave ^ 1) * T::WM + 16 * i + lr]);
@@ -300,15 +306,31 @@ __device__ __forceinline__ void quant_epilogue(v4f (&acc)[T::TM][T::TN], const Q
         const float rcp = 1.0f / s;
         const int64_t row = m0 + wm0 + 16 * i + lr;
         if (row < m_end && block_valid) {
+            const int r = 16 * i + lr;
             uint8_t* qrow = qo.q + row * N + n0 + wn0 + 4 * g;
 #pragma unroll
             for (int j = 0; j < T::TN; ++j) {
                 const uint32_t codes = e4m3_encode4<true>(
                     quotient(acc[i][j][0], s, rcp), quotient(acc[i][j][1], s, rcp),
                     quotient(acc[i][j][2], s, rcp), quotient(acc[i][j][3], s, rcp));
-                *(uint32_t*)(qrow + 16 * j) = codes;
+                if (staged)
+                    *(uint32_t*)(cbuf + r * 64 + ((j ^ ((r >> 2) & 3)) << 4) + 4 * g) = codes;
+                else
+                    *(uint32_t*)(qrow + 16 * j) = codes;
             }
             if (g == 0 && (wn0 & 127) == 0) qo.qs[row * nbq + ((n0 + wn0) >> 7)] = s;
+        }
+    }
+    if (staged && block_valid) {
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+        for (int q = 0; q < T::WM / 16; ++q) {
+            const int r = 16 * q + (lane >> 2), ch = lane & 3;
+            const int64_t row = m0 + wm0 + r;
+            if (row < m_end) {
+                const uint4 v = *(const uint4*)(cbuf + r * 64 + ((ch ^ ((r >> 2) & 3)) << 4));
+                *(uint4*)(qo.q + row * N + n0 + wn0 + ch * 16) = v;
+            }
         }
     }
 }
@@ -762,7 +784,7 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
     }
     // epilogue: lane holds row m0 + wm0 + 16 i + lr, columns n0 + wn0 + 16 j + 4 (lane >> 4) + 0..3
     if constexpr (kEpi == kEpiQuant) {
-        quant_epilogue<T>(acc, qo, m0, m_end, n0, N, wave, wm0, wn0, lane, st.p[0]);
+        quant_epilogue<T>(acc, qo, m0, m_end, n0, N, wave, wm0, wn0, lane, st.p[0], st.p[1]);
         return;
     }
     if constexpr (kEpi == kEpiSwiglu) {
