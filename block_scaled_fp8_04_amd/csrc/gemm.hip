@@ -808,39 +808,43 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
     const int cq = 4 * (lane >> 4);
     const bool interior = (m0 + T::BM <= m_end) && (n0 + T::BN <= N);
     const bool vec = interior && (N % 4 == 0) && (((uintptr_t)c & 7u) == 0);
-    if constexpr (kStagedStore && T::NSTAGE == 2 && T::WN == 64 && T::TM % 4 == 0) {
-        // Two-stage tiles: after a barrier the first stage is free.  Each wave
-        // turns 64 of its rows at a time into bf16 rows of 128 bytes there
-        // (16-byte chunks XOR-swizzled by row), then stores whole 128-byte
-        // row pieces, 16 bytes per lane.
+    // rows per pass of the staged store: 64 where every wave's 8 KB fits one stage, else 32
+    constexpr int kRP = T::WAVES * 64 * 128 <= T::STAGE ? 64 : 32;
+    constexpr int kSub = kRP / 16;                          // sub-tile rows per pass
+    if constexpr (kStagedStore && T::WN == 64 && T::TM % kSub == 0 &&
+                  T::WAVES * kRP * 128 <= T::STAGE) {
+        // After a barrier (no loads are in flight after the last K block) the
+        // first stage is free.  Each wave turns kRP of its rows at a time into
+        // bf16 rows of 128 bytes there (16-byte chunks XOR-swizzled by row),
+        // then stores whole 128-byte row pieces, 16 bytes per lane.
         if (vec && (N % 8 == 0) && (((uintptr_t)c & 15u) == 0)) {
             __syncthreads();                      // every wave is past its last LDS read
-            uint8_t* buf = st.p[0] + wave * 8192;
+            uint8_t* buf = st.p[0] + wave * (kRP * 128);
 #pragma unroll
-            for (int h = 0; h < T::TM / 4; ++h) {
+            for (int h = 0; h < T::TM / kSub; ++h) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
+                for (int i = 0; i < kSub; ++i) {
                     const int r = 16 * i + lr;
 #pragma unroll
                     for (int j = 0; j < T::TN; ++j) {
                         const int byte = (16 * j + cq) * 2;
                         uint2 v;
-                        v.x = pack_bf16x2(acc[4 * h + i][j][0], acc[4 * h + i][j][1]);
-                        v.y = pack_bf16x2(acc[4 * h + i][j][2], acc[4 * h + i][j][3]);
+                        v.x = pack_bf16x2(acc[kSub * h + i][j][0], acc[kSub * h + i][j][1]);
+                        v.y = pack_bf16x2(acc[kSub * h + i][j][2], acc[kSub * h + i][j][3]);
                         *(uint2*)(buf + r * 128 + ((((byte >> 4) ^ (r & 7))) << 4) + (byte & 15)) = v;
                     }
                 }
                 __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-                uint4 o[8];
+                uint4 o[kRP / 8];
 #pragma unroll
-                for (int q = 0; q < 8; ++q) {
+                for (int q = 0; q < kRP / 8; ++q) {
                     const int r = 8 * q + (lane >> 3), ch = lane & 7;
                     o[q] = *(const uint4*)(buf + r * 128 + ((ch ^ (r & 7)) << 4));
                 }
 #pragma unroll
-                for (int q = 0; q < 8; ++q) {
+                for (int q = 0; q < kRP / 8; ++q) {
                     const int r = 8 * q + (lane >> 3), ch = lane & 7;
-                    *(uint4*)(c + (m0 + wm0 + 64 * h + r) * N + n0 + wn0 + ch * 8) = o[q];
+                    *(uint4*)(c + (m0 + wm0 + kRP * h + r) * N + n0 + wn0 + ch * 8) = o[q];
                 }
                 __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
             }
