@@ -210,6 +210,48 @@ __device__ __forceinline__ void bf16_tile(const uint16_t* __restrict__ a,
     // epilogue: lane holds row m0 + wm0 + 16 i + lr, columns n0 + wn0 + 16 j + 4 g + 0..3
     const bool interior = (m0 + T::BM <= M) && (n0 + T::BN <= N);
     const bool vec = interior && (N % 4 == 0) && (((uintptr_t)c & 7u) == 0);
+    // Staged store (as in the fp8 GEMM): after a barrier (no loads are in
+    // flight after the last K step) the first stage is free; each wave turns
+    // kRP of its rows at a time into bf16 rows of 128 bytes there (16-byte
+    // chunks XOR-swizzled by row) and stores whole 128-byte row pieces, 16
+    // bytes per lane, instead of 8 bytes per lane and sub-tile.
+    constexpr int kRP = T::WAVES * 64 * 128 <= T::STAGE ? 64 : 32;
+    constexpr int kSub = kRP / 16;
+    if constexpr (T::WN == 64 && T::TM % kSub == 0 && T::WAVES * kRP * 128 <= T::STAGE) {
+        if (vec && (N % 8 == 0) && (((uintptr_t)c & 15u) == 0)) {
+            __syncthreads();                      // every wave is past its last LDS read
+            uint8_t* buf = st.p[0] + wave * (kRP * 128);
+#pragma unroll
+            for (int h = 0; h < T::TM / kSub; ++h) {
+#pragma unroll
+                for (int i = 0; i < kSub; ++i) {
+                    const int r = 16 * i + lr;
+#pragma unroll
+                    for (int j = 0; j < T::TN; ++j) {
+                        const int byte = (16 * j + 4 * g) * 2;
+                        uint2 v;
+                        v.x = pack_bf16x2(acc[kSub * h + i][j][0], acc[kSub * h + i][j][1]);
+                        v.y = pack_bf16x2(acc[kSub * h + i][j][2], acc[kSub * h + i][j][3]);
+                        *(uint2*)(buf + r * 128 + (((byte >> 4) ^ (r & 7)) << 4) + (byte & 15)) = v;
+                    }
+                }
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                uint4 o[kRP / 8];
+#pragma unroll
+                for (int q = 0; q < kRP / 8; ++q) {
+                    const int r = 8 * q + (lane >> 3), ch = lane & 7;
+                    o[q] = *(const uint4*)(buf + r * 128 + ((ch ^ (r & 7)) << 4));
+                }
+#pragma unroll
+                for (int q = 0; q < kRP / 8; ++q) {
+                    const int r = 8 * q + (lane >> 3), ch = lane & 7;
+                    *(uint4*)(c + (m0 + wm0 + kRP * h + r) * N + n0 + wn0 + ch * 8) = o[q];
+                }
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            }
+            return;
+        }
+    }
     if (vec) {
 #pragma unroll
         for (int i = 0; i < T::TM; ++i) {
