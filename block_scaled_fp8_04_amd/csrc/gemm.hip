@@ -427,9 +427,9 @@ __device__ __forceinline__ void swiglu_quant_epilogue(v4f (&acc)[T::TM][T::TN], 
 // kHwScale: every activation and weight scale is a power of two (the e8m0
 // reading of scale_fmt), so the MFMA applies them itself (its per-row e8m0
 // scale operands) and accumulates across K blocks with no fold.
-// kStagedStore: interior bf16 tiles of the two-stage tile store through LDS
-// (whole 128-byte row pieces); the grouped kernel leaves it off, since the
-// extra epilogue path makes its heavy tile spill.
+// kStagedStore: interior bf16 tiles store through LDS (whole 128-byte row
+// pieces); the grouped kernel leaves it off, since the extra epilogue path
+// makes its heavy tile spill.
 template <class T, bool kGuard, int kEpi = kEpiBf16, bool kHwScale = false,
           bool kStagedStore = true>
 __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,

@@ -15,8 +15,9 @@
 //    change the sum.  The MFMA accumulates straight into the fp32 sum (no
 //    block scales on this branch).
 //  * Operands go weight-first, so a lane owns one output row and four
-//    consecutive columns of each sub-tile (8-byte bf16 stores), as in the fp8
-//    kernel.
+//    consecutive columns of each sub-tile, as in the fp8 kernel; interior
+//    tiles of the two larger shapes store them through LDS as whole 128-byte
+//    row pieces, other tiles directly (8 bytes per lane and sub-tile).
 //  * Tiles 256x256 (8 waves of 128x64, 2 LDS stages of 64 KB), 256x128
 //    (8 waves of 64x64, 3 stages of 48 KB) and 64x64 (4 waves of 32x32,
 //    3 stages of 16 KB) by problem size.  A and B steps go straight to LDS
