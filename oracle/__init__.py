@@ -4,7 +4,7 @@ TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
 CPU-baseline leg are the only callers.  The product path never imports this
 package, and this package never imports the product package.
 
-Every function is a thin ctypes call into ``bfp8_oracle.c`` (plain loops, no
+Every function is a thin ctypes call into ``bfp8_oracle.cpp`` (plain loops, no
 blocking or reordering).  Conventions:
 
 * bf16 tensors travel as ``numpy.uint16`` arrays of bit patterns;
@@ -32,7 +32,7 @@ E4M3_MAX = 448.0
 
 
 class Oracle:
-    """ctypes front end over one build of ``bfp8_oracle.c``.
+    """ctypes front end over one build of ``bfp8_oracle.cpp``.
 
     The module-level functions use the library built in this folder; the
     tests also load deliberately broken builds through this class to show

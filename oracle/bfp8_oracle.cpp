@@ -1,5 +1,5 @@
 /*
- * bfp8_oracle.c - plain, slow CPU oracle for the block-scaled FP8 linear path.
+ * bfp8_oracle.cpp - plain, slow CPU oracle for the block-scaled FP8 linear path.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing in the product path links, loads or
  * calls this file; only the test suite, the smoke check and the benchmark's
@@ -46,16 +46,37 @@
  * brute force, closed forms, torch's own e4m3/bf16 casts or exact rational
  * arithmetic, except the value of ORACLE_AMAX_FLOOR (the pages give none),
  * which is "parity unpinned".
+ *
+ * Plain C++17: loops over rows and elements, std::thread over output rows for
+ * the GEMM references, every export extern "C" so ctypes can load it.
  */
 #include <math.h>
-#include <pthread.h>
 #include <stdint.h>
-#include <stdlib.h>
 #include <string.h>
+
+#include <thread>
+#include <vector>
 
 #define ORACLE_BLOCK 128
 #define ORACLE_E4M3_MAX 448.0f
 #define ORACLE_AMAX_FLOOR 1e-4f
+
+/* Runs worker(jobs[t]) for t = 0 .. n-1, job 0 on the calling thread; a job
+ * whose thread cannot be started runs on the calling thread too. */
+template <class Job, class Fn>
+static void run_jobs(std::vector<Job>& jobs, Fn worker) {
+    std::vector<std::thread> th;
+    size_t t = 1;
+    try {
+        for (; t < jobs.size(); ++t) th.emplace_back(worker, &jobs[t]);
+    } catch (...) {
+        for (; t < jobs.size(); ++t) worker(&jobs[t]);
+    }
+    worker(&jobs[0]);
+    for (auto& x : th) x.join();
+}
+
+extern "C" {
 
 /* ---------------------------------------------------------------- formats */
 
@@ -229,7 +250,7 @@ void oracle_weight_dequant(const uint8_t* w, const float* S, uint16_t* out,
  * (each product is an integer multiple of 2^-18 below 2^18 in size, and 128 of
  * them stay below 2^53 units).  Only the listed rows are computed, into
  * out[i*N + n] for rows[i]. */
-typedef struct {
+struct gemm_job {
     const uint8_t *a, *b;
     const float *sa, *sb;
     int64_t N, K;
@@ -240,7 +261,7 @@ typedef struct {
     double* out;
     int tid, nthreads;
     float table[256];
-} gemm_job;
+};
 
 static void gemm_row(const gemm_job* J, const uint8_t* b, const float* sb,
                      int64_t m, double* out_row) {
@@ -262,8 +283,7 @@ static void gemm_row(const gemm_job* J, const uint8_t* b, const float* sb,
     }
 }
 
-static void* gemm_worker(void* arg) {
-    gemm_job* J = (gemm_job*)arg;
+static void gemm_worker(gemm_job* J) {
     int64_t KB = J->K / ORACLE_BLOCK;
     int64_t NB = (J->N + ORACLE_BLOCK - 1) / ORACLE_BLOCK;
     for (int64_t i = J->tid; i < J->nrows; i += J->nthreads) {
@@ -280,7 +300,6 @@ static void* gemm_worker(void* arg) {
         gemm_row(J, J->b + (int64_t)g * J->N * J->K, J->sb + (int64_t)g * NB * KB,
                  m, out_row);
     }
-    return NULL;
 }
 
 static int run_gemm_rows(const uint8_t* a, const float* sa, const uint8_t* b,
@@ -289,9 +308,7 @@ static int run_gemm_rows(const uint8_t* a, const float* sa, const uint8_t* b,
                          double* out, int nthreads) {
     if (nthreads < 1) nthreads = 1;
     if (nthreads > 256) nthreads = 256;
-    gemm_job* jobs = (gemm_job*)calloc((size_t)nthreads, sizeof(gemm_job));
-    pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
-    if (!jobs || !th) { free(jobs); free(th); return -2; }
+    std::vector<gemm_job> jobs((size_t)nthreads);
     for (int t = 0; t < nthreads; ++t) {
         gemm_job* J = &jobs[t];
         J->a = a; J->b = b; J->sa = sa; J->sb = sb; J->N = N; J->K = K;
@@ -300,16 +317,7 @@ static int run_gemm_rows(const uint8_t* a, const float* sa, const uint8_t* b,
         J->tid = t; J->nthreads = nthreads;
         for (int c = 0; c < 256; ++c) J->table[c] = oracle_e4m3_decode((uint8_t)c);
     }
-    int started = 0;
-    for (int t = 1; t < nthreads; ++t) {
-        if (pthread_create(&th[t], NULL, gemm_worker, &jobs[t]) != 0) break;
-        started = t;
-    }
-    /* rows of threads that failed to start are done on this thread */
-    for (int t = started + 1; t < nthreads; ++t) gemm_worker(&jobs[t]);
-    gemm_worker(&jobs[0]);
-    for (int t = 1; t <= started; ++t) pthread_join(th[t], NULL);
-    free(jobs); free(th);
+    run_jobs(jobs, gemm_worker);
     return 0;
 }
 
@@ -346,19 +354,17 @@ int oracle_gemm_grouped_rows(const uint8_t* a, const float* sa, const uint8_t* b
  *     out[i, n] = sum_k a[rows[i], k] * b[n, k]   in fp64,
  * a bf16 [M,K], b bf16 [N,K] (bit patterns), C = A * B^T.  Each product of
  * two bf16 values is exact in fp64; only the sum rounds. */
-typedef struct {
+struct gemm_bf16_job {
     const uint16_t *a, *b;
     int64_t N, K;
     const int64_t* rows;
     int64_t nrows;
     double* out;
     int tid, nthreads;
-} gemm_bf16_job;
+};
 
-static void* gemm_bf16_worker(void* arg) {
-    gemm_bf16_job* J = (gemm_bf16_job*)arg;
-    double* arow = (double*)malloc((size_t)J->K * sizeof(double));
-    if (!arow) return NULL;
+static void gemm_bf16_worker(gemm_bf16_job* J) {
+    std::vector<double> arow((size_t)J->K);
     for (int64_t i = J->tid; i < J->nrows; i += J->nthreads) {
         const uint16_t* a = J->a + J->rows[i] * J->K;
         for (int64_t k = 0; k < J->K; ++k) arow[k] = (double)oracle_bf16_to_f32(a[k]);
@@ -369,8 +375,6 @@ static void* gemm_bf16_worker(void* arg) {
             J->out[i * J->N + n] = sum;
         }
     }
-    free(arow);
-    return NULL;
 }
 
 int oracle_gemm_bf16_rows(const uint16_t* a, const uint16_t* b, int64_t M, int64_t N, int64_t K,
@@ -380,24 +384,14 @@ int oracle_gemm_bf16_rows(const uint16_t* a, const uint16_t* b, int64_t M, int64
         if (rows[i] < 0 || rows[i] >= M) return -1;
     if (nthreads < 1) nthreads = 1;
     if (nthreads > 256) nthreads = 256;
-    gemm_bf16_job* jobs = (gemm_bf16_job*)calloc((size_t)nthreads, sizeof(gemm_bf16_job));
-    pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
-    if (!jobs || !th) { free(jobs); free(th); return -2; }
+    std::vector<gemm_bf16_job> jobs((size_t)nthreads);
     for (int t = 0; t < nthreads; ++t) {
         gemm_bf16_job* J = &jobs[t];
         J->a = a; J->b = b; J->N = N; J->K = K;
         J->rows = rows; J->nrows = nrows; J->out = out;
         J->tid = t; J->nthreads = nthreads;
     }
-    int started = 0;
-    for (int t = 1; t < nthreads; ++t) {
-        if (pthread_create(&th[t], NULL, gemm_bf16_worker, &jobs[t]) != 0) break;
-        started = t;
-    }
-    for (int t = started + 1; t < nthreads; ++t) gemm_bf16_worker(&jobs[t]);
-    gemm_bf16_worker(&jobs[0]);
-    for (int t = 1; t <= started; ++t) pthread_join(th[t], NULL);
-    free(jobs); free(th);
+    run_jobs(jobs, gemm_bf16_worker);
     return 0;
 }
 
@@ -469,3 +463,5 @@ void oracle_moe_combine(const uint16_t* out, const int32_t* slot_row, const floa
             y[t * N + n] = acc;
         }
 }
+
+}  /* extern "C" */

@@ -1,6 +1,6 @@
 """Plants plausible mistakes in copies of the CPU oracle and checks that the pins catch each.
 
-Every mutant is a text edit of ``oracle/bfp8_oracle.c`` compiled into a
+Every mutant is a text edit of ``oracle/bfp8_oracle.cpp`` compiled into a
 temporary folder; the real oracle is never touched.  A mutant survives only if
 every pin in tests/pins.py still passes, which would mean the pins cannot tell
 that mistake from the method.
@@ -12,8 +12,9 @@ import pytest
 
 import oracle
 import pins
+from oracle import build as oracle_build
 
-SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "bfp8_oracle.c")
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "bfp8_oracle.cpp")
 
 MUTANTS = {
     # power-of-two scale rounded down instead of up
@@ -95,11 +96,10 @@ def test_mutant_is_caught(name, mutant_dir):
     src = open(SRC).read()
     assert src.count(old) >= 1, f"mutation target for {name} not found"
     mutated = src.replace(old, new)
-    c_path = mutant_dir / f"{name}.c"
+    c_path = mutant_dir / f"{name}.cpp"
     so_path = mutant_dir / f"lib_{name}.so"
     c_path.write_text(mutated)
-    subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared", "-pthread",
-                    str(c_path), "-o", str(so_path), "-lm"], check=True)
+    subprocess.run(oracle_build.compile_cmd(str(c_path), str(so_path), ["-w"]), check=True)
     orc = oracle.Oracle(str(so_path))
     failed = []
     for pin in pins.ALL_PINS:
