@@ -55,7 +55,8 @@ def test_gemm_bf16_tile_configs_exercised():
 
 def test_linear_bf16_dense_full_size():
     """x [8192,7168] through the BF16 branch with W_up [18432,7168]: weight_dequant then
-    the bf16 GEMM, sampled rows against the oracle's dequant and bf16 GEMM."""
+    the bf16 GEMM; the first and last row of every 128-row block (plus seeded rows)
+    against the oracle's dequant and bf16 GEMM."""
     wl = workload(3)
     x, w, s = wl.tensors["x"], wl.tensors["w1"], wl.tensors["s1"]
     wd = bfp8.weight_dequant(w.to(dev()), s.to(dev()))
@@ -63,7 +64,7 @@ def test_linear_bf16_dense_full_size():
     torch.cuda.synchronize()
     ref_wd = oracle.weight_dequant(u8(w), s.numpy())
     assert np.array_equal(bits16(wd), ref_wd)
-    rows = np.array([0, 1, 255, 256, 4097, 8191], np.int64)
+    rows = sample_rows(8192, 16, 820)
     ref = oracle.gemm_bf16(bits16(x), ref_wd, rows=rows)
     worst = gemm_check(c[torch.from_numpy(rows).to(dev())], ref, "linear_bf16 dense")
     announce(f"linear_bf16 dense-mlp up: worst err/bound {worst:.3f}")

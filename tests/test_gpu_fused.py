@@ -1,9 +1,13 @@
 """GPU parity of the fp8 GEMM with act_quant fused into its epilogue.
 
-Two checks per case:
+Three checks per case:
   * consistency: the fused kernel's codes and scales equal bfp8_act_quant of
     bfp8_gemm's bf16 output, bit for bit (both on the GPU; the fused epilogue
     rounds to bf16 first exactly as the stored output is rounded);
+  * stage-wise parity: the oracle's act_quant of the GPU's own bf16 GEMM
+    output equals the fused codes and scales bit for bit, on every checked
+    row (the chain's act_quant of the first GEMM's output is exact given that
+    output);
   * parity with the oracle on sampled rows: the dequantized codes
     deq(q) * s approximate the oracle's fp64 product C within the GEMM
     tolerance plus what the bf16 rounding and the e4m3 quantization may add:
@@ -19,7 +23,7 @@ import torch
 import oracle
 import block_scaled_fp8_04_amd as bfp8
 from block_scaled_fp8_04_amd import synth
-from gpu_helpers import GEMM_REL, GEMM_RMS, announce, dev, sample_rows, u8, workload
+from gpu_helpers import GEMM_REL, GEMM_RMS, announce, bits16, dev, gemm_check, sample_rows, u8, workload
 
 pytestmark = pytest.mark.gpu
 BLOCK = 128
@@ -58,9 +62,14 @@ def _case(q_a, s_a, w, s_w, what, rows=None):
     assert torch.equal(q, q2), f"{what}: codes differ from act_quant(gemm)"
     assert torch.equal(qs, qs2), f"{what}: scales differ from act_quant(gemm)"
     r = np.arange(M) if rows is None else rows
-    ref = oracle.gemm(u8(q_a), s_a.cpu().numpy(), u8(w), s_w.cpu().numpy(), rows=r)
     rt = torch.from_numpy(np.asarray(r)).to(dev())
+    # stage-wise: the oracle's act_quant of the GPU's own bf16 output, row by row
+    qo, so = oracle.act_quant(bits16(c[rt]))
+    assert np.array_equal(qo, u8(q[rt])), f"{what}: codes differ from the oracle's act_quant of C"
+    assert np.array_equal(so, qs[rt].cpu().numpy()), f"{what}: scales differ from the oracle's act_quant of C"
+    ref = oracle.gemm(u8(q_a), s_a.cpu().numpy(), u8(w), s_w.cpu().numpy(), rows=r)
     _check(u8(q[rt]), qs[rt].cpu().numpy(), ref, what)
+    return q, qs
 
 
 def test_fused_quant_shapes():
@@ -88,13 +97,27 @@ def test_fused_quant_zero_rows():
 
 
 def test_fused_quant_dense_chain_full_size():
-    """The dense MLP up projection with H quantized in the epilogue, then the down GEMM on it."""
+    """The dense MLP up projection with H quantized in the epilogue, then the down GEMM on it.
+
+    Rows: the first and last of every 128-row block plus seeded ones.  The down GEMM
+    8192 x 7168 x 18432 runs on the fused codes and scales, and its output is held to
+    the GEMM tolerance against the oracle's fp64 product of those same codes."""
     wl = workload(3)
     x = wl.tensors["x"].to(dev())
     w1, s1 = wl.tensors["w1"].to(dev()), wl.tensors["s1"].to(dev())
+    w2, s2 = wl.tensors["w2"].to(dev()), wl.tensors["s2"].to(dev())
     q_a, s_a = bfp8.act_quant(x)
-    rows = np.array([0, 1, 2047, 2048, 6000, 8191], np.int64)
-    _case(q_a, s_a, w1, s1, "dense-mlp up 8192x18432x7168", rows)
+    rows = sample_rows(8192, 16, 680)
+    qh, qhs = _case(q_a, s_a, w1, s1, "dense-mlp up 8192x18432x7168", rows)
+    M, N2, K2 = 8192, w2.shape[0], w2.shape[1]
+    need = bfp8.bfp8_gemm_workspace_size(M, N2, K2)
+    work = torch.empty(max(need, 4) // 4, dtype=torch.float32, device=dev()) if need else None
+    y = bfp8.gemm(qh, qhs, w2, s2, workspace=work)
+    torch.cuda.synchronize()
+    rt = torch.from_numpy(rows).to(dev())
+    ref = oracle.gemm(u8(qh[rt]), qhs[rt].cpu().numpy(), u8(w2), s2.cpu().numpy())
+    worst = gemm_check(y[rt], ref, "dense-mlp down on the fused codes")
+    announce(f"dense-mlp down 8192x7168x18432 on the fused codes: worst err/bound {worst:.3f}")
 
 
 # ------------------------------------------------------------------- gated FFN
