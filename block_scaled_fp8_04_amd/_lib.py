@@ -25,13 +25,17 @@ BFP8_ERR_WORKSPACE = 4
 BFP8_ERR_GROUPS = 5
 BFP8_ERR_HIP = 6
 BFP8_ERR_ARG = 7
+BFP8_ERR_SCRATCH = 8
+
+# bytes of the device scratch array behind bfp8_gemm_noalloc (include/bfp8.h)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 EXPORTS = ("bfp8_act_quant", "bfp8_weight_dequant", "bfp8_gemm", "bfp8_gemm_workspace_size",
            "bfp8_gemm_grouped", "bfp8_e4m3_encode_range", "bfp8_bf16_round_range",
            "bfp8_gemm_kernel_name", "bfp8_moe_dispatch_workspace_size", "bfp8_moe_dispatch",
            "bfp8_act_quant_rows", "bfp8_moe_combine", "bfp8_gemm_bf16",
            "bfp8_gemm_act_quant", "bfp8_gemm_swiglu_act_quant", "bfp8_act_quant_ue8m0",
-           "bfp8_gemm_ue8m0", "bfp8_linear_fp8_workspace_size", "bfp8_linear_fp8",
+           "bfp8_gemm_ue8m0", "bfp8_linear_fp8_workspace_size", "bfp8_linear_fp8", "bfp8_gemm_noalloc",
            "bfp8_status_string", "bfp8_version")
 
 _lib = None
@@ -59,6 +63,8 @@ def library():
     lib.bfp8_weight_dequant.restype = ctypes.c_int
     lib.bfp8_gemm.argtypes = [P, P, P, P, P, I64, I64, I64, P, ctypes.c_size_t, P]
     lib.bfp8_gemm.restype = ctypes.c_int
+    lib.bfp8_gemm_noalloc.argtypes = [P, P, P, P, P, I64, I64, I64, P]
+    lib.bfp8_gemm_noalloc.restype = ctypes.c_int
     lib.bfp8_gemm_workspace_size.argtypes = [I64, I64, I64]
     lib.bfp8_gemm_workspace_size.restype = ctypes.c_size_t
     lib.bfp8_gemm_grouped.argtypes = [P, P, P, P, P, P, I32, I64, I64, I64, P]
@@ -224,6 +230,22 @@ def bfp8_gemm(a, a_s, b, b_s, c, workspace=None, stream=None):
     _check("bfp8_gemm", library().bfp8_gemm(_ptr(a), _ptr(a_s), _ptr(b), _ptr(b_s), _ptr(c),
                                             M, N, K, _ptr(workspace), ws_bytes,
                                             _stream(stream, a.device)))
+
+
+def bfp8_gemm_noalloc(a, a_s, b, b_s, c, stream=None):
+    """bfp8_gemm with its workspace in the library's fixed per-GPU scratch array (no allocation)."""
+    a, b = _bytes_view(a), _bytes_view(b)
+    _cuda_contig(a, a_s, b, b_s, c)
+    M, K = a.shape
+    N = b.shape[0]
+    _need(b.shape[1] == K, "a and b must share K")
+    _need(a_s.dtype == torch.float32 and b_s.dtype == torch.float32, "scales must be fp32")
+    _need(a_s.shape == (M, K // BLOCK), "a_s must be [M, K/128]")
+    _need(b_s.shape == (-(-N // BLOCK), K // BLOCK), "b_s must be [ceil(N/128), K/128]")
+    _need(c.dtype == torch.bfloat16 and c.shape == (M, N), "c must be bf16 [M, N]")
+    _check("bfp8_gemm_noalloc", library().bfp8_gemm_noalloc(_ptr(a), _ptr(a_s), _ptr(b), _ptr(b_s),
+                                                            _ptr(c), M, N, K,
+                                                            _stream(stream, a.device)))
 
 
 def bfp8_gemm_act_quant(a, a_s, b, b_s, q, q_scales, stream=None):

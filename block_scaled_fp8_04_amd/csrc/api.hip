@@ -52,6 +52,7 @@ const char* bfp8_status_string(int status) {
         case BFP8_ERR_GROUPS: return "group count out of range (below 1, or above the dispatch limit)";
         case BFP8_ERR_HIP: return "HIP runtime error at launch";
         case BFP8_ERR_ARG: return "invalid argument";
+        case BFP8_ERR_SCRATCH: return "problem needs more scratch than the no-allocation entry point's fixed buffer holds";
         default: return "unknown status";
     }
 }
@@ -114,6 +115,19 @@ int bfp8_gemm(const void* a, const float* a_s, const void* b, const float* b_s, 
     }
     return from_hip(bfp8::launch_gemm(a, a_s, b, b_s, c_bf16, M, N, K, workspace,
                                       workspace ? workspace_bytes : 0, (hipStream_t)stream));
+}
+
+int bfp8_gemm_noalloc(const void* a, const float* a_s, const void* b, const float* b_s,
+                      void* c_bf16, int64_t M, int64_t N, int64_t K, void* stream) {
+    static_assert(BFP8_NOALLOC_SCRATCH_BYTES == bfp8::kNoAllocScratchBytes, "scratch size");
+    if (M < 0 || N < 0 || !gemm_k_ok(K)) return BFP8_ERR_SHAPE;
+    if (M == 0 || N == 0) return BFP8_OK;
+    if (!a || !a_s || !b || !b_s || !c_bf16) return BFP8_ERR_NULL;
+    if (!aligned(a, 16) || !aligned(b, 16) || !aligned(a_s, 4) || !aligned(b_s, 4) ||
+        !aligned(c_bf16, 2))
+        return BFP8_ERR_ALIGN;
+    if (bfp8::gemm_workspace_bytes(M, N, K) > BFP8_NOALLOC_SCRATCH_BYTES) return BFP8_ERR_SCRATCH;
+    return from_hip(bfp8::launch_gemm_noalloc(a, a_s, b, b_s, c_bf16, M, N, K, (hipStream_t)stream));
 }
 
 int bfp8_gemm_act_quant(const void* a, const float* a_s, const void* b, const float* b_s,

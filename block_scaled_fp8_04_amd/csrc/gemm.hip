@@ -41,6 +41,8 @@
 //    and a fixed-order reduction).
 //  * Rows past M (or past a group's end) and columns past N read a clamped,
 //    valid row and are never stored.
+#include <mutex>
+
 #include "device_codec.hpp"
 #include "internal.hpp"
 
@@ -1474,6 +1476,52 @@ hipError_t launch_gemm_grouped(const void* a, const float* as, const void* b, co
                                void* c, const int32_t* off, int32_t G, int64_t total_M,
                                int64_t N, int64_t K, hipStream_t stream) {
     return launch_grouped_pair<BFP8_GROUPED_PAIR>(a, as, b, bs, c, off, G, total_M, N, K, stream);
+}
+
+// The no-allocation GEMM: the workspace bfp8_gemm takes from its caller (the
+// split-K partial sums of skinny problems and the split last round of large
+// ones) lives instead in this fixed device array, one per GPU, held until the
+// process ends.  64 MiB covers every shape whose last round is split (at most
+// 2 x 128 tiles of 256 x 256 fp32 partials) and the skinny split plans up to
+// that size.  Host code never passes `scratch` itself to a kernel (in host
+// code the name is a host-side stand-in): its device address is looked up
+// once per device with hipGetSymbolAddress, with that device current, and that
+// address is what the kernels receive.  Every call on one GPU shares the
+// array, so calls that overlap on one GPU (different streams, no ordering)
+// race on it.  No kernel needs it zeroed: every partial is written before it
+// is read.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+static hipError_t scratch_address(void** out) {
+    static std::mutex mu;
+    static void* addr[64] = {nullptr};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return hipSuccess;
+}
+
+hipError_t launch_gemm_noalloc(const void* a, const float* as, const void* b, const float* bs,
+                               void* c, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+    const size_t need = gemm_workspace_bytes(M, N, K);
+    if (need > kNoAllocScratchBytes) return hipErrorInvalidValue;   // rejected by the ABI first
+    void* ws = nullptr;
+    if (need > 0) {
+        const hipError_t e = scratch_address(&ws);
+        if (e != hipSuccess) return e;
+    }
+    // the same plans and kernels as launch_gemm with a caller workspace of `need` bytes
+    return launch_gemm(a, as, b, bs, c, M, N, K, ws, need, stream);
 }
 
 }  // namespace bfp8

@@ -45,6 +45,11 @@ hipError_t launch_gemm_swiglu_quant(const void* a, const float* as, const void* 
                                     const float* s13, void* q, float* qs, int64_t M, int64_t n_out,
                                     int64_t K, hipStream_t stream);
 size_t linear_workspace_bytes(int64_t M, int64_t N, int64_t K);
+// Size of the library-owned device scratch array behind the no-allocation GEMM
+// entry point (one per GPU, resident until the process ends).
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+hipError_t launch_gemm_noalloc(const void* a, const float* as, const void* b, const float* bs,
+                               void* c, int64_t M, int64_t N, int64_t K, hipStream_t stream);
 hipError_t launch_linear_fp8(const void* x, const void* b, const float* bs, void* c, int64_t M,
                              int64_t N, int64_t K, void* workspace, hipStream_t stream);
 hipError_t launch_gemm_grouped(const void* a, const float* as, const void* b, const float* bs,

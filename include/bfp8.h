@@ -18,7 +18,8 @@
  * Conventions shared by every entry point:
  *   - Every tensor pointer is a DEVICE pointer to row-major, densely packed
  *     memory owned by the caller.  The library never allocates, frees or
- *     keeps a pointer after the call returns.
+ *     keeps a pointer after the call returns.  The one exception is the fixed
+ *     device array behind bfp8_gemm_noalloc (see there).
  *   - e4m3 means the OCP FP8 E4M3 format (torch.float8_e4m3fn): bias 7, no
  *     infinities, largest finite value 448 (code 0x7E); one byte per element.
  *   - bf16 is the upper half of an IEEE binary32; two bytes per element.
@@ -29,7 +30,8 @@
  *     launches nothing and returns the status code.  A zero-sized problem
  *     (M == 0, N == 0, total_M == 0) returns BFP8_OK without a launch.
  *   - Outputs must not alias inputs.  Calls on different streams that write
- *     different outputs may overlap; the library keeps no state between calls.
+ *     different outputs may overlap; the library keeps no state between calls
+ *     (bfp8_gemm_noalloc's scratch array aside).
  *   - Block edge: BFP8_BLOCK = 128 everywhere (every call site on the pages uses
  *     128-element activation blocks and a 128x128 weight-scale grid).
  */
@@ -44,7 +46,9 @@ extern "C" {
 #endif
 
 #define BFP8_BLOCK 128
-#define BFP8_VERSION 7
+#define BFP8_VERSION 8
+/* bytes of the device scratch array behind bfp8_gemm_noalloc (per GPU) */
+#define BFP8_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 #define BFP8_MOE_MAX_GROUPS 1024
 
 typedef enum bfp8_status {
@@ -56,7 +60,9 @@ typedef enum bfp8_status {
     BFP8_ERR_WORKSPACE = 4, /* workspace smaller than the matching *_workspace_size() */
     BFP8_ERR_GROUPS = 5,    /* G < 1, or G > BFP8_MOE_MAX_GROUPS (MoE dispatch) */
     BFP8_ERR_HIP = 6,       /* the HIP runtime reported an error at launch */
-    BFP8_ERR_ARG = 7        /* any other invalid argument */
+    BFP8_ERR_ARG = 7,       /* any other invalid argument */
+    BFP8_ERR_SCRATCH = 8    /* bfp8_gemm_noalloc: the problem needs more than
+                               BFP8_NOALLOC_SCRATCH_BYTES of scratch */
 } bfp8_status;
 
 /* act_quant ([DF] FP8 bullet; [PY] "FP8 with per-block scales").
@@ -112,6 +118,26 @@ int bfp8_weight_dequant(const void* w_e4m3, const float* s, void* out_bf16,
 int bfp8_gemm(const void* a, const float* a_s, const void* b, const float* b_s,
               void* c_bf16, int64_t M, int64_t N, int64_t K,
               void* workspace, size_t workspace_bytes, void* stream);
+
+/* bfp8_gemm for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, kernels and results (bit for bit) as bfp8_gemm with a workspace
+ * of bfp8_gemm_workspace_size(M, N, K) bytes, but that workspace is a
+ * library-owned device array of BFP8_NOALLOC_SCRATCH_BYTES (64 MiB), one per
+ * GPU, reserved when the library's code is loaded on that GPU and held until
+ * the process ends.  The call itself allocates nothing (no hipMalloc, hipFree
+ * or allocating library routine); its first call on a device looks up that
+ * device's array address, with that device current.  `stream` must belong to
+ * the current device.  Every call on one GPU shares its array and leaves its
+ * contents behind: calls that may overlap on one GPU (different streams with
+ * no ordering between them) race on it and must not be issued.  Nothing in the
+ * array needs to start at zero.
+ * Errors: as bfp8_gemm, plus BFP8_ERR_SCRATCH if bfp8_gemm_workspace_size(M,
+ * N, K) exceeds BFP8_NOALLOC_SCRATCH_BYTES (checked before any HIP call; the
+ * problem can still run through bfp8_gemm with a caller workspace, or with
+ * none). */
+int bfp8_gemm_noalloc(const void* a, const float* a_s, const void* b, const float* b_s,
+                      void* c_bf16, int64_t M, int64_t N, int64_t K, void* stream);
 
 /* fp8_gemm with the next linear()'s act_quant fused into its epilogue ([DF]
  * FP8 bullet: a linear() output is quantized in 128-element blocks before the

@@ -44,8 +44,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert bfp8.bfp8_version() == 7
-    for code in range(8):
+    assert bfp8.bfp8_version() == 8
+    for code in range(9):
         assert bfp8.bfp8_status_string(code)
     assert bfp8.bfp8_status_string(0) == "ok"
     assert "unknown" in bfp8.bfp8_status_string(99)
@@ -340,3 +340,21 @@ def test_python_binding_rejects_bad_tensors():
                             torch.zeros(4, 2, dtype=torch.float32))
     with pytest.raises(TypeError):
         bfp8.bfp8_gemm(torch.zeros(4, 256, dtype=torch.int16), None, None, None, None)
+
+
+def test_gemm_noalloc_validation(lib):
+    f = lib.bfp8_gemm_noalloc
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 64, 100, None) == _lib.BFP8_ERR_SHAPE    # K % 128
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 64, 128, None) == _lib.BFP8_ERR_SHAPE
+    assert f(None, FAKE, FAKE, FAKE, FAKE, 64, 64, 128, None) == _lib.BFP8_ERR_NULL
+    assert f(FAKE, FAKE, FAKE, FAKE, None, 64, 64, 128, None) == _lib.BFP8_ERR_NULL
+    assert f(ODD, FAKE, FAKE, FAKE, FAKE, 64, 64, 128, None) == _lib.BFP8_ERR_ALIGN
+    assert f(None, None, None, None, None, 0, 64, 128, None) == _lib.BFP8_OK
+    # a skinny, long-K problem whose split-K partials exceed the fixed scratch array
+    M, N, K = 64, 12288, 128 * 1000
+    assert lib.bfp8_gemm_workspace_size(M, N, K) > _lib.NOALLOC_SCRATCH_BYTES
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, M, N, K, None) == _lib.BFP8_ERR_SCRATCH
+    assert "scratch" in bfp8.bfp8_status_string(_lib.BFP8_ERR_SCRATCH)
+    # the configurations it serves fit: the dense MLP's down projection needs exactly the maximum
+    assert lib.bfp8_gemm_workspace_size(8192, 7168, 18432) == _lib.NOALLOC_SCRATCH_BYTES
+    assert 0 < lib.bfp8_gemm_workspace_size(64, 1536, 7168) < _lib.NOALLOC_SCRATCH_BYTES
