@@ -987,38 +987,54 @@ __global__ __launch_bounds__(T::THREADS, 1) void gemm_quant_kernel(
         gemm_tile_big<T, true, kEpi>(a, as, b, bs, nullptr, m0, M, (int64_t)tn * T::BN, N, K, lds, qo);
 }
 
-// Persistent grouped kernel on the large tiles.
+// ------------------------------------------------------------- grouped GEMM
 //
-// Tiles.  Group g (rows off[g] .. off[g+1]) has n_g / HBM full heavy M-tiles
-// and, when HBM does not divide n_g, a remainder.  A remainder of at least LBM
-// rows (the light tile's height) takes one more, partial, heavy tile; a
-// smaller one takes a light tile.  Routed experts hold a few rows more or
-// fewer than a multiple of the heavy height, so a light tile is typically a
-// handful of rows.  The heavy tiles and the light tiles are
-// two launches of this kernel (kLight): heavy tiles run the full-tile loop
-// (rows past the group's end are computed on clamped inputs and not
-// stored), light tiles the guarded loop that skips sub-tile rows past the
-// group's end.  Keeping the two loops in separate kernels keeps each one's
-// registers to itself, and the light tiles fill a pass of their own instead
-// of stretching every round of the heavy pass.
+// One persistent launch over every group's tiles ("Behavior traces", MoE
+// trace; pyshine tour, "Honest Limits": one fused grouped GEMM instead of a
+// loop over experts).  Routed experts hold about as many rows as one 256-row
+// tile, a few more or fewer, and the weights are streamed from HBM once per
+// M-tile.  So a tile here is 256 rows plus up to 64 more: the group's last
+// tile takes a remainder of at most 64 rows into the same K loop (the same B
+// blocks in LDS), and every group's weight is read once.  A group of n rows
+// gets n / 256 tiles when n % 256 <= 64 (the last one tall), else one more,
+// partial, tile.
 //
-// Order and placement.  Inside each list: group by group, N-tile by N-tile,
-// M-tile fastest.  Workgroups are dealt round-robin over the 8 XCDs; in each
-// round the workgroups of one XCD take a contiguous run of tiles, so one XCD
-// works on a few experts' weights and rows at a time.  Every workgroup
-// leaves the loop once the rounds cover all tiles of its list.
-struct GroupTiles {
-    int64_t m_heavy, m_light;   // M-tiles of one group by kind
+// Tile: 320 x 256 at most, 8 waves in 2 (M) x 4 (N).  Wave (wm, wn) owns
+// columns 64 wn .. 64 wn + 63 and ten 16-row sub-tile rows: the main rows
+// 128 wm + 16 i (i < 8) and the extra rows 256 + 16 wm + 32 x (x = 0, 1), so
+// the two wave rows share a remainder.  Sub-tile rows past the group's end are
+// skipped (a wave-uniform test).  Two LDS stages of 74 KB (A 320 rows, B 256
+// rows, the row scales, the weight-scale line); waves 0..3 issue the A and B
+// loads of the next K block right after each block's barrier (waves 4..7 run
+// one priority level up and only multiply).  A and B rows of a load
+// instruction are eight consecutive rows, so the per-lane offset depends only
+// on the instruction's parity (the LDS swizzle) and the rest goes into the
+// scalar offset; rows past the tile's valid rows fall outside the buffer
+// resource, which reads them as zeros (never stored).  The weight is read with
+// the non-temporal hint: each block is used once, and it should not push the
+// activation rows, shared by the group's N-tiles, out of L2.  The fold is
+// acc += P * (a_s[row] * b_s) per 16 x 16 block product, as in the dense tile.
+struct GroupedTile {
+    static constexpr int BM = 256, XM = 64, ROWS = BM + XM, BN = 256;
+    static constexpr int WAVES = 8, THREADS = 64 * WAVES, LOADERS = 4;
+    static constexpr int WM = 128, WN = 64, TM = 8, TN = 4, TR_MAX = TM + XM / 32;
+    static constexpr int A_BYTES = ROWS * kBlock, B_BYTES = BN * kBlock;
+    static constexpr int B_INSTR = BN / 8 / LOADERS;
+    // row scales: lane row t (0..15) of wave row wm, sub-tile row i sits at
+    // float t * SP + 12 wm + i (16-byte aligned groups of four; SP / 4 odd, so
+    // the 16 lanes of a read hit distinct bank groups)
+    static constexpr int SP = 28, S_FLOATS = 16 * SP, S_INSTR = S_FLOATS / 64;
+    static constexpr int S_OFF = A_BYTES + B_BYTES, SB_OFF = S_OFF + S_FLOATS * 4;
+    static constexpr int STAGE = (SB_OFF + 256 + 1023) / 1024 * 1024;
+    static_assert(BM % (8 * LOADERS) == 0 && BN % (8 * LOADERS) == 0, "rows split over loaders");
+    static_assert(S_FLOATS % 64 == 0 && S_INSTR <= WAVES, "one scale instruction per wave");
+    static_assert(2 * STAGE <= 158 * 1024, "two stages fit in LDS");
 };
 
-template <int HBM, int LBM>
-__device__ __forceinline__ GroupTiles group_tiles(int64_t rows) {
-    const int64_t full = rows / HBM;
-    const int64_t rem = rows - full * HBM;
-    GroupTiles t;
-    t.m_heavy = full + (rem >= LBM ? 1 : 0);
-    t.m_light = (rem > 0 && rem < LBM) ? 1 : 0;
-    return t;
+// Tiles of a group of `rows` rows (see above).
+__device__ __forceinline__ int64_t grouped_m_tiles(int64_t rows) {
+    const int64_t full = rows / GroupedTile::BM, rem = rows - full * GroupedTile::BM;
+    return full + ((rem > GroupedTile::XM || (rem > 0 && full == 0)) ? 1 : 0);
 }
 
 // Rows of group g: the device offsets clamped into [0, total_M] (and the end
@@ -1033,47 +1049,283 @@ __device__ __forceinline__ void group_rows(const int32_t* __restrict__ off, int 
     hi = b;
 }
 
-template <class T, bool kLight, int HBM, int LBM>
-__global__ __launch_bounds__(T::THREADS, 1) void gemm_grouped_big_kernel(
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+    const uint64_t u = (uint64_t)v;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Where tile t lies (tiles ordered group by group, N-tile by N-tile, M-tile
+// fastest): the groups are scanned 64 at a time, one group per lane (a
+// coalesced load of its offsets, its tile count, a wave prefix sum of the
+// counts), so finding a tile costs one memory round trip per 64 groups.
+// Every wave of the workgroup does the same scan; the results are
+// wave-uniform.  Returns false when t lies past the last tile.
+struct TileAt {
+    int g;
+    int64_t m0, m_end, n0;
+};
+
+__device__ __forceinline__ bool locate_tile(const int32_t* __restrict__ off, int G, int64_t total_M,
+                                            int nt, int64_t t, TileAt& at) {
+    // the lane id is hidden from the compiler here, so nothing of this scan is hoisted
+    // out of the caller's tile loop to stay live (in VGPRs) through every tile's K loop
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+    int64_t base = 0;
+    for (int g0 = 0; g0 < G; g0 += 64) {
+        const int g = g0 + lane;
+        int64_t lo = 0, hi = 0;
+        int mcount = 0;
+        if (g < G) {
+            group_rows(off, g, total_M, lo, hi);
+            mcount = (int)grouped_m_tiles(hi - lo);
+        }
+        // tile counts of 64 groups: below 2^31 (rows < 2^31 per call, N-tiles < 2^16)
+        const int cnt = mcount * nt;
+        int inc = cnt;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int v = __shfl_up(inc, d);
+            if (lane >= d) inc += v;
+        }
+        const int64_t start = base + (inc - cnt);
+        const unsigned long long hit = __ballot(g < G && t >= start && t < start + cnt);
+        if (hit != 0ull) {
+            const int src = __builtin_amdgcn_readfirstlane(__ffsll(hit) - 1);
+            const int64_t rest = t - uniform64(__shfl(start, src));
+            const int64_t mc = __builtin_amdgcn_readfirstlane(__shfl(mcount, src));
+            const int64_t glo = uniform64(__shfl(lo, src)), ghi = uniform64(__shfl(hi, src));
+            const int64_t tm = rest % mc;
+            at.g = g0 + src;
+            at.m0 = glo + tm * GroupedTile::BM;
+            at.m_end = (tm == mc - 1) ? ghi : at.m0 + GroupedTile::BM;   // the last tile takes the rest
+            at.n0 = (rest / mc) * GroupedTile::BN;
+            return true;
+        }
+        base += __builtin_amdgcn_readfirstlane(__shfl(inc, 63));
+    }
+    return false;
+}
+
+// Row of the tile that sub-tile row i of wave row wm starts at.
+__device__ __forceinline__ int grouped_row(int wm, int i) {
+    return i < GroupedTile::TM ? GroupedTile::WM * wm + 16 * i : GroupedTile::BM + 16 * wm + 32 * (i - GroupedTile::TM);
+}
+
+__device__ __forceinline__ void buf_lds16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                             void* lds_dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t)lds_dst, 16, voff, soff, 0, 2);
+}
+
+// One tile with TX extra sub-tile rows per wave row (TX = 0: up to 256 rows;
+// 1: up to 288; 2: up to 320).  Each variant runs its K loop with no branch
+// inside (a branch would make the compiler wait for the next block's loads
+// before the LDS reads that follow it); rows past the tile's valid rows are
+// multiplied (their inputs read as zeros) but never stored.
+template <int TX>
+__device__ __forceinline__ void grouped_tile(const uint8_t* __restrict__ a,
+                                             const float* __restrict__ as,
+                                             const uint8_t* __restrict__ b,
+                                             const float* __restrict__ bs,
+                                             uint16_t* __restrict__ c, int64_t m0, int64_t m_end,
+                                             int64_t n0, int64_t N, int64_t K, uint8_t* st0,
+                                             uint8_t* st1) {
+    using T = GroupedTile;
+    constexpr int TR = T::TM + TX;                         // sub-tile rows per wave
+    constexpr int A_INSTR = (T::BM + 32 * TX) / 8 / T::LOADERS;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / 4, wn = wave % 4;
+    const int64_t KB = K / kBlock;
+    const int64_t NBK = (N + kBlock - 1) / kBlock;
+    const int rows_a = (int)(m_end - m0);                 // 1 .. 256 + 32 TX
+    const int rows_b = (int)((N - n0) < T::BN ? (N - n0) : T::BN);
+    // rows past rows_a / rows_b lie outside these resources and read as zeros
+    const __amdgpu_buffer_rsrc_t rs_a = make_rsrc(a + m0 * K, (uint64_t)rows_a * K);
+    const __amdgpu_buffer_rsrc_t rs_b = make_rsrc(b + n0 * K, (uint64_t)rows_b * K);
+    const __amdgpu_buffer_rsrc_t rs_as = make_rsrc(as + m0 * KB, (uint64_t)rows_a * KB * 4);
+    const __amdgpu_buffer_rsrc_t rs_bs = make_rsrc(bs, (uint64_t)NBK * KB * 4);
+
+    // loading wave w < LOADERS: A instruction i fills rows 8 (w A_INSTR + i) .. + 7, B
+    // instruction i rows 8 (w B_INSTR + i) .. + 7; lane l writes physical chunk l & 7 of
+    // row + (l >> 3), which holds logical chunk (l & 7) ^ swz(row); with eight rows per
+    // instruction swz(row) = (l >> 3) ^ (parity of the instruction's first row / 8)
+    const int lrow = lane >> 3;
+    uint32_t voff_a[2], voff_b[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        voff_a[p] = (uint32_t)((wave * A_INSTR * 8 + lrow) * K +
+                               (((lane & 7) ^ lrow ^ ((wave * A_INSTR + p) & 1)) * 16));
+        voff_b[p] = (uint32_t)((wave * T::B_INSTR * 8 + lrow) * K +
+                               (((lane & 7) ^ lrow ^ ((wave * T::B_INSTR + p) & 1)) * 16));
+    }
+    // row-scale slot q = wave * 64 + lane (waves < S_INSTR): lane row t = q / SP, wave row
+    // and sub-tile row from q % SP; unused slots load row 0
+    uint32_t as_off;
+    {
+        const int q = wave * 64 + lane, t = q / T::SP, k = q % T::SP;
+        const int r_wm = k / 12, r_i = k % 12;
+        const int row = (r_wm < 2 && r_i < T::TR_MAX) ? grouped_row(r_wm, r_i) + t : 0;
+        as_off = (uint32_t)(row * KB * 4);
+    }
+    uint32_t bs_off;
+    {
+        int64_t nb = (n0 >> 7) + lane;
+        nb = nb < NBK ? nb : NBK - 1;
+        bs_off = (uint32_t)(nb * KB * 4);
+    }
+
+    const uint32_t k8 = (uint32_t)(8 * K);                 // byte step of eight rows
+    auto issue = [&](int64_t kb, uint8_t* base) __attribute__((always_inline)) {
+        const uint32_t ko = (uint32_t)(kb * kBlock);
+        if (wave < T::LOADERS) {
+            // the scalar offset advances by eight rows per instruction; the empty asm keeps
+            // the compiler from precomputing every instruction's offset into its own SGPR
+            uint32_t so = ko;
+#pragma unroll
+            for (int i = 0; i < A_INSTR; ++i) {
+                buf_lds16(rs_a, voff_a[i & 1], so, base + (wave * A_INSTR + i) * 1024);
+                so += k8;
+                asm volatile("" : "+s"(so));
+            }
+            so = ko;
+#pragma unroll
+            for (int i = 0; i < T::B_INSTR; ++i) {
+                buf_lds16_nt(rs_b, voff_b[i & 1], so, base + T::A_BYTES + (wave * T::B_INSTR + i) * 1024);
+                so += k8;
+                asm volatile("" : "+s"(so));
+            }
+        }
+        const uint32_t so = (uint32_t)(kb * 4);
+        if (wave < T::S_INSTR) buf_lds4(rs_as, as_off, so, base + T::S_OFF + wave * 256);
+        if (wave == T::WAVES - 1) buf_lds4(rs_bs, bs_off, so, base + T::SB_OFF);
+    };
+
+    v4f acc[TR][T::TN];
+#pragma unroll
+    for (int i = 0; i < TR; ++i)
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    // a workgroup walking several tiles must not refill a stage a slower wave still reads
+    wait_vmcnt<0>();
+    barrier_lds();
+    issue(0, st0);
+
+    const int lr = lane & 15;
+    const int lk = (lane >> 4) * 2;
+    const int off0 = ((lk ^ swz(lr)) << 4);
+    const int off1 = (((lk + 1) ^ swz(lr)) << 4);
+    const int sread = lr * T::SP + 12 * wm;
+
+    auto step = [&](int64_t kb, uint8_t* cur, uint8_t* nxt) __attribute__((always_inline)) {
+        wait_vmcnt<0>();              // this wave's loads of block kb
+        barrier_lds();                // everyone's loads of kb landed; block kb - 1 fully read
+        if (kb + 1 < KB) issue(kb + 1, nxt);
+        const uint8_t* As = cur;
+        const uint8_t* Bs = cur + T::A_BYTES;
+        const float* Ss = (const float*)(cur + T::S_OFF);
+        const float* Sb = (const float*)(cur + T::SB_OFF);
+        v8i fb[T::TN];
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j) {
+            const uint8_t* q = Bs + (T::WN * wn + 16 * j + lr) * kBlock;
+            fb[j] = frag_from(*(const uint4*)(q + off0), *(const uint4*)(q + off1));
+        }
+        const float sbv = Sb[wn >> 1];
+        const v4f s0 = *(const v4f*)(Ss + sread), s1 = *(const v4f*)(Ss + sread + 4);
+        float2 s2 = float2{0.f, 0.f};
+        if constexpr (TX > 0) s2 = *(const float2*)(Ss + sread + 8);
+#pragma unroll
+        for (int i = 0; i < TR; ++i) {
+            const uint8_t* r = As + (grouped_row(wm, i) + lr) * kBlock;
+            const v8i fa = frag_from(*(const uint4*)(r + off0), *(const uint4*)(r + off1));
+            const float sa = i < 4 ? s0[i] : (i < 8 ? s1[i - 4] : (i == 8 ? s2.x : s2.y));
+            const float sc = sa * sbv;
+            // the row's MFMAs in groups of PP, each group's folds after it (the first fold of a
+            // group waits on its first MFMA only); the tallest tile keeps two products in
+            // flight instead of four, to stay within the register file
+            constexpr int PP = TX == 2 ? 2 : 4;
+#pragma unroll
+            for (int j0 = 0; j0 < T::TN; j0 += PP) {
+                v4f pp[PP];
+#pragma unroll
+                for (int j = 0; j < PP; ++j)
+                    pp[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        fb[j0 + j], fa, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+                for (int j = 0; j < PP; ++j) acc[i][j0 + j] = pp[j] * sc + acc[i][j0 + j];
+                __builtin_amdgcn_sched_group_barrier(0x008, PP, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 4 * PP, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    if (wave >= 4) __builtin_amdgcn_s_setprio(1);
+    for (int64_t kb = 0; kb < KB; kb += 2) {
+        step(kb, st0, st1);
+        if (kb + 1 < KB) step(kb + 1, st1, st0);
+    }
+    if (wave >= 4) __builtin_amdgcn_s_setprio(0);
+
+    // epilogue: lane holds row m0 + grouped_row(wm, i) + lr, columns n0 + 64 wn + 16 j + 4 (lane >> 4) + 0..3
+    const int cq = 4 * (lane >> 4);
+    const bool fast = (N % 4 == 0) && (((uintptr_t)c & 7u) == 0) && (n0 + T::BN <= N);
+    uint16_t* cbase = c + m0 * N + n0 + T::WN * wn + cq;
+#pragma unroll
+    for (int i = 0; i < TR; ++i) {
+        const int r = grouped_row(wm, i) + lr;
+        if (r >= rows_a) continue;
+        uint16_t* crow = cbase + (int64_t)r * N;
+        if (fast) {
+#pragma unroll
+            for (int j = 0; j < T::TN; ++j) {
+                uint2 v;
+                v.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+                v.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+                *(uint2*)(crow + 16 * j) = v;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (n0 + T::WN * wn + 16 * j + cq + e < N)
+                        crow[16 * j + e] = (uint16_t)bf16_rne_bits(acc[i][j][e]);
+        }
+    }
+}
+
+// Persistent: workgroups are dealt round-robin over the 8 XCDs, and in each
+// round the workgroups of one XCD take a contiguous run of tiles, so one XCD
+// works on a few groups' rows (shared by their N-tiles through L2) at a time.
+__global__ __launch_bounds__(GroupedTile::THREADS, 1) void gemm_grouped_kernel(
     const uint8_t* __restrict__ a, const float* __restrict__ as, const uint8_t* __restrict__ b,
     const float* __restrict__ bs, uint16_t* __restrict__ c, const int32_t* __restrict__ off,
     int G, int64_t total_M, int64_t N, int64_t K, int nt) {
-    BIG_TILE_STAGES(T, lds);
+    __shared__ __attribute__((aligned(1024))) uint8_t st0[GroupedTile::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t st1[GroupedTile::STAGE];
     const int64_t KB = K / kBlock;
     const int64_t NB = (N + kBlock - 1) / kBlock;
-    int64_t total = 0;
-    for (int g = 0; g < G; ++g) {
-        int64_t lo, hi;
-        group_rows(off, g, total_M, lo, hi);
-        const GroupTiles gt = group_tiles<HBM, LBM>(hi - lo);
-        total += (kLight ? gt.m_light : gt.m_heavy) * nt;
-    }
     const int nwg = gridDim.x;                    // a multiple of 8
     const int xcd = blockIdx.x % 8, local = blockIdx.x / 8;
     const int per_xcd = nwg / 8;
-    for (int64_t round = 0; round * nwg < total; ++round) {
+    for (int64_t round = 0;; ++round) {
         const int64_t t = round * nwg + (int64_t)xcd * per_xcd + local;
-        if (t >= total) continue;
-        int64_t rest = t;
-        int g = 0;
-        int64_t tm = 0, tn = 0, g_lo = 0, g_hi = 0;
-        for (; g < G; ++g) {
-            group_rows(off, g, total_M, g_lo, g_hi);
-            const GroupTiles gt = group_tiles<HBM, LBM>(g_hi - g_lo);
-            const int64_t mcount = kLight ? gt.m_light : gt.m_heavy;
-            if (rest < mcount * nt) {
-                // a light tile starts after the group's heavy tiles (it holds fewer
-                // than LBM = T::BM rows, so one tile covers them)
-                tm = kLight ? gt.m_heavy : rest % mcount;
-                tn = rest / mcount;
-                break;
-            }
-            rest -= mcount * nt;
-        }
-        const int64_t m0 = g_lo + tm * (kLight ? HBM : T::BM), m_end = g_hi;
-        gemm_tile_big<T, kLight, kEpiBf16, false, false>(a, as, b + (int64_t)g * N * K,
-                                                         bs + (int64_t)g * NB * KB, c, m0, m_end,
-                                                         tn * T::BN, N, K, lds);
+        TileAt at;
+        if (!locate_tile(off, G, total_M, nt, t, at)) break;           // past the last tile
+        const uint8_t* bg = b + (int64_t)at.g * N * K;
+        const float* bsg = bs + (int64_t)at.g * NB * KB;
+        const int64_t rows = at.m_end - at.m0;
+        if (rows <= GroupedTile::BM)
+            grouped_tile<0>(a, as, bg, bsg, c, at.m0, at.m_end, at.n0, N, K, st0, st1);
+        else if (rows <= GroupedTile::BM + 32)
+            grouped_tile<1>(a, as, bg, bsg, c, at.m0, at.m_end, at.n0, N, K, st0, st1);
+        else
+            grouped_tile<2>(a, as, bg, bsg, c, at.m0, at.m_end, at.n0, N, K, st0, st1);
     }
 }
 
@@ -1294,7 +1546,6 @@ using BigSquare = BigTile<256, 256, 2, 4, 2>;   // 8 waves of 128 x 64, 2 stages
 
 using BigWide = BigTile<256, 128, 4, 2, 3>;     // 8 waves of 64 x 64, 3 stages
 using BigMid = BigTile<128, 128, 2, 2, 3>;      // 4 waves of 64 x 64, 3 stages
-using BigLight = BigTile<64, 128, 1, 4, 4>;     // 4 waves of 64 x 32, 4 stages (grouped light tiles)
 
 template <class T>
 static void launch_big(const void* a, const float* as, const void* b, const float* bs, void* c,
@@ -1438,44 +1689,21 @@ hipError_t launch_gemm_swiglu_quant(const void* a, const float* as, const void* 
     return launch_quant<BigSquare, kEpiSwiglu>(a, as, w13, s13, q, qs, M, 2 * n_out, K, stream);
 }
 
-// Heavy tiles on TH, light tiles (the remainder rows of a group, fewer than
-// TL::BM) on the smaller TL.  The light pass streams the weights of the
-// groups with a remainder for a few rows each, so TL is short (64 rows) with
-// four stages: three K blocks of weight loads in flight per workgroup.
-template <class TH, class TL>
-static hipError_t launch_grouped_pair(const void* a, const float* as, const void* b,
-                                      const float* bs, void* c, const int32_t* off, int32_t G,
-                                      int64_t total_M, int64_t N, int64_t K, hipStream_t stream) {
-    static_assert(TL::BM <= TH::BM, "light tiles hold the remainders below TL::BM rows");
-    const int nt_h = (int)((N + TH::BN - 1) / TH::BN);
-    const int nt_l = (int)((N + TL::BN - 1) / TL::BN);
-    // upper bounds of the tile counts (the exact ones depend on the device offsets)
-    const int64_t max_heavy = ((total_M + TL::BM - 1) / TL::BM) * (int64_t)nt_h;
-    const int64_t max_light = (int64_t)G * nt_l;
-    const int64_t cus = device_cu_count();
-    int64_t grid_h = max_heavy < cus ? max_heavy : cus;
-    int64_t grid_l = max_light < cus ? max_light : cus;
-    grid_h = (grid_h + 7) / 8 * 8;
-    grid_l = (grid_l + 7) / 8 * 8;
-    hipLaunchKernelGGL((gemm_grouped_big_kernel<TH, false, TH::BM, TL::BM>), dim3((unsigned)grid_h),
-                       dim3(TH::THREADS), 0, stream, (const uint8_t*)a, as, (const uint8_t*)b, bs,
-                       (uint16_t*)c, off, (int)G, total_M, N, K, nt_h);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gemm_grouped_big_kernel<TL, true, TH::BM, TL::BM>), dim3((unsigned)grid_l),
-                       dim3(TL::THREADS), 0, stream, (const uint8_t*)a, as, (const uint8_t*)b, bs,
-                       (uint16_t*)c, off, (int)G, total_M, N, K, nt_l);
-    return hipGetLastError();
-}
-
-#ifndef BFP8_GROUPED_PAIR
-#define BFP8_GROUPED_PAIR BigSquare, BigLight
-#endif
-
 hipError_t launch_gemm_grouped(const void* a, const float* as, const void* b, const float* bs,
                                void* c, const int32_t* off, int32_t G, int64_t total_M,
                                int64_t N, int64_t K, hipStream_t stream) {
-    return launch_grouped_pair<BFP8_GROUPED_PAIR>(a, as, b, bs, c, off, G, total_M, N, K, stream);
+    using T = GroupedTile;
+    const int nt = (int)((N + T::BN - 1) / T::BN);
+    // an upper bound of the tile count (the exact one depends on the device offsets):
+    // at most total_M / 256 full tiles plus one more per group
+    const int64_t max_tiles = (total_M / T::BM + G) * (int64_t)nt;
+    const int64_t cus = device_cu_count();
+    int64_t grid = max_tiles < cus ? max_tiles : cus;
+    grid = (grid + 7) / 8 * 8;
+    hipLaunchKernelGGL(gemm_grouped_kernel, dim3((unsigned)grid), dim3(T::THREADS), 0, stream,
+                       (const uint8_t*)a, as, (const uint8_t*)b, bs, (uint16_t*)c, off, (int)G,
+                       total_M, N, K, nt);
+    return hipGetLastError();
 }
 
 // The no-allocation GEMM: the workspace bfp8_gemm takes from its caller (the

@@ -457,9 +457,12 @@ def test_grouped_small_cases():
     from block_scaled_fp8_04_amd import synth
     g = torch.Generator().manual_seed(41)
     K, N = 256, 300
-    # light tiles hold remainders below 64 rows; 64 and more take a partial heavy tile
+    # a group's last tile takes a remainder of up to 64 rows past a full 256 (tiles of 257 ..
+    # 288 and 289 .. 320 rows are separate code paths); a larger remainder, or a group below
+    # 256 rows, takes a partial tile; N = 300 leaves a ragged last N-tile
     for counts in ([3, 0, 5, 1, 0, 4], [0, 0, 130], [129], [1] * 9, [0, 257, 0, 0, 64, 1],
-                   [63, 100, 326, 191]):
+                   [63, 100, 326, 191], [256, 288, 289, 320, 321, 512, 575, 576, 577, 0, 65, 1],
+                   [304, 214, 287, 2, 800]):
         counts = np.array(counts)
         G = len(counts)
         off = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32))
