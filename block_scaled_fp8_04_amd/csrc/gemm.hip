@@ -1000,35 +1000,44 @@ __global__ __launch_bounds__(T::THREADS, 1) void gemm_quant_kernel(
 // partial, tile.
 //
 // Tile: 320 x 256 at most, 8 waves in 2 (M) x 4 (N).  Wave (wm, wn) owns
-// columns 64 wn .. 64 wn + 63 and ten 16-row sub-tile rows: the main rows
-// 128 wm + 16 i (i < 8) and the extra rows 256 + 16 wm + 32 x (x = 0, 1), so
-// the two wave rows share a remainder.  Sub-tile rows past the group's end are
-// skipped (a wave-uniform test).  Two LDS stages of 74 KB (A 320 rows, B 256
-// rows, the row scales, the weight-scale line); waves 0..3 issue the A and B
-// loads of the next K block right after each block's barrier (waves 4..7 run
-// one priority level up and only multiply).  A and B rows of a load
-// instruction are eight consecutive rows, so the per-lane offset depends only
-// on the instruction's parity (the LDS swizzle) and the rest goes into the
-// scalar offset; rows past the tile's valid rows fall outside the buffer
-// resource, which reads them as zeros (never stored).  The weight is read with
-// the non-temporal hint: each block is used once, and it should not push the
-// activation rows, shared by the group's N-tiles, out of L2.  The fold is
-// acc += P * (a_s[row] * b_s) per 16 x 16 block product, as in the dense tile.
+// columns 64 wn .. 64 wn + 63 and up to ten 16-row sub-tile rows: the main
+// rows 128 wm + 16 i (i < 8) and the extra rows 256 + 16 wm + 32 x (x = 0, 1),
+// so the two wave rows share a remainder.  A tile runs one of three variants
+// (no extra row, one, or two per wave row), each a K loop without branches.
+// LDS per stage: A (the ten sub-tile rows of wave row wm at rows 160 wm ..
+// 160 wm + 159, so one base address and immediate offsets reach them all), B
+// (256 rows), and one line of row scales and weight scales; every region is
+// its own array, so the compiler sees that a fill of one stage never aliases
+// the reads of the other.  Waves 0..3 issue the A and B loads of the next K
+// block right after each block's barrier (waves 4..7 run one priority level
+// up and only multiply).  Rows past the tile's valid rows, and weight rows
+// past N, fall outside the buffer resources, which read them as zeros; they
+// are never stored.  The weight is loaded with the non-temporal hint: each
+// block is used once, and should not push the group's rows (shared by its
+// N-tiles) out of L2.  The fold is acc += P * (a_s[row] * b_s) per 16 x 16
+// block product, as in the dense tile, software-pipelined one MFMA deep.
 struct GroupedTile {
-    static constexpr int BM = 256, XM = 64, ROWS = BM + XM, BN = 256;
+    static constexpr int BM = 256, XM = 64, BN = 256;
     static constexpr int WAVES = 8, THREADS = 64 * WAVES, LOADERS = 4;
     static constexpr int WM = 128, WN = 64, TM = 8, TN = 4, TR_MAX = TM + XM / 32;
-    static constexpr int A_BYTES = ROWS * kBlock, B_BYTES = BN * kBlock;
-    static constexpr int B_INSTR = BN / 8 / LOADERS;
+    static constexpr int WROWS = 16 * TR_MAX;                  // LDS rows per wave row (160)
+    static constexpr int A_BYTES = 2 * WROWS * kBlock, B_BYTES = BN * kBlock;
+    static constexpr int MAIN_INSTR = BM / 8 / LOADERS, B_INSTR = BN / 8 / LOADERS;
     // row scales: lane row t (0..15) of wave row wm, sub-tile row i sits at
     // float t * SP + 12 wm + i (16-byte aligned groups of four; SP / 4 odd, so
-    // the 16 lanes of a read hit distinct bank groups)
+    // the 16 lanes of a read hit distinct bank groups); the 64-float weight-scale
+    // line follows
     static constexpr int SP = 28, S_FLOATS = 16 * SP, S_INSTR = S_FLOATS / 64;
-    static constexpr int S_OFF = A_BYTES + B_BYTES, SB_OFF = S_OFF + S_FLOATS * 4;
-    static constexpr int STAGE = (SB_OFF + 256 + 1023) / 1024 * 1024;
-    static_assert(BM % (8 * LOADERS) == 0 && BN % (8 * LOADERS) == 0, "rows split over loaders");
-    static_assert(S_FLOATS % 64 == 0 && S_INSTR <= WAVES, "one scale instruction per wave");
-    static_assert(2 * STAGE <= 158 * 1024, "two stages fit in LDS");
+    static constexpr int SB_OFF = S_FLOATS, S_LINE = S_FLOATS + 64;
+    static_assert(MAIN_INSTR % 2 == 0 && B_INSTR % 2 == 0, "instruction parity picks the offset");
+    static_assert(S_FLOATS % 64 == 0 && S_INSTR < WAVES, "one scale instruction per wave");
+    static_assert(2 * (A_BYTES + B_BYTES + 4 * S_LINE) <= 158 * 1024, "two stages fit in LDS");
+};
+
+struct GroupedLds {
+    uint8_t* a[2];
+    uint8_t* b[2];
+    float* s[2];
 };
 
 // Tiles of a group of `rows` rows (see above).
@@ -1130,11 +1139,9 @@ __device__ __forceinline__ void grouped_tile(const uint8_t* __restrict__ a,
                                              const uint8_t* __restrict__ b,
                                              const float* __restrict__ bs,
                                              uint16_t* __restrict__ c, int64_t m0, int64_t m_end,
-                                             int64_t n0, int64_t N, int64_t K, uint8_t* st0,
-                                             uint8_t* st1) {
+                                             int64_t n0, int64_t N, int64_t K, const GroupedLds& L) {
     using T = GroupedTile;
     constexpr int TR = T::TM + TX;                         // sub-tile rows per wave
-    constexpr int A_INSTR = (T::BM + 32 * TX) / 8 / T::LOADERS;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / 4, wn = wave % 4;
@@ -1148,19 +1155,22 @@ __device__ __forceinline__ void grouped_tile(const uint8_t* __restrict__ a,
     const __amdgpu_buffer_rsrc_t rs_as = make_rsrc(as + m0 * KB, (uint64_t)rows_a * KB * 4);
     const __amdgpu_buffer_rsrc_t rs_bs = make_rsrc(bs, (uint64_t)NBK * KB * 4);
 
-    // loading wave w < LOADERS: A instruction i fills rows 8 (w A_INSTR + i) .. + 7, B
-    // instruction i rows 8 (w B_INSTR + i) .. + 7; lane l writes physical chunk l & 7 of
-    // row + (l >> 3), which holds logical chunk (l & 7) ^ swz(row); with eight rows per
-    // instruction swz(row) = (l >> 3) ^ (parity of the instruction's first row / 8)
+    // Loads of loading wave w < LOADERS.  Main A instruction i (k = 8 w + i) brings tile rows
+    // 8 k .. 8 k + 7 (LDS rows 160 (k / 16) + 8 (k % 16) ..); extra A instruction x (e = w +
+    // 4 x < 4 TX) tile rows 256 + 8 e .. (LDS rows 160 ((e / 2) % 2) + 128 + 16 (e / 4) +
+    // 8 (e % 2) ..); B instruction i (k = 8 w + i) weight rows 8 k ... Lane l writes
+    // physical chunk l & 7 of the LDS row + (l >> 3), which holds logical chunk
+    // (l & 7) ^ swz(LDS row); with eight rows per instruction swz = (l >> 3) ^ (parity of
+    // k, or of e).  The per-lane offsets depend only on that parity; the eight-row steps go
+    // into the scalar offset.
     const int lrow = lane >> 3;
-    uint32_t voff_a[2], voff_b[2];
+    uint32_t voff_a[2], voff_b[2], voff_x;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-        voff_a[p] = (uint32_t)((wave * A_INSTR * 8 + lrow) * K +
-                               (((lane & 7) ^ lrow ^ ((wave * A_INSTR + p) & 1)) * 16));
-        voff_b[p] = (uint32_t)((wave * T::B_INSTR * 8 + lrow) * K +
-                               (((lane & 7) ^ lrow ^ ((wave * T::B_INSTR + p) & 1)) * 16));
+        voff_a[p] = (uint32_t)((wave * T::MAIN_INSTR * 8 + lrow) * K + (((lane & 7) ^ lrow ^ p) * 16));
+        voff_b[p] = (uint32_t)((wave * T::B_INSTR * 8 + lrow) * K + (((lane & 7) ^ lrow ^ p) * 16));
     }
+    voff_x = (uint32_t)((T::BM + 8 * wave + lrow) * K + (((lane & 7) ^ lrow ^ (wave & 1)) * 16));
     // row-scale slot q = wave * 64 + lane (waves < S_INSTR): lane row t = q / SP, wave row
     // and sub-tile row from q % SP; unused slots load row 0
     uint32_t as_off;
@@ -1178,29 +1188,39 @@ __device__ __forceinline__ void grouped_tile(const uint8_t* __restrict__ a,
     }
 
     const uint32_t k8 = (uint32_t)(8 * K);                 // byte step of eight rows
-    auto issue = [&](int64_t kb, uint8_t* base) __attribute__((always_inline)) {
+    auto issue = [&](int64_t kb, auto S_) __attribute__((always_inline)) {
+        constexpr int S = decltype(S_)::value;
         const uint32_t ko = (uint32_t)(kb * kBlock);
+        uint8_t* la = L.a[S];
+        uint8_t* lb = L.b[S];
         if (wave < T::LOADERS) {
             // the scalar offset advances by eight rows per instruction; the empty asm keeps
             // the compiler from precomputing every instruction's offset into its own SGPR
             uint32_t so = ko;
 #pragma unroll
-            for (int i = 0; i < A_INSTR; ++i) {
-                buf_lds16(rs_a, voff_a[i & 1], so, base + (wave * A_INSTR + i) * 1024);
+            for (int i = 0; i < T::MAIN_INSTR; ++i) {
+                const int k = wave * T::MAIN_INSTR + i;
+                buf_lds16(rs_a, voff_a[i & 1], so, la + ((k >> 4) * T::WROWS + (k & 15) * 8) * kBlock);
                 so += k8;
                 asm volatile("" : "+s"(so));
+            }
+#pragma unroll
+            for (int x = 0; x < TX; ++x) {
+                const int e = wave + 4 * x;
+                buf_lds16(rs_a, voff_x, ko + (uint32_t)(x * 4) * k8,
+                          la + (((e >> 1) & 1) * T::WROWS + T::TM * 16 + 16 * (e >> 2) + 8 * (e & 1)) * kBlock);
             }
             so = ko;
 #pragma unroll
             for (int i = 0; i < T::B_INSTR; ++i) {
-                buf_lds16_nt(rs_b, voff_b[i & 1], so, base + T::A_BYTES + (wave * T::B_INSTR + i) * 1024);
+                buf_lds16_nt(rs_b, voff_b[i & 1], so, lb + (wave * T::B_INSTR + i) * 1024);
                 so += k8;
                 asm volatile("" : "+s"(so));
             }
         }
         const uint32_t so = (uint32_t)(kb * 4);
-        if (wave < T::S_INSTR) buf_lds4(rs_as, as_off, so, base + T::S_OFF + wave * 256);
-        if (wave == T::WAVES - 1) buf_lds4(rs_bs, bs_off, so, base + T::SB_OFF);
+        if (wave < T::S_INSTR) buf_lds4(rs_as, as_off, so, L.s[S] + wave * 64);
+        if (wave == T::WAVES - 1) buf_lds4(rs_bs, bs_off, so, L.s[S] + T::SB_OFF);
     };
 
     v4f acc[TR][T::TN];
@@ -1212,62 +1232,80 @@ __device__ __forceinline__ void grouped_tile(const uint8_t* __restrict__ a,
     // a workgroup walking several tiles must not refill a stage a slower wave still reads
     wait_vmcnt<0>();
     barrier_lds();
-    issue(0, st0);
+    issue(0, StageId<0>{});
 
     const int lr = lane & 15;
     const int lk = (lane >> 4) * 2;
     const int off0 = ((lk ^ swz(lr)) << 4);
     const int off1 = (((lk + 1) ^ swz(lr)) << 4);
+    const int arow = (wm * T::WROWS + lr) * kBlock;        // this lane's row of sub-tile row 0
+    const int brow = (T::WN * wn + lr) * kBlock;
     const int sread = lr * T::SP + 12 * wm;
 
-    auto step = [&](int64_t kb, uint8_t* cur, uint8_t* nxt) __attribute__((always_inline)) {
+    auto step = [&](int64_t kb, auto S_) __attribute__((always_inline)) {
+        constexpr int S = decltype(S_)::value;
         wait_vmcnt<0>();              // this wave's loads of block kb
         barrier_lds();                // everyone's loads of kb landed; block kb - 1 fully read
-        if (kb + 1 < KB) issue(kb + 1, nxt);
-        const uint8_t* As = cur;
-        const uint8_t* Bs = cur + T::A_BYTES;
-        const float* Ss = (const float*)(cur + T::S_OFF);
-        const float* Sb = (const float*)(cur + T::SB_OFF);
+        if (kb + 1 < KB) issue(kb + 1, StageId<1 - S>{});
+        const uint8_t* As = L.a[S] + arow;
+        const uint8_t* Bs = L.b[S] + brow;
+        const float* Ss = L.s[S];
+        // The block as one software pipeline over the (row, column) sub-tiles: each MFMA is
+        // followed by the four folds of the previous sub-tile's product, which has landed
+        // while this MFMA was issued, so neither the MFMA pipe nor the wave waits on a fold;
+        // two product registers alternate.  The next row's A fragment is read after the
+        // row's first MFMA, the B fragments during row 0's MFMAs.
         v8i fb[T::TN];
-#pragma unroll
-        for (int j = 0; j < T::TN; ++j) {
-            const uint8_t* q = Bs + (T::WN * wn + 16 * j + lr) * kBlock;
-            fb[j] = frag_from(*(const uint4*)(q + off0), *(const uint4*)(q + off1));
-        }
-        const float sbv = Sb[wn >> 1];
+        v8i fa, fa_nxt;
+        fa_nxt = frag_from(*(const uint4*)(As + off0), *(const uint4*)(As + off1));
+        fb[0] = frag_from(*(const uint4*)(Bs + off0), *(const uint4*)(Bs + off1));
         const v4f s0 = *(const v4f*)(Ss + sread), s1 = *(const v4f*)(Ss + sread + 4);
         float2 s2 = float2{0.f, 0.f};
         if constexpr (TX > 0) s2 = *(const float2*)(Ss + sread + 8);
+        const float sbv = Ss[T::SB_OFF + (wn >> 1)];
+        __builtin_amdgcn_sched_barrier(0);
+        v4f pr[2];
+        float sc_prev = 0.f;
 #pragma unroll
         for (int i = 0; i < TR; ++i) {
-            const uint8_t* r = As + (grouped_row(wm, i) + lr) * kBlock;
-            const v8i fa = frag_from(*(const uint4*)(r + off0), *(const uint4*)(r + off1));
+            fa = fa_nxt;
             const float sa = i < 4 ? s0[i] : (i < 8 ? s1[i - 4] : (i == 8 ? s2.x : s2.y));
             const float sc = sa * sbv;
-            // the row's MFMAs in groups of PP, each group's folds after it (the first fold of a
-            // group waits on its first MFMA only); the tallest tile keeps two products in
-            // flight instead of four, to stay within the register file
-            constexpr int PP = TX == 2 ? 2 : 4;
 #pragma unroll
-            for (int j0 = 0; j0 < T::TN; j0 += PP) {
-                v4f pp[PP];
-#pragma unroll
-                for (int j = 0; j < PP; ++j)
-                    pp[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        fb[j0 + j], fa, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-#pragma unroll
-                for (int j = 0; j < PP; ++j) acc[i][j0 + j] = pp[j] * sc + acc[i][j0 + j];
-                __builtin_amdgcn_sched_group_barrier(0x008, PP, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 4 * PP, 0);
+            for (int j = 0; j < T::TN; ++j) {
+                const int idx = i * T::TN + j;
+                pr[idx & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    fb[j], fa, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                if (i == 0 && j + 1 < T::TN) {
+                    const uint8_t* q = Bs + 16 * (j + 1) * kBlock;
+                    fb[j + 1] = frag_from(*(const uint4*)(q + off0), *(const uint4*)(q + off1));
+                }
+                if (j == 0 && i + 1 < TR) {
+                    const uint8_t* r = As + 16 * (i + 1) * kBlock;
+                    fa_nxt = frag_from(*(const uint4*)(r + off0), *(const uint4*)(r + off1));
+                }
+                if (idx > 0) {
+                    const int pi = (idx - 1) / T::TN, pj = (idx - 1) % T::TN;
+                    acc[pi][pj] = pr[(idx - 1) & 1] * (pj == T::TN - 1 ? sc_prev : sc) + acc[pi][pj];
+                }
+                // pin the order: this MFMA, the reads, the previous product's folds
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if ((i == 0 && j + 1 < T::TN) || (j == 0 && i + 1 < TR))
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                if (idx > 0 && j == 0) __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+                if (idx > 0 && j > 0) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
+            sc_prev = sc;
         }
+        acc[TR - 1][T::TN - 1] = pr[(TR * T::TN - 1) & 1] * sc_prev + acc[TR - 1][T::TN - 1];
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     if (wave >= 4) __builtin_amdgcn_s_setprio(1);
     for (int64_t kb = 0; kb < KB; kb += 2) {
-        step(kb, st0, st1);
-        if (kb + 1 < KB) step(kb + 1, st1, st0);
+        step(kb, StageId<0>{});
+        if (kb + 1 < KB) step(kb + 1, StageId<1>{});
     }
     if (wave >= 4) __builtin_amdgcn_s_setprio(0);
 
@@ -1306,8 +1344,14 @@ __global__ __launch_bounds__(GroupedTile::THREADS, 1) void gemm_grouped_kernel(
     const uint8_t* __restrict__ a, const float* __restrict__ as, const uint8_t* __restrict__ b,
     const float* __restrict__ bs, uint16_t* __restrict__ c, const int32_t* __restrict__ off,
     int G, int64_t total_M, int64_t N, int64_t K, int nt) {
-    __shared__ __attribute__((aligned(1024))) uint8_t st0[GroupedTile::STAGE];
-    __shared__ __attribute__((aligned(1024))) uint8_t st1[GroupedTile::STAGE];
+    using T = GroupedTile;
+    __shared__ __attribute__((aligned(1024))) uint8_t la0[T::A_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t la1[T::A_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t lb0[T::B_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t lb1[T::B_BYTES];
+    __shared__ __attribute__((aligned(256))) float ls0[T::S_LINE];
+    __shared__ __attribute__((aligned(256))) float ls1[T::S_LINE];
+    const GroupedLds L = {{la0, la1}, {lb0, lb1}, {ls0, ls1}};
     const int64_t KB = K / kBlock;
     const int64_t NB = (N + kBlock - 1) / kBlock;
     const int nwg = gridDim.x;                    // a multiple of 8
@@ -1320,12 +1364,12 @@ __global__ __launch_bounds__(GroupedTile::THREADS, 1) void gemm_grouped_kernel(
         const uint8_t* bg = b + (int64_t)at.g * N * K;
         const float* bsg = bs + (int64_t)at.g * NB * KB;
         const int64_t rows = at.m_end - at.m0;
-        if (rows <= GroupedTile::BM)
-            grouped_tile<0>(a, as, bg, bsg, c, at.m0, at.m_end, at.n0, N, K, st0, st1);
-        else if (rows <= GroupedTile::BM + 32)
-            grouped_tile<1>(a, as, bg, bsg, c, at.m0, at.m_end, at.n0, N, K, st0, st1);
+        if (rows <= T::BM)
+            grouped_tile<0>(a, as, bg, bsg, c, at.m0, at.m_end, at.n0, N, K, L);
+        else if (rows <= T::BM + 32)
+            grouped_tile<1>(a, as, bg, bsg, c, at.m0, at.m_end, at.n0, N, K, L);
         else
-            grouped_tile<2>(a, as, bg, bsg, c, at.m0, at.m_end, at.n0, N, K, st0, st1);
+            grouped_tile<2>(a, as, bg, bsg, c, at.m0, at.m_end, at.n0, N, K, L);
     }
 }
 
