@@ -15,7 +15,14 @@ Printed: one JSON line.  `value` is the step's GEMM FLOP divided by the step's
 wall time (TFLOP/s); `kernels` gives each kernel's average duration from HIP
 events recorded around every launch inside the timed region, with its
 algorithmic FLOP or bytes per launch and its fraction of the MI355X peak that
-bounds it; `roofline` repeats that for the dominant kernel; `cpu_baseline`
+bounds it, and, after the timed region, the same launch timed alone: rounds of
+back-to-back launches between one event pair (so the event overhead of one
+short launch does not count), median and min per launch over the rounds;
+HBM-bound launches are also timed "cold", cycling over copies of their
+buffers totalling more than 1 GB so no launch finds its data in the 256 MB
+Infinity Cache or in L2.  `roofline` repeats the timed-region figure for the
+dominant kernel; `clock` is the GPU's shader clock and socket power sampled
+from sysfs during the timed region (and the board power cap); `cpu_baseline`
 times the CPU oracle on a bounded, proportional sample of the same step.
 
 Other workloads (parity-test shapes, measured on demand): --workload tiny |
@@ -87,6 +94,28 @@ def sha_of(t: torch.Tensor) -> str:
 
 # ------------------------------------------------------------------ the steps
 
+class Launch:
+    """One named launch: op(*args), with its algorithmic work and the peak that bounds it.
+    Copies of the launch (for cold timing) run the same op on clones of every tensor."""
+
+    def __init__(self, name, op, args, flop, nbytes, bound):
+        self.name, self.op, self.args = name, op, tuple(args)
+        self.flop, self.bytes, self.bound = flop, nbytes, bound
+
+    def __call__(self):
+        self.op(*self.args)
+
+    def footprint(self):
+        return sum(a.numel() * a.element_size() for a in self.args if isinstance(a, torch.Tensor))
+
+    def copies(self, n):
+        out = []
+        for _ in range(n):
+            args = tuple(a.clone() if isinstance(a, torch.Tensor) else a for a in self.args)
+            out.append(Launch(self.name, self.op, args, self.flop, self.bytes, self.bound))
+        return out
+
+
 class Step:
     """Device buffers and the ordered launches of one step; every launch is named."""
 
@@ -119,14 +148,19 @@ class Step:
                 copies = [(w.clone(), s.clone()) for _ in range(n_copies)]
             self.copies, self.turn = copies, 0
 
-            def gemm_step():
+            def gemm_step(q, qs, y, work):
                 wc, sc = self.copies[self.turn % len(self.copies)]
                 self.turn += 1
                 bfp8.bfp8_gemm(q, qs, wc, sc, y, work)
+            if cold:
+                gemm_launch = Launch("fp8_gemm", gemm_step, (q, qs, y, work), 2 * M * N * K,
+                                     gemm_bytes(M, N, K), "mfma" if c == 0 else "hbm")
+            else:
+                gemm_launch = Launch("fp8_gemm", bfp8.bfp8_gemm, (q, qs, w, s, y, work), 2 * M * N * K,
+                                     gemm_bytes(M, N, K), "mfma" if c == 0 else "hbm")
             self.launches += [
-                ("act_quant", lambda: bfp8.bfp8_act_quant(x, q, qs), 0, act_quant_bytes(M, K), "hbm"),
-                ("fp8_gemm", gemm_step, 2 * M * N * K,
-                 gemm_bytes(M, N, K), "mfma" if c == 0 else "hbm"),
+                Launch("act_quant", bfp8.bfp8_act_quant, (x, q, qs), 0, act_quant_bytes(M, K), "hbm"),
+                gemm_launch,
             ]
             self.shape = dict(M=M, N=N, K=K)
             self.dominant, self.dominant_kernel = ["fp8_gemm"], "gemm"
@@ -143,17 +177,17 @@ class Step:
             y = torch.empty(M, N2, dtype=torch.bfloat16, device=dev)
             work1, work2 = gemm_workspace(M, N1, K1, dev), gemm_workspace(M, N2, K2, dev)
             self.launches += [
-                ("act_quant_x", lambda: bfp8.bfp8_act_quant(x, q, qs), 0, act_quant_bytes(M, K1), "hbm"),
-                ("fp8_gemm_1", lambda: bfp8.bfp8_gemm(q, qs, w1, s1, h, work1), 2 * M * N1 * K1,
-                 gemm_bytes(M, N1, K1), "mfma"),
-                ("act_quant_h", lambda: bfp8.bfp8_act_quant(h, qh, qhs), 0, act_quant_bytes(M, K2), "hbm"),
-                ("fp8_gemm_2", lambda: bfp8.bfp8_gemm(qh, qhs, w2, s2, y, work2), 2 * M * N2 * K2,
-                 gemm_bytes(M, N2, K2), "mfma"),
+                Launch("act_quant_x", bfp8.bfp8_act_quant, (x, q, qs), 0, act_quant_bytes(M, K1), "hbm"),
+                Launch("fp8_gemm_1", bfp8.bfp8_gemm, (q, qs, w1, s1, h, work1), 2 * M * N1 * K1,
+                       gemm_bytes(M, N1, K1), "mfma"),
+                Launch("act_quant_h", bfp8.bfp8_act_quant, (h, qh, qhs), 0, act_quant_bytes(M, K2), "hbm"),
+                Launch("fp8_gemm_2", bfp8.bfp8_gemm, (qh, qhs, w2, s2, y, work2), 2 * M * N2 * K2,
+                       gemm_bytes(M, N2, K2), "mfma"),
             ]
             if c == 3:
                 wd = torch.empty(N1, K1, dtype=torch.bfloat16, device=dev)
-                self.launches.append(("weight_dequant", lambda: bfp8.bfp8_weight_dequant(w1, s1, wd), 0,
-                                      dequant_bytes(N1, K1), "hbm"))
+                self.launches.append(Launch("weight_dequant", bfp8.bfp8_weight_dequant, (w1, s1, wd), 0,
+                                            dequant_bytes(N1, K1), "hbm"))
             self.shape = dict(M=M, N1=N1, K1=K1, N2=N2, K2=K2)
             # both GEMMs run the same kernel with the same FLOP count per launch
             self.dominant, self.dominant_kernel = ["fp8_gemm_1", "fp8_gemm_2"], "gemm"
@@ -168,9 +202,9 @@ class Step:
             qs = torch.empty(T, K // BLOCK, dtype=torch.float32, device=dev)
             y = torch.empty(T, N, dtype=torch.bfloat16, device=dev)
             self.launches += [
-                ("act_quant", lambda: bfp8.bfp8_act_quant(xg, q, qs), 0, act_quant_bytes(T, K), "hbm"),
-                ("fp8_gemm_grouped", lambda: bfp8.bfp8_gemm_grouped(q, qs, b, bs, y, off_d),
-                 2 * T * N * K, gemm_bytes(T, N, K, G), "hbm"),
+                Launch("act_quant", bfp8.bfp8_act_quant, (xg, q, qs), 0, act_quant_bytes(T, K), "hbm"),
+                Launch("fp8_gemm_grouped", bfp8.bfp8_gemm_grouped, (q, qs, b, bs, y, off_d),
+                       2 * T * N * K, gemm_bytes(T, N, K, G), "hbm"),
             ]
             counts = (off[1:] - off[:-1]).tolist()
             self.shape = dict(T=T, G=G, N=N, K=K, tokens_per_expert_min=min(counts),
@@ -191,13 +225,13 @@ class Step:
             wd = torch.empty(N1, K1, dtype=torch.bfloat16, device=dev)
             work2 = gemm_workspace(M, N2, K2, dev)
             self.launches += [
-                ("act_quant_x", lambda: bfp8.bfp8_act_quant(x, q, qs), 0, act_quant_bytes(M, K1), "hbm"),
-                ("fp8_gemm_1_quant", lambda: bfp8.bfp8_gemm_act_quant(q, qs, w1, s1, qh, qhs),
-                 2 * M * N1 * K1, M * K1 + N1 * K1 + M * N1 + 4 * M * (N1 // BLOCK), "mfma"),
-                ("fp8_gemm_2", lambda: bfp8.bfp8_gemm(qh, qhs, w2, s2, y, work2), 2 * M * N2 * K2,
-                 gemm_bytes(M, N2, K2), "mfma"),
-                ("weight_dequant", lambda: bfp8.bfp8_weight_dequant(w1, s1, wd), 0,
-                 dequant_bytes(N1, K1), "hbm"),
+                Launch("act_quant_x", bfp8.bfp8_act_quant, (x, q, qs), 0, act_quant_bytes(M, K1), "hbm"),
+                Launch("fp8_gemm_1_quant", bfp8.bfp8_gemm_act_quant, (q, qs, w1, s1, qh, qhs),
+                       2 * M * N1 * K1, M * K1 + N1 * K1 + M * N1 + 4 * M * (N1 // BLOCK), "mfma"),
+                Launch("fp8_gemm_2", bfp8.bfp8_gemm, (qh, qhs, w2, s2, y, work2), 2 * M * N2 * K2,
+                       gemm_bytes(M, N2, K2), "mfma"),
+                Launch("weight_dequant", bfp8.bfp8_weight_dequant, (w1, s1, wd), 0,
+                       dequant_bytes(N1, K1), "hbm"),
             ]
             self.shape = dict(M=M, N1=N1, K1=K1, N2=N2, K2=K2)
             self.dominant, self.dominant_kernel = ["fp8_gemm_1_quant", "fp8_gemm_2"], "gemm"
@@ -215,11 +249,11 @@ class Step:
             qhs = torch.empty(M, K2 // BLOCK, dtype=torch.float32, device=dev)
             y = torch.empty(M, N2, dtype=torch.bfloat16, device=dev)
             self.launches += [
-                ("act_quant_x", lambda: bfp8.bfp8_act_quant(x, q, qs), 0, act_quant_bytes(M, K1), "hbm"),
-                ("fp8_gemm_w13_swiglu_quant", lambda: bfp8.bfp8_gemm_swiglu_act_quant(q, qs, w13, s13, qh, qhs),
-                 2 * M * 2 * N1 * K1, M * K1 + 2 * N1 * K1 + M * N1 + 4 * M * (N1 // BLOCK), "mfma"),
-                ("fp8_gemm_w2", lambda: bfp8.bfp8_gemm(qh, qhs, w2, s2, y), 2 * M * N2 * K2,
-                 gemm_bytes(M, N2, K2), "mfma"),
+                Launch("act_quant_x", bfp8.bfp8_act_quant, (x, q, qs), 0, act_quant_bytes(M, K1), "hbm"),
+                Launch("fp8_gemm_w13_swiglu_quant", bfp8.bfp8_gemm_swiglu_act_quant, (q, qs, w13, s13, qh, qhs),
+                       2 * M * 2 * N1 * K1, M * K1 + 2 * N1 * K1 + M * N1 + 4 * M * (N1 // BLOCK), "mfma"),
+                Launch("fp8_gemm_w2", bfp8.bfp8_gemm, (qh, qhs, w2, s2, y), 2 * M * N2 * K2,
+                       gemm_bytes(M, N2, K2), "mfma"),
             ]
             self.shape = dict(M=M, N_gate_up=2 * N1, N_out=N1, K1=K1, N2=N2, K2=K2, activation="silu (stated reading)")
             self.dominant, self.dominant_kernel = ["fp8_gemm_w13_swiglu_quant"], "gemm"
@@ -239,14 +273,14 @@ class Step:
             qhs = torch.empty(M, K2 // BLOCK, dtype=torch.float32, device=dev)
             y = torch.empty(M, N2, dtype=torch.bfloat16, device=dev)
             self.launches += [
-                ("act_quant_ue8m0_x", lambda: bfp8.bfp8_act_quant_ue8m0(x, q, qs), 0,
-                 act_quant_bytes(M, K1), "hbm"),
-                ("fp8_gemm_ue8m0_1", lambda: bfp8.bfp8_gemm_ue8m0(q, qs, w1, s1, h), 2 * M * N1 * K1,
-                 gemm_bytes(M, N1, K1), "mfma"),
-                ("act_quant_ue8m0_h", lambda: bfp8.bfp8_act_quant_ue8m0(h, qh, qhs), 0,
-                 act_quant_bytes(M, K2), "hbm"),
-                ("fp8_gemm_ue8m0_2", lambda: bfp8.bfp8_gemm_ue8m0(qh, qhs, w2, s2, y), 2 * M * N2 * K2,
-                 gemm_bytes(M, N2, K2), "mfma"),
+                Launch("act_quant_ue8m0_x", bfp8.bfp8_act_quant_ue8m0, (x, q, qs), 0,
+                       act_quant_bytes(M, K1), "hbm"),
+                Launch("fp8_gemm_ue8m0_1", bfp8.bfp8_gemm_ue8m0, (q, qs, w1, s1, h), 2 * M * N1 * K1,
+                       gemm_bytes(M, N1, K1), "mfma"),
+                Launch("act_quant_ue8m0_h", bfp8.bfp8_act_quant_ue8m0, (h, qh, qhs), 0,
+                       act_quant_bytes(M, K2), "hbm"),
+                Launch("fp8_gemm_ue8m0_2", bfp8.bfp8_gemm_ue8m0, (qh, qhs, w2, s2, y), 2 * M * N2 * K2,
+                       gemm_bytes(M, N2, K2), "mfma"),
             ]
             self.shape = dict(M=M, N1=N1, K1=K1, N2=N2, K2=K2, scales="powers of two (e8m0)")
             self.dominant, self.dominant_kernel = ["fp8_gemm_ue8m0_1", "fp8_gemm_ue8m0_2"], "gemm_ue8m0"
@@ -260,14 +294,14 @@ class Step:
             h = torch.empty(M, N1, dtype=torch.bfloat16, device=dev)
             y = torch.empty(M, N2, dtype=torch.bfloat16, device=dev)
             self.launches += [
-                ("weight_dequant_1", lambda: bfp8.bfp8_weight_dequant(w1, s1, w1d), 0,
-                 dequant_bytes(N1, K1), "hbm"),
-                ("bf16_gemm_1", lambda: bfp8.bfp8_gemm_bf16(x, w1d, h), 2 * M * N1 * K1,
-                 2 * M * K1 + 2 * N1 * K1 + 2 * M * N1, "mfma_bf16"),
-                ("weight_dequant_2", lambda: bfp8.bfp8_weight_dequant(w2, s2, w2d), 0,
-                 dequant_bytes(N2, K2), "hbm"),
-                ("bf16_gemm_2", lambda: bfp8.bfp8_gemm_bf16(h, w2d, y), 2 * M * N2 * K2,
-                 2 * M * K2 + 2 * N2 * K2 + 2 * M * N2, "mfma_bf16"),
+                Launch("weight_dequant_1", bfp8.bfp8_weight_dequant, (w1, s1, w1d), 0,
+                       dequant_bytes(N1, K1), "hbm"),
+                Launch("bf16_gemm_1", bfp8.bfp8_gemm_bf16, (x, w1d, h), 2 * M * N1 * K1,
+                       2 * M * K1 + 2 * N1 * K1 + 2 * M * N1, "mfma_bf16"),
+                Launch("weight_dequant_2", bfp8.bfp8_weight_dequant, (w2, s2, w2d), 0,
+                       dequant_bytes(N2, K2), "hbm"),
+                Launch("bf16_gemm_2", bfp8.bfp8_gemm_bf16, (h, w2d, y), 2 * M * N2 * K2,
+                       2 * M * K2 + 2 * N2 * K2 + 2 * M * N2, "mfma_bf16"),
             ]
             self.shape = dict(M=M, N1=N1, K1=K1, N2=N2, K2=K2)
             self.dominant, self.dominant_kernel = ["bf16_gemm_1", "bf16_gemm_2"], "gemm_bf16"
@@ -290,14 +324,14 @@ class Step:
             y = torch.empty(Tt, N, dtype=torch.bfloat16, device=dev)
             nrows = off_d[G:]
             self.launches += [
-                ("moe_dispatch", lambda: bfp8.bfp8_moe_dispatch(topk_d, 0, off_d, row_token, slot_row, ws),
-                 0, dispatch_bytes(Tt, k, rows, G), "hbm"),
-                ("act_quant_rows", lambda: bfp8.bfp8_act_quant_rows(x, row_token, nrows, q, qs),
-                 0, act_quant_bytes(rows, K) + 4 * rows, "hbm"),
-                ("fp8_gemm_grouped", lambda: bfp8.bfp8_gemm_grouped(q, qs, b, bs, h, off_d),
-                 2 * rows * N * K, gemm_bytes(rows, N, K, G), "hbm"),
-                ("moe_combine", lambda: bfp8.bfp8_moe_combine(h, slot_row, w_d, y),
-                 0, combine_bytes(Tt, k, rows, N), "hbm"),
+                Launch("moe_dispatch", lambda topk_d, off_d, rt, sr, ws: bfp8.bfp8_moe_dispatch(topk_d, 0, off_d, rt, sr, ws),
+                       (topk_d, off_d, row_token, slot_row, ws), 0, dispatch_bytes(Tt, k, rows, G), "hbm"),
+                Launch("act_quant_rows", bfp8.bfp8_act_quant_rows, (x, row_token, nrows, q, qs),
+                       0, act_quant_bytes(rows, K) + 4 * rows, "hbm"),
+                Launch("fp8_gemm_grouped", bfp8.bfp8_gemm_grouped, (q, qs, b, bs, h, off_d),
+                       2 * rows * N * K, gemm_bytes(rows, N, K, G), "hbm"),
+                Launch("moe_combine", bfp8.bfp8_moe_combine, (h, slot_row, w_d, y),
+                       0, combine_bytes(Tt, k, rows, N), "hbm"),
             ]
             counts = (off[1:] - off[:-1]).tolist()
             self.shape = dict(tokens=Tt, top_k=k, local_experts=G, rows=rows, row_capacity=cap,
@@ -308,10 +342,10 @@ class Step:
             raise ValueError(c)
 
     def run(self, events=None):
-        for i, (_, fn, _, _, _) in enumerate(self.launches):
+        for i, launch in enumerate(self.launches):
             if events is not None:
                 events[i].record()
-            fn()
+            launch()
         if events is not None:
             events[len(self.launches)].record()
 
@@ -386,6 +420,7 @@ def cpu_baseline(wl, target_s=12.0, kind=None):
     rows = int(min(M, max(probe, probe * target_s / max(dt, 1e-6))))
     dt, flop = run(rows)
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": (f"{rows} of {M} {'tokens' if kind == 'moe-layer' else 'rows'} of every stage "
                        f"of one step ({dt:.1f} s of CPU work)")}
 
@@ -414,6 +449,121 @@ def read_traffic(kernel_name, workload):
         return None
 
 
+# ------------------------------------------------------------------ clock and power
+
+class ClockSampler:
+    """Samples the GPU's shader clock and socket power from sysfs every few ms while
+    active: the level marked current in pp_dpm_sclk (as the driver reports it), and hwmon
+    power1_average (else power1_input); the board power cap from hwmon power1_cap.
+    Reading sysfs costs the GPU nothing; fields are None where a file is absent."""
+
+    def __init__(self, period_s=0.005):
+        import glob
+        import threading
+        self.sclk_path = self.power_path = self.cap_path = None
+        for dev_dir in sorted(glob.glob("/sys/class/drm/card*/device")):
+            if os.path.exists(os.path.join(dev_dir, "pp_dpm_sclk")):
+                self.sclk_path = os.path.join(dev_dir, "pp_dpm_sclk")
+                for name in ("power1_average", "power1_input"):
+                    hits = sorted(glob.glob(os.path.join(dev_dir, "hwmon", "hwmon*", name)))
+                    if hits:
+                        self.power_path = hits[0]
+                        break
+                caps = sorted(glob.glob(os.path.join(dev_dir, "hwmon", "hwmon*", "power1_cap")))
+                self.cap_path = caps[0] if caps else None
+                break
+        self.period = period_s
+        self.sclk, self.power = [], []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._loop, daemon=True)
+
+    @staticmethod
+    def _read(path):
+        try:
+            with open(path) as f:
+                return f.read()
+        except OSError:
+            return None
+
+    def _sample(self):
+        text = self._read(self.sclk_path) if self.sclk_path else None
+        if text:
+            for line in text.splitlines():
+                if line.rstrip().endswith("*"):
+                    digits = "".join(ch for ch in line.split(":", 1)[-1] if ch.isdigit())
+                    if digits:
+                        self.sclk.append(int(digits))
+        text = self._read(self.power_path) if self.power_path else None
+        if text and text.strip().isdigit():
+            self.power.append(int(text.strip()) / 1e6)
+
+    def _loop(self):
+        while not self._stop.is_set():
+            self._sample()
+            self._stop.wait(self.period)
+
+    def start(self):
+        self._thread.start()
+        return self
+
+    def stop(self):
+        self._stop.set()
+        self._thread.join()
+        cap = self._read(self.cap_path) if self.cap_path else None
+        return {"sclk_mhz_median": float(np.median(self.sclk)) if self.sclk else None,
+                "sclk_mhz_range": [min(self.sclk), max(self.sclk)] if self.sclk else None,
+                "socket_power_w_median": float(np.median(self.power)) if self.power else None,
+                "power_cap_w": int(cap.strip()) / 1e6 if cap and cap.strip().isdigit() else None,
+                "samples": len(self.sclk), "source": "sysfs pp_dpm_sclk (current level), hwmon power1",
+                "window": "warmup, timed steps and the isolated per-kernel timing"}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+# ------------------------------------------------------------------ isolated timing
+
+def time_isolated(launches, est_us, rounds=5, min_round_ms=2.0):
+    """Per-launch duration of `launches` (copies of one launch, called in turn), timed as
+    `rounds` rounds of back-to-back calls between one event pair; returns the median and
+    min over the rounds of the mean duration per call, in us."""
+    n = len(launches)
+    reps = max(n, int(np.ceil(min_round_ms * 1e3 / max(est_us, 1.0))))
+    reps = -(-reps // n) * n
+    per_call = []
+    for _ in range(rounds):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for r in range(reps):
+            launches[r % n]()
+        e1.record()
+        torch.cuda.synchronize()
+        per_call.append(e0.elapsed_time(e1) * 1e3 / reps)
+    return {"median_us": float(np.median(per_call)), "min_us": float(min(per_call)),
+            "rounds": rounds, "launches_per_round": reps}
+
+
+def rates(entry, us):
+    """TFLOP/s, GB/s and roofline fraction of a launch that takes `us`."""
+    out = {"gbs": entry["bytes"] / (us * 1e-6) / 1e9}
+    if entry["flop"]:
+        out["tflops"] = entry["flop"] / (us * 1e-6) / 1e12
+    if entry["bound"] == "mfma":
+        out["frac"] = out["tflops"] / PEAK_FP8_TFLOPS
+    elif entry["bound"] == "mfma_bf16":
+        out["frac"] = out["tflops"] / PEAK_BF16_TFLOPS
+    else:
+        out["frac"] = out["gbs"] / PEAK_HBM_GBS
+    return out
+
+
 # ------------------------------------------------------------------ main
 
 def main():
@@ -430,6 +580,9 @@ def main():
                     help="decode: rotate over weight copies totalling > 512 MB so every step "
                          "reads its weight from HBM (eager launches only)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-isolated", action="store_true",
+                    help="skip the per-kernel isolated (warm / cold) timing after the timed region "
+                         "(profiler runs: every launch then belongs to the timed steps)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy three times (reference for the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -467,9 +620,10 @@ def main():
     step = Step(wl, dev, args.workload, cold=args.cold)
     gen_s = time.time() - t0
     print(f"# workload {wl.name}: inputs built in {gen_s:.1f}s; launches "
-          f"{[l[0] for l in step.launches]}", file=sys.stderr, flush=True)
+          f"{[l.name for l in step.launches]}", file=sys.stderr, flush=True)
 
     nl = len(step.launches)
+    sampler = ClockSampler().start()
     for _ in range(args.warmup):
         step.run()
     torch.cuda.synchronize()
@@ -484,19 +638,34 @@ def main():
     ms_per_step = (t_end - t_start) * 1e3 / args.steps
 
     kernels = {}
-    for i, (name, _, flop, nbytes, bound) in enumerate(step.launches):
-        ms = float(np.mean([events[k][i].elapsed_time(events[k][i + 1]) for k in range(args.steps)]))
-        entry = {"avg_us": ms * 1e3, "flop": flop, "bytes": nbytes, "bound": bound}
-        if flop:
-            entry["tflops"] = flop / (ms * 1e-3) / 1e12
-        entry["gbs"] = nbytes / (ms * 1e-3) / 1e9
-        if bound == "mfma":
-            entry["frac"] = entry["tflops"] / PEAK_FP8_TFLOPS
-        elif bound == "mfma_bf16":
-            entry["frac"] = entry["tflops"] / PEAK_BF16_TFLOPS
-        else:
-            entry["frac"] = entry["gbs"] / PEAK_HBM_GBS
-        kernels[name] = entry
+    for i, launch in enumerate(step.launches):
+        per = [events[k][i].elapsed_time(events[k][i + 1]) * 1e3 for k in range(args.steps)]
+        entry = {"avg_us": float(np.mean(per)), "median_us": float(np.median(per)),
+                 "min_us": float(min(per)), "flop": launch.flop, "bytes": launch.bytes,
+                 "bound": launch.bound}
+        entry.update(rates(entry, entry["avg_us"]))
+        kernels[launch.name] = entry
+
+    # each launch alone, after the timed region: back-to-back rounds on the same buffers
+    # (warm), and for the HBM-bound ones over copies of their buffers totalling > 1 GB
+    # (cold: no launch finds its data in the Infinity Cache or L2)
+    if not args.cold and not args.no_isolated:
+        for launch in step.launches:
+            entry = kernels[launch.name]
+            iso = time_isolated([launch], entry["avg_us"])
+            iso.update({k: v for k, v in rates(entry, iso["median_us"]).items()})
+            entry["isolated_warm"] = iso
+            if launch.bound == "hbm" and launch.footprint() > 0:
+                n_copies = int(min(16, max(2, -(-(1 << 30) // launch.footprint()))))
+                copies = launch.copies(n_copies)
+                torch.cuda.synchronize()
+                iso = time_isolated(copies, entry["avg_us"])
+                iso.update({k: v for k, v in rates(entry, iso["median_us"]).items()})
+                iso["buffer_copies"] = n_copies
+                entry["isolated_cold"] = iso
+                del copies
+                torch.cuda.empty_cache()
+    clock = sampler.stop()
 
     launch_mode = "eager"
     if args.graph:
@@ -517,7 +686,7 @@ def main():
         ms_per_step = (time.perf_counter() - t_start) * 1e3 / args.steps
         launch_mode = f"hip-graph replay ({args.steps} steps in one graph)"
 
-    gemm_flop = sum(l[2] for l in step.launches)
+    gemm_flop = sum(l.flop for l in step.launches)
     value = gemm_flop / (ms_per_step * 1e-3) / 1e12
 
     # dominant kernel: the launches of the kernel that takes most of the step
@@ -546,7 +715,7 @@ def main():
                if args.workload in ("moe-layer", "bf16-branch", "dense-mlp-unfused", "expert-ffn",
                                     "dense-mlp-ue8m0") else wl.name)
     config = {"workload": wl_name, "shape": step.shape,
-              "step": " -> ".join(l[0] for l in step.launches),
+              "step": " -> ".join(l.name for l in step.launches),
               "value_definition": "GEMM FLOP per step / wall time per step",
               "input_sha256_16": step.hashes, "seeds": "1000*config+tensor_id",
               "parallelism": "single-gpu", "launch": launch_mode,
@@ -558,7 +727,8 @@ def main():
            "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": dtype,
            "data": "synthetic (seeded; DeepSeek-V3 projection shapes, random-init)",
-           "config": config, "kernels": kernels, "roofline": roof, "cpu_baseline": cpu}
+           "config": config, "kernels": kernels, "roofline": roof, "clock": clock,
+           "cpu_baseline": cpu}
     print(json.dumps(out), flush=True)
 
 

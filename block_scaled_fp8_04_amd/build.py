@@ -7,7 +7,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIBRARY = os.path.join(HERE, "libbfp8.so")
-SOURCES = ["api.hip", "quant.hip", "dequant.hip", "gemm.hip", "gemm_bf16.hip", "moe.hip"]
+SOURCES = ["api.hip", "quant.hip", "dequant.hip", "gemm.hip", "grouped.hip", "gemm_bf16.hip", "moe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -O3, no fast-math: fp32 division stays correctly rounded (act_quant relies on
