@@ -580,6 +580,10 @@ def main():
                     help="decode: rotate over weight copies totalling > 512 MB so every step "
                          "reads its weight from HBM (eager launches only)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--stream-calibration", action="store_true",
+                    help="only time plain device copies of 1 GiB (read + write, cycling over three buffer "
+                         "pairs, so no copy finds its data in the Infinity Cache) and exit: the streaming "
+                         "rate this box reaches, the practical ceiling of the HBM-bound kernels")
     ap.add_argument("--no-isolated", action="store_true",
                     help="skip the per-kernel isolated (warm / cold) timing after the timed region "
                          "(profiler runs: every launch then belongs to the timed steps)")
@@ -612,6 +616,28 @@ def main():
         ms = e0.elapsed_time(e1) / 3
         print(json.dumps({"copy_calibration_bytes": n, "copies": 3, "copy_ms": ms,
                           "copy_gbs": 2 * n / (ms * 1e-3) / 1e9}), flush=True)
+        return
+    if args.stream_calibration:
+        n = 1 << 30
+        pairs = [(torch.full((n,), i + 1, dtype=torch.uint8, device=dev),
+                  torch.empty(n, dtype=torch.uint8, device=dev)) for i in range(3)]
+        for i in range(3):
+            pairs[i][1].copy_(pairs[i][0])
+        torch.cuda.synchronize()
+        times = []
+        for r in range(9):
+            src, dst = pairs[r % 3]
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            dst.copy_(src)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        ms = float(np.median(times))
+        print(json.dumps({"stream_calibration": "torch copy of 1 GiB, 3 rotating buffer pairs",
+                          "bytes_moved": 2 * n, "copy_ms_median": ms,
+                          "copy_gbs_median": 2 * n / (ms * 1e-3) / 1e9,
+                          "copy_gbs_best": 2 * n / (min(times) * 1e-3) / 1e9}), flush=True)
         return
     bfp8.library()
 
