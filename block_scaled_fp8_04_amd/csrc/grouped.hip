@@ -144,11 +144,13 @@ __device__ __forceinline__ int grouped_row(int wm, int i) {
     return i < GroupedTile::TM ? GroupedTile::WM * wm + 16 * i : GroupedTile::BM + 16 * wm + 32 * (i - GroupedTile::TM);
 }
 
-// One tile with TX extra sub-tile rows per wave row (TX = 0: up to 256 rows;
-// 1: up to 288; 2: up to 320).  Each variant runs its K loop with no branch
-// inside (a branch would make the compiler wait for the next block's loads
-// before the LDS reads that follow it); rows past the tile's valid rows are
-// multiplied (their inputs read as zeros) but never stored.
+// One tile with TX extra sub-tile rows in this wave's row (wave row 0 takes
+// its first extra row past 256 rows, wave row 1 past 272, the second ones past
+// 288 and 304); the loading waves, in wave row 0, load the A rows of their TX.
+// Each variant runs its K loop with no branch inside (a branch would make the
+// compiler wait for the next block's loads before the LDS reads that follow
+// it); rows past the tile's valid rows are multiplied (their inputs read as
+// zeros) but never stored.
 template <int TX>
 __device__ __forceinline__ void grouped_tile(const uint8_t* __restrict__ a,
                                              const float* __restrict__ as,
@@ -379,10 +381,15 @@ __global__ __launch_bounds__(GroupedTile::THREADS, 1) void gemm_grouped_kernel(
         if (!locate_tile(off, G, total_M, nt, t, at)) break;           // past the last tile
         const uint8_t* bg = b + (int64_t)at.g * N * K;
         const float* bsg = bs + (int64_t)at.g * NB * KB;
+        // extra sub-tile rows this wave row needs (its rows 256 + 16 wm + 32 x hold tile rows);
+        // the loading waves are in wave row 0, which needs at least as many as wave row 1,
+        // so they load every extra row the tile has
         const int64_t rows = at.m_end - at.m0;
-        if (rows <= T::BM)
+        const int wm = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6) / 4);
+        const int tx = (rows > T::BM + 16 * wm ? 1 : 0) + (rows > T::BM + 32 + 16 * wm ? 1 : 0);
+        if (tx == 0)
             grouped_tile<0>(a, as, bg, bsg, c, at.m0, at.m_end, at.n0, N, K, L);
-        else if (rows <= T::BM + 32)
+        else if (tx == 1)
             grouped_tile<1>(a, as, bg, bsg, c, at.m0, at.m_end, at.n0, N, K, L);
         else
             grouped_tile<2>(a, as, bg, bsg, c, at.m0, at.m_end, at.n0, N, K, L);
