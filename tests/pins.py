@@ -657,6 +657,52 @@ def pin_act_quant_pow2_bounds(orc):
     assert np.all(mx <= 448.0) and np.all(mx > 224.0 - 1e-9)
 
 
+def _e4m3_brute(v: Fraction) -> int:
+    """e4m3 magnitude code of the exact value v by search: the nearest of the 127 finite
+    magnitudes, ties to the even code, saturating at 448 (written from the OCP format,
+    independently of the oracle's encoder); the caller adds the sign bit."""
+    mags = []
+    for c in range(127):
+        e, m = c >> 3, c & 7
+        mags.append(Fraction(m, 8) * Fraction(2) ** -6 if e == 0 else (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7))
+    a = abs(v)
+    return min(range(127), key=lambda c: (abs(mags[c] - a), c & 1))
+
+
+def pin_act_quant_pow2_exact_rational(orc):
+    """P3: act_quant with power-of-two scales against exact rational arithmetic: y is the
+    fp32-rounded max(amax, 1e-4f) / 448, the scale the smallest power of two >= y found by
+    stepping exponents, and each code the brute-force nearest e4m3 value of x / scale
+    (exact, a power-of-two division).  Blocks: random, a max of exactly 448 * 2^-5 (y is
+    itself a power of two, so the scale equals y), a block below the floor, a zero block."""
+    rng = np.random.default_rng(1302)
+    x = (rng.standard_normal((3, 256)) * 3).astype(np.float32)
+    x[1, :128] = (rng.standard_normal(128) * 2).astype(np.float32).clip(-13, 13)
+    x[1, 7] = 14.0                                    # 448 * 2^-5
+    x[1, 128:256] = (rng.standard_normal(128) * 1e-6).astype(np.float32)
+    x[2, 128:256] = 0.0
+    xb = torch_bf16(x).reshape(x.shape)
+    q, s = orc.act_quant_pow2(xb)
+    xf = bf16_bits_to_f32(xb)
+    floor32 = Fraction(float(np.float32(1e-4)))
+    for m in range(3):
+        for kb in range(2):
+            blk = [Fraction(float(v)) for v in xf[m, 128 * kb:128 * kb + 128]]
+            amax = max(abs(v) for v in blk)
+            y = Fraction(float(np.float32(float(max(amax, floor32) / 448))))   # one fp32 rounding
+            k = -200
+            while Fraction(2) ** k < y:
+                k += 1
+            scale = Fraction(2) ** k
+            assert Fraction(float(s[m, kb])) == scale, (m, kb, float(s[m, kb]), float(scale))
+            for j, v in enumerate(blk):
+                want = _e4m3_brute(v / scale)
+                if v < 0:
+                    want |= 0x80
+                assert q[m, 128 * kb + j] == want, (m, kb, j)
+    assert float(s[1, 0]) == 2.0 ** -5
+
+
 # ------------------------------------------------------ MoE dispatch / combine pins
 #
 # Source: "Behavior traces - deepseek-ai/DeepSeek-V3" (codevetter), MoE trace
