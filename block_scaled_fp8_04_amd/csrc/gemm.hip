@@ -163,10 +163,12 @@ struct Stages {
 // holds output row m = l & 15 of the sub-tile and the four consecutive columns
 // n = 4 (l >> 4) + 0..3.  Each lane therefore needs one activation scale per
 // sub-tile row block, and the epilogue writes 8 contiguous bytes per sub-tile.
-// kGuard: some rows of this tile lie past m_end.  Each wave then skips the
-// MFMAs and folds of its 16-row sub-tile rows that lie entirely past m_end
-// (a wave-uniform test); full tiles run the unguarded, explicitly scheduled
-// loop.
+// kGuard: some rows of this tile lie past m_end.  Their loads read the last
+// valid row again, so the explicitly scheduled fold loop multiplies every row
+// as in a full tile (finite values, never stored) and only the epilogue tests
+// rows against m_end: a partial tile takes no longer than a full one.  The
+// power-of-two-scale loop skips the MFMAs of each wave's 16-row sub-tile rows
+// that lie entirely past m_end (a wave-uniform test).
 // Where the tile's result goes (the epilogue mode): kEpiBf16 stores bf16 C;
 // kEpiQuant writes act_quant of the bf16-rounded result, e4m3 codes q [M, N]
 // and scales qs [M, N/128]; kEpiSwiglu multiplies a 64-row-interleaved
@@ -536,8 +538,8 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
             wait_vmcnt<0>();
         barrier_lds();
         const bool more = kb + T::NSTAGE - 1 < KE;
-        // (the spread issue lives in the full-tile fold loop; other loops issue here)
-        if ((kGuard || !kSpread || kHwScale) && more) issue(kb + T::NSTAGE - 1, st.p[SF]);
+        // (the spread issue lives in the fold loop; the power-of-two-scale loop issues here)
+        if ((!kSpread || kHwScale) && more) issue(kb + T::NSTAGE - 1, st.p[SF]);
 
         const uint8_t* As = st.p[S];
         const uint8_t* Bs = As + T::A_BYTES;
@@ -582,7 +584,7 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
-        } else if (!kGuard) {
+        } else {
             // The K block as a fixed sequence of small scheduling regions
             // (sched_barrier keeps the compiler from reordering across them):
             // a wave starts multiplying once A row 0 and B fragment 0 are in
@@ -667,36 +669,6 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
                 __builtin_amdgcn_sched_barrier(0);
             }
             sc_last = sc[T::TM - 1];
-        } else {
-            v8i fb[T::TN];
-#pragma unroll
-            for (int j = 0; j < T::TN; ++j) {
-                const uint8_t* q = Bs + (wn0 + 16 * j + lr) * kBlock;
-                fb[j] = frag_from(*(const uint4*)(q + off0), *(const uint4*)(q + off1));
-            }
-            const float sbv = Sb[sb_slot];
-            float sc[T::TM];
-#pragma unroll
-            for (int i = 0; i < T::TM; i += 4) {
-                const v4f s4 = *(const v4f*)(Ss + sread + i);
-                sc[i] = s4[0] * sbv; sc[i + 1] = s4[1] * sbv;
-                sc[i + 2] = s4[2] * sbv; sc[i + 3] = s4[3] * sbv;
-            }
-#pragma unroll
-            for (int i = 0; i < T::TM; ++i) {
-                if (i < tm_valid) {
-                    const uint8_t* r = As + (wm0 + 16 * i + lr) * kBlock;
-                    const v8i fa = frag_from(*(const uint4*)(r + off0), *(const uint4*)(r + off1));
-#pragma unroll
-                    for (int j = 0; j < T::TN; ++j) {
-                        const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            fb[j], fa, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-                        acc[i][j] = p * sc[i] + acc[i][j];
-                    }
-                }
-                // one row at a time: hoisting every row's A reads spills registers
-                __builtin_amdgcn_sched_barrier(0);
-            }
         }
     };
 
@@ -711,8 +683,8 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
         }
     }
 
-    // the last block's last row (the unguarded fold loop carries it into the next block)
-    if constexpr (!kGuard && !kHwScale) {
+    // the last block's last row (the fold loop carries it into the next block)
+    if constexpr (!kHwScale) {
 #pragma unroll
         for (int j = 0; j < T::TN; ++j) acc[T::TM - 1][j] = prev[j] * sc_last + acc[T::TM - 1][j];
     }
@@ -741,7 +713,8 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
     }
     const int cq = 4 * (lane >> 4);
     const bool interior = (m0 + T::BM <= m_end) && (n0 + T::BN <= N);
-    const bool vec = interior && (N % 4 == 0) && (((uintptr_t)c & 7u) == 0);
+    // 8-byte stores wherever the tile's columns are whole; rows tested one by one
+    const bool vec = (n0 + T::BN <= N) && (N % 4 == 0) && (((uintptr_t)c & 7u) == 0);
     // rows per pass of the staged store: 64 where every wave's 8 KB fits one stage, else 32
     constexpr int kRP = T::WAVES * 64 * 128 <= T::STAGE ? 64 : 32;
     constexpr int kSub = kRP / 16;                          // sub-tile rows per pass
@@ -751,7 +724,7 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
         // first stage is free.  Each wave turns kRP of its rows at a time into
         // bf16 rows of 128 bytes there (16-byte chunks XOR-swizzled by row),
         // then stores whole 128-byte row pieces, 16 bytes per lane.
-        if (vec && (N % 8 == 0) && (((uintptr_t)c & 15u) == 0)) {
+        if (interior && vec && (N % 8 == 0) && (((uintptr_t)c & 15u) == 0)) {
             __syncthreads();                      // every wave is past its last LDS read
             uint8_t* buf = st.p[0] + wave * (kRP * 128);
 #pragma unroll
@@ -788,6 +761,7 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
     if (vec) {
 #pragma unroll
         for (int i = 0; i < T::TM; ++i) {
+            if (kGuard && m0 + wm0 + 16 * i + lr >= m_end) continue;
             uint16_t* crow = c + (m0 + wm0 + 16 * i + lr) * N + n0 + wn0 + cq;
 #pragma unroll
             for (int j = 0; j < T::TN; ++j) {
