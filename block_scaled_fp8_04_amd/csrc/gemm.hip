@@ -138,6 +138,10 @@ struct BigTile {
     static constexpr int LOADS_PER_STAGE = A_INSTR + B_INSTR + 2;
 
     static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
+    // Workgroups per CU the kernels are built for: two for four-wave tiles whose stages fit
+    // twice in LDS (registers then capped at 256 per lane), so that one workgroup's waves
+    // keep the SIMDs busy while the other's wait at its barrier; else one.
+    static constexpr int OCC = (WAVES == 4 && 2 * NSTAGE * STAGE <= 160 * 1024) ? 2 : 1;
     static_assert(BM % (8 * LOADERS) == 0 && BN % (8 * LOADERS) == 0,
                   "tile rows must split over the loading waves");
     static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns must share one scale block");
@@ -814,7 +818,7 @@ __device__ __forceinline__ void tile_of(int id, int nwg, int mt, int nt, int& tm
 }
 
 template <class T>
-__global__ __launch_bounds__(T::THREADS, 1) void gemm_big_kernel(const uint8_t* __restrict__ a,
+__global__ __launch_bounds__(T::THREADS, T::OCC) void gemm_big_kernel(const uint8_t* __restrict__ a,
                                                                  const float* __restrict__ as,
                                                                  const uint8_t* __restrict__ b,
                                                                  const float* __restrict__ bs,
@@ -860,7 +864,7 @@ __global__ __launch_bounds__(T::THREADS, 1) void gemm_tail_kernel(
 
 // The GEMM with power-of-two scales applied by the MFMA (kHwScale).
 template <class T>
-__global__ __launch_bounds__(T::THREADS, 1) void gemm_ue8m0_kernel(
+__global__ __launch_bounds__(T::THREADS, T::OCC) void gemm_ue8m0_kernel(
     const uint8_t* __restrict__ a, const float* __restrict__ as, const uint8_t* __restrict__ b,
     const float* __restrict__ bs, uint16_t* __restrict__ c, int64_t M, int64_t N, int64_t K, int mt,
     int nt) {
@@ -878,7 +882,7 @@ __global__ __launch_bounds__(T::THREADS, 1) void gemm_ue8m0_kernel(
 // gated activation of an interleaved [w1; w3] product (kEpiSwiglu), fused
 // into the epilogue.
 template <class T, int kEpi>
-__global__ __launch_bounds__(T::THREADS, 1) void gemm_quant_kernel(
+__global__ __launch_bounds__(T::THREADS, T::OCC) void gemm_quant_kernel(
     const uint8_t* __restrict__ a, const float* __restrict__ as, const uint8_t* __restrict__ b,
     const float* __restrict__ bs, uint8_t* __restrict__ q, float* __restrict__ qs, int64_t M,
     int64_t N, int64_t K, int mt, int nt) {
@@ -1109,7 +1113,7 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 using BigSquare = BigTile<256, 256, 2, 4, 2>;   // 8 waves of 128 x 64, 2 stages
 
 using BigWide = BigTile<256, 128, 4, 2, 3>;     // 8 waves of 64 x 64, 3 stages
-using BigMid = BigTile<128, 128, 2, 2, 3>;      // 4 waves of 64 x 64, 3 stages
+using BigMid = BigTile<128, 128, 2, 2, 2>;      // 4 waves of 64 x 64, 2 stages, 2 per CU
 
 template <class T>
 static void launch_big(const void* a, const float* as, const void* b, const float* bs, void* c,
@@ -1137,9 +1141,11 @@ GemmConfig gemm_config(int64_t M, int64_t N, int64_t /*K*/) {
     const int64_t tiles_wide = ((M + 255) / 256) * ((N + 127) / 128);
     // 256 x 256 from 5/8 of a tile per CU up: at 160-288 tiles it beat 256 x 128 by 6-30%
     // (one round of the more efficient tile against several of the smaller one); at 128
-    // tiles, half the CUs idle and 256 x 128 is 25% faster
+    // tiles, half the CUs idle and 256 x 128 is 25% faster.  256 x 128 from one full round
+    // of its tiles up; below that, 128 x 128 tiles two per CU were 5-25% faster (2048 x
+    // 2048 x 7168: 45.6 against 53.4 us) and even with it at 4096 x 2048 x 7168.
     if (M > 128 && tiles_sq >= cus * 5 / 8) return GemmConfig::kBig256x256;
-    if (M > 128 && tiles_wide >= cus / 2) return GemmConfig::kBig256x128;
+    if (M > 128 && tiles_wide >= cus) return GemmConfig::kBig256x128;
     return GemmConfig::kBig128x128;
 }
 
@@ -1147,7 +1153,7 @@ const char* gemm_config_name(GemmConfig cfg) {
     switch (cfg) {
         case GemmConfig::kBig256x256: return "lds-direct 256x256, 8 waves of 128x64";
         case GemmConfig::kBig256x128: return "lds-direct 256x128, 8 waves of 64x64";
-        case GemmConfig::kBig128x128: return "lds-direct 128x128, 4 waves of 64x64";
+        case GemmConfig::kBig128x128: return "lds-direct 128x128, 4 waves of 64x64, 2 per CU";
     }
     return "unknown";
 }
@@ -1241,7 +1247,9 @@ hipError_t launch_gemm_ue8m0(const void* a, const float* as, const void* b, cons
                              void* c, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
     switch (gemm_config(M, N, K)) {
         case GemmConfig::kBig256x256: return launch_ue8m0<BigSquare>(a, as, b, bs, c, M, N, K, stream);
-        case GemmConfig::kBig256x128: return launch_ue8m0<BigWide>(a, as, b, bs, c, M, N, K, stream);
+        // the e8m0 loop has no fold: 128 x 128 tiles two per CU measured 6% faster than
+        // 256 x 128 here too (4096 x 2048 x 7168)
+        case GemmConfig::kBig256x128: return launch_ue8m0<BigMid>(a, as, b, bs, c, M, N, K, stream);
         case GemmConfig::kBig128x128: return launch_ue8m0<BigMid>(a, as, b, bs, c, M, N, K, stream);
     }
     return hipErrorInvalidValue;
