@@ -1,4 +1,4 @@
-// gemm.hip - block-scaled fp8 GEMM (plain and grouped) on gfx950.
+// gemm.hip - block-scaled fp8 GEMM on gfx950 (the grouped GEMM is in grouped.hip).
 //
 // c[m, n] = bf16( sum_kb P_kb[m, n] * a_s[m, kb] * b_s[n/128, kb] ),
 // P_kb[m, n] = sum_{k in block kb} a[m, k] * b[n, k]
@@ -16,12 +16,12 @@
 //    same for all of a wave's columns (a wave's N range lies inside one
 //    128-column block), so the fold needs one scale per row.
 //  * Large tiles (BigTile): 256x256 (8 waves of 128x64, 2 LDS stages),
-//    256x128 (8 waves of 64x64, 3 stages), 128x128 (4 waves of 64x64,
-//    3 stages) and, for the grouped GEMM's remainder rows, 64x128 (4 waves of
-//    64x32, 4 stages).  A and B rows of one K block go straight from global memory
-//    into LDS with buffer loads; the stages are distinct LDS arrays and the K
-//    loop is unrolled by the stage count, so every stage is named at compile
-//    time.  A vmcnt-counted wait and one barrier open each K block.
+//    256x128 (8 waves of 64x64, 3 stages) and 128x128 (4 waves of 64x64,
+//    2 stages, built for two workgroups per CU).  A and B rows of one K block
+//    go straight from global memory into LDS with buffer loads; the stages are
+//    distinct LDS arrays and the K loop is unrolled by the stage count, so
+//    every stage is named at compile time.  A vmcnt-counted wait and one
+//    barrier open each K block.
 //  * Wave roles in the eight-wave tiles: waves w and w + 4 share a SIMD, and
 //    waves 4..7 run one priority level up.  In the two-stage 256x256 tile
 //    waves 0..3 also issue all of the tile's A and B loads, so waves 4..7
@@ -39,8 +39,8 @@
 //    consecutive columns 4 (l >> 4) + 0..3.
 //  * Skinny problems (M <= 64) with a workspace use split-K (gemm_skinny_kernel
 //    and a fixed-order reduction).
-//  * Rows past M (or past a group's end) and columns past N read a clamped,
-//    valid row and are never stored.
+//  * Rows past M and columns past N read a clamped, valid row; partial tiles
+//    run the same K loop as full ones and only their stores are guarded.
 #include <mutex>
 
 #include "device_codec.hpp"
