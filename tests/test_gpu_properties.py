@@ -14,8 +14,11 @@ workspace plan splits K).  Hence, bit for bit:
 * tile-configuration independence: the first rows of a GEMM equal the GEMM of those rows
   alone, which runs on other tiles (256 x 256, 256 x 128, or 128 x 128 two per CU, with
   partial tiles);
-* the fused act_quant epilogue is row-equivariant too (quantization is row-local).
+* the fused act_quant epilogue is row-equivariant too (quantization is row-local);
+* the grouped GEMM's rows equal the plain GEMM of each group's rows with its expert's
+  weight, and reversing the group order reverses its output's row blocks.
 """
+import numpy as np
 import pytest
 import torch
 
@@ -90,3 +93,48 @@ def test_fused_quant_row_permutation(dense):
     q2, s2 = bfp8.gemm_act_quant(q[:M][perm].contiguous(), s[:M][perm].contiguous(), w, ws)
     torch.cuda.synchronize()
     assert torch.equal(q2, q1[perm]) and torch.equal(s2, s1[perm])
+
+
+# ------------------------------------------------------------------ grouped GEMM
+
+@pytest.fixture(scope="module")
+def routed():
+    wl = workload(4)
+    ids, off = wl.tensors["token_ids"], wl.tensors["offsets"]
+    xg = wl.tensors["x"][ids].contiguous().to(dev())
+    q, s = bfp8.act_quant(xg)
+    b, bs = wl.tensors["w1"].to(dev()), wl.tensors["s1"].to(dev())
+    c = bfp8.gemm_grouped(q, s, b, bs, off.to(dev()))
+    torch.cuda.synchronize()
+    return q, s, b, bs, off, c
+
+
+def test_grouped_equals_per_group_gemm_full_size(routed):
+    """Every row of the grouped GEMM (32 experts, 8195 routed rows, each group's remainder
+    rows riding in its last tile) equals the plain GEMM of that group's rows with its
+    expert's weight, bit for bit."""
+    q, s, b, bs, off, c = routed
+    announce(f"grouped vs per-group GEMM: {len(off) - 1} groups, {int(off[-1])} rows")
+    for g in range(len(off) - 1):
+        lo, hi = int(off[g]), int(off[g + 1])
+        if hi == lo:
+            continue
+        cg = bfp8.gemm(q[lo:hi].contiguous(), s[lo:hi].contiguous(), b[g], bs[g])
+        torch.cuda.synchronize()
+        assert torch.equal(cg, c[lo:hi]), f"group {g} ({hi - lo} rows) differs"
+
+
+def test_grouped_group_permutation_full_size(routed):
+    """Reversing the order of the groups (their rows and their weights) reverses the
+    output's row blocks, bit for bit."""
+    q, s, b, bs, off, c = routed
+    G = len(off) - 1
+    counts = (off[1:] - off[:-1]).tolist()
+    order = list(range(G))[::-1]
+    rows = torch.cat([torch.arange(int(off[g]), int(off[g + 1])) for g in order]).to(dev())
+    off2 = torch.tensor([0] + list(np.cumsum([counts[g] for g in order])), dtype=torch.int32)
+    announce(f"grouped GEMM with the {G} groups in reverse order")
+    c2 = bfp8.gemm_grouped(q[rows].contiguous(), s[rows].contiguous(), b.flip(0).contiguous(),
+                           bs.flip(0).contiguous(), off2.to(dev()))
+    torch.cuda.synchronize()
+    assert torch.equal(c2, c[rows])
