@@ -16,7 +16,9 @@ workspace plan splits K).  Hence, bit for bit:
   partial tiles);
 * the fused act_quant epilogue is row-equivariant too (quantization is row-local);
 * the grouped GEMM's rows equal the plain GEMM of each group's rows with its expert's
-  weight, and reversing the group order reverses its output's row blocks.
+  weight, and reversing the group order reverses its output's row blocks;
+* the BF16 branch's GEMM and the power-of-two-scale GEMM are row-equivariant and give the
+  same bits for leading rows run alone.
 """
 import numpy as np
 import pytest
@@ -138,3 +140,47 @@ def test_grouped_group_permutation_full_size(routed):
                            bs.flip(0).contiguous(), off2.to(dev()))
     torch.cuda.synchronize()
     assert torch.equal(c2, c[rows])
+
+
+# ------------------------------------------------------------- BF16 branch and e8m0
+
+def test_bf16_gemm_row_permutation_and_leading_rows():
+    """The BF16 branch's GEMM (dense MLP up projection on the dequantized weight): permuting
+    the rows of x permutes the rows of the output, and leading rows alone (other tiles)
+    give the same bits."""
+    wl = workload(3)
+    x = wl.tensors["x"].to(dev())
+    wd = bfp8.weight_dequant(wl.tensors["w1"].to(dev()), wl.tensors["s1"].to(dev()))
+    c = bfp8.gemm_bf16(x, wd)
+    g = torch.Generator(device=dev()).manual_seed(44)
+    perm = torch.randperm(x.shape[0], generator=g, device=dev())
+    announce("bf16 GEMM row permutation")
+    cp = bfp8.gemm_bf16(x[perm].contiguous(), wd)
+    torch.cuda.synchronize()
+    assert torch.equal(cp, c[perm])
+    for rows in (3000, 200):
+        cr = bfp8.gemm_bf16(x[:rows].contiguous(), wd)
+        torch.cuda.synchronize()
+        assert torch.equal(cr, c[:rows]), f"bf16 GEMM: the first {rows} rows differ when run alone"
+
+
+def test_ue8m0_gemm_row_permutation_and_leading_rows():
+    """The power-of-two-scale GEMM at the dense MLP up shape: row equivariance and leading
+    rows alone (256 x 256 tiles, then 128 x 128 tiles two per CU)."""
+    wl = workload(3)
+    x = wl.tensors["x"].to(dev())
+    q, s = bfp8.act_quant_ue8m0(x)
+    from block_scaled_fp8_04_amd import synth
+    w, ws = synth.weight(18432, 7168, 4401, 4402, pow2=True)
+    w, ws = w.to(dev()), ws.to(dev())
+    c = bfp8.gemm_ue8m0(q, s, w, ws)
+    g = torch.Generator(device=dev()).manual_seed(45)
+    perm = torch.randperm(q.shape[0], generator=g, device=dev())
+    announce("e8m0 GEMM row permutation")
+    cp = bfp8.gemm_ue8m0(q[perm].contiguous(), s[perm].contiguous(), w, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(cp, c[perm])
+    for rows in (3000, 300):
+        cr = bfp8.gemm_ue8m0(q[:rows].contiguous(), s[:rows].contiguous(), w, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(cr, c[:rows]), f"e8m0 GEMM: the first {rows} rows differ when run alone"
