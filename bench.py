@@ -26,7 +26,8 @@ from sysfs during the timed region (and the board power cap); `cpu_baseline`
 times the CPU oracle on a bounded, proportional sample of the same step.
 
 Other workloads (parity-test shapes, measured on demand): --workload tiny |
-decode | moe-pair | dense-mlp-unfused | grouped | moe-layer | bf16-branch |
+decode | moe-pair (the expert pair, act_quant of H fused into the first GEMM as in the
+dense step) | moe-pair-unfused | dense-mlp-unfused | grouped | moe-layer | bf16-branch |
 expert-ffn (one expert's gated FFN with the SiLU gate and act_quant fused into the
 [w1; w3] GEMM's epilogue) | dense-mlp-ue8m0 (power-of-two scales applied by the MFMA).  moe-layer is the routed
 experts of one GPU end to end on the device: moe_dispatch(topk) ->
@@ -55,8 +56,9 @@ PEAK_FP8_TFLOPS = 5000.0          # MI355X dense fp8 MFMA (no sparsity)
 PEAK_HBM_GBS = 8000.0             # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0         # MI355X dense bf16 MFMA (no sparsity)
 
-WORKLOADS = {"tiny": 0, "decode": 1, "moe-pair": 2, "dense-mlp": 3, "grouped": 4, "moe-layer": 4,
-             "bf16-branch": 3, "dense-mlp-unfused": 3, "expert-ffn": 2, "dense-mlp-ue8m0": 3}
+WORKLOADS = {"tiny": 0, "decode": 1, "moe-pair": 2, "moe-pair-unfused": 2, "dense-mlp": 3,
+             "grouped": 4, "moe-layer": 4, "bf16-branch": 3, "dense-mlp-unfused": 3, "expert-ffn": 2,
+             "dense-mlp-ue8m0": 3}
 
 
 # ------------------------------------------------------------------ accounting
@@ -124,7 +126,8 @@ class Step:
         self.dev = dev
         t = wl.tensors
         c = wl.config
-        if kind in ("moe-layer", "bf16-branch", "dense-mlp", "expert-ffn", "dense-mlp-ue8m0"):
+        if kind in ("moe-layer", "bf16-branch", "dense-mlp", "expert-ffn", "dense-mlp-ue8m0",
+                    "moe-pair"):
             c = kind
         self.launches = []            # (name, callable, flops, bytes, bound)
         self.hashes = {}
@@ -210,9 +213,10 @@ class Step:
             self.shape = dict(T=T, G=G, N=N, K=K, tokens_per_expert_min=min(counts),
                               tokens_per_expert_max=max(counts))
             self.dominant, self.dominant_kernel = ["fp8_gemm_grouped"], "gemm_grouped"
-        elif c == "dense-mlp":
-            # the dense chain with act_quant of H fused into the up projection's epilogue
-            # (bit-identical codes and scales to act_quant of the stored bf16 H)
+        elif c in ("dense-mlp", "moe-pair"):
+            # the chain with act_quant of H fused into the first GEMM's epilogue (bit-identical
+            # codes and scales to act_quant of the stored bf16 H); the dense MLP step also
+            # dequantizes its up-projection weight
             M, N1, K1, N2, K2 = (wl.meta[k] for k in ("M", "N1", "K1", "N2", "K2"))
             x = t["x"].to(dev)
             w1, s1 = t["w1"].to(dev), t["s1"].to(dev)
@@ -222,7 +226,6 @@ class Step:
             qh = torch.empty(M, K2, dtype=torch.uint8, device=dev)
             qhs = torch.empty(M, K2 // BLOCK, dtype=torch.float32, device=dev)
             y = torch.empty(M, N2, dtype=torch.bfloat16, device=dev)
-            wd = torch.empty(N1, K1, dtype=torch.bfloat16, device=dev)
             work2 = gemm_workspace(M, N2, K2, dev)
             self.launches += [
                 Launch("act_quant_x", bfp8.bfp8_act_quant, (x, q, qs), 0, act_quant_bytes(M, K1), "hbm"),
@@ -230,9 +233,11 @@ class Step:
                        2 * M * N1 * K1, M * K1 + N1 * K1 + M * N1 + 4 * M * (N1 // BLOCK), "mfma"),
                 Launch("fp8_gemm_2", bfp8.bfp8_gemm, (qh, qhs, w2, s2, y, work2), 2 * M * N2 * K2,
                        gemm_bytes(M, N2, K2), "mfma"),
-                Launch("weight_dequant", bfp8.bfp8_weight_dequant, (w1, s1, wd), 0,
-                       dequant_bytes(N1, K1), "hbm"),
             ]
+            if c == "dense-mlp":
+                wd = torch.empty(N1, K1, dtype=torch.bfloat16, device=dev)
+                self.launches.append(Launch("weight_dequant", bfp8.bfp8_weight_dequant, (w1, s1, wd), 0,
+                                            dequant_bytes(N1, K1), "hbm"))
             self.shape = dict(M=M, N1=N1, K1=K1, N2=N2, K2=K2)
             self.dominant, self.dominant_kernel = ["fp8_gemm_1_quant", "fp8_gemm_2"], "gemm"
         elif c == "expert-ffn":
@@ -739,7 +744,7 @@ def main():
 
     wl_name = (f"{args.workload}-{wl.name}"
                if args.workload in ("moe-layer", "bf16-branch", "dense-mlp-unfused", "expert-ffn",
-                                    "dense-mlp-ue8m0") else wl.name)
+                                    "dense-mlp-ue8m0", "moe-pair-unfused") else wl.name)
     config = {"workload": wl_name, "shape": step.shape,
               "step": " -> ".join(l.name for l in step.launches),
               "value_definition": "GEMM FLOP per step / wall time per step",

@@ -120,6 +120,16 @@ def test_fused_quant_dense_chain_full_size():
     announce(f"dense-mlp down 8192x7168x18432 on the fused codes: worst err/bound {worst:.3f}")
 
 
+def test_fused_quant_expert_pair_full_size():
+    """The expert pair's first GEMM, 4096 x 2048 x 7168 (256 x 128 tiles), with H quantized in
+    its epilogue, on the first and last row of every 128-row block plus seeded rows."""
+    wl = workload(2)
+    x = wl.tensors["x"].to(dev())
+    w1, s1 = wl.tensors["w1"].to(dev()), wl.tensors["s1"].to(dev())
+    q_a, s_a = bfp8.act_quant(x)
+    _case(q_a, s_a, w1, s1, "expert pair up 4096x2048x7168", sample_rows(4096, 16, 690))
+
+
 # ------------------------------------------------------------------- gated FFN
 
 def _swiglu_case(M, N, K, seed, what, rows=None):
