@@ -37,8 +37,9 @@
 //    pairs the same position of A and B.  Operands go weight-first, so the
 //    16x16 result is C^T: lane l holds output row (l & 15) and the four
 //    consecutive columns 4 (l >> 4) + 0..3.
-//  * Skinny problems (M <= 64) with a workspace use split-K (gemm_skinny_kernel
-//    and a fixed-order reduction).
+//  * Skinny problems (M <= 64, or M <= 256 with at most 32 tiles of 128 x 128)
+//    with a workspace use split-K (gemm_skinny_kernel and a fixed-order
+//    reduction).
 //  * Rows past M and columns past N read a clamped, valid row; partial tiles
 //    run the same K loop as full ones and only their stores are guarded.
 #include <mutex>
@@ -897,7 +898,7 @@ __global__ __launch_bounds__(T::THREADS, T::OCC) void gemm_quant_kernel(
         gemm_tile_big<T, true, kEpi>(a, as, b, bs, nullptr, m0, M, (int64_t)tn * T::BN, N, K, lds, qo);
 }
 
-// Split-K kernel for skinny problems (M <= 64).  A workgroup owns a 64 x 64
+// Split-K kernel for skinny problems (those split_plan splits).  A workgroup owns a 64 x 64
 // output tile and a run of at most SK_DEEP_KB K blocks; it issues every
 // direct-to-LDS load of that run at once (one memory latency per workgroup
 // instead of one per K block), waits once, then multiplies.  Four waves of
@@ -1014,21 +1015,25 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint8_t* __restr
 }
 
 
-// Split-K plan for skinny problems (M <= 64).  Deep splits of up to 8 K
-// blocks when that makes at most 512 workgroups (the decode-sized shapes:
-// fewer partial sums to write and add, measured 10-16% faster on
-// 64 x 1536 x 7168, 64 x 7168 x 2048 and 32 x 2048 x 7168); otherwise enough
-// (tile, split) pairs for about 384 workgroups, at most 4 and at least 2 K
-// blocks per split (wide or long-K shapes, e.g. 64 x 18432 x 7168 and
-// 16 x 7168 x 18432, were faster that way).  Host-only arithmetic, so
-// bfp8_gemm_workspace_size needs no device.
+// Split-K plan for skinny problems: M <= 64, or M <= 256 when the problem
+// makes at most 32 tiles of 128 x 128 (an eighth of the chip's CUs; those
+// ran one round of mostly idle CUs: 128 x 2048 x 7168 took 16.5 us split
+// against 33.4 us whole, 256 x 1536 x 7168 24.1 against 33.6, 100 x 4096 x
+// 7168 26.7 against 38.7, while 256 x 4096 x 7168 was slower split).  Deep
+// splits of up to 8 K blocks when that makes at most 512 workgroups (the
+// decode-sized shapes: fewer partial sums to write and add, measured 10-16%
+// faster on 64 x 1536 x 7168, 64 x 7168 x 2048 and 32 x 2048 x 7168);
+// otherwise enough (tile, split) pairs for about 384 workgroups, at most 4
+// and at least 2 K blocks per split (wide or long-K shapes, e.g.
+// 64 x 18432 x 7168 and 16 x 7168 x 18432, were faster that way).
+// Host-only arithmetic, so bfp8_gemm_workspace_size needs no device.
 struct SplitPlan {
     int splits, kb_per;
 };
 
 static SplitPlan split_plan(int64_t M, int64_t N, int64_t K) {
     SplitPlan p{1, (int)(K / kBlock)};
-    if (M > 64) return p;
+    if (M > 256 || (M > 64 && ((M + 127) / 128) * ((N + 127) / 128) > 32)) return p;
     const int64_t tiles = ((M + 63) / 64) * ((N + 63) / 64);
     const int64_t KB = K / kBlock;
     if (KB > SK_DEEP_KB) {
@@ -1054,8 +1059,12 @@ static SplitPlan split_plan(int64_t M, int64_t N, int64_t K) {
 // that last round is whole columns of tiles (rem = mt * nt_tail), the tail
 // columns run as two K halves (twice the workgroups) into an fp32 workspace,
 // then one reduction.  Measured on 8192 x 7168 x 18432 (3.5 rounds): the half
-// round cost 0.79 of a full round before.  Host-only arithmetic, planned for
-// 256 CUs, so bfp8_gemm_workspace_size needs no device.
+// round cost 0.79 of a full round before.  Only for K of 80 blocks and more:
+// on 8192 x 7168 x K the split tail won at K = 12288 and 18432 (915.9 against
+// 931.8 us at 18432) and lost from K = 7168 down (134 against 115 us at
+// 2048), where the partial sums' write and reduction outweigh the half round.
+// Host-only arithmetic, planned for 256 CUs, so bfp8_gemm_workspace_size
+// needs no device.
 struct TailPlan {
     int nt_main = 0, nt_tail = 0, splits = 0;
     int64_t kb_per = 0;
@@ -1067,7 +1076,7 @@ static TailPlan tail_plan(int64_t M, int64_t N, int64_t K) {
     if (M <= 128 || M % 256 != 0 || N % 256 != 0) return p;
     const int64_t mt = M / 256, nt = N / 256, tiles = mt * nt, KB = K / kBlock;
     const int64_t rem = tiles % kCUs;
-    if (tiles < kCUs || rem == 0 || rem % mt != 0 || 2 * rem > kCUs || KB < 8) return p;
+    if (tiles < kCUs || rem == 0 || rem % mt != 0 || 2 * rem > kCUs || KB < 80) return p;
     p.nt_tail = (int)(rem / mt);
     p.nt_main = (int)(nt - p.nt_tail);
     p.splits = 2;

@@ -107,8 +107,9 @@ int bfp8_weight_dequant(const void* w_e4m3, const float* s, void* out_bf16,
  *   b   : e4m3 [N, K], 16-byte aligned         b_s : fp32 [ceil(N/128), K/128]
  *   c_bf16 : bf16 [M, N] output, 4-byte aligned (N odd: 2-byte)
  *   workspace : optional fp32 scratch: split-K partial sums on skinny problems
- *     (M <= 64), and on large problems whose last round of 256 x 256 tiles is
- *     at most half full, the partial sums of those tiles' two K halves.  NULL
+ *     (M <= 64, or M <= 256 with at most 32 output tiles of 128 x 128), and on
+ *     large problems (K >= 80 * 128) whose last round of 256 x 256 tiles is at
+ *     most half full, the partial sums of those tiles' two K halves.  NULL
  *     disables both (one pass over K per tile).  If non-NULL it must hold at
  *     least bfp8_gemm_workspace_size(M, N, K) bytes and be 16-byte aligned;
  *     its contents on entry do not matter.

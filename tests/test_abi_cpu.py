@@ -114,21 +114,39 @@ def test_gemm_workspace_contract(lib):
 
 def test_gemm_tail_split_plan():
     """The workspace a large GEMM asks for: only when its 256 x 256 tiles leave a last round
-    (of 256 CUs) at most half full that is whole tile columns, and K has at least 8 blocks;
+    (of 256 CUs) at most half full that is whole tile columns, and K has at least 80 blocks;
     then 2 halves x M x (tail columns) fp32 partial sums."""
     ws = bfp8.bfp8_gemm_workspace_size
     # dense down projection: 32 x 28 tiles = 3.5 rounds, tail = 4 tile columns
     assert ws(8192, 7168, 18432) == 2 * 8192 * 4 * 256 * 4
     assert ws(8192, 5120, 18432) == 2 * 8192 * 4 * 256 * 4       # 2.5 rounds
+    assert ws(8192, 7168, 10240) == 2 * 8192 * 4 * 256 * 4       # exactly 80 K blocks
+    assert ws(8192, 7168, 10112) == 0                               # 79 K blocks
+    assert ws(8192, 7168, 7168) == 0
     assert ws(8192, 18432, 7168) == 0                               # 9 whole rounds
     assert ws(8192, 6144, 18432) == 0                               # 3 whole rounds
-    assert ws(4096, 7168, 2048) == 0                                # 1.75 rounds: tail too full
-    assert ws(512, 33024, 1024) == 2 * 512 * 1 * 256 * 4            # 2 x 129 tiles
-    assert ws(2048, 8448, 1152) == 2 * 2048 * 1 * 256 * 4           # 8 x 33 tiles, 9 K blocks
+    assert ws(4096, 7168, 18432) == 0                               # 1.75 rounds: tail too full
+    assert ws(512, 33024, 10240) == 2 * 512 * 1 * 256 * 4           # 2 x 129 tiles
+    assert ws(2048, 8448, 10368) == 2 * 2048 * 1 * 256 * 4          # 8 x 33 tiles, 81 K blocks
     assert ws(8192 + 128, 7168, 18432) == 0                         # M not a multiple of 256
     assert ws(8192, 7168 + 128, 18432) == 0                         # N not a multiple of 256
-    assert ws(8192, 7168, 896) == 0                                 # fewer than 8 K blocks
-    assert ws(256, 256, 256) == 0                                   # less than one round
+    assert ws(512, 512, 18432) == 0                                 # less than one round
+
+
+def test_gemm_skinny_split_plan():
+    """Split-K (splits x M x N fp32 partial sums) for M <= 64, and for M <= 256 only when the
+    problem makes at most 32 output tiles of 128 x 128."""
+    ws = bfp8.bfp8_gemm_workspace_size
+    assert ws(64, 18432, 7168) > 0
+    assert ws(128, 2048, 7168) > 0                                  # 1 x 16 tiles
+    assert ws(128, 4096, 7168) > 0                                  # 1 x 32 tiles
+    assert ws(128, 4224, 7168) == 0                                 # 1 x 33 tiles
+    assert ws(256, 2048, 7168) > 0                                  # 2 x 16 tiles
+    assert ws(256, 4096, 7168) == 0                                 # 2 x 32 tiles
+    assert ws(257, 128, 7168) == 0                                  # M > 256
+    for (M, N, K) in ((128, 2048, 7168), (256, 1536, 7168), (37, 300, 1152)):
+        need = ws(M, N, K)
+        assert need % (M * N * 4) == 0 and need // (M * N * 4) >= 2
 
 
 def test_gemm_grouped_validation(lib):

@@ -86,20 +86,24 @@ def test_linear_decode_config():
     (64, 7168, 2048),     # the decode down-projection shape of an expert
     (50, 129, 640),       # a ragged column tail in a one-tile-wide problem
     (8, 4096, 7168),
+    (65, 300, 1152),      # M > 64, 3 tiles of 128 x 128
+    (200, 2048, 7168),    # 2 x 16 tiles
 ])
 def test_linear_split_k_shapes(shape):
     M, N, K = shape
+    assert bfp8.bfp8_gemm_workspace_size(M, N, K) > 0
     _case(M, N, K, seed=M + N)
 
 
 @pytest.mark.parametrize("shape", [
     (16, 128, 256),       # two K blocks: no split
-    (65, 300, 1152),      # M > 64
     (8, 24576, 1024),     # 384 tiles: no split
-    (200, 2048, 7168),
+    (200, 4608, 7168),    # 2 x 36 tiles of 128 x 128: no split
+    (257, 1024, 2048),    # M > 256
 ])
 def test_linear_unsplit_shapes(shape):
     M, N, K = shape
+    assert bfp8.bfp8_gemm_workspace_size(M, N, K) == 0
     rows = None if M <= 64 else np.array([0, 1, M // 2, M - 2, M - 1])
     _case(M, N, K, seed=3 * M + N, oracle_rows=rows)
 

@@ -273,7 +273,8 @@ def test_gemm_split_k_workspace():
     from block_scaled_fp8_04_amd import synth
     g = torch.Generator().manual_seed(6)
     for (M, N, K) in ((64, 1536, 7168), (37, 300, 1152), (1, 3000, 1024), (64, 7168, 2048),
-                      (50, 129, 640)):
+                      (50, 129, 640), (128, 2048, 7168), (256, 1536, 7168), (193, 1000, 2304),
+                      (100, 4096, 1152)):
         need = bfp8.bfp8_gemm_workspace_size(M, N, K)
         assert need > 0, (M, N, K)
         x = torch.randn(M, K, generator=g).to(torch.bfloat16).to(dev())
@@ -296,8 +297,9 @@ def test_gemm_tail_split_workspace():
     canaries intact, independent of what the workspace held, too small a workspace refused."""
     from block_scaled_fp8_04_amd import synth
     g = torch.Generator().manual_seed(8)
-    # (M, N, K): 2 x 129 tiles (2 in the tail), 4 x 65 tiles (4), 8 x 33 tiles (8, odd K blocks)
-    for (M, N, K) in ((512, 33024, 1024), (1024, 16640, 2048), (2048, 8448, 1152)):
+    # (M, N, K): 4 x 65 tiles (4 in the tail), 8 x 33 tiles (8, odd K blocks), 16 x 18 tiles
+    # (32 in two tail columns), all with the at least 80 K blocks the split tail needs
+    for (M, N, K) in ((1024, 16640, 10240), (2048, 8448, 10368), (4096, 4608, 10240)):
         need = bfp8.bfp8_gemm_workspace_size(M, N, K)
         assert need > 0, (M, N, K)
         x = torch.randn(M, K, generator=g).to(torch.bfloat16).to(dev())
@@ -316,8 +318,9 @@ def test_gemm_tail_split_workspace():
 
 
 def test_gemm_workspace_paths_random_shapes():
-    """Seeded random shapes through both workspace paths: skinny problems (deep or shallow
-    split-K, whichever the plan picks) and large ones whose last round of tiles is split over
+    """Seeded random shapes through both workspace paths: skinny problems (M <= 64, and
+    64 < M <= 256 with at most 32 tiles of 128 x 128; deep or shallow split-K, whichever the
+    plan picks) and large ones whose last round of tiles is split over
     K.  Each runs with and without the workspace; both within tolerance of the oracle on
     sampled rows, canaries intact."""
     from block_scaled_fp8_04_amd import synth
@@ -329,23 +332,31 @@ def test_gemm_workspace_paths_random_shapes():
         N = int(rng.integers(1, 40)) * 64 + int(rng.integers(0, 64))
         K = int(rng.integers(9, 40)) * 128
         shapes.append((M, N, K))
-    for mt, rem_cols in ((2, 1), (4, 2), (8, 1)):        # large: whole rounds + a short tail
+    for mt, rem_cols in ((8, 1), (16, 2), (32, 1)):      # large: whole rounds + a short tail
         nt = 256 // mt + rem_cols
-        K = int(rng.integers(8, 24)) * 128
+        K = int(rng.integers(80, 96)) * 128
         shapes.append((mt * 256, nt * 256, K))
+    for _ in range(4):                                   # skinny: 64 < M <= 256, <= 32 tiles
+        M = int(rng.integers(65, 257))
+        mt = (M + 127) // 128
+        N = int(rng.integers(1, 32 // mt)) * 128 + int(rng.integers(0, 128))
+        K = int(rng.integers(9, 60)) * 128
+        shapes.append((M, N, K))
     for (M, N, K) in shapes:
         need = bfp8.bfp8_gemm_workspace_size(M, N, K)
         x = torch.randn(M, K, generator=g).to(torch.bfloat16).to(dev())
         q, s = bfp8.act_quant(x)
         w, ws = synth.weight(N, K, 1300 + M, 1400 + N)
         w, ws = w.to(dev()), ws.to(dev())
-        rows = None if M <= 64 else sample_rows(M, extra=8, seed=M)
+        rows = None if M <= 256 else sample_rows(M, extra=8, seed=M)
         _gemm_case(q, s, w, ws, f"random[{M},{N},{K}] no workspace", rows=rows)
         if need:
             work = torch.full((need // 4,), float("nan"), dtype=torch.float32, device=dev())
             _gemm_case(q, s, w, ws, f"random[{M},{N},{K}] workspace {need} B", rows=rows,
                        workspace=work)
-    assert sum(1 for (M, N, K) in shapes if M > 64 and bfp8.bfp8_gemm_workspace_size(M, N, K)) == 3
+    ws_size = bfp8.bfp8_gemm_workspace_size
+    assert sum(1 for (M, N, K) in shapes if M > 256 and ws_size(M, N, K)) == 3
+    assert sum(1 for (M, N, K) in shapes if 64 < M <= 256 and ws_size(M, N, K)) == 4
 
 
 def test_gemm_identity_bit_exact():

@@ -51,8 +51,8 @@ def _compare(M, N, K, seed, oracle_rows=None):
 
 
 def test_noalloc_two_calls_larger_then_smaller():
-    # 2048 x 10240 x 1024: 320 tiles of 256 x 256, the last 64 split over K (32 MiB of partials)
-    big = _compare(2048, 10240, 1024, seed=1, oracle_rows=np.array([0, 127, 1000, 2047], np.int64))
+    # 2048 x 10240 x 10240: 320 tiles of 256 x 256, the last 64 split over K (32 MiB of partials)
+    big = _compare(2048, 10240, 10240, seed=1, oracle_rows=np.array([0, 127, 1000, 2047], np.int64))
     assert big == 32 << 20
     # then the decode-shaped projection 64 x 1536 x 7168 (split-K, 2.75 MiB of partials)
     small = _compare(64, 1536, 7168, seed=2, oracle_rows=np.arange(64, dtype=np.int64))
