@@ -486,6 +486,27 @@ def test_grouped_small_cases():
         _grouped_case(q, s, b, b_s, off, f"counts={counts.tolist()}")
 
 
+def test_grouped_random_offsets():
+    """Seeded random group sizes, including runs of empty groups, more than 64 groups (the
+    tile lookup scans the offsets 64 groups at a time) and groups past 320 rows (several
+    tiles, the last one partial or tall), against the oracle on every row."""
+    from block_scaled_fp8_04_amd import synth
+    rng = np.random.default_rng(71)
+    g = torch.Generator().manual_seed(72)
+    for G, hi, K, N in ((130, 70, 256, 320), (70, 600, 384, 256), (65, 2, 128, 130)):
+        counts = rng.integers(0, hi + 1, size=G)
+        counts[rng.random(G) < 0.25] = 0
+        off = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32))
+        T = int(off[-1])
+        assert T > 0
+        x = torch.randn(T, K, generator=g).to(torch.bfloat16).to(dev())
+        q, s = bfp8.act_quant(x)
+        ws = [synth.weight(N, K, 1500 + i, 1600 + i) for i in range(G)]
+        b = torch.stack([w for w, _ in ws]).to(dev())
+        b_s = torch.stack([sc for _, sc in ws]).to(dev())
+        _grouped_case(q, s, b, b_s, off, f"random G={G} T={T} K={K} N={N}")
+
+
 def test_grouped_single_group_equals_gemm():
     wl = workload(0)
     q, s = _quantized_x(wl)
