@@ -11,8 +11,12 @@
 // so a wave64 reads 2 KB of contiguous memory per step, and the block max is
 // an xor butterfly over the 8 lanes.  Each lane writes its 16 codes as one
 // 16-byte store; the group's first lane writes the scale.  The kernel is HBM
-// bound (3.03 bytes per element); two independent blocks per lane are in
-// flight per iteration to keep enough loads outstanding.
+// bound (3.03 bytes per element).  The grid covers every block at once (one
+// block per eight lanes; the loop only matters past 2^35 blocks): against a
+// grid capped at 16 workgroups per CU with two blocks per lane per iteration,
+// [8192, 7168] took 29.6 instead of 32.9 us (inputs in the Infinity Cache)
+// and 31.8 instead of 35.0 us (from HBM), [8192, 18432] 78.9 instead of 91.5
+// us from HBM; four blocks per lane per iteration were slower still.
 //
 // Per element the work is: widen bf16, one max, a three-operation correctly
 // rounded quotient (see quotient()), and the gfx950 fp32 -> e4m3 conversion
@@ -72,27 +76,8 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint4* __restrict_
                                                         int64_t nblocks) {
     const int lane8 = threadIdx.x & 7;
     const int64_t groups = ((int64_t)gridDim.x * blockDim.x) >> 3;
-    int64_t blk = (((int64_t)blockIdx.x * blockDim.x) + threadIdx.x) >> 3;
-    // two blocks per iteration: blk and blk + groups
-    for (; blk + groups < nblocks; blk += 2 * groups) {
-        const uint4* p0 = x + blk * 16 + lane8 * 2;
-        const uint4* p1 = x + (blk + groups) * 16 + lane8 * 2;
-        const uint4 a0 = load_nt(p0);
-        const uint4 a1 = load_nt(p0 + 1);
-        const uint4 b0 = load_nt(p1);
-        const uint4 b1 = load_nt(p1 + 1);
-        uint4 qa, qb;
-        float sa, sb;
-        quant_block_part<kHw, kPow2>(a0, a1, lane8, qa, sa);
-        quant_block_part<kHw, kPow2>(b0, b1, lane8, qb, sb);
-        q[blk * 8 + lane8] = qa;
-        q[(blk + groups) * 8 + lane8] = qb;
-        if (lane8 == 0) {
-            s[blk] = sa;
-            s[blk + groups] = sb;
-        }
-    }
-    if (blk < nblocks) {
+    for (int64_t blk = (((int64_t)blockIdx.x * blockDim.x) + threadIdx.x) >> 3; blk < nblocks;
+         blk += groups) {
         const uint4* p0 = x + blk * 16 + lane8 * 2;
         const uint4 a0 = load_nt(p0);
         const uint4 a1 = load_nt(p0 + 1);
@@ -108,9 +93,9 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint4* __restrict_
 // row_token[r], for r < min(*num_rows, M); rows past that, and rows whose
 // token lies outside [0, T), are not written.  Quantization is row-local, so
 // this equals gathering rows of act_quant(x).  Same mapping as
-// act_quant_kernel (eight lanes per 128-element block, two blocks per lane
-// per iteration); the block index splits into (output row, k-block) and the
-// source block is (row_token[row], k-block).
+// act_quant_kernel (eight lanes per 128-element block, a grid covering every
+// block); the block index splits into (output row, k-block) and the source
+// block is (row_token[row], k-block).
 __device__ __forceinline__ bool rows_source(const uint4* __restrict__ x,
                                             const int32_t* __restrict__ row_token, int64_t T,
                                             int64_t KB, int64_t blk, const uint4*& src) {
@@ -135,34 +120,8 @@ __global__ __launch_bounds__(256) void act_quant_rows_kernel(
     const int64_t nblocks = rows * KB;
     const int lane8 = threadIdx.x & 7;
     const int64_t groups = ((int64_t)gridDim.x * blockDim.x) >> 3;
-    int64_t blk = (((int64_t)blockIdx.x * blockDim.x) + threadIdx.x) >> 3;
-    for (; blk + groups < nblocks; blk += 2 * groups) {
-        const uint4 *pa = nullptr, *pb = nullptr;
-        const bool va = rows_source(x, row_token, T, KB, blk, pa);
-        const bool vb = rows_source(x, row_token, T, KB, blk + groups, pb);
-        uint4 a0{}, a1{}, b0{}, b1{};
-        if (va) {
-            a0 = load_nt(pa + lane8 * 2);
-            a1 = load_nt(pa + lane8 * 2 + 1);
-        }
-        if (vb) {
-            b0 = load_nt(pb + lane8 * 2);
-            b1 = load_nt(pb + lane8 * 2 + 1);
-        }
-        uint4 qa, qb;
-        float sa, sb;
-        if (va) {
-            quant_block_part<kHw>(a0, a1, lane8, qa, sa);
-            q[blk * 8 + lane8] = qa;
-            if (lane8 == 0) s[blk] = sa;
-        }
-        if (vb) {
-            quant_block_part<kHw>(b0, b1, lane8, qb, sb);
-            q[(blk + groups) * 8 + lane8] = qb;
-            if (lane8 == 0) s[blk + groups] = sb;
-        }
-    }
-    if (blk < nblocks) {
+    for (int64_t blk = (((int64_t)blockIdx.x * blockDim.x) + threadIdx.x) >> 3; blk < nblocks;
+         blk += groups) {
         const uint4* pa = nullptr;
         if (rows_source(x, row_token, T, KB, blk, pa)) {
             const uint4 a0 = load_nt(pa + lane8 * 2);
@@ -223,12 +182,18 @@ hipError_t launch_bf16_round_range(uint32_t first, int64_t count, void* out, int
 // The encoder act_quant uses.
 constexpr bool kActQuantHwEncode = true;
 
+// Workgroups (256 lanes, 32 blocks) that cover n blocks at once; past 2^30
+// workgroups the kernels loop.
+static int quant_grid(int64_t nblocks) {
+    const int64_t need = (nblocks + 31) / 32;
+    const int64_t cap = (int64_t)1 << 30;
+    return (int)(need < cap ? (need > 0 ? need : 1) : cap);
+}
+
 hipError_t launch_act_quant(const void* x, void* q, float* s, int64_t M, int64_t K,
                             hipStream_t stream) {
     const int64_t nblocks = M * (K / kBlock);
-    const int64_t wg_needed = (nblocks + 63) / 64;             // 32 blocks per WG-iteration, x2 unroll
-    const int64_t wg_cap = (int64_t)device_cu_count() * 16;   // 1-3% faster than 8 per CU (measured)
-    const int grid = (int)(wg_needed < wg_cap ? (wg_needed > 0 ? wg_needed : 1) : wg_cap);
+    const int grid = quant_grid(nblocks);
     hipLaunchKernelGGL(act_quant_kernel<kActQuantHwEncode>, dim3(grid), dim3(256), 0, stream,
                        (const uint4*)x, (uint4*)q, s, nblocks);
     return hipGetLastError();
@@ -239,9 +204,14 @@ hipError_t launch_act_quant_rows(const void* x, int64_t T, const int32_t* row_to
                                  hipStream_t stream) {
     const int64_t KB = K / kBlock;
     const int64_t nblocks = M * KB;                            // upper bound: *num_rows may be less
-    const int64_t wg_needed = (nblocks + 63) / 64;
-    const int64_t wg_cap = (int64_t)device_cu_count() * 16;
-    const int grid = (int)(wg_needed < wg_cap ? (wg_needed > 0 ? wg_needed : 1) : wg_cap);
+    // M is a capacity that the rows on the device may fill only in part, so the grid
+    // stops at 32 workgroups per CU and loops: with room for 65536 rows and 8195 used
+    // ([8192, 7168] source) that took 33.0 us against 53.4 for a grid covering the
+    // capacity and 36.2 for 16 per CU with two blocks per lane; 33.1 against 34.2 us
+    // with exactly 8195 rows
+    int grid = quant_grid(nblocks);
+    const int cap = (int)device_cu_count() * 32;
+    grid = grid < cap ? grid : cap;
     hipLaunchKernelGGL(act_quant_rows_kernel<kActQuantHwEncode>, dim3(grid), dim3(256), 0, stream,
                        (const uint4*)x, T, row_token, num_rows, (uint4*)q, s, M, KB);
     return hipGetLastError();
@@ -250,9 +220,7 @@ hipError_t launch_act_quant_rows(const void* x, int64_t T, const int32_t* row_to
 hipError_t launch_act_quant_pow2(const void* x, void* q, float* s, int64_t M, int64_t K,
                                  hipStream_t stream) {
     const int64_t nblocks = M * (K / kBlock);
-    const int64_t wg_needed = (nblocks + 63) / 64;
-    const int64_t wg_cap = (int64_t)device_cu_count() * 16;
-    const int grid = (int)(wg_needed < wg_cap ? (wg_needed > 0 ? wg_needed : 1) : wg_cap);
+    const int grid = quant_grid(nblocks);
     hipLaunchKernelGGL((act_quant_kernel<kActQuantHwEncode, true>), dim3(grid), dim3(256), 0, stream,
                        (const uint4*)x, (uint4*)q, s, nblocks);
     return hipGetLastError();
