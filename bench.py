@@ -277,6 +277,9 @@ class Step:
             qh = torch.empty(M, K2, dtype=torch.uint8, device=dev)
             qhs = torch.empty(M, K2 // BLOCK, dtype=torch.float32, device=dev)
             y = torch.empty(M, N2, dtype=torch.bfloat16, device=dev)
+            # the down GEMM's half-full last round split over K, as in the fp8 step
+            n_ws = bfp8.bfp8_gemm_ue8m0_workspace_size(M, N2, K2)
+            ws2 = torch.empty(max(1, n_ws // 4), dtype=torch.float32, device=dev) if n_ws else None
             self.launches += [
                 Launch("act_quant_ue8m0_x", bfp8.bfp8_act_quant_ue8m0, (x, q, qs), 0,
                        act_quant_bytes(M, K1), "hbm"),
@@ -284,7 +287,7 @@ class Step:
                        gemm_bytes(M, N1, K1), "mfma"),
                 Launch("act_quant_ue8m0_h", bfp8.bfp8_act_quant_ue8m0, (h, qh, qhs), 0,
                        act_quant_bytes(M, K2), "hbm"),
-                Launch("fp8_gemm_ue8m0_2", bfp8.bfp8_gemm_ue8m0, (qh, qhs, w2, s2, y), 2 * M * N2 * K2,
+                Launch("fp8_gemm_ue8m0_2", bfp8.bfp8_gemm_ue8m0, (qh, qhs, w2, s2, y, ws2), 2 * M * N2 * K2,
                        gemm_bytes(M, N2, K2), "mfma"),
             ]
             self.shape = dict(M=M, N1=N1, K1=K1, N2=N2, K2=K2, scales="powers of two (e8m0)")

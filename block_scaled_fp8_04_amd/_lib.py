@@ -35,7 +35,7 @@ EXPORTS = ("bfp8_act_quant", "bfp8_weight_dequant", "bfp8_gemm", "bfp8_gemm_work
            "bfp8_gemm_kernel_name", "bfp8_moe_dispatch_workspace_size", "bfp8_moe_dispatch",
            "bfp8_act_quant_rows", "bfp8_moe_combine", "bfp8_gemm_bf16",
            "bfp8_gemm_act_quant", "bfp8_gemm_swiglu_act_quant", "bfp8_act_quant_ue8m0",
-           "bfp8_gemm_ue8m0", "bfp8_linear_fp8_workspace_size", "bfp8_linear_fp8", "bfp8_gemm_noalloc",
+           "bfp8_gemm_ue8m0", "bfp8_gemm_ue8m0_workspace_size", "bfp8_linear_fp8_workspace_size", "bfp8_linear_fp8", "bfp8_gemm_noalloc",
            "bfp8_status_string", "bfp8_version")
 
 _lib = None
@@ -89,8 +89,10 @@ def library():
     lib.bfp8_gemm_swiglu_act_quant.restype = ctypes.c_int
     lib.bfp8_act_quant_ue8m0.argtypes = [P, P, P, I64, I64, P]
     lib.bfp8_act_quant_ue8m0.restype = ctypes.c_int
-    lib.bfp8_gemm_ue8m0.argtypes = [P, P, P, P, P, I64, I64, I64, P]
+    lib.bfp8_gemm_ue8m0.argtypes = [P, P, P, P, P, I64, I64, I64, P, ctypes.c_size_t, P]
     lib.bfp8_gemm_ue8m0.restype = ctypes.c_int
+    lib.bfp8_gemm_ue8m0_workspace_size.argtypes = [I64, I64, I64]
+    lib.bfp8_gemm_ue8m0_workspace_size.restype = ctypes.c_size_t
     lib.bfp8_linear_fp8_workspace_size.argtypes = [I64, I64, I64]
     lib.bfp8_linear_fp8_workspace_size.restype = ctypes.c_size_t
     lib.bfp8_linear_fp8.argtypes = [P, P, P, P, I64, I64, I64, P, ctypes.c_size_t, P]
@@ -185,18 +187,24 @@ def bfp8_act_quant_ue8m0(x, q, scales, stream=None):
                                                                   _stream(stream, x.device)))
 
 
-def bfp8_gemm_ue8m0(a, a_s, b, b_s, c, stream=None):
+def bfp8_gemm_ue8m0(a, a_s, b, b_s, c, workspace=None, stream=None):
     """bfp8_gemm for power-of-two scales, applied by the MFMA itself."""
     a, b = _bytes_view(a), _bytes_view(b)
-    _cuda_contig(a, a_s, b, b_s, c)
+    _cuda_contig(a, a_s, b, b_s, c, workspace)
     M, K = a.shape
     N = b.shape[0]
     _need(b.shape[1] == K, "a and b must share K")
     _need(a_s.shape == (M, K // BLOCK) and b_s.shape == (-(-N // BLOCK), K // BLOCK),
           "a_s [M, K/128], b_s [ceil(N/128), K/128]")
     _need(c.dtype == torch.bfloat16 and c.shape == (M, N), "c must be bf16 [M, N]")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("bfp8_gemm_ue8m0", library().bfp8_gemm_ue8m0(_ptr(a), _ptr(a_s), _ptr(b), _ptr(b_s), _ptr(c),
-                                                        M, N, K, _stream(stream, a.device)))
+                                                        M, N, K, _ptr(workspace), ws_bytes,
+                                                        _stream(stream, a.device)))
+
+
+def bfp8_gemm_ue8m0_workspace_size(M, N, K) -> int:
+    return int(library().bfp8_gemm_ue8m0_workspace_size(int(M), int(N), int(K)))
 
 
 def bfp8_weight_dequant(w, s, out, stream=None):
@@ -486,9 +494,9 @@ def act_quant_ue8m0(x, stream=None):
     return q, s
 
 
-def gemm_ue8m0(a, a_s, b, b_s, stream=None):
+def gemm_ue8m0(a, a_s, b, b_s, workspace=None, stream=None):
     c = torch.empty((a.shape[0], b.shape[0]), dtype=torch.bfloat16, device=a.device)
-    bfp8_gemm_ue8m0(a, a_s, b, b_s, c, stream)
+    bfp8_gemm_ue8m0(a, a_s, b, b_s, c, workspace, stream)
     return c
 
 

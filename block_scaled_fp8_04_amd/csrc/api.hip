@@ -75,15 +75,26 @@ int bfp8_act_quant_ue8m0(const void* x_bf16, void* q_e4m3, float* scales, int64_
     return from_hip(bfp8::launch_act_quant_pow2(x_bf16, q_e4m3, scales, M, K, (hipStream_t)stream));
 }
 
+size_t bfp8_gemm_ue8m0_workspace_size(int64_t M, int64_t N, int64_t K) {
+    if (M <= 0 || N <= 0 || K <= 0 || K % BFP8_BLOCK != 0) return 0;
+    return bfp8::gemm_ue8m0_workspace_bytes(M, N, K);
+}
+
 int bfp8_gemm_ue8m0(const void* a, const float* a_s, const void* b, const float* b_s, void* c_bf16,
-                    int64_t M, int64_t N, int64_t K, void* stream) {
+                    int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                    void* stream) {
     if (M < 0 || N < 0 || !gemm_k_ok(K)) return BFP8_ERR_SHAPE;
     if (M == 0 || N == 0) return BFP8_OK;
     if (!a || !a_s || !b || !b_s || !c_bf16) return BFP8_ERR_NULL;
     if (!aligned(a, 16) || !aligned(b, 16) || !aligned(a_s, 4) || !aligned(b_s, 4) ||
         !aligned(c_bf16, 2))
         return BFP8_ERR_ALIGN;
-    return from_hip(bfp8::launch_gemm_ue8m0(a, a_s, b, b_s, c_bf16, M, N, K, (hipStream_t)stream));
+    if (workspace) {
+        if (!aligned(workspace, 16)) return BFP8_ERR_ALIGN;
+        if (workspace_bytes < bfp8::gemm_ue8m0_workspace_bytes(M, N, K)) return BFP8_ERR_WORKSPACE;
+    }
+    return from_hip(bfp8::launch_gemm_ue8m0(a, a_s, b, b_s, c_bf16, M, N, K, workspace,
+                                            workspace ? workspace_bytes : 0, (hipStream_t)stream));
 }
 
 int bfp8_weight_dequant(const void* w_e4m3, const float* s, void* out_bf16, int64_t N, int64_t K,

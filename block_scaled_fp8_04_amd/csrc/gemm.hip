@@ -841,8 +841,9 @@ __global__ __launch_bounds__(T::THREADS, T::OCC) void gemm_big_kernel(const uint
 // runs of kb_per blocks, so twice as many workgroups fill the round.  Split s
 // writes its fp32 partial sums to ws[s][M][N - n1]; tail_reduce_kernel adds
 // them in split order.  Workgroup id = s * tiles + tile, the tiles of one
-// split laid out over the XCDs as in gemm_big_kernel.
-template <class T>
+// split laid out over the XCDs as in gemm_big_kernel.  kHw: the power-of-two
+// scale GEMM (scales applied by the MFMA).
+template <class T, bool kHw = false>
 __global__ __launch_bounds__(T::THREADS, 1) void gemm_tail_kernel(
     const uint8_t* __restrict__ a, const float* __restrict__ as, const uint8_t* __restrict__ b,
     const float* __restrict__ bs, float* __restrict__ ws, int64_t M, int64_t N, int64_t K, int mt,
@@ -859,8 +860,8 @@ __global__ __launch_bounds__(T::THREADS, 1) void gemm_tail_kernel(
     po.ldw = N - n1;
     po.ws = ws + (int64_t)split * M * po.ldw;
     po.n_base = n1;
-    gemm_tile_big<T, false, kEpiF32>(a, as, b, bs, nullptr, (int64_t)tm * T::BM, M,
-                                     n1 + (int64_t)tn * T::BN, N, K, lds, QuantOut{}, po);
+    gemm_tile_big<T, false, kEpiF32, kHw>(a, as, b, bs, nullptr, (int64_t)tm * T::BM, M,
+                                          n1 + (int64_t)tn * T::BN, N, K, lds, QuantOut{}, po);
 }
 
 // The GEMM with power-of-two scales applied by the MFMA (kHwScale).
@@ -1167,6 +1168,41 @@ const char* gemm_config_name(GemmConfig cfg) {
     return "unknown";
 }
 
+// Whole rounds of 256 x 256 tiles over columns [0, n1), then the tail columns as
+// two K halves into the fp32 workspace, then the ordered reduction (tail_plan).
+// kHw: the power-of-two-scale GEMM's kernels.
+template <bool kHw>
+static hipError_t launch_split_last_round(const void* a, const float* as, const void* b,
+                                          const float* bs, void* c, int64_t M, int64_t N,
+                                          int64_t K, void* workspace, hipStream_t stream) {
+    const TailPlan tp = tail_plan(M, N, K);
+    const int mt = (int)(M / 256);
+    const int64_t n1 = (int64_t)tp.nt_main * 256;
+    if constexpr (kHw)
+        hipLaunchKernelGGL(gemm_ue8m0_kernel<BigSquare>, dim3(mt * tp.nt_main),
+                           dim3(BigSquare::THREADS), 0, stream, (const uint8_t*)a, as,
+                           (const uint8_t*)b, bs, (uint16_t*)c, M, N, K, mt, tp.nt_main);
+    else
+        hipLaunchKernelGGL(gemm_big_kernel<BigSquare>, dim3(mt * tp.nt_main),
+                           dim3(BigSquare::THREADS), 0, stream, (const uint8_t*)a, as,
+                           (const uint8_t*)b, bs, (uint16_t*)c, M, N, K, mt, tp.nt_main);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((gemm_tail_kernel<BigSquare, kHw>), dim3(mt * tp.nt_tail * tp.splits),
+                       dim3(BigSquare::THREADS), 0, stream, (const uint8_t*)a, as,
+                       (const uint8_t*)b, bs, (float*)workspace, M, N, K, mt, tp.nt_tail, n1,
+                       tp.kb_per);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t quads = M * (N - n1) / 4;
+    int64_t grid = (quads + 255) / 256;
+    const int64_t cap = (int64_t)device_cu_count() * 8;
+    grid = grid < cap ? grid : cap;
+    hipLaunchKernelGGL(tail_reduce_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                       (const float*)workspace, (uint16_t*)c, M, N, n1, tp.splits);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm(const void* a, const float* as, const void* b, const float* bs, void* c,
                        int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
                        hipStream_t stream) {
@@ -1190,31 +1226,9 @@ hipError_t launch_gemm(const void* a, const float* as, const void* b, const floa
         return hipGetLastError();
     }
     const GemmConfig cfg = gemm_config(M, N, K);
-    const TailPlan tp = tail_plan(M, N, K);
-    if (cfg == GemmConfig::kBig256x256 && workspace && tp.splits > 0 &&
-        workspace_bytes >= tail_workspace_bytes(M, N, K) && ((uintptr_t)c & 7u) == 0) {
-        // whole rounds of 256 x 256 tiles over columns [0, n1), then the tail
-        const int mt = (int)(M / 256);
-        const int64_t n1 = (int64_t)tp.nt_main * 256;
-        hipLaunchKernelGGL(gemm_big_kernel<BigSquare>, dim3(mt * tp.nt_main), dim3(BigSquare::THREADS),
-                           0, stream, (const uint8_t*)a, as, (const uint8_t*)b, bs, (uint16_t*)c, M,
-                           N, K, mt, tp.nt_main);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(gemm_tail_kernel<BigSquare>, dim3(mt * tp.nt_tail * tp.splits),
-                           dim3(BigSquare::THREADS), 0, stream, (const uint8_t*)a, as,
-                           (const uint8_t*)b, bs, (float*)workspace, M, N, K, mt, tp.nt_tail, n1,
-                           tp.kb_per);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        const int64_t quads = M * (N - n1) / 4;
-        int64_t grid = (quads + 255) / 256;
-        const int64_t cap = (int64_t)device_cu_count() * 8;
-        grid = grid < cap ? grid : cap;
-        hipLaunchKernelGGL(tail_reduce_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
-                           (const float*)workspace, (uint16_t*)c, M, N, n1, tp.splits);
-        return hipGetLastError();
-    }
+    if (cfg == GemmConfig::kBig256x256 && workspace && tail_plan(M, N, K).splits > 0 &&
+        workspace_bytes >= tail_workspace_bytes(M, N, K) && ((uintptr_t)c & 7u) == 0)
+        return launch_split_last_round<false>(a, as, b, bs, c, M, N, K, workspace, stream);
     switch (cfg) {
         case GemmConfig::kBig256x256:
             launch_big<BigSquare>(a, as, b, bs, c, M, N, K, stream);
@@ -1252,9 +1266,19 @@ static hipError_t launch_ue8m0(const void* a, const float* as, const void* b, co
     return hipGetLastError();
 }
 
+// The power-of-two-scale GEMM takes a workspace only for the split last round.
+size_t gemm_ue8m0_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    return tail_workspace_bytes(M, N, K);
+}
+
 hipError_t launch_gemm_ue8m0(const void* a, const float* as, const void* b, const float* bs,
-                             void* c, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-    switch (gemm_config(M, N, K)) {
+                             void* c, int64_t M, int64_t N, int64_t K, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+    const GemmConfig cfg = gemm_config(M, N, K);
+    if (cfg == GemmConfig::kBig256x256 && workspace && tail_plan(M, N, K).splits > 0 &&
+        workspace_bytes >= tail_workspace_bytes(M, N, K) && ((uintptr_t)c & 7u) == 0)
+        return launch_split_last_round<true>(a, as, b, bs, c, M, N, K, workspace, stream);
+    switch (cfg) {
         case GemmConfig::kBig256x256: return launch_ue8m0<BigSquare>(a, as, b, bs, c, M, N, K, stream);
         // the e8m0 loop has no fold: 128 x 128 tiles two per CU measured 6% faster than
         // 256 x 128 here too (4096 x 2048 x 7168)

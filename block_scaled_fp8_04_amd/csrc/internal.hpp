@@ -20,7 +20,9 @@ hipError_t launch_act_quant(const void* x, void* q, float* s, int64_t M, int64_t
 hipError_t launch_act_quant_pow2(const void* x, void* q, float* s, int64_t M, int64_t K,
                                  hipStream_t stream);
 hipError_t launch_gemm_ue8m0(const void* a, const float* as, const void* b, const float* bs,
-                             void* c, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+                             void* c, int64_t M, int64_t N, int64_t K, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+size_t gemm_ue8m0_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_act_quant_rows(const void* x, int64_t T, const int32_t* row_token,
                                  const int32_t* num_rows, void* q, float* s, int64_t M, int64_t K,
                                  hipStream_t stream);

@@ -195,9 +195,19 @@ int bfp8_act_quant_ue8m0(const void* x_bf16, void* q_e4m3, float* scales, int64_
  *     c[m, n] = bf16_rne( sum_kb P_kb[m, n] * a_s[m, kb] * b_s[n/128, kb] )
  * Every scale must be a power of two in [2^-127, 2^127] stored as fp32 (as
  * bfp8_act_quant_ue8m0 writes); for any other value only its exponent is used.
- * Same arguments, layouts and errors as bfp8_gemm without a workspace. */
+ * Same arguments, layouts and errors as bfp8_gemm, except that the optional
+ * workspace serves only large problems (K >= 80 * 128) whose last round of
+ * 256 x 256 tiles is at most half full (the partial sums of those tiles' two
+ * K halves); it must hold bfp8_gemm_ue8m0_workspace_size(M, N, K) bytes
+ * (BFP8_ERR_WORKSPACE otherwise), 16-byte aligned, contents irrelevant. */
 int bfp8_gemm_ue8m0(const void* a, const float* a_s, const void* b, const float* b_s,
-                    void* c_bf16, int64_t M, int64_t N, int64_t K, void* stream);
+                    void* c_bf16, int64_t M, int64_t N, int64_t K, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* Bytes of fp32 workspace bfp8_gemm_ue8m0 would use at this shape (0 when its
+ * last round is not split).  Pure host function (planned for the 256 CUs of
+ * MI355X). */
+size_t bfp8_gemm_ue8m0_workspace_size(int64_t M, int64_t N, int64_t K);
 
 /* The FP8 branch of linear() in one call ([DF] FP8 bullet: act_quant of the
  * input, then fp8_gemm with the weight and its scale):

@@ -218,10 +218,20 @@ def test_ue8m0_validation(lib):
     assert f(ODD, FAKE, FAKE, 4, 128, None) == _lib.BFP8_ERR_ALIGN
     assert f(None, None, None, 0, 128, None) == _lib.BFP8_OK
     g = lib.bfp8_gemm_ue8m0
-    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 64, 200, None) == _lib.BFP8_ERR_SHAPE
-    assert g(FAKE, None, FAKE, FAKE, FAKE, 64, 64, 256, None) == _lib.BFP8_ERR_NULL
-    assert g(ODD, FAKE, FAKE, FAKE, FAKE, 64, 64, 256, None) == _lib.BFP8_ERR_ALIGN
-    assert g(None, FAKE, FAKE, FAKE, FAKE, 0, 64, 256, None) == _lib.BFP8_OK
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 64, 200, None, 0, None) == _lib.BFP8_ERR_SHAPE
+    assert g(FAKE, None, FAKE, FAKE, FAKE, 64, 64, 256, None, 0, None) == _lib.BFP8_ERR_NULL
+    assert g(ODD, FAKE, FAKE, FAKE, FAKE, 64, 64, 256, None, 0, None) == _lib.BFP8_ERR_ALIGN
+    assert g(None, FAKE, FAKE, FAKE, FAKE, 0, 64, 256, None, 0, None) == _lib.BFP8_OK
+    # a workspace for the split last round: misaligned or too small is refused before any launch
+    M, N, K = 8192, 7168, 18432
+    need = lib.bfp8_gemm_ue8m0_workspace_size(M, N, K)
+    assert need == lib.bfp8_gemm_workspace_size(M, N, K) == 2 * 8192 * 4 * 256 * 4
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, M, N, K, ODD, need, None) == _lib.BFP8_ERR_ALIGN
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, M, N, K, FAKE, need - 16, None) == _lib.BFP8_ERR_WORKSPACE
+    # nothing to split: no workspace (skinny problems do not split K on this path)
+    assert lib.bfp8_gemm_ue8m0_workspace_size(64, 1536, 7168) == 0
+    assert lib.bfp8_gemm_ue8m0_workspace_size(8192, 18432, 7168) == 0
+    assert lib.bfp8_gemm_ue8m0_workspace_size(0, 7168, 18432) == 0
 
 
 def test_gemm_k_limit(lib):
@@ -232,7 +242,7 @@ def test_gemm_k_limit(lib):
     assert lib.bfp8_gemm(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0, K - 128, None, 0, None) == _lib.BFP8_OK
     assert lib.bfp8_gemm_act_quant(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 128, K, None) == _lib.BFP8_ERR_SHAPE
     assert lib.bfp8_gemm_swiglu_act_quant(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 256, K, None) == _lib.BFP8_ERR_SHAPE
-    assert lib.bfp8_gemm_ue8m0(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, K, None) == _lib.BFP8_ERR_SHAPE
+    assert lib.bfp8_gemm_ue8m0(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, K, None, 0, None) == _lib.BFP8_ERR_SHAPE
     assert lib.bfp8_linear_fp8(FAKE, FAKE, FAKE, FAKE, 1, 1, K, big, 1 << 30, None) == _lib.BFP8_ERR_SHAPE
     off = ctypes.c_void_p(0x200000)
     assert lib.bfp8_gemm_grouped(FAKE, FAKE, FAKE, FAKE, FAKE, off, 1, 1, 1, K, None) == _lib.BFP8_ERR_SHAPE

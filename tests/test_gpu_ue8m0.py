@@ -76,3 +76,31 @@ def test_gemm_ue8m0_shapes():
 def test_gemm_ue8m0_dense_full_size():
     """Rows: the first and last of every 128-row block plus seeded ones."""
     _gemm_case(8192, 18432, 7168, 990, "dense-mlp up", rows=sample_rows(8192, 16, 991))
+
+
+def test_gemm_ue8m0_split_last_round():
+    """With a workspace, shapes whose last round of 256 x 256 tiles is at most half full run
+    that round as two K halves into the workspace: within tolerance of the oracle on sampled
+    rows, independent of what the workspace held, a too-small workspace refused; the dense
+    down projection among them."""
+    for i, (M, N, K) in enumerate([(2048, 8448, 10368), (8192, 7168, 18432)]):
+        need = bfp8.bfp8_gemm_ue8m0_workspace_size(M, N, K)
+        assert need > 0, (M, N, K)
+        g = torch.Generator().manual_seed(1700 + i)
+        x = torch.randn(M, K, generator=g).to(torch.bfloat16).to(dev())
+        q, s = bfp8.act_quant_ue8m0(x)
+        w, ws = synth.weight(N, K, 1710 + i, 1720 + i, pow2=True)
+        wd, wsd = w.to(dev()), ws.to(dev())
+        work = torch.full((need // 4,), float("nan"), dtype=torch.float32, device=dev())
+        announce(f"gemm_ue8m0 split last round M={M} N={N} K={K}, workspace {need} B")
+        c1 = bfp8.gemm_ue8m0(q, s, wd, wsd, workspace=work)
+        work.fill_(1e30)
+        c2 = bfp8.gemm_ue8m0(q, s, wd, wsd, workspace=work)
+        torch.cuda.synchronize()
+        assert torch.equal(c1, c2), "the result depends on the workspace contents"
+        rows = sample_rows(M, 8, 1730 + i)
+        ref = oracle.gemm(u8(q), s.cpu().numpy(), u8(w), ws.numpy(), rows=rows)
+        worst = gemm_check(c1[torch.from_numpy(rows).to(dev())], ref, f"split last round {i}")
+        announce(f"gemm_ue8m0 split last round {i}: worst err/bound {worst:.3f}")
+        with pytest.raises(bfp8.Bfp8Error):
+            bfp8.bfp8_gemm_ue8m0(q, s, wd, wsd, torch.empty_like(c1), work[: need // 4 - 4])
