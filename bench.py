@@ -301,6 +301,9 @@ class Step:
             w2d = torch.empty(N2, K2, dtype=torch.bfloat16, device=dev)
             h = torch.empty(M, N1, dtype=torch.bfloat16, device=dev)
             y = torch.empty(M, N2, dtype=torch.bfloat16, device=dev)
+            # the down GEMM's half-full last round split over K, as in the fp8 step
+            n_ws = bfp8.bfp8_gemm_bf16_workspace_size(M, N2, K2)
+            ws2 = torch.empty(max(1, n_ws // 4), dtype=torch.float32, device=dev) if n_ws else None
             self.launches += [
                 Launch("weight_dequant_1", bfp8.bfp8_weight_dequant, (w1, s1, w1d), 0,
                        dequant_bytes(N1, K1), "hbm"),
@@ -308,7 +311,7 @@ class Step:
                        2 * M * K1 + 2 * N1 * K1 + 2 * M * N1, "mfma_bf16"),
                 Launch("weight_dequant_2", bfp8.bfp8_weight_dequant, (w2, s2, w2d), 0,
                        dequant_bytes(N2, K2), "hbm"),
-                Launch("bf16_gemm_2", bfp8.bfp8_gemm_bf16, (h, w2d, y), 2 * M * N2 * K2,
+                Launch("bf16_gemm_2", bfp8.bfp8_gemm_bf16, (h, w2d, y, ws2), 2 * M * N2 * K2,
                        2 * M * K2 + 2 * N2 * K2 + 2 * M * N2, "mfma_bf16"),
             ]
             self.shape = dict(M=M, N1=N1, K1=K1, N2=N2, K2=K2)

@@ -11,7 +11,8 @@ from ._lib import (  # noqa: F401
     bfp8_gemm, bfp8_gemm_grouped, bfp8_gemm_kernel_name, bfp8_gemm_workspace_size, bfp8_status_string, bfp8_version,
     bfp8_weight_dequant, gemm, gemm_grouped, library, linear_fp8, status_string, weight_dequant,
     bfp8_act_quant_rows, bfp8_moe_combine, bfp8_moe_dispatch, bfp8_moe_dispatch_workspace_size,
-    moe_combine, moe_dispatch, moe_experts_fp8, bfp8_gemm_bf16, gemm_bf16, linear_bf16,
+    moe_combine, moe_dispatch, moe_experts_fp8, bfp8_gemm_bf16, bfp8_gemm_bf16_workspace_size,
+    gemm_bf16, linear_bf16,
     bfp8_gemm_act_quant, gemm_act_quant, bfp8_gemm_swiglu_act_quant, gemm_swiglu_act_quant,
     interleave_w13, bfp8_act_quant_ue8m0, bfp8_gemm_ue8m0, bfp8_gemm_ue8m0_workspace_size, act_quant_ue8m0,
     gemm_ue8m0,

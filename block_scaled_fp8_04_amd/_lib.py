@@ -33,7 +33,7 @@ NOALLOC_SCRATCH_BYTES = 64 << 20
 EXPORTS = ("bfp8_act_quant", "bfp8_weight_dequant", "bfp8_gemm", "bfp8_gemm_workspace_size",
            "bfp8_gemm_grouped", "bfp8_e4m3_encode_range", "bfp8_bf16_round_range",
            "bfp8_gemm_kernel_name", "bfp8_moe_dispatch_workspace_size", "bfp8_moe_dispatch",
-           "bfp8_act_quant_rows", "bfp8_moe_combine", "bfp8_gemm_bf16",
+           "bfp8_act_quant_rows", "bfp8_moe_combine", "bfp8_gemm_bf16", "bfp8_gemm_bf16_workspace_size",
            "bfp8_gemm_act_quant", "bfp8_gemm_swiglu_act_quant", "bfp8_act_quant_ue8m0",
            "bfp8_gemm_ue8m0", "bfp8_gemm_ue8m0_workspace_size", "bfp8_linear_fp8_workspace_size", "bfp8_linear_fp8", "bfp8_gemm_noalloc",
            "bfp8_status_string", "bfp8_version")
@@ -97,8 +97,10 @@ def library():
     lib.bfp8_linear_fp8_workspace_size.restype = ctypes.c_size_t
     lib.bfp8_linear_fp8.argtypes = [P, P, P, P, I64, I64, I64, P, ctypes.c_size_t, P]
     lib.bfp8_linear_fp8.restype = ctypes.c_int
-    lib.bfp8_gemm_bf16.argtypes = [P, P, P, I64, I64, I64, P]
+    lib.bfp8_gemm_bf16.argtypes = [P, P, P, I64, I64, I64, P, ctypes.c_size_t, P]
     lib.bfp8_gemm_bf16.restype = ctypes.c_int
+    lib.bfp8_gemm_bf16_workspace_size.argtypes = [I64, I64, I64]
+    lib.bfp8_gemm_bf16_workspace_size.restype = ctypes.c_size_t
     lib.bfp8_status_string.argtypes = [ctypes.c_int]
     lib.bfp8_status_string.restype = ctypes.c_char_p
     lib.bfp8_version.argtypes = []
@@ -348,16 +350,22 @@ def bfp8_gemm_grouped(a, a_s, b, b_s, c, group_offsets, stream=None):
         _stream(stream, a.device)))
 
 
-def bfp8_gemm_bf16(a, b, c, stream=None):
+def bfp8_gemm_bf16(a, b, c, workspace=None, stream=None):
     """c bf16 [M,N] = a bf16 [M,K] x b bf16 [N,K]^T (the BF16 branch's matmul)."""
-    _cuda_contig(a, b, c)
+    _cuda_contig(a, b, c, workspace)
     _need(a.dtype == torch.bfloat16 and b.dtype == torch.bfloat16 and c.dtype == torch.bfloat16,
           "a, b and c must be bf16")
     M, K = a.shape
     N = b.shape[0]
     _need(b.shape[1] == K and c.shape == (M, N), "shapes must be a [M,K], b [N,K], c [M,N]")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("bfp8_gemm_bf16", library().bfp8_gemm_bf16(_ptr(a), _ptr(b), _ptr(c), M, N, K,
+                                                      _ptr(workspace), ws_bytes,
                                                       _stream(stream, a.device)))
+
+
+def bfp8_gemm_bf16_workspace_size(M, N, K) -> int:
+    return int(library().bfp8_gemm_bf16_workspace_size(int(M), int(N), int(K)))
 
 
 def bfp8_e4m3_encode_range(first, count, out, variant=0, stream=None):
@@ -459,15 +467,15 @@ def gemm_grouped(a, a_s, b, b_s, group_offsets, stream=None):
     return c
 
 
-def gemm_bf16(a, b, stream=None):
+def gemm_bf16(a, b, workspace=None, stream=None):
     c = torch.empty((a.shape[0], b.shape[0]), dtype=torch.bfloat16, device=a.device)
-    bfp8_gemm_bf16(a, b, c, stream)
+    bfp8_gemm_bf16(a, b, c, workspace, stream)
     return c
 
 
-def linear_bf16(x, w, w_s, stream=None):
+def linear_bf16(x, w, w_s, workspace=None, stream=None):
     """The BF16 branch of linear(): weight_dequant(w, w.scale) then the bf16 matmul."""
-    return gemm_bf16(x, weight_dequant(w, w_s, stream), stream)
+    return gemm_bf16(x, weight_dequant(w, w_s, stream), workspace, stream)
 
 
 def gemm_act_quant(a, a_s, b, b_s, stream=None):

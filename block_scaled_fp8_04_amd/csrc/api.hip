@@ -201,13 +201,23 @@ int bfp8_gemm_grouped(const void* a, const float* a_s, const void* b, const floa
                                               N, K, (hipStream_t)stream));
 }
 
+size_t bfp8_gemm_bf16_workspace_size(int64_t M, int64_t N, int64_t K) {
+    if (M <= 0 || N <= 0 || K <= 0 || K % 64 != 0) return 0;
+    return bfp8::tail_workspace_bytes(M, N, K);
+}
+
 int bfp8_gemm_bf16(const void* a_bf16, const void* b_bf16, void* c_bf16, int64_t M, int64_t N,
-                   int64_t K, void* stream) {
+                   int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
     if (M < 0 || N < 0 || K <= 0 || K % 64 != 0 || K >= ((int64_t)1 << 22)) return BFP8_ERR_SHAPE;
     if (M == 0 || N == 0) return BFP8_OK;
     if (!a_bf16 || !b_bf16 || !c_bf16) return BFP8_ERR_NULL;
     if (!aligned(a_bf16, 16) || !aligned(b_bf16, 16) || !aligned(c_bf16, 2)) return BFP8_ERR_ALIGN;
-    return from_hip(bfp8::launch_gemm_bf16(a_bf16, b_bf16, c_bf16, M, N, K, (hipStream_t)stream));
+    if (workspace) {
+        if (!aligned(workspace, 16)) return BFP8_ERR_ALIGN;
+        if (workspace_bytes < bfp8::tail_workspace_bytes(M, N, K)) return BFP8_ERR_WORKSPACE;
+    }
+    return from_hip(bfp8::launch_gemm_bf16(a_bf16, b_bf16, c_bf16, M, N, K, workspace,
+                                           workspace ? workspace_bytes : 0, (hipStream_t)stream));
 }
 
 size_t bfp8_moe_dispatch_workspace_size(int64_t T, int32_t k, int32_t G) {

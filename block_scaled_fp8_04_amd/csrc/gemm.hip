@@ -1066,12 +1066,7 @@ static SplitPlan split_plan(int64_t M, int64_t N, int64_t K) {
 // 2048), where the partial sums' write and reduction outweigh the half round.
 // Host-only arithmetic, planned for 256 CUs, so bfp8_gemm_workspace_size
 // needs no device.
-struct TailPlan {
-    int nt_main = 0, nt_tail = 0, splits = 0;
-    int64_t kb_per = 0;
-};
-
-static TailPlan tail_plan(int64_t M, int64_t N, int64_t K) {
+TailPlan tail_plan(int64_t M, int64_t N, int64_t K) {
     TailPlan p;
     constexpr int64_t kCUs = 256;
     if (M <= 128 || M % 256 != 0 || N % 256 != 0) return p;
@@ -1085,7 +1080,7 @@ static TailPlan tail_plan(int64_t M, int64_t N, int64_t K) {
     return p;
 }
 
-static size_t tail_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+size_t tail_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     const TailPlan p = tail_plan(M, N, K);
     if (p.splits == 0) return 0;
     return (size_t)p.splits * (size_t)M * (size_t)p.nt_tail * 256 * sizeof(float);
@@ -1168,6 +1163,17 @@ const char* gemm_config_name(GemmConfig cfg) {
     return "unknown";
 }
 
+hipError_t launch_tail_reduce(const float* ws, void* c, int64_t M, int64_t N, int64_t n1,
+                              int splits, hipStream_t stream) {
+    const int64_t quads = M * (N - n1) / 4;
+    int64_t grid = (quads + 255) / 256;
+    const int64_t cap = (int64_t)device_cu_count() * 8;
+    grid = grid < cap ? grid : cap;
+    hipLaunchKernelGGL(tail_reduce_kernel, dim3((unsigned)grid), dim3(256), 0, stream, ws,
+                       (uint16_t*)c, M, N, n1, splits);
+    return hipGetLastError();
+}
+
 // Whole rounds of 256 x 256 tiles over columns [0, n1), then the tail columns as
 // two K halves into the fp32 workspace, then the ordered reduction (tail_plan).
 // kHw: the power-of-two-scale GEMM's kernels.
@@ -1194,13 +1200,7 @@ static hipError_t launch_split_last_round(const void* a, const float* as, const 
                        tp.kb_per);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t quads = M * (N - n1) / 4;
-    int64_t grid = (quads + 255) / 256;
-    const int64_t cap = (int64_t)device_cu_count() * 8;
-    grid = grid < cap ? grid : cap;
-    hipLaunchKernelGGL(tail_reduce_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
-                       (const float*)workspace, (uint16_t*)c, M, N, n1, tp.splits);
-    return hipGetLastError();
+    return launch_tail_reduce((const float*)workspace, c, M, N, n1, tp.splits, stream);
 }
 
 hipError_t launch_gemm(const void* a, const float* as, const void* b, const float* bs, void* c,

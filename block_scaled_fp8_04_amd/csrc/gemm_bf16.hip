@@ -90,18 +90,27 @@ struct BfStageId {
     static constexpr int value = S;
 };
 
-template <class T, bool kGuard>
+// Where a tile's sums go when it runs only K steps [ks_lo, ks_hi) of the
+// split last round: fp32 row r, column n at ws[r * ldw + n - n_base].
+struct BfPartial {
+    int64_t ks_lo = 0, ks_hi = -1;      // ks_hi < 0: all K steps, bf16 output
+    float* ws = nullptr;
+    int64_t ldw = 0, n_base = 0;
+};
+
+template <class T, bool kGuard, bool kPartial = false>
 __device__ __forceinline__ void bf16_tile(const uint16_t* __restrict__ a,
                                           const uint16_t* __restrict__ b,
                                           uint16_t* __restrict__ c, int64_t m0, int64_t M,
                                           int64_t n0, int64_t N, int64_t K,
-                                          const BfStages<T>& st) {
+                                          const BfStages<T>& st, BfPartial part = BfPartial{}) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm0 = (wave / T::WAVES_N) * T::WM;
     const int wn0 = (wave % T::WAVES_N) * T::WN;
-    const int64_t KS = K / kStep;
+    // the K steps this tile multiplies: [KS0, KS)
+    const int64_t KS0 = part.ks_lo, KS = part.ks_hi < 0 ? K / kStep : part.ks_hi;
     const int64_t rows_a = (M - m0) < T::BM ? (M - m0) : T::BM;
     const int64_t rows_b = (N - n0) < T::BN ? (N - n0) : T::BN;
     const int64_t row_bytes = 2 * K;
@@ -153,8 +162,8 @@ __device__ __forceinline__ void bf16_tile(const uint16_t* __restrict__ a,
         tm_valid = __builtin_amdgcn_readfirstlane(tm_valid);
     }
 
-    issue(0, st.p[0]);
-    if (T::NSTAGE > 2 && 1 < KS) issue(1, st.p[1]);
+    issue(KS0, st.p[0]);
+    if (T::NSTAGE > 2 && KS0 + 1 < KS) issue(KS0 + 1, st.p[1]);
 
     const int lr = lane & 15;
     const int g = lane >> 4;
@@ -200,7 +209,7 @@ __device__ __forceinline__ void bf16_tile(const uint16_t* __restrict__ a,
         }
     };
 
-    for (int64_t ks0 = 0; ks0 < KS; ks0 += T::NSTAGE) {
+    for (int64_t ks0 = KS0; ks0 < KS; ks0 += T::NSTAGE) {
         step(ks0, BfStageId<0>{});
         if (ks0 + 1 < KS) step(ks0 + 1, BfStageId<1>{});
         if constexpr (T::NSTAGE > 2) {
@@ -209,6 +218,19 @@ __device__ __forceinline__ void bf16_tile(const uint16_t* __restrict__ a,
     }
 
     // epilogue: lane holds row m0 + wm0 + 16 i + lr, columns n0 + wn0 + 16 j + 4 g + 0..3
+    if constexpr (kPartial) {
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i) {
+            const int64_t row = m0 + wm0 + 16 * i + lr;
+#pragma unroll
+            for (int j = 0; j < T::TN; ++j) {
+                const int64_t col = n0 + wn0 + 16 * j + 4 * g;
+                if (row < M && col + 3 < N)
+                    *(v4f*)(part.ws + row * part.ldw + (col - part.n_base)) = acc[i][j];
+            }
+        }
+        return;
+    }
     const bool interior = (m0 + T::BM <= M) && (n0 + T::BN <= N);
     const bool vec = interior && (N % 4 == 0) && (((uintptr_t)c & 7u) == 0);
     // Staged store (as in the fp8 GEMM): after a barrier (no loads are in
@@ -316,6 +338,32 @@ __global__ __launch_bounds__(T::THREADS, 1) void gemm_bf16_kernel(const uint16_t
         bf16_tile<T, true>(a, b, c, m0, M, (int64_t)tn * T::BN, N, K, st);
 }
 
+// The split last round's tail columns: tile t of split s (blockIdx = s * tiles
+// + t) multiplies K steps [s * ks_per, (s + 1) * ks_per) of tile t of the
+// columns from n1 and writes fp32 sums to ws[s][M][N - n1].
+template <class T>
+__global__ __launch_bounds__(T::THREADS, 1) void gemm_bf16_tail_kernel(
+    const uint16_t* __restrict__ a, const uint16_t* __restrict__ b, float* __restrict__ ws,
+    int64_t M, int64_t N, int64_t K, int mt, int nt_tail, int64_t n1, int64_t ks_per) {
+    __shared__ __attribute__((aligned(1024))) uint8_t st0[T::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t st1[T::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t st2[T::NSTAGE > 2 ? T::STAGE : 16];
+    const BfStages<T> st = {{st0, st1, st2}};
+    const int tiles = mt * nt_tail;
+    const int split = blockIdx.x / tiles;
+    int tm, tn;
+    bf16_tile_of(blockIdx.x - split * tiles, tiles, mt, nt_tail, tm, tn);
+    const int64_t KS = K / kStep;
+    BfPartial part;
+    part.ks_lo = split * ks_per;
+    part.ks_hi = part.ks_lo + ks_per < KS ? part.ks_lo + ks_per : KS;
+    part.ldw = N - n1;
+    part.ws = ws + (int64_t)split * M * part.ldw;
+    part.n_base = n1;
+    bf16_tile<T, false, true>(a, b, nullptr, (int64_t)tm * T::BM, M, n1 + (int64_t)tn * T::BN, N,
+                              K, st, part);
+}
+
 using BfSquare = BfTile<256, 256, 2, 4, 2>;
 using BfWide = BfTile<256, 128, 4, 2, 3>;
 using BfSmall = BfTile<64, 64, 2, 2, 3>;
@@ -342,8 +390,30 @@ const char* gemm_bf16_config_name(int64_t M, int64_t N, int64_t K) {
 }
 
 hipError_t launch_gemm_bf16(const void* a, const void* b, void* c, int64_t M, int64_t N, int64_t K,
-                            hipStream_t stream) {
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
     const int64_t cus = device_cu_count();
+    // with a workspace, the split last round of the fp8 GEMM (tail_plan); its plan takes
+    // the 256 x 256 tile, which this shape then uses too (at least 256 tiles)
+    const TailPlan tp = tail_plan(M, N, K);
+    if (workspace && tp.splits > 0 && workspace_bytes >= tail_workspace_bytes(M, N, K) &&
+        ((uintptr_t)c & 7u) == 0) {
+        const int mt = (int)(M / 256);
+        const int64_t n1 = (int64_t)tp.nt_main * 256;
+        hipLaunchKernelGGL(gemm_bf16_kernel<BfSquare>, dim3(mt * tp.nt_main),
+                           dim3(BfSquare::THREADS), 0, stream, (const uint16_t*)a,
+                           (const uint16_t*)b, (uint16_t*)c, M, N, K, mt, tp.nt_main);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        // the K steps of 64 shared out over the splits (K need only be a multiple of 64)
+        const int64_t ks = K / kStep, ks_per = (ks + tp.splits - 1) / tp.splits;
+        hipLaunchKernelGGL(gemm_bf16_tail_kernel<BfSquare>, dim3(mt * tp.nt_tail * tp.splits),
+                           dim3(BfSquare::THREADS), 0, stream, (const uint16_t*)a,
+                           (const uint16_t*)b, (float*)workspace, M, N, K, mt, tp.nt_tail, n1,
+                           ks_per);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_tail_reduce((const float*)workspace, c, M, N, n1, tp.splits, stream);
+    }
     // 256 x 256 from 5/8 of a tile per CU up (measured 20-22% faster than 256 x 128 at
     // 256-448 tiles), as for the fp8 GEMM
     if (M > 128 && ((M + 255) / 256) * ((N + 255) / 256) >= cus * 5 / 8)

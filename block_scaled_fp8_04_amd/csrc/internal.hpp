@@ -34,6 +34,21 @@ hipError_t launch_weight_dequant(const void* w, const float* s, void* out, int64
                                  hipStream_t stream);
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
+// The split last round of large GEMMs on 256 x 256 tiles (the fp8, power-of-two
+// scale and bf16 GEMMs share it): when the tiles fill whole rounds of the 256 CUs
+// and a last round at most half full of whole tile columns, the nt_tail last
+// columns of tiles run as `splits` K ranges of kb_per 128-wide blocks each into
+// an fp32 workspace [splits][M][N - 256 nt_main], then one ordered reduction.
+struct TailPlan {
+    int nt_main = 0, nt_tail = 0, splits = 0;
+    int64_t kb_per = 0;
+};
+TailPlan tail_plan(int64_t M, int64_t N, int64_t K);
+size_t tail_workspace_bytes(int64_t M, int64_t N, int64_t K);
+// Adds the K ranges' partial sums in order and writes bf16 columns [n1, N) of c.
+hipError_t launch_tail_reduce(const float* ws, void* c, int64_t M, int64_t N, int64_t n1,
+                              int splits, hipStream_t stream);
+
 enum class GemmConfig { kBig256x256, kBig256x128, kBig128x128 };
 GemmConfig gemm_config(int64_t M, int64_t N, int64_t K);
 const char* gemm_config_name(GemmConfig cfg);
@@ -59,7 +74,7 @@ hipError_t launch_gemm_grouped(const void* a, const float* as, const void* b, co
                                int64_t N, int64_t K, hipStream_t stream);
 
 hipError_t launch_gemm_bf16(const void* a, const void* b, void* c, int64_t M, int64_t N, int64_t K,
-                            hipStream_t stream);
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 const char* gemm_bf16_config_name(int64_t M, int64_t N, int64_t K);
 
 size_t moe_dispatch_workspace_bytes(int64_t T, int32_t k, int32_t G);

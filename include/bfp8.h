@@ -260,10 +260,19 @@ int bfp8_gemm_grouped(const void* a, const float* a_s, const void* b, const floa
  *   a_bf16 : bf16 [M, K], 16-byte aligned
  *   b_bf16 : bf16 [N, K], 16-byte aligned (e.g. bfp8_weight_dequant's output)
  *   c_bf16 : bf16 [M, N] output, 2-byte aligned
+ *   workspace : optional fp32 scratch for large problems (K >= 80 * 128) whose
+ *     last round of 256 x 256 tiles is at most half full: those tiles run as two
+ *     K halves into it, then one ordered reduction.  NULL: every tile runs its
+ *     whole K range.  If non-NULL it must hold bfp8_gemm_bf16_workspace_size
+ *     (M, N, K) bytes and be 16-byte aligned; its contents do not matter.
  * Errors: BFP8_ERR_SHAPE if M < 0, N < 0, K <= 0, K % 64 != 0 or K >= 2^22;
- * BFP8_ERR_NULL; BFP8_ERR_ALIGN. */
+ * BFP8_ERR_NULL; BFP8_ERR_ALIGN; BFP8_ERR_WORKSPACE (workspace too small). */
 int bfp8_gemm_bf16(const void* a_bf16, const void* b_bf16, void* c_bf16, int64_t M, int64_t N,
-                   int64_t K, void* stream);
+                   int64_t K, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of fp32 workspace bfp8_gemm_bf16 would use at this shape (0 when its
+ * last round is not split).  Pure host function (planned for 256 CUs). */
+size_t bfp8_gemm_bf16_workspace_size(int64_t M, int64_t N, int64_t K);
 
 /* ----------------------------------------------------------------------
  * MoE dispatch and combine around the grouped GEMM ([BT] "MoE trace": per

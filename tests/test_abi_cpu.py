@@ -269,8 +269,8 @@ def test_linear_fp8_validation(lib):
 def test_gemm_bf16_validation(lib):
     f = lib.bfp8_gemm_bf16
 
-    def call(a=FAKE, b=FAKE, c=FAKE, M=64, N=64, K=128):
-        return f(a, b, c, M, N, K, None)
+    def call(a=FAKE, b=FAKE, c=FAKE, M=64, N=64, K=128, ws=None, wsb=0):
+        return f(a, b, c, M, N, K, ws, wsb, None)
 
     assert call(K=100) == _lib.BFP8_ERR_SHAPE
     assert call(K=0) == _lib.BFP8_ERR_SHAPE
@@ -281,6 +281,14 @@ def test_gemm_bf16_validation(lib):
     assert call(a=ctypes.c_void_p(0x10008)) == _lib.BFP8_ERR_ALIGN
     assert call(c=ODD) == _lib.BFP8_ERR_ALIGN
     assert call(a=None, M=0) == _lib.BFP8_OK
+    # the split last round's workspace: the fp8 GEMM's plan, misaligned or short refused
+    M, N, K = 8192, 7168, 18432
+    need = lib.bfp8_gemm_bf16_workspace_size(M, N, K)
+    assert need == lib.bfp8_gemm_workspace_size(M, N, K) > 0
+    assert lib.bfp8_gemm_bf16_workspace_size(8192, 18432, 7168) == 0
+    assert lib.bfp8_gemm_bf16_workspace_size(8192, 7168, 100) == 0
+    assert call(M=M, N=N, K=K, ws=ODD, wsb=need) == _lib.BFP8_ERR_ALIGN
+    assert call(M=M, N=N, K=K, ws=FAKE, wsb=need - 16) == _lib.BFP8_ERR_WORKSPACE
 
 
 def test_moe_dispatch_validation(lib):

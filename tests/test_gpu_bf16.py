@@ -92,3 +92,30 @@ def test_gemm_bf16_deterministic():
     c2 = bfp8.gemm_bf16(a.to(dev()), b.to(dev()))
     torch.cuda.synchronize()
     assert torch.equal(c1, c2)
+
+
+def test_gemm_bf16_split_last_round():
+    """With a workspace, a shape whose last round of 256 x 256 tiles is at most half full
+    runs it as two K halves (K = 10304 = 161 steps of 64, an odd count) into the workspace:
+    within tolerance of the oracle on sampled rows, independent of the workspace contents,
+    a short workspace refused."""
+    M, N, K = 2048, 8448, 10304
+    need = bfp8.bfp8_gemm_bf16_workspace_size(M, N, K)
+    assert need > 0
+    a, b = _bf16((M, K), 830), _bf16((N, K), 831, 0.05)
+    ad, bd = a.to(dev()), b.to(dev())
+    work = torch.full((need // 4,), float("nan"), dtype=torch.float32, device=dev())
+    announce(f"gemm_bf16 split last round M={M} N={N} K={K}, workspace {need} B")
+    raw, c1, pad = with_canary((M, N), torch.bfloat16)
+    bfp8.bfp8_gemm_bf16(ad, bd, c1, work)
+    work.fill_(1e30)
+    c2 = bfp8.gemm_bf16(ad, bd, workspace=work)
+    torch.cuda.synchronize()
+    assert canary_intact(raw, pad), "wrote outside the output"
+    assert torch.equal(c1, c2), "the result depends on the workspace contents"
+    rows = sample_rows(M, 8, 832)
+    ref = oracle.gemm_bf16(bits16(a), bits16(b), rows=rows)
+    worst = gemm_check(c1[torch.from_numpy(rows).to(dev())], ref, "bf16 split last round")
+    announce(f"gemm_bf16 split last round: worst err/bound {worst:.3f}")
+    with pytest.raises(bfp8.Bfp8Error):
+        bfp8.bfp8_gemm_bf16(ad, bd, torch.empty_like(c1), work[: need // 4 - 4])

@@ -48,7 +48,7 @@ def test_empty_problems_touch_nothing():
     assert lib.bfp8_weight_dequant(P(w), P(ws), P(y), 0, K, stream) == 0
     assert lib.bfp8_gemm(P(q), P(s), P(w), P(ws), P(y), 0, 256, K, None, 0, stream) == 0
     assert lib.bfp8_gemm(P(q), P(s), P(w), P(ws), P(y), 4, 0, K, None, 0, stream) == 0
-    assert lib.bfp8_gemm_bf16(P(x), P(x), P(y), 0, 4, K, stream) == 0
+    assert lib.bfp8_gemm_bf16(P(x), P(x), P(y), 0, 4, K, None, 0, stream) == 0
     work = torch.zeros(1 << 16, dtype=torch.uint8, device=dev())
     assert lib.bfp8_linear_fp8(P(x), P(w), P(ws), P(y), 0, 256, K, P(work), work.numel(), stream) == 0
     # grouped: two groups, neither holds a row
