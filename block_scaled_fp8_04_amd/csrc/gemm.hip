@@ -285,8 +285,11 @@ __device__ __forceinline__ void quant_epilogue(v4f (&acc)[T::TM][T::TN], const Q
 // Output: h = bf16( bf16( silu(g) ) * u ), the operations a bf16 model does
 // on bf16 g and u (silu(x) = x / (1 + e^-x), evaluated in fp32 and rounded
 // once); then act_quant of h's 128-column block exactly as quant_epilogue.
-// The u waves hand their values to the g waves through LDS (lane-major, no
-// bank conflicts); the two g waves of a row meet in LDS for the block max.
+// The two waves of a pair (g and u of the same columns) split the rows: each
+// hands the other, through LDS (lane-major, no bank conflicts), the values of
+// the rows the other finishes, so silu and the quantization run on all eight
+// waves (6% faster than the g waves alone on 4096 x 2048 x 7168, same bits);
+// the two pairs of a row meet in LDS for the block max.
 template <class T>
 __device__ __forceinline__ void swiglu_quant_epilogue(v4f (&acc)[T::TM][T::TN], const QuantOut& qo,
                                                       int64_t m0, int64_t m_end, int64_t n0,
@@ -294,75 +297,98 @@ __device__ __forceinline__ void swiglu_quant_epilogue(v4f (&acc)[T::TM][T::TN], 
                                                       int lane, const Stages<T>& st) {
     static_assert(T::WN == 64 && T::WAVES_N == 4 && T::BN == 256 && T::WAVES_M == 2,
                   "the gated epilogue runs on the 256 x 256 tile");
-    constexpr int PER_LANE = T::TM * T::TN * 4;
-    static_assert(2 * PER_LANE * 64 * 4 <= T::A_BYTES + T::B_BYTES, "u hand-off fits one stage");
     const int lr = lane & 15, g = lane >> 4;
     const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
     const bool is_up = (wn & 1) != 0;
+    constexpr int HALF = T::TM / 2;                       // sub-tile rows each wave of a pair finishes
+    constexpr int XFER = HALF * T::TN * 4;                // floats per lane handed to the partner
+    static_assert(2 * 2 * XFER * 64 * 4 <= T::A_BYTES + T::B_BYTES, "hand-offs fit one stage");
 #pragma unroll
     for (int i = 0; i < T::TM; ++i)
 #pragma unroll
         for (int j = 0; j < T::TN; ++j)
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[i][j][r] = bf16_round_f32(acc[i][j][r]);
-    // stage wm carries the u values of the two column groups of wave row wm
-    float* xu = (float*)(wm == 0 ? st.p[0] : st.p[1]) + (wn >> 1) * PER_LANE * 64;
-    float* part = (float*)(st.p[0] + T::A_BYTES + T::B_BYTES);     // [2 x 2 waves][WM] maxima
+    // The pair (g wave wn, u wave wn + 1) splits the rows: the g wave finishes sub-tile
+    // rows 0 .. HALF-1, the u wave rows HALF .. TM-1.  Each hands the partner the values of
+    // the rows the partner finishes: stage wm, column group wn >> 1 holds [g -> u | u -> g].
+    float* x_gu = (float*)(wm == 0 ? st.p[0] : st.p[1]) + (wn >> 1) * 2 * XFER * 64;
+    float* x_ug = x_gu + XFER * 64;
+    // per-row maxima of the four waves of wave row wm: [4][WM], in that stage's scale area
+    float* part = (float*)((wm == 0 ? st.p[0] : st.p[1]) + T::A_BYTES + T::B_BYTES);
     __syncthreads();                                               // every wave left the K loop
     if (is_up) {
 #pragma unroll
-        for (int i = 0; i < T::TM; ++i)
+        for (int i = 0; i < HALF; ++i)
 #pragma unroll
             for (int j = 0; j < T::TN; ++j)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) xu[((i * T::TN + j) * 4 + r) * 64 + lane] = acc[i][j][r];
+                for (int r = 0; r < 4; ++r) x_ug[((i * T::TN + j) * 4 + r) * 64 + lane] = acc[i][j][r];
+    } else {
+#pragma unroll
+        for (int i = 0; i < HALF; ++i)
+#pragma unroll
+            for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    x_gu[((i * T::TN + j) * 4 + r) * 64 + lane] = acc[HALF + i][j][r];
     }
     __syncthreads();
-    float pm[T::TM];
-    if (!is_up) {
+    // h = bf16(bf16(silu(g)) * u) for this wave's rows, kept in acc[HALF-offset rows]
+    float pm[HALF];
+    auto finish = [&](auto OFF_) __attribute__((always_inline)) {
+        constexpr int OFF = decltype(OFF_)::value;       // 0: g wave, HALF: u wave
 #pragma unroll
-        for (int i = 0; i < T::TM; ++i) {
+        for (int i = 0; i < HALF; ++i) {
             float m = 0.f;
 #pragma unroll
             for (int j = 0; j < T::TN; ++j)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float gv = acc[i][j][r];
-                    const float u = xu[((i * T::TN + j) * 4 + r) * 64 + lane];
+                    const int x = ((i * T::TN + j) * 4 + r) * 64 + lane;
+                    const float gv = OFF == 0 ? acc[i][j][r] : x_gu[x];
+                    const float u = OFF == 0 ? x_ug[x] : acc[OFF + i][j][r];
                     const float sg = bf16_round_f32(gv / (1.0f + expf(-gv)));
                     const float h = bf16_round_f32(sg * u);
-                    acc[i][j][r] = h;
+                    acc[OFF + i][j][r] = h;
                     m = fmaxf(m, fabsf(h));
                 }
             m = fmaxf(m, __shfl_xor(m, 16));
             m = fmaxf(m, __shfl_xor(m, 32));
             pm[i] = m;
-            if (g == 0) part[(wm * 2 + (wn >> 1)) * T::WM + 16 * i + lr] = m;
+            if (g == 0) part[wn * T::WM + 16 * (OFF + i) + lr] = m;
         }
-    }
+    };
+    if (is_up) finish(StageId<HALF>{});
+    else finish(StageId<0>{});
     __syncthreads();
-    if (is_up) return;
     const int64_t nout = N / 2;
     const int64_t nbq = nout / kBlock;
-    const int64_t h0 = n0 / 2 + (wn >> 1) * 64;                  // this wave's first h column
+    const int64_t h0 = n0 / 2 + (wn >> 1) * 64;                  // this pair's first h column
+    // a 128-column block of h is the pair's 64 columns and the other pair's (wave wn ^ 2)
+    auto encode = [&](auto OFF_) __attribute__((always_inline)) {
+        constexpr int OFF = decltype(OFF_)::value;
 #pragma unroll
-    for (int i = 0; i < T::TM; ++i) {
-        const float amax = fmaxf(pm[i], part[(wm * 2 + ((wn >> 1) ^ 1)) * T::WM + 16 * i + lr]);
-        const float s = fmaxf(amax, kAmaxFloor) / kE4m3Max;
-        const float rcp = 1.0f / s;
-        const int64_t row = m0 + wm0 + 16 * i + lr;
-        if (row < m_end) {
-            uint8_t* qrow = qo.q + row * nout + h0 + 4 * g;
+        for (int i = 0; i < HALF; ++i) {
+            const float amax = fmaxf(pm[i], part[(wn ^ 2) * T::WM + 16 * (OFF + i) + lr]);
+            const float s = fmaxf(amax, kAmaxFloor) / kE4m3Max;
+            const float rcp = 1.0f / s;
+            const int64_t row = m0 + wm0 + 16 * (OFF + i) + lr;
+            if (row < m_end) {
+                uint8_t* qrow = qo.q + row * nout + h0 + 4 * g;
 #pragma unroll
-            for (int j = 0; j < T::TN; ++j) {
-                const uint32_t codes = e4m3_encode4<true>(
-                    quotient(acc[i][j][0], s, rcp), quotient(acc[i][j][1], s, rcp),
-                    quotient(acc[i][j][2], s, rcp), quotient(acc[i][j][3], s, rcp));
-                *(uint32_t*)(qrow + 16 * j) = codes;
+                for (int j = 0; j < T::TN; ++j) {
+                    const uint32_t codes = e4m3_encode4<true>(
+                        quotient(acc[OFF + i][j][0], s, rcp), quotient(acc[OFF + i][j][1], s, rcp),
+                        quotient(acc[OFF + i][j][2], s, rcp), quotient(acc[OFF + i][j][3], s, rcp));
+                    *(uint32_t*)(qrow + 16 * j) = codes;
+                }
+                if (g == 0 && (wn >> 1) == 0) qo.qs[row * nbq + (n0 >> 8)] = s;
             }
-            if (g == 0 && wn == 0) qo.qs[row * nbq + (n0 >> 8)] = s;
         }
-    }
+    };
+    if (is_up) encode(StageId<HALF>{});
+    else encode(StageId<0>{});
 }
 
 // kHwScale: every activation and weight scale is a power of two (the e8m0
