@@ -119,3 +119,23 @@ def test_gemm_bf16_split_last_round():
     announce(f"gemm_bf16 split last round: worst err/bound {worst:.3f}")
     with pytest.raises(bfp8.Bfp8Error):
         bfp8.bfp8_gemm_bf16(ad, bd, torch.empty_like(c1), work[: need // 4 - 4])
+
+
+def test_gemm_bf16_split_last_round_random_shapes():
+    """Seeded large shapes whose last round of 256 x 256 tiles is whole tile columns and at
+    most half full (8 or 16 M-tiles, one or two tail columns, K from 80 to 96 blocks of 128
+    in steps of 64): with a workspace, within tolerance of the oracle on sampled rows."""
+    rng = np.random.default_rng(840)
+    for mt, rem_cols in ((8, 1), (16, 2)):
+        M, N = mt * 256, (256 // mt + rem_cols) * 256
+        K = int(rng.integers(160, 192)) * 64
+        need = bfp8.bfp8_gemm_bf16_workspace_size(M, N, K)
+        assert need > 0, (M, N, K)
+        a, b = _bf16((M, K), 841 + mt), _bf16((N, K), 842 + mt, 0.05)
+        work = torch.full((need // 4,), float("nan"), dtype=torch.float32, device=dev())
+        announce(f"gemm_bf16 random split last round M={M} N={N} K={K}")
+        c = bfp8.gemm_bf16(a.to(dev()), b.to(dev()), workspace=work)
+        torch.cuda.synchronize()
+        rows = sample_rows(M, 8, 843 + mt)
+        ref = oracle.gemm_bf16(bits16(a), bits16(b), rows=rows)
+        gemm_check(c[torch.from_numpy(rows).to(dev())], ref, f"bf16 random split [{M},{N},{K}]")

@@ -104,3 +104,27 @@ def test_gemm_ue8m0_split_last_round():
         announce(f"gemm_ue8m0 split last round {i}: worst err/bound {worst:.3f}")
         with pytest.raises(bfp8.Bfp8Error):
             bfp8.bfp8_gemm_ue8m0(q, s, wd, wsd, torch.empty_like(c1), work[: need // 4 - 4])
+
+
+def test_gemm_ue8m0_split_last_round_random_shapes():
+    """Seeded large shapes with a split last round (8 or 16 M-tiles, one or two tail columns,
+    K from 80 to 96 blocks): the e8m0 GEMM with a workspace within tolerance of the oracle
+    on sampled rows."""
+    rng = np.random.default_rng(1750)
+    for mt, rem_cols in ((8, 1), (16, 2)):
+        M, N = mt * 256, (256 // mt + rem_cols) * 256
+        K = int(rng.integers(80, 96)) * 128
+        need = bfp8.bfp8_gemm_ue8m0_workspace_size(M, N, K)
+        assert need > 0, (M, N, K)
+        g = torch.Generator().manual_seed(1751 + mt)
+        x = torch.randn(M, K, generator=g).to(torch.bfloat16).to(dev())
+        q, s = bfp8.act_quant_ue8m0(x)
+        w, ws = synth.weight(N, K, 1760 + mt, 1770 + mt, pow2=True)
+        wd, wsd = w.to(dev()), ws.to(dev())
+        work = torch.full((need // 4,), float("nan"), dtype=torch.float32, device=dev())
+        announce(f"gemm_ue8m0 random split last round M={M} N={N} K={K}")
+        c = bfp8.gemm_ue8m0(q, s, wd, wsd, workspace=work)
+        torch.cuda.synchronize()
+        rows = sample_rows(M, 8, 1780 + mt)
+        ref = oracle.gemm(u8(q), s.cpu().numpy(), u8(w), ws.numpy(), rows=rows)
+        gemm_check(c[torch.from_numpy(rows).to(dev())], ref, f"ue8m0 random split [{M},{N},{K}]")
