@@ -110,3 +110,50 @@ def test_moe_chain_graph_replays():
         torch.cuda.synchronize()
         announce(f"moe graph replay {r}")
         assert torch.equal(y, ref), f"replay {r} differs from the eager result"
+
+
+def test_split_last_round_graph_replays():
+    """The three GEMM forms with a split last round (main tiles, the two K halves of the
+    tail columns into the workspace, the ordered reduction) captured once; each replay equals
+    the eager result bit for bit, the workspace filled with NaN between replays."""
+    from block_scaled_fp8_04_amd import synth
+    M, N, K = 2048, 8448, 10368
+    g = torch.Generator().manual_seed(91)
+    x = torch.randn(M, K, generator=g).to(torch.bfloat16).to(dev())
+    q, qs = bfp8.act_quant(x)
+    qe, qes = bfp8.act_quant_ue8m0(x)
+    w, ws = synth.weight(N, K, 92, 93)
+    wp, wps = synth.weight(N, K, 94, 95, pow2=True)
+    w, ws, wp, wps = w.to(dev()), ws.to(dev()), wp.to(dev()), wps.to(dev())
+    wd = bfp8.weight_dequant(w, ws)
+    need = max(bfp8.bfp8_gemm_workspace_size(M, N, K), bfp8.bfp8_gemm_ue8m0_workspace_size(M, N, K),
+               bfp8.bfp8_gemm_bf16_workspace_size(M, N, K))
+    assert need > 0
+    work = torch.empty(need // 4, dtype=torch.float32, device=dev())
+    y1 = torch.empty(M, N, dtype=torch.bfloat16, device=dev())
+    y2 = torch.empty_like(y1)
+    y3 = torch.empty_like(y1)
+
+    def step():
+        bfp8.bfp8_gemm(q, qs, w, ws, y1, work)
+        bfp8.bfp8_gemm_ue8m0(qe, qes, wp, wps, y2, work)
+        bfp8.bfp8_gemm_bf16(x, wd, y3, work)
+
+    step()
+    torch.cuda.synchronize()
+    refs = [y1.clone(), y2.clone(), y3.clone()]
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        step()
+    for r in range(3):
+        for y in (y1, y2, y3):
+            y.zero_()
+        work.fill_(float("nan"))
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        announce(f"split last round graph replay {r}")
+        for name, y, ref in zip(("fp8", "e8m0", "bf16"), (y1, y2, y3), refs):
+            assert torch.equal(y, ref), f"replay {r}: the {name} GEMM differs from the eager result"
+        _ = (x.float() * 2).sum()
+        torch.cuda.synchronize()
