@@ -43,6 +43,7 @@
 //  * Rows past M and columns past N read a clamped, valid row; partial tiles
 //    run the same K loop as full ones and only their stores are guarded.
 #include <mutex>
+#include <type_traits>
 
 #include "device_codec.hpp"
 #include "internal.hpp"
@@ -162,6 +163,9 @@ struct BigTile {
 template <class T>
 struct Stages {
     uint8_t* p[4];
+    // The split schedule (below) keeps each stage's weight rows and scales in an
+    // array of their own, b[s]; p[s] then holds only the A rows.  Null otherwise.
+    uint8_t* b[4];
 };
 // The MFMA is issued with the weight fragment as its first operand and the
 // activation fragment as its second, so the 16 x 16 result is C^T: lane l
@@ -209,9 +213,10 @@ template <class T>
 __device__ __forceinline__ void quant_epilogue(v4f (&acc)[T::TM][T::TN], const QuantOut& qo,
                                                int64_t m0, int64_t m_end, int64_t n0, int64_t N,
                                                int wave, int wm0, int wn0, int lane,
-                                               uint8_t* lds_scratch, uint8_t* lds_codes) {
+                                               uint8_t* lds_scratch, uint8_t* cbuf) {
     static_assert(T::WN == 64, "a 128-column block spans two waves of 64 columns");
     static_assert(T::WAVES * T::WM * 64 <= T::STAGE, "the staged codes fit one stage");
+    static_assert(T::WAVES / 2 * T::WM * 64 <= T::A_BYTES, "half the staged codes fit the A rows");
     const int lr = lane & 15, g = lane >> 4;
     float pm[T::TM];
 #pragma unroll
@@ -239,7 +244,6 @@ __device__ __forceinline__ void quant_epilogue(v4f (&acc)[T::TM][T::TN], const Q
     const bool block_valid = n0 + wn0 < N;          // N % 128 == 0: the whole block or none
     const int64_t nbq = N / kBlock;
     const bool staged = ((uintptr_t)qo.q & 15u) == 0;
-    uint8_t* cbuf = lds_codes + wave * (T::WM * 64);
 #pragma unroll
     for (int i = 0; i < T::TM; ++i) {
         const float amax = fmaxf(pm[i], part[(wave ^ 1) * T::WM + 16 * i + lr]);
@@ -397,9 +401,10 @@ __device__ __forceinline__ void swiglu_quant_epilogue(v4f (&acc)[T::TM][T::TN], 
 // kStagedStore: interior bf16 tiles store through LDS (whole 128-byte row
 // pieces); the grouped kernel leaves it off, since the extra epilogue path
 // makes its heavy tile spill.
-template <class T, bool kGuard, int kEpi = kEpiBf16, bool kHwScale = false,
-          bool kStagedStore = true>
-__device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
+// kCls: 0 = every wave runs the same K loop; 1 and 2 = waves 0..3 and 4..7 of the
+// split schedule (gemm_tile_big below).
+template <class T, bool kGuard, int kEpi, bool kHwScale, bool kStagedStore, int kCls>
+__device__ __forceinline__ void gemm_tile_body(const uint8_t* __restrict__ a,
                                               const float* __restrict__ as,
                                               const uint8_t* __restrict__ b,
                                               const float* __restrict__ bs,
@@ -472,6 +477,64 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
         bs_off = (uint32_t)(nb * KB * 4);
     }
 
+    // Split schedule.  Class 1 (waves 0..3) loads the A rows of block kb + 1 into
+    // p[SF] after block kb's first sub-tile row; class 2 (waves 4..7) loads the weight
+    // rows and scales of block kb + 2 into b[S] once every wave has read block kb's
+    // (they are read into registers at the start of the block), after a second
+    // barrier.  So the weight rows get two blocks of lead with two stages, and each
+    // class is held by the vector-memory path for half a block's loads.  Offsets are
+    // the instruction's parity (the swizzle) with the eight-row steps in the scalar
+    // offset; rows past the tile read as zeros.
+    static_assert(kCls == 0 || (T::NSTAGE == 2 && T::WAVES == 8 && T::LOADERS == 4 && !kHwScale &&
+                                T::A_INSTR % 2 == 0 && T::B_INSTR % 2 == 0),
+                  "the split schedule runs on the two-stage eight-wave tile");
+    constexpr int kRowsBeforeSync = 5;                // class 2: sub-tile rows before barrier 2
+    constexpr int kLoadsB = T::B_INSTR + 2;           // class 2: loads per wave per block
+    const uint32_t K32 = (uint32_t)K;
+    uint32_t v_par[2];
+    v_par[0] = (uint32_t)lrow * K32 + (uint32_t)(((lane & 7) ^ lrow) << 4);
+    v_par[1] = (uint32_t)lrow * K32 + (uint32_t)(((lane & 7) ^ lrow ^ 1) << 4);
+    // class 2 wave cw's two scale loads: row-scale instruction 2 cw + h while there is
+    // one (S_INSTR of them), else the weight-scale line; wave 7 repeats instruction 4
+    // and the line, so every wave counts the same loads
+    const int cw = wave - 4;
+    uint32_t sc_off[2], sc_lds[2];
+    bool sc_row[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        int idx = 2 * cw + h;
+        if (idx == 6) idx = T::S_INSTR - 1;
+        sc_row[h] = idx < T::S_INSTR;
+        const int pq = (sc_row[h] ? idx : 0) * 64 + lane;
+        const int t = pq / T::SPITCH, i = pq % T::SPITCH;
+        int row = (t < 16 && i < T::BM / 16) ? 16 * i + t : 0;
+        row = row < rows_a ? row : (int)rows_a - 1;
+        sc_off[h] = sc_row[h] ? (uint32_t)(row * KB * 4) : bs_off;
+        sc_lds[h] = sc_row[h] ? (uint32_t)(T::B_BYTES + idx * 256) : (uint32_t)(T::B_BYTES + T::SB_OFF);
+    }
+    auto issue_a = [&](int64_t kb, uint8_t* base) __attribute__((always_inline)) {
+        const uint32_t ko = (uint32_t)(kb * kBlock);
+#pragma unroll
+        for (int i = 0; i < T::A_INSTR; ++i) {
+            const uint32_t r0 = (uint32_t)((wave * T::A_INSTR + i) * 8);
+            buf_lds16(rs_a, v_par[i & 1], ko + r0 * K32, base + (wave * T::A_INSTR + i) * 1024);
+        }
+    };
+    auto issue_b = [&](int64_t kb, uint8_t* base) __attribute__((always_inline)) {
+        const uint32_t ko = (uint32_t)(kb * kBlock);
+#pragma unroll
+        for (int i = 0; i < T::B_INSTR; ++i) {
+            const uint32_t r0 = (uint32_t)((cw * T::B_INSTR + i) * 8);
+            buf_lds16(rs_b, v_par[i & 1], ko + r0 * K32, base + (cw * T::B_INSTR + i) * 1024);
+        }
+        const uint32_t so = (uint32_t)(kb * 4);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            if (sc_row[h]) buf_lds4(rs_as, sc_off[h], so, base + sc_lds[h]);
+            else buf_lds4(rs_bs, sc_off[h], so, base + sc_lds[h]);
+        }
+    };
+
     auto issue = [&](int64_t kb, uint8_t* base) __attribute__((always_inline)) {
         const uint32_t ko = (uint32_t)(kb * kBlock);
         if (T::LOADERS == T::WAVES || wave < T::LOADERS) {
@@ -540,11 +603,21 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
     // while the other runs alone; raising waves 4..7 one priority level keeps
     // each pair even (2-6% faster on the eight-wave tiles, same bits; raising
     // waves 0..3 instead, or alternating by block, measured no better).
-    if (T::WAVES == 8 && wave >= 4) __builtin_amdgcn_s_setprio(1);
+    // In the split schedule class 1 runs one level up instead: it is the class whose
+    // multiplies end the block (measured 0.5-1% faster than raising class 2).
+    if (kCls != 0 ? kCls == 1 : (T::WAVES == 8 && wave >= 4)) __builtin_amdgcn_s_setprio(1);
 
-    // prologue: K blocks 0 .. NSTAGE-2 in flight, block s in stage s
-    issue(K0, st.p[0]);
-    if (T::NSTAGE > 2 && K0 + 1 < KE) issue(K0 + 1, st.p[1]);
+    // prologue: K blocks 0 .. NSTAGE-2 in flight, block s in stage s (split schedule:
+    // the A rows of block 0 and the weight rows of blocks 0 and 1)
+    if constexpr (kCls == 1) {
+        issue_a(K0, st.p[0]);
+    } else if constexpr (kCls == 2) {
+        issue_b(K0, st.b[0]);
+        issue_b(K0 + 1 < KE ? K0 + 1 : K0, st.b[1]);
+    } else {
+        issue(K0, st.p[0]);
+    }
+    if (kCls == 0 && T::NSTAGE > 2 && K0 + 1 < KE) issue(K0 + 1, st.p[1]);
     if (T::NSTAGE > 3 && K0 + 2 < KE) issue(K0 + 2, st.p[2]);
 
     const int lr = lane & 15;
@@ -563,17 +636,25 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
         // blocks kb+1 .. kb+NSTAGE-2 are outstanding (loads complete in issue
         // order); the barrier then makes every wave's loads visible and
         // guarantees stage SF (block kb - 1) is no longer being read
-        if (kb + T::NSTAGE - 2 < KE)
-            wait_vmcnt<T::LOADS_PER_STAGE * (T::NSTAGE - 2)>();
-        else
+        // (split schedule: class 1 waits for its A rows of block kb, class 2 for its
+        // weight rows of block kb while those of kb + 1 may still be in flight)
+        if constexpr (kCls == 2) {
+            wait_vmcnt<kLoadsB>();
+        } else if constexpr (kCls == 1) {
             wait_vmcnt<0>();
+        } else {
+            if (kb + T::NSTAGE - 2 < KE)
+                wait_vmcnt<T::LOADS_PER_STAGE * (T::NSTAGE - 2)>();
+            else
+                wait_vmcnt<0>();
+        }
         barrier_lds();
         const bool more = kb + T::NSTAGE - 1 < KE;
         // (the spread issue lives in the fold loop; the power-of-two-scale loop issues here)
-        if ((!kSpread || kHwScale) && more) issue(kb + T::NSTAGE - 1, st.p[SF]);
+        if (kCls == 0 && (!kSpread || kHwScale) && more) issue(kb + T::NSTAGE - 1, st.p[SF]);
 
         const uint8_t* As = st.p[S];
-        const uint8_t* Bs = As + T::A_BYTES;
+        const uint8_t* Bs = kCls != 0 ? st.b[S] : As + T::A_BYTES;
         const float* Ss = (const float*)(Bs + T::B_BYTES);
         const float* Sb = (const float*)(Bs + T::B_BYTES + T::SB_OFF);
         if constexpr (kHwScale) {
@@ -665,6 +746,17 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 1; i < T::TM; ++i) {
+                if constexpr (kCls != 0) {
+                    if (i == (kCls == 1 ? 1 : kRowsBeforeSync)) {
+                        if constexpr (kCls == 1) {
+                            if (more) issue_a(kb + 1, st.p[SF]);
+                        }
+                        // barrier 2: every wave has read block kb's weight rows and scales
+                        barrier_lds();
+                        // (past the last block the last one is loaded again, never read)
+                        if constexpr (kCls == 2) issue_b(kb + 2 < KE ? kb + 2 : KE - 1, st.b[S]);
+                    }
+                }
                 if (kSpread && more) {
                     constexpr int NQ = T::LOADS_PER_STAGE;
                     const int q0 = 2 * (i - 1);
@@ -703,9 +795,12 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
         }
     };
 
+    // (the split schedule needs an even block count: class 2 runs the second step
+    // unconditionally, which keeps the compiler's wait for its in-flight weight
+    // loads precise across the loop's back edge)
     for (int64_t kb0 = K0; kb0 < KE; kb0 += T::NSTAGE) {
         step(kb0, StageId<0>{});
-        if (kb0 + 1 < KE) step(kb0 + 1, StageId<1>{});
+        if (kCls == 2 || kb0 + 1 < KE) step(kb0 + 1, StageId<1>{});
         if constexpr (T::NSTAGE > 2) {
             if (kb0 + 2 < KE) step(kb0 + 2, StageId<2>{});
         }
@@ -714,6 +809,7 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
         }
     }
 
+    if constexpr (kCls != 0) wait_vmcnt<0>();      // class 2's reloads of the last block
     // the last block's last row (the fold loop carries it into the next block)
     if constexpr (!kHwScale) {
 #pragma unroll
@@ -721,7 +817,9 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
     }
     // epilogue: lane holds row m0 + wm0 + 16 i + lr, columns n0 + wn0 + 16 j + 4 (lane >> 4) + 0..3
     if constexpr (kEpi == kEpiQuant) {
-        quant_epilogue<T>(acc, qo, m0, m_end, n0, N, wave, wm0, wn0, lane, st.p[0], st.p[1]);
+        uint8_t* cbuf = kCls != 0 ? (wave < 4 ? st.p[1] : st.b[1]) + (wave & 3) * (T::WM * 64)
+                                  : st.p[1] + wave * (T::WM * 64);
+        quant_epilogue<T>(acc, qo, m0, m_end, n0, N, wave, wm0, wn0, lane, st.p[0], cbuf);
         return;
     }
     if constexpr (kEpi == kEpiSwiglu) {
@@ -757,7 +855,8 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
         // then stores whole 128-byte row pieces, 16 bytes per lane.
         if (interior && vec && (N % 8 == 0) && (((uintptr_t)c & 15u) == 0)) {
             __syncthreads();                      // every wave is past its last LDS read
-            uint8_t* buf = st.p[0] + wave * (kRP * 128);
+            uint8_t* buf = kCls != 0 ? (wave < 4 ? st.p[0] : st.b[0]) + (wave & 3) * (kRP * 128)
+                                     : st.p[0] + wave * (kRP * 128);
 #pragma unroll
             for (int h = 0; h < T::TM / kSub; ++h) {
 #pragma unroll
@@ -819,13 +918,53 @@ __device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
     }
 }
 
+// One large tile.  kSplit: the split schedule (gemm_tile_body), for the two-stage
+// eight-wave tile on whole tiles (rows m0 .. m0 + BM - 1 all valid) with an even
+// K-block count; the stages then hold the A rows in st.p[s] and the weight rows and
+// scales in st.b[s].  Against every wave issuing its share right after one barrier per
+// block (waves 0..3 all of it), the waves of each SIMD pair are held by the
+// vector-memory path half as long and the weight rows land a block earlier:
+// per-block cycles 2925 -> 2780, the raised waves' barrier wait 1473 -> 465
+// (8192 x 18432 x 7168, same bits).
+template <class T, bool kGuard, int kEpi = kEpiBf16, bool kHwScale = false,
+          bool kStagedStore = true, bool kSplit = false>
+__device__ __forceinline__ void gemm_tile_big(const uint8_t* __restrict__ a,
+                                              const float* __restrict__ as,
+                                              const uint8_t* __restrict__ b,
+                                              const float* __restrict__ bs,
+                                              uint16_t* __restrict__ c, int64_t m0, int64_t m_end,
+                                              int64_t n0, int64_t N, int64_t K,
+                                              const Stages<T>& st, QuantOut qo = QuantOut{},
+                                              PartialOut po = PartialOut{}) {
+    if constexpr (kSplit) {
+        static_assert(!kGuard, "the split schedule runs whole tiles");
+        if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < 4)
+            gemm_tile_body<T, false, kEpi, kHwScale, kStagedStore, 1>(a, as, b, bs, c, m0, m_end,
+                                                                      n0, N, K, st, qo, po);
+        else
+            gemm_tile_body<T, false, kEpi, kHwScale, kStagedStore, 2>(a, as, b, bs, c, m0, m_end,
+                                                                      n0, N, K, st, qo, po);
+    } else {
+        gemm_tile_body<T, kGuard, kEpi, kHwScale, kStagedStore, 0>(a, as, b, bs, c, m0, m_end, n0,
+                                                                   N, K, st, qo, po);
+    }
+}
+
 // The stage arrays of a large-tile kernel (unused ones are 16 bytes).
 #define BIG_TILE_STAGES(T, st)                                                            \
     __shared__ __attribute__((aligned(1024))) uint8_t st##_0[T::STAGE];                    \
     __shared__ __attribute__((aligned(1024))) uint8_t st##_1[T::STAGE];                    \
     __shared__ __attribute__((aligned(1024))) uint8_t st##_2[T::NSTAGE > 2 ? T::STAGE : 16]; \
     __shared__ __attribute__((aligned(1024))) uint8_t st##_3[T::NSTAGE > 3 ? T::STAGE : 16]; \
-    const Stages<T> st = {{st##_0, st##_1, st##_2, st##_3}}
+    const Stages<T> st = {{st##_0, st##_1, st##_2, st##_3}, {nullptr, nullptr, nullptr, nullptr}}
+
+// The split schedule's arrays: A rows, and weight rows with scales, per stage.
+#define BIG_TILE_SPLIT_STAGES(T, st)                                                      \
+    __shared__ __attribute__((aligned(1024))) uint8_t st##_a0[T::A_BYTES];                 \
+    __shared__ __attribute__((aligned(1024))) uint8_t st##_b0[T::B_BYTES + T::S_BYTES];    \
+    __shared__ __attribute__((aligned(1024))) uint8_t st##_a1[T::A_BYTES];                 \
+    __shared__ __attribute__((aligned(1024))) uint8_t st##_b1[T::B_BYTES + T::S_BYTES];    \
+    const Stages<T> st = {{st##_a0, st##_a1, nullptr, nullptr}, {st##_b0, st##_b1, nullptr, nullptr}}
 
 // Maps a workgroup id to a tile so that the workgroups resident on one XCD
 // (ids are dealt round-robin over the 8 XCDs) work on a compact block of
@@ -844,7 +983,9 @@ __device__ __forceinline__ void tile_of(int id, int nwg, int mt, int nt, int& tm
     tn = in_band / rows_in_band;
 }
 
-template <class T>
+// kSplit: the split schedule; the host launches it only for whole M tiles and an even
+// K-block count.
+template <class T, bool kSplit = false>
 __global__ __launch_bounds__(T::THREADS, T::OCC) void gemm_big_kernel(const uint8_t* __restrict__ a,
                                                                  const float* __restrict__ as,
                                                                  const uint8_t* __restrict__ b,
@@ -852,14 +993,20 @@ __global__ __launch_bounds__(T::THREADS, T::OCC) void gemm_big_kernel(const uint
                                                                  uint16_t* __restrict__ c,
                                                                  int64_t M, int64_t N, int64_t K,
                                                                  int mt, int nt) {
-    BIG_TILE_STAGES(T, lds);
     int tm, tn;
     tile_of(blockIdx.x, gridDim.x, mt, nt, tm, tn);
     const int64_t m0 = (int64_t)tm * T::BM;
-    if (m0 + T::BM <= M)
-        gemm_tile_big<T, false>(a, as, b, bs, c, m0, M, (int64_t)tn * T::BN, N, K, lds);
-    else
-        gemm_tile_big<T, true>(a, as, b, bs, c, m0, M, (int64_t)tn * T::BN, N, K, lds);
+    if constexpr (kSplit) {
+        BIG_TILE_SPLIT_STAGES(T, lds);
+        gemm_tile_big<T, false, kEpiBf16, false, true, true>(a, as, b, bs, c, m0, M,
+                                                            (int64_t)tn * T::BN, N, K, lds);
+    } else {
+        BIG_TILE_STAGES(T, lds);
+        if (m0 + T::BM <= M)
+            gemm_tile_big<T, false>(a, as, b, bs, c, m0, M, (int64_t)tn * T::BN, N, K, lds);
+        else
+            gemm_tile_big<T, true>(a, as, b, bs, c, m0, M, (int64_t)tn * T::BN, N, K, lds);
+    }
 }
 
 // The last, partly filled round of a large GEMM ("tail"): columns
@@ -909,20 +1056,27 @@ __global__ __launch_bounds__(T::THREADS, T::OCC) void gemm_ue8m0_kernel(
 // The same GEMM with act_quant of its output (kEpi = kEpiQuant), or of the
 // gated activation of an interleaved [w1; w3] product (kEpiSwiglu), fused
 // into the epilogue.
-template <class T, int kEpi>
+template <class T, int kEpi, bool kSplit = false>
 __global__ __launch_bounds__(T::THREADS, T::OCC) void gemm_quant_kernel(
     const uint8_t* __restrict__ a, const float* __restrict__ as, const uint8_t* __restrict__ b,
     const float* __restrict__ bs, uint8_t* __restrict__ q, float* __restrict__ qs, int64_t M,
     int64_t N, int64_t K, int mt, int nt) {
-    BIG_TILE_STAGES(T, lds);
     int tm, tn;
     tile_of(blockIdx.x, gridDim.x, mt, nt, tm, tn);
     const int64_t m0 = (int64_t)tm * T::BM;
     const QuantOut qo{q, qs};
-    if (m0 + T::BM <= M)
-        gemm_tile_big<T, false, kEpi>(a, as, b, bs, nullptr, m0, M, (int64_t)tn * T::BN, N, K, lds, qo);
-    else
-        gemm_tile_big<T, true, kEpi>(a, as, b, bs, nullptr, m0, M, (int64_t)tn * T::BN, N, K, lds, qo);
+    if constexpr (kSplit) {
+        static_assert(kEpi == kEpiQuant, "the split schedule serves the act_quant epilogue");
+        BIG_TILE_SPLIT_STAGES(T, lds);
+        gemm_tile_big<T, false, kEpi, false, true, true>(a, as, b, bs, nullptr, m0, M,
+                                                        (int64_t)tn * T::BN, N, K, lds, qo);
+    } else {
+        BIG_TILE_STAGES(T, lds);
+        if (m0 + T::BM <= M)
+            gemm_tile_big<T, false, kEpi>(a, as, b, bs, nullptr, m0, M, (int64_t)tn * T::BN, N, K, lds, qo);
+        else
+            gemm_tile_big<T, true, kEpi>(a, as, b, bs, nullptr, m0, M, (int64_t)tn * T::BN, N, K, lds, qo);
+    }
 }
 
 // Split-K kernel for skinny problems (those split_plan splits).  A workgroup owns a 64 x 64
@@ -1146,12 +1300,25 @@ using BigSquare = BigTile<256, 256, 2, 4, 2>;   // 8 waves of 128 x 64, 2 stages
 using BigWide = BigTile<256, 128, 4, 2, 3>;     // 8 waves of 64 x 64, 3 stages
 using BigMid = BigTile<128, 128, 2, 2, 2>;      // 4 waves of 64 x 64, 2 stages, 2 per CU
 
+// The split schedule serves the 256 x 256 tile when every M tile is whole and the K-block
+// count is even (its two steps per loop turn run unconditionally).
+template <class T>
+constexpr bool kSplitTile = std::is_same<T, BigSquare>::value;
+template <class T>
+static bool use_split(int64_t M, int64_t K) {
+    return kSplitTile<T> && M % T::BM == 0 && (K / kBlock) % 2 == 0;
+}
+
 template <class T>
 static void launch_big(const void* a, const float* as, const void* b, const float* bs, void* c,
                        int64_t M, int64_t N, int64_t K, hipStream_t stream) {
     const int mt = (int)((M + T::BM - 1) / T::BM), nt = (int)((N + T::BN - 1) / T::BN);
-    hipLaunchKernelGGL(gemm_big_kernel<T>, dim3(mt * nt), dim3(T::THREADS), 0, stream,
-                       (const uint8_t*)a, as, (const uint8_t*)b, bs, (uint16_t*)c, M, N, K, mt, nt);
+    if (use_split<T>(M, K))
+        hipLaunchKernelGGL((gemm_big_kernel<T, kSplitTile<T>>), dim3(mt * nt), dim3(T::THREADS), 0, stream,
+                           (const uint8_t*)a, as, (const uint8_t*)b, bs, (uint16_t*)c, M, N, K, mt, nt);
+    else
+        hipLaunchKernelGGL((gemm_big_kernel<T, false>), dim3(mt * nt), dim3(T::THREADS), 0, stream,
+                           (const uint8_t*)a, as, (const uint8_t*)b, bs, (uint16_t*)c, M, N, K, mt, nt);
 }
 
 template <class T, int kEpi = kEpiQuant>
@@ -1159,9 +1326,14 @@ static hipError_t launch_quant(const void* a, const float* as, const void* b, co
                                void* q, float* qs, int64_t M, int64_t N, int64_t K,
                                hipStream_t stream) {
     const int mt = (int)((M + T::BM - 1) / T::BM), nt = (int)((N + T::BN - 1) / T::BN);
-    hipLaunchKernelGGL((gemm_quant_kernel<T, kEpi>), dim3(mt * nt), dim3(T::THREADS), 0, stream,
-                       (const uint8_t*)a, as, (const uint8_t*)b, bs, (uint8_t*)q, qs, M, N, K, mt,
-                       nt);
+    if (kEpi == kEpiQuant && use_split<T>(M, K))
+        hipLaunchKernelGGL((gemm_quant_kernel<T, kEpi, kEpi == kEpiQuant && kSplitTile<T>>), dim3(mt * nt),
+                           dim3(T::THREADS), 0, stream, (const uint8_t*)a, as, (const uint8_t*)b,
+                           bs, (uint8_t*)q, qs, M, N, K, mt, nt);
+    else
+        hipLaunchKernelGGL((gemm_quant_kernel<T, kEpi, false>), dim3(mt * nt), dim3(T::THREADS),
+                           0, stream, (const uint8_t*)a, as, (const uint8_t*)b, bs, (uint8_t*)q,
+                           qs, M, N, K, mt, nt);
     return hipGetLastError();
 }
 
@@ -1214,8 +1386,12 @@ static hipError_t launch_split_last_round(const void* a, const float* as, const 
         hipLaunchKernelGGL(gemm_ue8m0_kernel<BigSquare>, dim3(mt * tp.nt_main),
                            dim3(BigSquare::THREADS), 0, stream, (const uint8_t*)a, as,
                            (const uint8_t*)b, bs, (uint16_t*)c, M, N, K, mt, tp.nt_main);
+    else if (use_split<BigSquare>(M, K))
+        hipLaunchKernelGGL((gemm_big_kernel<BigSquare, true>), dim3(mt * tp.nt_main),
+                           dim3(BigSquare::THREADS), 0, stream, (const uint8_t*)a, as,
+                           (const uint8_t*)b, bs, (uint16_t*)c, M, N, K, mt, tp.nt_main);
     else
-        hipLaunchKernelGGL(gemm_big_kernel<BigSquare>, dim3(mt * tp.nt_main),
+        hipLaunchKernelGGL((gemm_big_kernel<BigSquare, false>), dim3(mt * tp.nt_main),
                            dim3(BigSquare::THREADS), 0, stream, (const uint8_t*)a, as,
                            (const uint8_t*)b, bs, (uint16_t*)c, M, N, K, mt, tp.nt_main);
     hipError_t e = hipGetLastError();
