@@ -1016,12 +1016,11 @@ __global__ __launch_bounds__(T::THREADS, T::OCC) void gemm_big_kernel(const uint
 // them in split order.  Workgroup id = s * tiles + tile, the tiles of one
 // split laid out over the XCDs as in gemm_big_kernel.  kHw: the power-of-two
 // scale GEMM (scales applied by the MFMA).
-template <class T, bool kHw = false>
+template <class T, bool kHw = false, bool kSplit = false>
 __global__ __launch_bounds__(T::THREADS, 1) void gemm_tail_kernel(
     const uint8_t* __restrict__ a, const float* __restrict__ as, const uint8_t* __restrict__ b,
     const float* __restrict__ bs, float* __restrict__ ws, int64_t M, int64_t N, int64_t K, int mt,
     int nt_tail, int64_t n1, int64_t kb_per) {
-    BIG_TILE_STAGES(T, lds);
     const int tiles = mt * nt_tail;
     const int split = blockIdx.x / tiles;
     int tm, tn;
@@ -1033,8 +1032,17 @@ __global__ __launch_bounds__(T::THREADS, 1) void gemm_tail_kernel(
     po.ldw = N - n1;
     po.ws = ws + (int64_t)split * M * po.ldw;
     po.n_base = n1;
-    gemm_tile_big<T, false, kEpiF32, kHw>(a, as, b, bs, nullptr, (int64_t)tm * T::BM, M,
-                                          n1 + (int64_t)tn * T::BN, N, K, lds, QuantOut{}, po);
+    if constexpr (kSplit) {
+        // (the host launches this form when both K runs hold an even block count)
+        BIG_TILE_SPLIT_STAGES(T, lds);
+        gemm_tile_big<T, false, kEpiF32, false, true, true>(a, as, b, bs, nullptr, (int64_t)tm * T::BM,
+                                                           M, n1 + (int64_t)tn * T::BN, N, K, lds,
+                                                           QuantOut{}, po);
+    } else {
+        BIG_TILE_STAGES(T, lds);
+        gemm_tile_big<T, false, kEpiF32, kHw>(a, as, b, bs, nullptr, (int64_t)tm * T::BM, M,
+                                              n1 + (int64_t)tn * T::BN, N, K, lds, QuantOut{}, po);
+    }
 }
 
 // The GEMM with power-of-two scales applied by the MFMA (kHwScale).
@@ -1396,10 +1404,17 @@ static hipError_t launch_split_last_round(const void* a, const float* as, const 
                            (const uint8_t*)b, bs, (uint16_t*)c, M, N, K, mt, tp.nt_main);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gemm_tail_kernel<BigSquare, kHw>), dim3(mt * tp.nt_tail * tp.splits),
-                       dim3(BigSquare::THREADS), 0, stream, (const uint8_t*)a, as,
-                       (const uint8_t*)b, bs, (float*)workspace, M, N, K, mt, tp.nt_tail, n1,
-                       tp.kb_per);
+    // the split load schedule when both K runs (kb_per blocks and the rest) are even
+    if (!kHw && tp.kb_per % 2 == 0 && (K / kBlock - tp.kb_per) % 2 == 0)
+        hipLaunchKernelGGL((gemm_tail_kernel<BigSquare, false, true>),
+                           dim3(mt * tp.nt_tail * tp.splits), dim3(BigSquare::THREADS), 0, stream,
+                           (const uint8_t*)a, as, (const uint8_t*)b, bs, (float*)workspace, M, N,
+                           K, mt, tp.nt_tail, n1, tp.kb_per);
+    else
+        hipLaunchKernelGGL((gemm_tail_kernel<BigSquare, kHw, false>),
+                           dim3(mt * tp.nt_tail * tp.splits), dim3(BigSquare::THREADS), 0, stream,
+                           (const uint8_t*)a, as, (const uint8_t*)b, bs, (float*)workspace, M, N,
+                           K, mt, tp.nt_tail, n1, tp.kb_per);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_tail_reduce((const float*)workspace, c, M, N, n1, tp.splits, stream);
