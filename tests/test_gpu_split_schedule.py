@@ -85,3 +85,27 @@ def test_split_schedule_with_split_last_round():
     ref = oracle.gemm(u8(q[:M]), s[:M].cpu().numpy(), u8(w), w_s.cpu().numpy(), rows=rows)
     worst = gemm_check(c_split[torch.from_numpy(rows).to(dev())], ref, "split last round")
     announce(f"split schedule + split last round: oracle worst err/bound {worst:.3f}")
+
+
+def test_split_schedule_random_shapes():
+    # seeded shapes that take the split schedule: whole M tiles, an even K-block count and
+    # enough 256 x 256 tiles for that tile; N anywhere (partial last columns included)
+    rng = np.random.default_rng(2027)
+    done = 0
+    while done < 6:
+        M = 256 * int(rng.integers(4, 33))
+        N = 8 * int(rng.integers(128, 1537))
+        K = 128 * 2 * int(rng.integers(4, 41))
+        if not bfp8.bfp8_gemm_kernel_name(M, N, K).startswith("lds-direct 256x256"):
+            continue
+        done += 1
+        q, s, w, w_s = _operands(M + 1, N, K, seed=300 + done)
+        announce(f"split schedule random [{M},{N},{K}]")
+        c_split = bfp8.gemm(q[:M], s[:M], w, w_s)
+        c_other = bfp8.gemm(q, s, w, w_s)
+        torch.cuda.synchronize()
+        diff = int((bits16(c_split) != bits16(c_other[:M])).sum())
+        assert diff == 0, f"[{M},{N},{K}]: {diff} outputs differ between the two schedules"
+        rows = sample_rows(M, 4, 400 + done)
+        ref = oracle.gemm(u8(q[:M]), s[:M].cpu().numpy(), u8(w), w_s.cpu().numpy(), rows=rows)
+        gemm_check(c_split[torch.from_numpy(rows).to(dev())], ref, f"random [{M},{N},{K}]")
