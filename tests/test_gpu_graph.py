@@ -157,3 +157,48 @@ def test_split_last_round_graph_replays():
             assert torch.equal(y, ref), f"replay {r}: the {name} GEMM differs from the eager result"
         _ = (x.float() * 2).sum()
         torch.cuda.synchronize()
+
+
+def test_split_schedule_graph_replays():
+    """The 256 x 256 tile's split load schedule (whole M tiles, even K-block count) captured
+    once: the bf16 GEMM, the GEMM with act_quant fused, and a GEMM whose split last round
+    runs the schedule on both launches of tiles; every replay equals the eager result."""
+    from block_scaled_fp8_04_amd import synth
+    g = torch.Generator().manual_seed(97)
+    M, N, K = 2048, 5120, 7168
+    M2, N2, K2 = 2048, 10240, 10240
+    x = torch.randn(M2, max(K, K2), generator=g).to(torch.bfloat16).to(dev())
+    q, qs = bfp8.act_quant(x[:, :K].contiguous())
+    q2, qs2 = bfp8.act_quant(x[:, :K2].contiguous())
+    w, ws = (t.to(dev()) for t in synth.weight(N, K, 98, 99))
+    w2, ws2 = (t.to(dev()) for t in synth.weight(N2, K2, 100, 101))
+    need = bfp8.bfp8_gemm_workspace_size(M2, N2, K2)
+    assert need > 0
+    work = torch.empty(need // 4, dtype=torch.float32, device=dev())
+    y1 = torch.empty(M, N, dtype=torch.bfloat16, device=dev())
+    y2 = torch.empty(M2, N2, dtype=torch.bfloat16, device=dev())
+    yq = torch.empty(M, N, dtype=torch.uint8, device=dev())
+    yqs = torch.empty(M, N // 128, dtype=torch.float32, device=dev())
+
+    def step():
+        bfp8.bfp8_gemm(q[:M], qs[:M], w, ws, y1, None)
+        bfp8.bfp8_gemm_act_quant(q[:M], qs[:M], w, ws, yq, yqs)
+        bfp8.bfp8_gemm(q2, qs2, w2, ws2, y2, work)
+
+    step()
+    torch.cuda.synchronize()
+    refs = [y1.clone(), y2.clone(), yq.clone(), yqs.clone()]
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        step()
+    for r in range(3):
+        y1.zero_(); y2.zero_(); yq.zero_(); yqs.zero_()
+        work.fill_(float("nan"))
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        announce(f"split schedule graph replay {r}")
+        for name, t, ref in zip(("bf16", "split last round", "codes", "scales"), (y1, y2, yq, yqs), refs):
+            assert torch.equal(t, ref), f"replay {r}: {name} differ from the eager result"
+        _ = (x.float() * 2).sum()
+        torch.cuda.synchronize()
